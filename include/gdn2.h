@@ -1,0 +1,154 @@
+/*
+ * gdn2.h -- C ABI of the MI355X (gfx950) Gated DeltaNet-2 chunked prefill
+ * forward.
+ *
+ * The operation (FlashInfer chunk_gated_delta_rule2 documentation, recurrence
+ * display equation): for every packed sequence and every value head, with a
+ * K x V float32 state S,
+ *
+ *     S_t    = diag(exp(g_t)) S_{t-1}
+ *     vnew_t = w_t * v_t - (beta_t * k_t)^T S_t
+ *     S_t   += k_t vnew_t^T
+ *     o_t    = scale * q_t^T S_t
+ *
+ * evaluated in 64-token chunks through the WY form (the chunked evaluation
+ * the burn-gdn2 README "Fused CUDA kernels" section and the FlashRT card's
+ * 64-token WY chain describe), returning the output and the final state.
+ *
+ * All entry points are plain C: no exceptions cross the boundary, no C++ or
+ * framework types appear in the signatures.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN2_ABI_VERSION 1
+
+/* Element types a tensor descriptor may carry. */
+typedef enum gdn2_dtype {
+    GDN2_DTYPE_BF16 = 1, /* bfloat16 */
+    GDN2_DTYPE_F32 = 2,  /* IEEE float32 */
+    GDN2_DTYPE_I32 = 3   /* int32 */
+} gdn2_dtype;
+
+/*
+ * A view of caller-owned memory: `ndim` dimensions of `shape`, element
+ * strides in `stride` (row-major contiguous tensors have
+ * stride[d] = prod(shape[d+1..ndim-1])). `data` is a DEVICE pointer; it may
+ * be NULL only when the tensor has zero elements.
+ */
+typedef struct gdn2_tensor {
+    void *data;
+    int32_t dtype; /* gdn2_dtype */
+    int32_t ndim;
+    int64_t shape[4];
+    int64_t stride[4];
+} gdn2_tensor;
+
+/* Status codes. 0 is success; every failure is negative. */
+enum {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL_ARG = -1,    /* a required descriptor or pointer is NULL */
+    GDN2_ERR_DTYPE = -2,       /* a tensor has the wrong element type */
+    GDN2_ERR_SHAPE = -3,       /* ranks or extents disagree */
+    GDN2_ERR_HEADS = -4,       /* HV is not a positive multiple of H */
+    GDN2_ERR_UNSUPPORTED = -5, /* (K, V) not in {(64,64), (128,128)} */
+    GDN2_ERR_LAYOUT = -6,      /* a tensor is not row-major contiguous */
+    GDN2_ERR_ALIAS = -7,       /* an output overlaps an input */
+    GDN2_ERR_HIP = -8          /* the HIP runtime reported an error */
+};
+
+/*
+ * gdn2_chunk_fwd -- enqueue the GDN-2 chunked prefill forward on `stream`.
+ *
+ * Tensors (T = total packed tokens, N = number of sequences, H = q/k heads,
+ * HV = value heads, K = key dim, V = value dim), all row-major contiguous:
+ *   q, k           [T, H, K]       bf16
+ *   v, w           [T, HV, V]      bf16
+ *   g              [T, HV, K]      float32, natural-log decay, each value <= 0
+ *                                  and finite (precondition, not checked)
+ *   beta           [T, HV, K]      bf16 (erase gate, taken as given, e.g. in
+ *                                  [0, 1] or [0, 2]; not clamped)
+ *   initial_state  [N, HV, K, V]   float32, K-major (V innermost)
+ *   cu_seqlens     [N + 1]         int32, device memory; cu[0] = 0,
+ *                                  non-decreasing, cu[N] = T (precondition,
+ *                                  not checked on the device)
+ *   out            [T, HV, V]      bf16, written for every token
+ *   final_state    [N, HV, K, V]   float32
+ *
+ * Value head hv reads q/k head hv / (HV / H) (contiguous groups of value
+ * heads share one q/k head).
+ *
+ * Optional arguments (the FlashInfer parameter-list defaults): g NULL means
+ * g = 0, beta NULL means beta = 1, w NULL means w = 1, initial_state NULL
+ * means a zero state, final_state NULL means the final state is not written,
+ * cu_seqlens NULL means one sequence of T tokens (N = 1). scale == 0 means
+ * 1/sqrt(K). A descriptor whose `data` is NULL but which has elements is an
+ * error (NULL_ARG) for every tensor; an optional tensor is omitted by passing
+ * a NULL descriptor pointer.
+ *
+ * Supported: (K, V) = (64, 64) or (128, 128); any T >= 0, N >= 1, H >= 1,
+ * HV a multiple of H. Empty sequences are allowed (their final state equals
+ * their initial state).
+ *
+ * Ownership: the caller owns every buffer. Inputs and initial_state are only
+ * read; out and final_state must be preallocated and are fully written. The
+ * library keeps no pointer after the call returns and allocates no device
+ * memory.
+ *
+ * Layout: every tensor is row-major contiguous with a 16-byte aligned data
+ * pointer (GDN2_ERR_LAYOUT otherwise).
+ *
+ * Aliasing: neither output (out, final_state) may overlap any input or the
+ * other output; in particular final_state may not alias initial_state
+ * (FlashInfer docs, output_state: the incoming state is read while outgoing
+ * states are written): GDN2_ERR_ALIAS.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; on failure nothing is enqueued, the return value says why and
+ * gdn2_last_error() holds a message. Faults inside the kernel (e.g. a
+ * cu_seqlens that breaks its precondition) surface at the caller's next
+ * synchronisation with the stream.
+ *
+ * Semantics: asynchronous (returns after enqueueing, does not synchronise);
+ * deterministic (no atomics; the same inputs give the same bits); reentrant.
+ */
+int gdn2_chunk_fwd(const gdn2_tensor *q, const gdn2_tensor *k,
+                   const gdn2_tensor *v, const gdn2_tensor *g,
+                   const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                   const gdn2_tensor *initial_state,
+                   const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
+                   const gdn2_tensor *final_state, hipStream_t stream);
+
+/*
+ * gdn2_chunk_fwd_check -- the host-side argument validation of
+ * gdn2_chunk_fwd alone: same arguments (no stream), same return codes, same
+ * gdn2_last_error() message. Touches no device memory and makes no HIP call,
+ * so it can run on a machine without a GPU.
+ */
+int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
+                         const gdn2_tensor *v, const gdn2_tensor *g,
+                         const gdn2_tensor *beta, const gdn2_tensor *w,
+                         float scale, const gdn2_tensor *initial_state,
+                         const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
+                         const gdn2_tensor *final_state);
+
+/* Message describing the last failure on the calling thread ("" if none).
+ * The string stays valid until the next call on the same thread. */
+const char *gdn2_last_error(void);
+
+/* GDN2_ABI_VERSION of the built library. */
+int gdn2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

@@ -1,0 +1,47 @@
+"""Build ``libgdn2.so`` (C ABI + gfx950 kernels) in-tree with hipcc.
+
+The library is written for CDNA4 only: one offload target, gfx950. Packed
+FP32 VALU instructions are disabled for every HIP source.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libgdn2.so")
+SOURCES = [os.path.join(HERE, "csrc", "gdn2_api.cpp"), os.path.join(HERE, "csrc", "gdn2_fwd.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every source and link libgdn2.so; returns its path."""
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(HERE, "csrc", os.path.basename(src) + ".o")
+        cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [HIPCC, "-x", "hip"] + FLAGS + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True, stderr=subprocess.PIPE if not verbose else None)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

@@ -1,0 +1,133 @@
+"""Thin ctypes binding of ``libgdn2.so`` (see ``include/gdn2.h``).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the library's gfx950 kernels.
+There is no CPU fallback: if the library is missing, or a tensor is not on a
+GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn2.so")
+
+GDN2_DTYPE_BF16, GDN2_DTYPE_F32, GDN2_DTYPE_I32 = 1, 2, 3
+_DTYPES = {torch.bfloat16: GDN2_DTYPE_BF16, torch.float32: GDN2_DTYPE_F32, torch.int32: GDN2_DTYPE_I32}
+
+STATUS = {0: "OK", -1: "NULL_ARG", -2: "DTYPE", -3: "SHAPE", -4: "HEADS",
+          -5: "UNSUPPORTED", -6: "LAYOUT", -7: "ALIAS", -8: "HIP"}
+
+EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_check", "gdn2_last_error", "gdn2_abi_version"]
+
+
+class Gdn2Tensor(ctypes.Structure):
+    """Mirror of ``gdn2_tensor``."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"gdn2 error {code} ({STATUS.get(code, '?')}): {message}")
+        self.code = code
+        self.status = STATUS.get(code, "?")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libgdn2.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Gdn2Tensor)
+        lib.gdn2_chunk_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
+        lib.gdn2_chunk_fwd.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
+        lib.gdn2_chunk_fwd_check.restype = ctypes.c_int
+        lib.gdn2_last_error.argtypes = []
+        lib.gdn2_last_error.restype = ctypes.c_char_p
+        lib.gdn2_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load_library().gdn2_last_error().decode()
+
+
+def describe(t):
+    """Build a gdn2_tensor descriptor for a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    d = Gdn2Tensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPES.get(t.dtype, 0)
+    d.ndim = t.dim()
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def _scale_arg(scale):
+    return 0.0 if scale is None else float(scale)
+
+
+def check(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
+          cu_seqlens=None, out=None, final_state=None):
+    """Run the library's host-side validation only (no GPU needed).
+
+    Returns the status code (0 = valid); never touches device memory."""
+    lib = load_library()
+    ds = [describe(x) for x in (q, k, v, g, beta, w)]
+    rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
+    return lib.gdn2_chunk_fwd_check(*[_ptr(d) for d in ds], _scale_arg(scale),
+                                    *[_ptr(d) for d in rest])
+
+
+def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
+              cu_seqlens=None, output_final_state=True, out=None, final_state=None):
+    """GDN-2 chunked prefill forward on the current HIP stream.
+
+    q, k [T, H, K] bf16; v, w [T, HV, V] bf16; g [T, HV, K] float32;
+    beta [T, HV, K] bf16; initial_state [N, HV, K, V] float32;
+    cu_seqlens [N + 1] int32 (None: one sequence). ``scale`` None or 0 means
+    1/sqrt(K). Returns (out [T, HV, V] bf16, final_state or None).
+    Preallocated ``out`` / ``final_state`` are written in place.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w),
+                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    T, HV, V = v.shape
+    K = q.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
+    descs = [describe(x) for x in (q, k, v, g, beta, w)]
+    rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
+    stream = torch.cuda.current_stream(v.device).cuda_stream
+    rc = lib.gdn2_chunk_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
+                            *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
+    if rc != 0:
+        raise Gdn2Error(rc, last_error())
+    return out, final_state

@@ -1,0 +1,135 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the public
+header declares, and its host-side validation rejects each malformed call
+with the documented status. No GPU is touched: ``gdn2_chunk_fwd_check``
+runs the validation alone and descriptors may point at host memory.
+"""
+
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+
+@pytest.fixture(scope="module")
+def gdn2():
+    from linear_attention_rnn_gdn2_amd import gdn2 as mod
+    if not os.path.exists(mod.LIB_PATH):
+        from linear_attention_rnn_gdn2_amd._build import build_library
+        build_library()
+    mod.load_library()
+    return mod
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(gdn2):
+    import ctypes
+    lib = ctypes.CDLL(gdn2.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == set(gdn2.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_abi_version_matches_header(gdn2):
+    m = re.search(r"#define GDN2_ABI_VERSION (\d+)", open(HEADER).read())
+    assert gdn2.load_library().gdn2_abi_version() == int(m.group(1))
+
+
+def test_status_codes_match_header(gdn2):
+    src = open(HEADER).read()
+    codes = dict((int(v), k) for k, v in re.findall(r"GDN2_(?:ERR_)?(\w+) = (-?\d+)", src)
+                 if k not in ("DTYPE_BF16", "DTYPE_F32", "DTYPE_I32", "ABI_VERSION"))
+    assert codes == gdn2.STATUS
+
+
+def case(T=70, H=2, HV=4, K=64, V=64, N=2):
+    t = dict(q=torch.zeros(T, H, K, dtype=torch.bfloat16), k=torch.zeros(T, H, K, dtype=torch.bfloat16),
+             v=torch.zeros(T, HV, V, dtype=torch.bfloat16), g=torch.zeros(T, HV, K),
+             beta=torch.zeros(T, HV, K, dtype=torch.bfloat16), w=torch.zeros(T, HV, V, dtype=torch.bfloat16),
+             initial_state=torch.zeros(N, HV, K, V), cu_seqlens=torch.tensor([0, 30, T], dtype=torch.int32),
+             out=torch.zeros(T, HV, V, dtype=torch.bfloat16), final_state=torch.zeros(N, HV, K, V))
+    return t
+
+
+def status(gdn2, **kw):
+    rc = gdn2.check(**kw)
+    return gdn2.STATUS[rc], gdn2.last_error()
+
+
+def test_valid_calls(gdn2):
+    assert status(gdn2, **case()) == ("OK", "")
+    assert status(gdn2, **case(K=128, V=128))[0] == "OK"
+    c = case()
+    for opt in ("g", "beta", "w", "initial_state", "final_state"):
+        c2 = dict(c)
+        c2[opt] = None
+        assert status(gdn2, **c2)[0] == "OK", opt
+    c2 = dict(c)
+    c2["cu_seqlens"] = None
+    c2["initial_state"] = torch.zeros(1, 4, 64, 64)
+    c2["final_state"] = torch.zeros(1, 4, 64, 64)
+    assert status(gdn2, **c2)[0] == "OK"
+    assert status(gdn2, **case(T=0))[0] == "OK"
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda c: c.update(q=None), "NULL_ARG"),
+    (lambda c: c.update(v=None), "NULL_ARG"),
+    (lambda c: c.update(out=None), "NULL_ARG"),
+    (lambda c: c.update(q=c["q"].float()), "DTYPE"),
+    (lambda c: c.update(g=c["g"].bfloat16()), "DTYPE"),
+    (lambda c: c.update(initial_state=c["initial_state"].bfloat16()), "DTYPE"),
+    (lambda c: c.update(cu_seqlens=c["cu_seqlens"].long()), "DTYPE"),
+    (lambda c: c.update(out=c["out"].float()), "DTYPE"),
+    (lambda c: c.update(k=c["k"][:60]), "SHAPE"),
+    (lambda c: c.update(beta=c["beta"][:, :2]), "SHAPE"),
+    (lambda c: c.update(q=c["q"][None]), "SHAPE"),
+    (lambda c: c.update(final_state=torch.zeros(3, 4, 64, 64)), "SHAPE"),
+    (lambda c: c.update(cu_seqlens=torch.tensor([0], dtype=torch.int32)), "SHAPE"),
+    (lambda c: c.update(v=torch.zeros(70, 3, 64, dtype=torch.bfloat16)), "HEADS"),
+    (lambda c: c.update(v=torch.zeros(70, 1, 64, dtype=torch.bfloat16)), "HEADS"),
+    (lambda c: c.update(q=torch.zeros(70, 2, 96, dtype=torch.bfloat16), k=torch.zeros(70, 2, 96, dtype=torch.bfloat16)),
+     "UNSUPPORTED"),
+    (lambda c: c.update(v=torch.zeros(70, 4, 128, dtype=torch.bfloat16)), "UNSUPPORTED"),
+    (lambda c: c.update(v=torch.zeros(70, 64, 4, dtype=torch.bfloat16).transpose(1, 2)), "LAYOUT"),
+    (lambda c: c.update(q=torch.zeros(70 * 2 * 64 + 1, dtype=torch.bfloat16)[1:].view(70, 2, 64)), "LAYOUT"),
+])
+def test_rejections(gdn2, mutate, expect):
+    c = case()
+    mutate(c)
+    code, msg = status(gdn2, **c)
+    assert code == expect, (code, msg)
+    assert msg
+
+
+def test_alias_rules(gdn2):
+    c = case()
+    c["final_state"] = c["initial_state"]
+    assert status(gdn2, **c)[0] == "ALIAS"
+    c = case()
+    buf = torch.zeros(70, 4, 64, dtype=torch.bfloat16)
+    c["v"], c["out"] = buf, buf
+    assert status(gdn2, **c)[0] == "ALIAS"
+    c = case()
+    big = torch.zeros(2 * 70 * 4 * 64, dtype=torch.bfloat16)
+    c["w"] = big[: 70 * 4 * 64].view(70, 4, 64)
+    c["out"] = big[70 * 4 * 64 - 8: 2 * 70 * 4 * 64 - 8].view(70, 4, 64)  # overlaps the tail of w
+    assert status(gdn2, **c)[0] == "ALIAS"
+    c = case()
+    c["out"] = torch.zeros(70, 4, 64, dtype=torch.bfloat16)
+    assert status(gdn2, **c)[0] == "OK"
+
+
+def test_no_cpu_path(gdn2):
+    c = case()
+    with pytest.raises(ValueError):
+        gdn2.chunk_fwd(c["q"], c["k"], c["v"])
