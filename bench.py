@@ -1,0 +1,186 @@
+"""Benchmark of the GDN-2 chunked prefill forward on one MI355X.
+
+One step = one call of the fused forward (the whole hot path: decay cumsum,
+decay-scaled K K^T with the erase gate, triangular inverse, w/u recompute,
+sequential float32 state pass with intra + inter output, final state) over
+one packed batch resident in HBM. The default workload is the H32/D128
+varlen prefill: 8 sequences with lengths uniform in [256, 8192] (seed 2),
+H = HV = 32, K = V = 128, bf16 inputs, float32 log-decay and state.
+
+Prints ONE JSON line with the throughput (tokens/s), the HBM roofline of the
+kernel (algorithmic bytes per launch / mean launch time from HIP events on
+the launch stream) and the FP64 oracle timed on the host as a CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ID]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "GDN-2 chunk prefill tokens/s (H32 D128 bf16); % of MFMA/HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_varlen_h32_d128.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_rnn_gdn2_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(T, N, H, HV, K, V, has_init: bool, has_final: bool) -> int:
+    """Bytes that must cross HBM once: q, k (bf16, per q/k head), v, w, out
+    (bf16, per value head), beta (bf16) and g (float32) per value head and
+    key channel, the initial state read and the final state written."""
+    per_token = 2 * K * H * 2 + HV * (3 * 2 * V + 2 * K + 4 * K)
+    state = N * HV * K * V * 4
+    return T * per_token + (state if has_init else 0) + (state if has_final else 0)
+
+
+def measured_traffic(src_hash: str, launches_per_profile: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, workload):
+    from oracle.c_oracle import gdn2_recurrence_c, max_threads
+    names = ("q", "k", "v", "g", "beta", "w")
+    T = int(d["cu_seqlens"][-1])
+    t0 = time.perf_counter()
+    gdn2_recurrence_c(*[d[n] for n in names], d["scale"], d["initial_state"], d["cu_seqlens"])
+    wall = time.perf_counter() - t0
+    return {"value": T / wall, "unit": "tokens/s", "cores": max_threads(), "kind": "oracle",
+            "sample": f"whole {workload.name} workload ({len(d['lengths'])} sequences, {T} tokens x "
+                      f"{workload.HV} value heads), plain-C FP64 token-by-token oracle, "
+                      f"OpenMP over (sequence, head), wall {wall:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, twice (calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (every chain of the GDN-2 "
+              "prefill is independent; multi-GPU sharding is not implemented). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_rnn_gdn2_amd import gdn2
+    from linear_attention_rnn_gdn2_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_probe_mib} MiB twice")
+        return
+    gdn2.load_library()
+    log(f"drawing workload {args.workload}")
+    d = make_inputs(args.workload)
+    wl = d["workload"]
+    T = int(d["cu_seqlens"][-1])
+    N = len(d["lengths"])
+    names = ("q", "k", "v", "g", "beta", "w")
+    gpu = {n: d[n].to(dev) for n in names}
+    s0 = None if d["initial_state"] is None else d["initial_state"].to(dev)
+    cu = d["cu_seqlens"].to(dev)
+    out = torch.empty((T, wl.HV, wl.V), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((N, wl.HV, wl.K, wl.V), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        gdn2.chunk_fwd(**gpu, scale=d["scale"], initial_state=s0, cu_seqlens=cu, out=out, final_state=fin)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = T / (ms_per_step / 1e3)
+
+    algo = algorithmic_bytes(T, N, wl.H, wl.HV, wl.K, wl.V, s0 is not None, True)
+    achieved = algo / mean_launch_s / 1e9
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(src_hash)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {N} sequences, {T} tokens (lengths {d['lengths']}), "
+                               f"H={wl.H} HV={wl.HV} K={wl.K} V={wl.V}, chunk 64, seed {args.workload}",
+                   "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": algo, "mean_launch_ms": mean_launch_s * 1e3,
+                     "kernel_source_hash": src_hash},
+    }
+    log(f"mean launch {mean_launch_s*1e3:.3f} ms, wall/step {ms_per_step:.3f} ms, "
+        f"{value/1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
+    if not args.no_cpu_baseline:
+        log("timing the FP64 oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline(d, wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
