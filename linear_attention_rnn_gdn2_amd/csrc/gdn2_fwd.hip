@@ -100,32 +100,31 @@ struct Lds {
     static constexpr int AP = CH + 4;  // fp32 elements per A/T row
     static constexpr int GP = K + 4;   // fp32 elements per G row (exact path)
     // Region X, phases E/AP (factored path): MFMA operands of A and P
-    static constexpr int LB = 0;                   // beta k exp(G - G_mid)  [64][KP]
-    static constexpr int LQ = LB + CH * KP * 2;    // q exp(G - G_mid)       [64][KP]
-    static constexpr int RR = LQ + CH * KP * 2;    // R_i = k exp(G_mid(i) - G), 16(i+1) rows each
-    static constexpr int X_END1 = RR + 160 * KP * 2;
-    static constexpr int GF = 0;                   // exact path: G fp32     [64][GP]
-    // Region X, phases T/WY
-    static constexpr int KBT = 0;                  // (beta k exp(G))^T      [K][CP]
-    static constexpr int WVT = KBT + K * CP * 2;   // (w v)^T                [V][CP]
-    static constexpr int WYW = WVT + V * CP * 2;   // -wy_w                  [64][KP]
-    static constexpr int TB = WYW + CH * KP * 2;   // T in bf16              [64][CP]
-    static constexpr int X_END2 = TB + CH * CP * 2;
-    // Region X, phase S and the next chunk's phase E1: output staging
-    static constexpr int OST = 0;                  // out tile               [64][VP]
-    static constexpr int X_END = X_END1 > X_END2 ? X_END1 : X_END2;
+    static constexpr int LB = 0;                   // beta k exp(G - G_mid(tile))  [64][KP]
+    static constexpr int LQ = LB + CH * KP * 2;    // q exp(G - G_mid(tile))       [64][KP]
+    static constexpr int RR = LQ + CH * KP * 2;    // k exp(G_mid(tile) - G)       [64][KP]
+    static constexpr int X_END = RR + CH * KP * 2;
+    static constexpr int GF = 0;                   // exact path: G fp32           [64][GP]
+    // Region X, phases T/WY/S
+    static constexpr int WYW = 0;                  // -wy_w                        [64][KP]
+    static constexpr int TB = WYW + CH * KP * 2;   // T in bf16                    [64][CP]
+    static constexpr int OST = TB + CH * CP * 2;   // out tile (phase S -> next E1) [64][VP]
+    // Transposed operands, written in phase E, read in phase WY
+    static constexpr int KBT = X_END;              // (beta k exp(G))^T            [K][CP]
+    static constexpr int WVT = KBT + K * CP * 2;   // (w v)^T                      [V][CP]
     // Persistent buffers
-    static constexpr int QH = X_END;               // q exp(G)               [64][KP]
-    static constexpr int KHT = QH + CH * KP * 2;   // (k exp(G_last - G))^T  [K][CP]
+    static constexpr int QH = WVT + V * CP * 2;    // q exp(G)                     [64][KP]
+    static constexpr int KHT = QH + CH * KP * 2;   // (k exp(G_last - G))^T        [K][CP]
     static constexpr int AB = KHT + K * CP * 2;    // A, diagonal blocks of T, fp32 [64][AP]
-    static constexpr int PB = AB + CH * AP * 4;    // P bf16                 [64][CP]
-    static constexpr int GAM = PB + CH * CP * 2;   // exp(G_last) fp32       [K]
-    static constexpr int TT = GAM + K * 4;         // tile totals of G       [4][K]
-    static constexpr int TM = TT + 4 * K * 4;      // tile midpoints of G    [4][K]
-    static constexpr int SC = TM + 4 * K * 4;      // per-channel factors    [4][5][K]
-    static constexpr int FL = SC + 4 * 5 * K * 4;  // per-wave factored-path flags [4]
+    static constexpr int PB = AB + CH * AP * 4;    // P bf16                       [64][CP]
+    static constexpr int GAM = PB + CH * CP * 2;   // exp(G_last) fp32             [K]
+    static constexpr int TT = GAM + K * 4;         // tile totals of G             [4][K]
+    static constexpr int TM = TT + 4 * K * 4;      // tile midpoints of G          [4][K]
+    static constexpr int SE = TM + 4 * K * 4;      // exp(G_mid(i)), exp(G_last - G_mid(i)) [8][K]
+    static constexpr int SD = SE + 8 * K * 4;      // exp(G_mid(i) - G_mid(j)), i > j      [6][K]
+    static constexpr int FL = SD + 6 * K * 4;      // per-wave factored-path flags [4]
     static constexpr int TOTAL = FL + 16;
-    static_assert(OST + CH * VP * 2 <= WYW, "output staging must not overlap -wy_w");
+    static_assert(OST + CH * VP * 2 <= X_END, "phase T/WY/S view must fit region X");
     static_assert(GF + CH * GP * 4 <= X_END, "exact-path G must fit region X");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -140,18 +139,38 @@ __device__ __forceinline__ int opaque_zero()
     return z;
 }
 
-// Row offset of R_i (the column operand of row tile i) inside RR.
-__device__ __forceinline__ int r_off(int i) { return (i * (i + 1) / 2) * 16; }  // 0, 16, 48, 96
+// Phase-E thread map of one role (4 waves over a 64-row x NC-column chunk,
+// 8 columns per thread): wave w owns rows [16w, 16w + 16); inside a wave the
+// row group varies fastest. Consecutive lanes therefore write consecutive
+// rows of row-major arrays and consecutive tokens of [column][token] arrays,
+// which keeps both kinds of LDS store free of 8-way bank conflicts.
+template <int NC>
+struct EMap {
+    static constexpr int CG = NC / 8;              // column groups
+    static constexpr int RGW = 64 / CG;            // row groups per wave
+    static constexpr int RPT = 16 / RGW;           // rows per thread
+    int rgl, cg, row0, c0;
+    __device__ __forceinline__ explicit EMap(int rt)
+    {
+        const int lane = rt & 63, w = rt >> 6;
+        rgl = lane % RGW;
+        cg = lane / RGW;
+        row0 = (w * RGW + rgl) * RPT;
+        c0 = cg * 8;
+    }
+};
+
+// Slot of the pair (i, j), i > j, in SD.
+__device__ __forceinline__ int d_slot(int i, int j) { return i * (i - 1) / 2 + j; }
 
 // Raw inputs of one chunk as loaded from HBM (bf16 kept packed), in the key
 // waves' thread map: rows row0 + i, channels c0k .. c0k + 7 (key side) and
 // rows row0v + i, columns c0v .. c0v + 7 (value side). Rows past the end of
 // the sequence are zero.
-template <int RPT, int RPTV>
+template <int RPT>
 struct RawChunk {
     bf16x8 q[RPT], k[RPT], b[RPT];
     f32x4 g[RPT][2];
-    bf16x8 v[RPTV], w[RPTV];
 };
 
 // Stand-ins for omitted gates: one row of ones (beta, w) or zeros (g), read
@@ -162,54 +181,87 @@ __constant__ __attribute__((aligned(16))) float kZerosF32[8] = {0, 0, 0, 0, 0, 0
 
 // Straight-line loads: rows past the chunk end read the last valid row and
 // are zeroed afterwards; omitted gates read the stand-in row.
-template <int K, int V, int RPT, int RPTV>
-__device__ __forceinline__ void load_chunk(RawChunk<RPT, RPTV> &R, const FwdParams &p, int64_t c0, int len,
-                                           int hk, int hv, int row0, int c0k, int row0v, int c0v)
+template <int K, int RPT>
+__device__ __forceinline__ void load_decay(RawChunk<RPT> &R, const FwdParams &p, int64_t c0, int len, int hv,
+                                           int row0, int c0k)
+{
+    const float *gb = p.g ? p.g + (c0 * p.HV + hv) * K : kZerosF32;
+    const int sg = p.g ? p.HV * K : 0, cgg = p.g ? c0k : 0;
+    for (int i = 0; i < RPT; ++i) {
+        const int r = row0 + i;
+        const int rc = r < len ? r : len - 1;
+        const bool ok = r < len;
+        const f32x4 g0 = ldg_f32x4(gb + (uint32_t)(rc * sg + cgg));
+        const f32x4 g1 = ldg_f32x4(gb + (uint32_t)(rc * sg + cgg) + 4);
+        R.g[i][0] = ok ? g0 : f32x4{0, 0, 0, 0};
+        R.g[i][1] = ok ? g1 : f32x4{0, 0, 0, 0};
+    }
+}
+
+template <int K, int RPT>
+__device__ __forceinline__ void load_keys(RawChunk<RPT> &R, const FwdParams &p, int64_t c0, int len, int hk,
+                                          int hv, int row0, int c0k)
 {
     const bf16x8 zero = {};
     // wave-uniform chunk bases + 32-bit per-lane offsets
     const uint16_t *qb = p.q + (c0 * p.H + hk) * K;
     const uint16_t *kb = p.k + (c0 * p.H + hk) * K;
-    const uint16_t *vb = p.v + (c0 * p.HV + hv) * V;
     const uint16_t *bb = p.beta ? p.beta + (c0 * p.HV + hv) * K : kOnesBf16;
-    const float *gb = p.g ? p.g + (c0 * p.HV + hv) * K : kZerosF32;
-    const uint16_t *wb = p.w ? p.w + (c0 * p.HV + hv) * V : kOnesBf16;
-    const int sqk = p.H * K, sgb = p.HV * K, svw = p.HV * V;
-    const int sb = p.beta ? sgb : 0, sg = p.g ? sgb : 0, sw = p.w ? svw : 0;
-    const int cb = p.beta ? c0k : 0, cgg = p.g ? c0k : 0, cw = p.w ? c0v : 0;
+    const int sqk = p.H * K, sb = p.beta ? p.HV * K : 0, cb = p.beta ? c0k : 0;
     for (int i = 0; i < RPT; ++i) {
         const int r = row0 + i;
         const int rc = r < len ? r : len - 1;
         const bool ok = r < len;
         const bf16x8 q = ldg_bf16x8(qb + (uint32_t)(rc * sqk + c0k));
         const bf16x8 k = ldg_bf16x8(kb + (uint32_t)(rc * sqk + c0k));
-        const bf16x8 b = ldg_bf16x8(bb + (uint32_t)(rc * sb + cb));
-        const f32x4 g0 = ldg_f32x4(gb + (uint32_t)(rc * sg + cgg));
-        const f32x4 g1 = ldg_f32x4(gb + (uint32_t)(rc * sg + cgg) + 4);
         R.q[i] = ok ? q : zero;
         R.k[i] = ok ? k : zero;
-        R.b[i] = b;
-        R.g[i][0] = ok ? g0 : f32x4{0, 0, 0, 0};
-        R.g[i][1] = ok ? g1 : f32x4{0, 0, 0, 0};
-    }
-    for (int i = 0; i < RPTV; ++i) {
-        const int r = row0v + i;
-        const int rc = r < len ? r : len - 1;
-        const bf16x8 v = ldg_bf16x8(vb + (uint32_t)(rc * svw + c0v));
-        R.v[i] = r < len ? v : zero;
-        R.w[i] = ldg_bf16x8(wb + (uint32_t)(rc * sw + cw));
+        R.b[i] = ldg_bf16x8(bb + (uint32_t)(rc * sb + cb));
     }
 }
 
-// Write RPT consecutive bf16 values (one channel, consecutive tokens) to a
-// [channel][token] array.
-template <int RPT>
-__device__ __forceinline__ void st_col(char *smem, int off, const __bf16 *col)
+// Value-side rows of one chunk (state waves): v and w, rows row0 + i,
+// columns c0 .. c0 + 7; rows past the end are zero.
+template <int V, int RPTV>
+__device__ __forceinline__ void load_values(bf16x8 *v, bf16x8 *w, const FwdParams &p, int64_t c0, int len, int hv,
+                                            int row0, int c0v)
 {
-    if constexpr (RPT == 4)
-        lds_st<bf16x4>(smem, off, bf16x4{col[0], col[1], col[2], col[3]});
-    else
-        lds_st<bf16x2>(smem, off, bf16x2{col[0], col[1]});
+    const bf16x8 zero = {};
+    const uint16_t *vb = p.v + (c0 * p.HV + hv) * V;
+    const uint16_t *wb = p.w ? p.w + (c0 * p.HV + hv) * V : kOnesBf16;
+    const int svw = p.HV * V, sw = p.w ? svw : 0, cw = p.w ? c0v : 0;
+    for (int i = 0; i < RPTV; ++i) {
+        const int r = row0 + i;
+        const int rc = r < len ? r : len - 1;
+        const bf16x8 x = ldg_bf16x8(vb + (uint32_t)(rc * svw + c0v));
+        v[i] = r < len ? x : zero;
+        w[i] = ldg_bf16x8(wb + (uint32_t)(rc * sw + cw));
+    }
+}
+
+// Store RPT rows x 8 channels (bf16, one vector per row) transposed into a
+// [channel][token] array: channel c0 + j gets the RPT consecutive tokens
+// row0 .. row0 + RPT - 1. The 16-bit transposition is done with byte
+// permutes on packed pairs, so nothing is unpacked into separate registers.
+template <int RPT>
+__device__ __forceinline__ void st_transposed(char *smem, int base, int pitch, int c0, int row0, const bf16x8 *rows)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;  // low / high halves of (b, a)
+    u32x4 w[RPT];
+    for (int i = 0; i < RPT; ++i) w[i] = __builtin_bit_cast(u32x4, rows[i]);
+    for (int m = 0; m < 4; ++m) {
+        if constexpr (RPT == 4) {
+            const uint2 e = {__builtin_amdgcn_perm(w[1][m], w[0][m], LO), __builtin_amdgcn_perm(w[3][m], w[2][m], LO)};
+            const uint2 o = {__builtin_amdgcn_perm(w[1][m], w[0][m], HI), __builtin_amdgcn_perm(w[3][m], w[2][m], HI)};
+            lds_st<uint2>(smem, base + 2 * ((c0 + 2 * m) * pitch + row0), e);
+            lds_st<uint2>(smem, base + 2 * ((c0 + 2 * m + 1) * pitch + row0), o);
+        } else {
+            static_assert(RPT == 2, "2 or 4 rows per thread");
+            lds_st<uint32_t>(smem, base + 2 * ((c0 + 2 * m) * pitch + row0), __builtin_amdgcn_perm(w[1][m], w[0][m], LO));
+            lds_st<uint32_t>(smem, base + 2 * ((c0 + 2 * m + 1) * pitch + row0), __builtin_amdgcn_perm(w[1][m], w[0][m], HI));
+        }
+    }
 }
 
 // ----------------------------------------------------------- chain context --
@@ -242,10 +294,19 @@ __device__ __forceinline__ void phase_ap(char *smem, const FwdParams &p, const C
             const int t10 = isP ? tt - 10 : tt;
             const int i = kTriI[t10], j = kTriJ[t10];
             const int mb = isP ? L::LQ : L::LB;
+            // column operand of tile (i, j): k_s exp(G_mid(j) - G_s), times
+            // exp(G_mid(i) - G_mid(j)) <= 1 per channel when j < i
             f32x4 acc = {0, 0, 0, 0};
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 a = lds_ld<bf16x8>(smem, mb + 2 * ((16 * i + l16) * L::KP + 32 * ks + 8 * q4));
-                const bf16x8 b = lds_ld<bf16x8>(smem, L::RR + 2 * ((r_off(i) + 16 * j + l16) * L::KP + 32 * ks + 8 * q4));
+                const int ch8 = 32 * ks + 8 * q4;
+                const bf16x8 a = lds_ld<bf16x8>(smem, mb + 2 * ((16 * i + l16) * L::KP + ch8));
+                bf16x8 b = lds_ld<bf16x8>(smem, L::RR + 2 * ((16 * j + l16) * L::KP + ch8));
+                if (j < i) {
+                    const int ds = L::SD + 4 * (d_slot(i, j) * K + ch8);
+                    const f32x4 d0 = lds_ld<f32x4>(smem, ds), d1 = lds_ld<f32x4>(smem, ds + 16);
+                    const f32x8 dd = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+                    b = f32x8_to_bf16(bf16x8_to_f32(b) * dd);
+                }
                 acc = mfma_bf16(a, b, acc);
             }
             const int s = 16 * j + l16;
@@ -299,16 +360,15 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
     constexpr int CGK = K / 8;              // 8-channel groups along K
     constexpr int RPT = CH * CGK / NROLE;   // rows per thread
     constexpr int RGW = 64 / CGK;           // row groups per wave
-    constexpr int CGV = V / 8;
-    constexpr int RPTV = CH * CGV / NROLE;
     constexpr int NCTK = K / 64;            // -wy_w column tiles per key wave
     static_assert(RPT * RGW == 16, "a key wave covers one 16-row tile");
 
-    RawChunk<RPT, RPTV> R;
+    RawChunk<RPT> R;
     if (ch.tb < ch.te) {
         const int rt = tid & (NROLE - 1);
-        load_chunk<K, V>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hk, ch.hv, (rt / CGK) * RPT, (rt % CGK) * 8,
-                         (rt / CGV) * RPTV, (rt % CGV) * 8);
+        const EMap<K> em(rt);
+        load_decay<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hv, em.row0, em.c0);
+        load_keys<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hk, ch.hv, em.row0, em.c0);
     }
 
     char *const smem0 = smem;
@@ -320,24 +380,20 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         const int tid = tid0 + z;
         const int lane = tid & 63, rw = (tid >> 6) & 3, rt = tid & (NROLE - 1);
         const int l16 = lane & 15, q4 = lane >> 4;
-        const int cg = rt % CGK, rg = rt / CGK, row0 = rg * RPT, c0k = cg * 8;
-        const int rgl = rg % RGW;
-        const int row0v = (rt / CGV) * RPTV, c0v = (rt % CGV) * 8;
+        const EMap<K> em(rt);
+        const int cg = em.cg, row0 = em.row0, c0k = em.c0, rgl = em.rgl;
         const int len = chunk_len(c0, ch.te);
 
         // ---- E1: tile-local cumulative log decay, tile totals/midpoints
         float G[RPT][8], gmid[8];
-        bf16x8 wvb[RPTV];  // w * v, written after phase AP
         for (int i = 0; i < RPT; ++i)
             for (int j = 0; j < 8; ++j)
                 G[i][j] = (i ? G[i - 1][j] : 0.0f) + (j < 4 ? R.g[i][0][j] : R.g[i][1][j - 4]);
-        for (int i = 0; i < RPTV; ++i)
-            wvb[i] = f32x8_to_bf16(bf16x8_to_f32(R.v[i]) * bf16x8_to_f32(R.w[i]));
         for (int j = 0; j < 8; ++j) {
             const float tot = G[RPT - 1][j];
             float inc = tot;
             for (int d = 1; d < RGW; d <<= 1) {
-                const float o = __shfl_up(inc, d * CGK, 64);
+                const float o = __shfl_up(inc, d, 64);
                 if (rgl >= d) inc += o;
             }
             const float excl = inc - tot;
@@ -345,7 +401,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         }
         bool fast_ok = true;
         for (int j = 0; j < 8; ++j) {
-            gmid[j] = __shfl(G[7 % RPT][j], (7 / RPT) * CGK + cg, 64);
+            gmid[j] = __shfl(G[7 % RPT][j], cg * RGW + 7 / RPT, 64);
             for (int i = 0; i < RPT; ++i) fast_ok &= fabsf(G[i][j] - gmid[j]) <= HALF_SPAN_MAX;
         }
         const int wave_ok = __all(fast_ok);
@@ -362,45 +418,15 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         const bool fast = read_fast_flag(smem, L::FL);
         if (fast) __syncthreads();  // -------------------------------- B1b
 
-        // ---- E3: decay factors and operands
-        bf16x8 kbg_rows[RPT], kh_rows[RPT];  // beta k exp(G); k exp(G_last - G)
+        // ---- E3: decay factors and operands. Rows are handled in pairs so
+        // that only two rows of the transposed operands are held at once.
+        float eGm[8], eKm[8], base[8], glast[8];
         if (fast) {
-            float eGm[8], eKm[8];
             for (int j = 0; j < 8; ++j) {
-                eGm[j] = lds_ld<float>(smem, L::SC + 4 * ((rw * 5 + 0) * K + c0k + j));
-                eKm[j] = lds_ld<float>(smem, L::SC + 4 * ((rw * 5 + 1) * K + c0k + j));
-            }
-            for (int i = 0; i < RPT; ++i) {
-                const int r = row0 + i;
-                const f32x8 qf = bf16x8_to_f32(R.q[i]), kf = bf16x8_to_f32(R.k[i]);
-                const f32x8 bk = bf16x8_to_f32(R.b[i]) * kf;
-                f32x8 lb, lq, qh, kb, kh, rk;
-                for (int j = 0; j < 8; ++j) {
-                    const float x = G[i][j] - gmid[j];
-                    const float f = __expf(x), rf = __expf(-x);
-                    lb[j] = bk[j] * f;
-                    lq[j] = qf[j] * f;
-                    qh[j] = qf[j] * (eGm[j] * f);
-                    kb[j] = bk[j] * (eGm[j] * f);
-                    kh[j] = kf[j] * (eKm[j] * rf);
-                    rk[j] = kf[j] * rf;
-                }
-                lds_st<bf16x8>(smem, L::LB + 2 * (r * L::KP + c0k), f32x8_to_bf16(lb));
-                lds_st<bf16x8>(smem, L::LQ + 2 * (r * L::KP + c0k), f32x8_to_bf16(lq));
-                lds_st<bf16x8>(smem, L::QH + 2 * (r * L::KP + c0k), f32x8_to_bf16(qh));
-                lds_st<bf16x8>(smem, L::RR + 2 * ((r_off(rw) + r) * L::KP + c0k), f32x8_to_bf16(rk));
-                for (int t = 1; t < 4; ++t) {
-                    if (rw + t >= 4) break;
-                    const f32x4 d0 = lds_ld<f32x4>(smem, L::SC + 4 * ((rw * 5 + 1 + t) * K + c0k));
-                    const f32x4 d1 = lds_ld<f32x4>(smem, L::SC + 4 * ((rw * 5 + 1 + t) * K + c0k + 4));
-                    const f32x8 dd = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-                    lds_st<bf16x8>(smem, L::RR + 2 * ((r_off(rw + t) + r) * L::KP + c0k), f32x8_to_bf16(rk * dd));
-                }
-                kbg_rows[i] = f32x8_to_bf16(kb);
-                kh_rows[i] = f32x8_to_bf16(kh);
+                eGm[j] = lds_ld<float>(smem, L::SE + 4 * (rw * K + c0k + j));
+                eKm[j] = lds_ld<float>(smem, L::SE + 4 * ((4 + rw) * K + c0k + j));
             }
         } else {
-            float base[8], glast[8];
             for (int j = 0; j < 8; ++j) {
                 float acc = 0.0f;
                 base[j] = 0.0f;
@@ -410,50 +436,56 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                 }
                 glast[j] = acc;
             }
-            for (int i = 0; i < RPT; ++i) {
+        }
+        for (int pr = 0; pr < RPT; pr += 2) {
+            bf16x8 kbg_rows[2], kh_rows[2];  // beta k exp(G); k exp(G_last - G)
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const int i = pr + i2;
                 const int r = row0 + i;
                 const f32x8 qf = bf16x8_to_f32(R.q[i]), kf = bf16x8_to_f32(R.k[i]);
                 const f32x8 bk = bf16x8_to_f32(R.b[i]) * kf;
-                f32x8 qh, kb, kh, ga;
-                for (int j = 0; j < 8; ++j) {
-                    ga[j] = base[j] + G[i][j];
-                    const float eg = __expf(ga[j]), ek = __expf(glast[j] - ga[j]);
-                    qh[j] = qf[j] * eg;
-                    kb[j] = bk[j] * eg;
-                    kh[j] = kf[j] * ek;
+                if (fast) {
+                    f32x8 lb, lq, qh, kb, kh, rk;
+                    for (int j = 0; j < 8; ++j) {
+                        const float x = G[i][j] - gmid[j];
+                        const float f = __expf(x), rf = __expf(-x);
+                        lb[j] = bk[j] * f;
+                        lq[j] = qf[j] * f;
+                        qh[j] = qf[j] * (eGm[j] * f);
+                        kb[j] = bk[j] * (eGm[j] * f);
+                        kh[j] = kf[j] * (eKm[j] * rf);
+                        rk[j] = kf[j] * rf;
+                    }
+                    lds_st<bf16x8>(smem, L::LB + 2 * (r * L::KP + c0k), f32x8_to_bf16(lb));
+                    lds_st<bf16x8>(smem, L::LQ + 2 * (r * L::KP + c0k), f32x8_to_bf16(lq));
+                    lds_st<bf16x8>(smem, L::QH + 2 * (r * L::KP + c0k), f32x8_to_bf16(qh));
+                    lds_st<bf16x8>(smem, L::RR + 2 * (r * L::KP + c0k), f32x8_to_bf16(rk));
+                    kbg_rows[i2] = f32x8_to_bf16(kb);
+                    kh_rows[i2] = f32x8_to_bf16(kh);
+                } else {
+                    f32x8 qh, kb, kh, ga;
+                    for (int j = 0; j < 8; ++j) {
+                        ga[j] = base[j] + G[i][j];
+                        const float eg = __expf(ga[j]), ek = __expf(glast[j] - ga[j]);
+                        qh[j] = qf[j] * eg;
+                        kb[j] = bk[j] * eg;
+                        kh[j] = kf[j] * ek;
+                    }
+                    lds_st<f32x4>(smem, L::GF + 4 * (r * L::GP + c0k), f32x4{ga[0], ga[1], ga[2], ga[3]});
+                    lds_st<f32x4>(smem, L::GF + 4 * (r * L::GP + c0k + 4), f32x4{ga[4], ga[5], ga[6], ga[7]});
+                    lds_st<bf16x8>(smem, L::QH + 2 * (r * L::KP + c0k), f32x8_to_bf16(qh));
+                    kbg_rows[i2] = f32x8_to_bf16(kb);
+                    kh_rows[i2] = f32x8_to_bf16(kh);
                 }
-                lds_st<f32x4>(smem, L::GF + 4 * (r * L::GP + c0k), f32x4{ga[0], ga[1], ga[2], ga[3]});
-                lds_st<f32x4>(smem, L::GF + 4 * (r * L::GP + c0k + 4), f32x4{ga[4], ga[5], ga[6], ga[7]});
-                lds_st<bf16x8>(smem, L::QH + 2 * (r * L::KP + c0k), f32x8_to_bf16(qh));
-                kbg_rows[i] = f32x8_to_bf16(kb);
-                kh_rows[i] = f32x8_to_bf16(kh);
             }
+            st_transposed<2>(smem, L::KHT, L::CP, c0k, row0 + pr, kh_rows);
+            st_transposed<2>(smem, L::KBT, L::CP, c0k, row0 + pr, kbg_rows);
         }
-        for (int j = 0; j < 8; ++j) {
-            __bf16 col[RPT];
-            for (int i = 0; i < RPT; ++i) col[i] = kh_rows[i][j];
-            st_col<RPT>(smem, L::KHT + 2 * ((c0k + j) * L::CP + row0), col);
-        }
-        // prefetch the next chunk's rows; they land during phases AP..S
-        __builtin_amdgcn_sched_barrier(0);
-        if (c0 + CH < ch.te)
-            load_chunk<K, V>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k, row0v, c0v);
         __syncthreads();  // ------------------------------------------ B2
 
         phase_ap<K, V>(smem, p, ch, c0, len, fast, tid);
         __syncthreads();  // ------------------------------------------ B3
 
-        // deferred operands into region X: (beta k exp(G))^T and (w v)^T
-        for (int j = 0; j < 8; ++j) {
-            __bf16 col[RPT];
-            for (int i = 0; i < RPT; ++i) col[i] = kbg_rows[i][j];
-            st_col<RPT>(smem, L::KBT + 2 * ((c0k + j) * L::CP + row0), col);
-        }
-        for (int j = 0; j < 8; ++j) {
-            __bf16 col[RPTV];
-            for (int i = 0; i < RPTV; ++i) col[i] = wvb[i][j];
-            st_col<RPTV>(smem, L::WVT + 2 * ((c0v + j) * L::CP + row0v), col);
-        }
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- T2: block column j = rw of T by fp32 MFMA,
@@ -505,6 +537,15 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             }
         }
         __syncthreads();  // ------------------------------------------ B6
+        // Prefetch the next chunk while the state waves run phase S: every
+        // workgroup issues its loads at about the same time, so the issue
+        // stalls until HBM drains them; here that stall overlaps phase S.
+        // Nothing else is outstanding, so no later register reload waits on
+        // these loads (vector-memory operations complete in order).
+        if (c0 + CH < ch.te) {
+            load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
+            load_keys<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
+        }
         __syncthreads();  // ------------------------------------------ B7
     }
 }
@@ -515,6 +556,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
 {
     using L = Lds<K, V>;
     constexpr int CGV = V / 8;
+    constexpr int RPTV = CH * CGV / NROLE;
     constexpr int VW = V / 4;     // value columns per state wave
     constexpr int NCT = VW / 16;  // 16-column tiles per state wave
     constexpr int NRT = K / 16;   // 16-row tiles of the state
@@ -547,6 +589,12 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
         const int len = chunk_len(c0, ch.te);
+        // this chunk's v and w rows (consumed after phase E, so the load
+        // latency is hidden behind it)
+        const EMap<V> emv(rt);
+        const int row0v = emv.row0, c0v = emv.c0;
+        bf16x8 vr[RPTV], wr[RPTV];
+        load_values<V, RPTV>(vr, wr, p, c0, len, ch.hv, row0v, c0v);
         // store the previous chunk's staged output (a full chunk: only the
         // sequence's last chunk can be partial)
         if (c0 > ch.tb)
@@ -570,10 +618,10 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                 }
                 float gmi = gm[0];
                 for (int t = 1; t < 4; ++t) gmi = i == t ? gm[t] : gmi;
-                lds_st<float>(smem, L::SC + 4 * ((i * 5 + 0) * K + c), __expf(gmi));
-                lds_st<float>(smem, L::SC + 4 * ((i * 5 + 1) * K + c), __expf(acc - gmi));
-                for (int t = 1; t < 4; ++t)
-                    if (i + t < 4) lds_st<float>(smem, L::SC + 4 * ((i * 5 + 1 + t) * K + c), __expf(gm[i + t] - gmi));
+                lds_st<float>(smem, L::SE + 4 * (i * K + c), __expf(gmi));
+                lds_st<float>(smem, L::SE + 4 * ((4 + i) * K + c), __expf(acc - gmi));
+                for (int t = 0; t < 3; ++t)
+                    if (t < i) lds_st<float>(smem, L::SD + 4 * (d_slot(i, t) * K + c), __expf(gmi - gm[t]));
                 if (i == 0) lds_st<float>(smem, L::GAM + 4 * c, __expf(acc));
             }
             __syncthreads();  // -------------------------------------- B1b
@@ -582,29 +630,37 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int t = 0; t < 4; ++t) acc += lds_ld<float>(smem, L::TT + 4 * (t * K + rt));
             lds_st<float>(smem, L::GAM + 4 * rt, __expf(acc));
         }
+        {
+            // (w v)^T: column c0v + j, tokens row0v ..
+            bf16x8 wvb[RPTV];
+            for (int i = 0; i < RPTV; ++i) wvb[i] = f32x8_to_bf16(bf16x8_to_f32(vr[i]) * bf16x8_to_f32(wr[i]));
+            st_transposed<RPTV>(smem, L::WVT, L::CP, c0v, row0v, wvb);
+        }
         __syncthreads();  // ------------------------------------------ B2
 
         phase_ap<K, V>(smem, p, ch, c0, len, fast, tid);
         __syncthreads();  // ------------------------------------------ B3
 
         // ---- T1: diagonal block rw of T by forward substitution. Lane l16
-        // holds row l16 of A_ii and builds column l16 of T_ii; A_ii[r][s] is
-        // broadcast from lane r (readlane).
+        // builds column l16 of T_ii; row r of A_ii is read from LDS as a
+        // broadcast (every lane reads the same address).
         {
             const int d0 = 16 * rw;
-            float arow[16];
-            for (int s4 = 0; s4 < 16; s4 += 4) {
-                const f32x4 x = lds_ld<f32x4>(smem, L::AB + 4 * ((d0 + l16) * L::AP + d0 + s4));
-                for (int e = 0; e < 4; ++e) arow[s4 + e] = x[e];
-            }
+            // the whole strictly-lower triangle first (one wait), then a pure
+            // FMA chain
+            float a[16][16];
+            for (int r = 1; r < 16; ++r)
+                for (int s4 = 0; s4 < r; s4 += 4) {
+                    const f32x4 x = lds_ld<f32x4>(smem, L::AB + 4 * ((d0 + r) * L::AP + d0 + s4));
+                    for (int e = 0; e < 4; ++e) a[r][s4 + e] = x[e];
+                }
             float tc[16];
             tc[0] = l16 == 0 ? 1.0f : 0.0f;
             for (int r = 1; r < 16; ++r) {
                 float acc0 = 0.0f, acc1 = 0.0f;
                 for (int s2 = 0; s2 < r; ++s2) {
-                    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(arow[s2]), r));
-                    if (s2 & 1) acc1 += a * tc[s2];
-                    else acc0 += a * tc[s2];
+                    if (s2 & 1) acc1 += a[r][s2] * tc[s2];
+                    else acc0 += a[r][s2] * tc[s2];
                 }
                 tc[r] = r == l16 ? 1.0f : (r > l16 ? -(acc0 + acc1) : 0.0f);
             }
