@@ -120,8 +120,7 @@ struct Lds {
     static constexpr int GAM = PB + CH * CP * 2;   // exp(G_last) fp32             [K]
     static constexpr int TT = GAM + K * 4;         // tile totals of G             [4][K]
     static constexpr int TM = TT + 4 * K * 4;      // tile midpoints of G          [4][K]
-    static constexpr int SE = TM + 4 * K * 4;      // exp(G_mid(i)), exp(G_last - G_mid(i)) [8][K]
-    static constexpr int SD = SE + 8 * K * 4;      // exp(G_mid(i) - G_mid(j)), i > j      [6][K]
+    static constexpr int SD = TM + 4 * K * 4;      // exp(G_mid(i) - G_mid(j)), i > j      [6][K]
     static constexpr int FL = SD + 6 * K * 4;      // per-wave factored-path flags [4]
     static constexpr int TOTAL = FL + 16;
     static_assert(OST + CH * VP * 2 <= X_END, "phase T/WY/S view must fit region X");
@@ -351,8 +350,7 @@ __device__ __forceinline__ void phase_ap(char *smem, const FwdParams &p, const C
 }
 
 // ------------------------------------------------------------- key waves --
-// Barrier sequence per chunk (must match state_role): B1, [B1b if the chunk
-// takes the factored path], B2, B3, B4, B5, B6, B7.
+// Barrier sequence per chunk (must match state_role): B1 .. B7.
 template <int K, int V>
 __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const Chain &ch, int tid)
 {
@@ -389,19 +387,34 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         for (int i = 0; i < RPT; ++i)
             for (int j = 0; j < 8; ++j)
                 G[i][j] = (i ? G[i - 1][j] : 0.0f) + (j < 4 ? R.g[i][0][j] : R.g[i][1][j - 4]);
+        // inclusive scan of the row-group totals across the RGW lanes of a
+        // column group (consecutive lanes)
         for (int j = 0; j < 8; ++j) {
             const float tot = G[RPT - 1][j];
             float inc = tot;
-            for (int d = 1; d < RGW; d <<= 1) {
-                const float o = __shfl_up(inc, d, 64);
-                if (rgl >= d) inc += o;
+            if constexpr (RGW == 4) {  // quads: DPP row shifts by 1 and 2 lanes
+                const float o1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(inc), 0x111, 0xf, 0xf, false));
+                if (rgl >= 1) inc += o1;
+                const float o2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(inc), 0x112, 0xf, 0xf, false));
+                if (rgl >= 2) inc += o2;
+            } else {
+                for (int d = 1; d < RGW; d <<= 1) {
+                    const float o = __shfl_up(inc, d, 64);
+                    if (rgl >= d) inc += o;
+                }
             }
             const float excl = inc - tot;
             for (int i = 0; i < RPT; ++i) G[i][j] += excl;
         }
+        // tile midpoint (local row 7) from the lane that holds it
         bool fast_ok = true;
         for (int j = 0; j < 8; ++j) {
-            gmid[j] = __shfl(G[7 % RPT][j], cg * RGW + 7 / RPT, 64);
+            if constexpr (RGW == 4) {  // quad broadcast of lane 1 (rows 4..7)
+                static_assert(7 / RPT == 1, "row 7 sits in the quad's lane 1");
+                gmid[j] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(G[7 % RPT][j]), 0x55, 0xf, 0xf, false));
+            } else {
+                gmid[j] = __shfl(G[7 % RPT][j], cg * RGW + 7 / RPT, 64);
+            }
             for (int i = 0; i < RPT; ++i) fast_ok &= fabsf(G[i][j] - gmid[j]) <= HALF_SPAN_MAX;
         }
         const int wave_ok = __all(fast_ok);
@@ -416,27 +429,26 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         if (lane == 0) lds_st<int>(smem, L::FL + 4 * rw, wave_ok);
         __syncthreads();  // ------------------------------------------ B1
         const bool fast = read_fast_flag(smem, L::FL);
-        if (fast) __syncthreads();  // -------------------------------- B1b
 
         // ---- E3: decay factors and operands. Rows are handled in pairs so
         // that only two rows of the transposed operands are held at once.
+        // chunk-relative references of this wave's tile: base (start),
+        // glast (end of chunk); G_mid = base + gmid
         float eGm[8], eKm[8], base[8], glast[8];
-        if (fast) {
-            for (int j = 0; j < 8; ++j) {
-                eGm[j] = lds_ld<float>(smem, L::SE + 4 * (rw * K + c0k + j));
-                eKm[j] = lds_ld<float>(smem, L::SE + 4 * ((4 + rw) * K + c0k + j));
+        for (int j = 0; j < 8; ++j) {
+            float acc = 0.0f;
+            base[j] = 0.0f;
+            for (int t = 0; t < 4; ++t) {
+                if (t == rw) base[j] = acc;
+                acc += lds_ld<float>(smem, L::TT + 4 * (t * K + c0k + j));
             }
-        } else {
-            for (int j = 0; j < 8; ++j) {
-                float acc = 0.0f;
-                base[j] = 0.0f;
-                for (int t = 0; t < 4; ++t) {
-                    if (t == rw) base[j] = acc;
-                    acc += lds_ld<float>(smem, L::TT + 4 * (t * K + c0k + j));
-                }
-                glast[j] = acc;
-            }
+            glast[j] = acc;
         }
+        if (fast)
+            for (int j = 0; j < 8; ++j) {
+                eGm[j] = __expf(base[j] + gmid[j]);
+                eKm[j] = __expf(glast[j] - base[j] - gmid[j]);
+            }
         for (int pr = 0; pr < RPT; pr += 2) {
             bf16x8 kbg_rows[2], kh_rows[2];  // beta k exp(G); k exp(G_last - G)
             for (int i2 = 0; i2 < 2; ++i2) {
@@ -605,30 +617,21 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             }
         __syncthreads();  // ------------------------------------------ B1
         const bool fast = read_fast_flag(smem, L::FL);
-        // ---- E2: per (tile i, channel c): exp(G_mid(i)),
-        // exp(G_last - G_mid(i)), exp(G_mid(i2) - G_mid(i)) for i2 > i; and
-        // exp(G_last)
-        if (fast) {
-            for (int pc = rt; pc < 4 * K; pc += NROLE) {
-                const int i = pc / K, c = pc % K;
-                float gm[4], acc = 0.0f;
-                for (int t = 0; t < 4; ++t) {
-                    gm[t] = acc + lds_ld<float>(smem, L::TM + 4 * (t * K + c));
-                    acc += lds_ld<float>(smem, L::TT + 4 * (t * K + c));
-                }
-                float gmi = gm[0];
-                for (int t = 1; t < 4; ++t) gmi = i == t ? gm[t] : gmi;
-                lds_st<float>(smem, L::SE + 4 * (i * K + c), __expf(gmi));
-                lds_st<float>(smem, L::SE + 4 * ((4 + i) * K + c), __expf(acc - gmi));
+        // ---- E2 (overlaps the key waves' phase E3): cross-tile factors
+        // exp(G_mid(i) - G_mid(j)), i > j, for phase AP, and exp(G_last)
+        for (int pc = rt; pc < 4 * K; pc += NROLE) {
+            const int i = pc / K, c = pc % K;
+            float gm[4], acc = 0.0f;
+            for (int t = 0; t < 4; ++t) {
+                gm[t] = acc + lds_ld<float>(smem, L::TM + 4 * (t * K + c));
+                acc += lds_ld<float>(smem, L::TT + 4 * (t * K + c));
+            }
+            float gmi = gm[0];
+            for (int t = 1; t < 4; ++t) gmi = i == t ? gm[t] : gmi;
+            if (fast)
                 for (int t = 0; t < 3; ++t)
                     if (t < i) lds_st<float>(smem, L::SD + 4 * (d_slot(i, t) * K + c), __expf(gmi - gm[t]));
-                if (i == 0) lds_st<float>(smem, L::GAM + 4 * c, __expf(acc));
-            }
-            __syncthreads();  // -------------------------------------- B1b
-        } else if (rt < K) {
-            float acc = 0.0f;
-            for (int t = 0; t < 4; ++t) acc += lds_ld<float>(smem, L::TT + 4 * (t * K + rt));
-            lds_st<float>(smem, L::GAM + 4 * rt, __expf(acc));
+            if (i == 0) lds_st<float>(smem, L::GAM + 4 * c, __expf(acc));
         }
         {
             // (w v)^T: column c0v + j, tokens row0v ..
