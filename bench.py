@@ -68,6 +68,94 @@ def measured_traffic(src_hash: str, launches_per_profile: int = 1):
     return rec.get("hbm_bytes_per_launch")
 
 
+PROFILE_STEPS = {
+    # name: (rocprofv3 options, bench.py options)
+    "kt": ("--kernel-trace --stats", "--steps 10 --warmup 2 --no-cpu-baseline"),
+    "pmc_fetch": ("--pmc FETCH_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline"),
+    "pmc_write": ("--pmc WRITE_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline"),
+    "cal_fetch": ("--pmc FETCH_SIZE", "--copy-probe-mib 1024"),
+    "cal_write": ("--pmc WRITE_SIZE", "--copy-probe-mib 1024"),
+}
+KERNEL_TAG = "chunk_fwd_kernel"
+
+
+def profile_command(name: str) -> str:
+    opts, bench_opts = PROFILE_STEPS[name]
+    return (f"rocprofv3 {opts} -f csv -d gpurun_out/{name} -o {name} -- "
+            f"python -u bench.py {bench_opts}")
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def summarize_profiles(outdir: str, tag: str):
+    """Turn the rocprofv3 CSVs of the PROFILE_STEPS runs under ``outdir`` into
+    the committed text summaries: the kernel-trace statistics, and the HBM
+    bytes per launch of the forward kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by the same counter's reading for a plain
+    device copy of 1 GiB (so that bytes per KiB-unit are calibrated, not
+    assumed)."""
+    src_hash = kernel_source_hash()
+    stats = _csv_rows(_find(os.path.join(outdir, "kt"), "_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel-trace statistics: GDN-2 forward, {tag}", "",
+             f"kernel source hash (sha256 over csrc/*.hip, *.cpp, *.h, first 16 hex): {src_hash}",
+             "command (from the repository root):", "  " + profile_command("kt"), "",
+             f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
+    for r in stats:
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
+                     f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {r['Name']}")
+
+    def counter(name, want_kernel, value_min=0.0):
+        rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
+        vals = [float(r["Counter_Value"]) for r in rows if want_kernel(r["Kernel_Name"])
+                and float(r["Counter_Value"]) >= value_min]
+        if not vals:
+            raise ValueError(f"{name}: no matching dispatch")
+        return vals
+
+    fwd = lambda n: KERNEL_TAG in n
+    copy = lambda n: "copyBuffer" in n
+    copy_bytes = 1024 * (1 << 20)
+    cal_f = max(counter("cal_fetch", copy))
+    cal_w = max(counter("cal_write", copy))
+    fetch_scale = copy_bytes / (cal_f * 1024)  # bytes per counted byte
+    write_scale = copy_bytes / (cal_w * 1024)
+    kf = counter("pmc_fetch", fwd)
+    kw = counter("pmc_write", fwd)
+    fetch = sum(kf) / len(kf) * 1024 * fetch_scale
+    write = sum(kw) / len(kw) * 1024 * write_scale
+    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc, one counter per run)", "",
+              "commands:", "  " + profile_command("pmc_fetch"), "  " + profile_command("pmc_write"),
+              "  " + profile_command("cal_fetch"), "  " + profile_command("cal_write"), "",
+              f"copy calibration: 1 GiB device copy reads FETCH_SIZE {cal_f:.1f} KiB, WRITE_SIZE {cal_w:.1f} KiB",
+              f"  -> scale factors: fetch x{fetch_scale:.3f}, write x{write_scale:.3f}",
+              f"forward kernel: FETCH_SIZE {sum(kf)/len(kf):.1f} KiB/dispatch ({len(kf)} dispatches), "
+              f"WRITE_SIZE {sum(kw)/len(kw):.1f} KiB/dispatch ({len(kw)} dispatches)",
+              f"  -> HBM read {fetch/1e6:.2f} MB, write {write/1e6:.2f} MB, total {(fetch+write)/1e6:.2f} MB per launch"]
+    txt = os.path.join(ROOT, "profiles", f"{KERNEL_TAG}_{tag}.txt")
+    with open(txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump({"kernel_source_hash": src_hash, "hbm_bytes_per_launch": fetch + write,
+                   "hbm_read_bytes": fetch, "hbm_write_bytes": write,
+                   "fetch_scale": fetch_scale, "write_scale": write_scale,
+                   "commands": [profile_command(n) for n in ("pmc_fetch", "pmc_write", "cal_fetch", "cal_write")]},
+                  f, indent=1)
+        f.write("\n")
+    log("\n".join(lines))
+
+
 def cpu_baseline(d, workload):
     from oracle.c_oracle import gdn2_recurrence_c, max_threads
     names = ("q", "k", "v", "g", "beta", "w")
@@ -88,10 +176,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="host only: write the committed profile summaries from the rocprofv3 CSVs "
+                         "of the runs printed by --print-profile-commands, found under DIR")
+    ap.add_argument("--print-profile-commands", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, twice (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     args = ap.parse_args()
+    if args.print_profile_commands:
+        for n in PROFILE_STEPS:
+            print(profile_command(n))
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, "varlen_h32_d128")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU only (every chain of the GDN-2 "
