@@ -5,18 +5,17 @@
 //
 //   state waves 0-3  hold the K x V float32 state in registers (result layout
 //                    of v_mfma_f32_16x16x32_bf16, V split four ways), invert
-//                    the four 16x16 diagonal blocks of (I + A) and run the
-//                    sequential state pass;
+//                    (I + A) and run the sequential state pass;
 //   key waves 4-7    hold the next chunk's raw q, k, beta, g in registers
 //                    (prefetched), build the decay factors and MFMA operands,
-//                    and finish the inverse and the pseudo-keys.
+//                    and the pseudo-keys.
 //
 // Per chunk (rows r, s are positions in the chunk; G = inclusive in-chunk
 // cumulative sum of the log-decay g per key channel, kept in log2 units;
 // S = state entering the chunk):
 //
 //   E   cumulative sum of g (in-thread + wave DPP + LDS exchange of tile
-//       totals), then the operands  KB = beta k 2^G,  QH = scale q 2^G,
+//       totals), then the operands  KB = beta k 2^G,  QH = q 2^G,
 //       RR = k 2^-G,  KT = k 2^(G_last - G)  (bf16, row-major in LDS)
 //   AP  A_rs = sum_c KB_rc RR_sc   (s < r),   P_rs = sum_c QH_rc RR_sc  (s <= r)
 //       on MFMA. 2^G_r 2^-G_s is exp(G_r - G_s) with one reference per
@@ -27,7 +26,7 @@
 //       substitution, then the block columns by fp32 MFMA chains
 //       T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
 //   WY  wy_w = T KB,  wy_u = T (w v)                              (bf16 MFMA)
-//   S   U = wy_u - wy_w S;  O = QH S + P U;
+//   S   U = wy_u - wy_w S;  O = scale (QH S + P U);
 //       S <- diag(2^G_last) S + KT^T U                             (bf16 MFMA)
 //
 // The two roles are software-pipelined across chunks: while the key waves
@@ -121,8 +120,12 @@ __device__ __forceinline__ int opaque_zero()
 // (row tile i, column tile j). Tiles 0-3 are A's diagonal tiles, taken by
 // the state waves so that each can invert its block at once; the key waves
 // take tiles 4..19.
-__constant__ int8_t kTileI[20] = {0, 1, 2, 3, 1, 2, 2, 3, 3, 3, 0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kTileJ[20] = {0, 1, 2, 3, 0, 0, 1, 0, 1, 2, 0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// Packed 2 bits per tile (no memory access, so no wait on the vector
+// memory counter, which also counts the outstanding prefetch):
+//   i = 0 1 2 3 1 2 2 3 3 3 0 1 1 2 2 2 3 3 3 3
+//   j = 0 1 2 3 0 0 1 0 1 2 0 0 1 0 1 2 0 1 2 3
+__device__ __forceinline__ int tile_i(int t) { return (int)((0xffa94fe9e4ull >> (2 * t)) & 3); }
+__device__ __forceinline__ int tile_j(int t) { return (int)((0xe4910910e4ull >> (2 * t)) & 3); }
 
 // ------------------------------------------------------------ LDS layout --
 // Byte offsets into one static LDS array. Row pitches carry 16 bytes of
@@ -138,14 +141,14 @@ struct Lds {
 
     static constexpr int KB = 0;                                   // beta k 2^G          [64][KP]  E -> WY
     static constexpr int RR = KB + CH * KP * 2;                    // k 2^-G              [64][KP]  E -> AP
-    static constexpr int TB = RR;                                  // T bf16              [64][CP]  T -> WY
     static constexpr int PF = RR;                                  // P fp32 (exact path) [64][AP]  AP only
-    static constexpr int RR_SZ = cmax(cmax(CH * KP * 2, CH * CP * 2), CH * AP * 4);
-    static constexpr int QH = RR + RR_SZ;                          // scale q 2^G, by chunk parity [2][64][KP]
+    static constexpr int RR_SZ = cmax(CH * KP * 2, CH * AP * 4);
+    static constexpr int TB = RR + RR_SZ;                          // T bf16; blocks (0,1), (2,3) stay 0 [64][CP]
+    static constexpr int QH = TB + CH * CP * 2;                    // q 2^G, by chunk parity [2][64][KP]
     static constexpr int QH_SZ = CH * KP * 2;
     static constexpr int KT = QH + 2 * QH_SZ;                      // k 2^(G_last - G)    [64][KP]  E -> S
     static constexpr int WV = KT + CH * KP * 2;                    // w v                 [64][VP]  T -> WY
-    static constexpr int SB = WV;                                  // exact channels: G, beta k, scale q, k (fp32) [4][NXB][64]
+    static constexpr int SB = WV;                                  // exact channels: G, beta k, q, k (fp32) [4][NXB][64]
     static constexpr int WV_SZ = cmax(CH * VP * 2, 4 * NXB * CH * 4);
     static constexpr int AB = WV + WV_SZ;                          // A, then T blocks, fp32 [64][AP]  AP -> T
     static constexpr int WYW = AB;                                 // -wy_w bf16          [64][KP]  WY -> S
@@ -325,7 +328,7 @@ __device__ __forceinline__ f32x4 ap_mask(f32x4 x, bool diag, bool isP, int l16, 
 // Exact-channel path of phase AP, run by all 512 threads with an identical
 // barrier sequence. MFMA tiles give the contribution of the channels with
 // bounded |G| (RR is zero on the others); every exact channel then adds
-// beta_r k_r k_s exp(G_r - G_s) and scale q_r k_s exp(G_r - G_s) per pair,
+// beta_r k_r k_s exp(G_r - G_s) and q_r k_s exp(G_r - G_s) per pair,
 // NXB channels per batch, with G rebuilt from g in float32.
 template <int K, int V>
 __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_t c0, int len, int qb, int tid)
@@ -334,7 +337,7 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
     constexpr int NXB = L::NXB;
     constexpr int TPC = NTHR / NXB;  // threads per channel in the fill step
     constexpr int RPX = CH / TPC;    // rows per thread in the fill step
-    const int lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l16 = lane & 15, q4 = lane >> 4;
 
     // compact list of the exact channels (wave 0)
     if (wv == 0) {
@@ -352,7 +355,7 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
     for (int m = 0; m < 3; ++m) {
         const int t = wv + 8 * m;
         if (t < 20) {
-            const int i = kTileI[t], j = kTileJ[t];
+            const int i = tile_i(t), j = tile_j(t);
             acc[m] = ap_tile<K, V>(smem, i, j, t >= 10 ? qb : L::KB, l16, q4);
         }
     }
@@ -360,7 +363,7 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
     for (int m = 0; m < 3; ++m) {
         const int t = wv + 8 * m;
         if (t < 20) {
-            const int i = kTileI[t], j = kTileJ[t];
+            const int i = tile_i(t), j = tile_j(t);
             const bool isP = t >= 10;
             const f32x4 x = ap_mask(acc[m], i == j, isP, l16, q4);
             lds_st<f32x4>(smem, (isP ? L::PF : L::AB) + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * q4), x);
@@ -393,7 +396,7 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
                 run += gv;
                 gs[u] = run;
                 bk[u] = bv * kk;
-                qs[u] = qv * p.scale;
+                qs[u] = qv;
                 kv[u] = kk;
             }
             // inclusive scan of the per-thread totals over the channel's TPC lanes
@@ -457,10 +460,10 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
 // Diagonal block i of T = (I + A)^{-1} by forward substitution,
 // T_rc = delta_rc - sum_{s<r} A_rs T_sc: lane l16 builds column l16 (every
 // lane group redundantly), reading row r of A as a broadcast when it is
-// needed. The block is written back over A's block in AB (fp32); the lane's
-// rows 4 q4 .. 4 q4 + 3 of column l16 are returned for the bf16 copy.
+// needed. The block is written over A's block in AB (fp32) and into TB
+// (bf16); lane group q4 writes rows 4 q4 .. 4 q4 + 3.
 template <int K, int V>
-__device__ __forceinline__ f32x4 t1_block(char *smem, int i, int l16, int q4)
+__device__ __forceinline__ void t1_block(char *smem, int i, int l16, int q4)
 {
     using L = Lds<K, V>;
     const int d0 = 16 * i;
@@ -480,8 +483,10 @@ __device__ __forceinline__ f32x4 t1_block(char *smem, int i, int l16, int q4)
     f32x4 out;
     for (int e = 0; e < 4; ++e)
         out[e] = q4 == 0 ? t[e] : q4 == 1 ? t[4 + e] : q4 == 2 ? t[8 + e] : t[12 + e];
-    for (int e = 0; e < 4; ++e) lds_st<float>(smem, L::AB + 4 * ((d0 + 4 * q4 + e) * L::AP + d0 + l16), out[e]);
-    return out;
+    for (int e = 0; e < 4; ++e) {
+        lds_st<float>(smem, L::AB + 4 * ((d0 + 4 * q4 + e) * L::AP + d0 + l16), out[e]);
+        lds_st<__bf16>(smem, L::TB + 2 * ((d0 + 4 * q4 + e) * L::CP + d0 + l16), (__bf16)out[e]);
+    }
 }
 
 // ------------------------------------------------------------- key waves --
@@ -511,7 +516,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         const int z = opaque_zero();
         char *smem = smem0 + z;
         const int tid = tid0 + z;
-        const int lane = tid & 63, rw = (tid >> 6) & 3, rt = tid & (NROLE - 1);
+        const int lane = tid & 63, rw = __builtin_amdgcn_readfirstlane((tid >> 6) & 3), rt = tid & (NROLE - 1);
         const int l16 = lane & 15, q4 = lane >> 4;
         const EMap<K> em(rt);
         const int rgl = em.rgl, row0 = em.row0, c0k = em.c0;
@@ -584,7 +589,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             for (int i = 0; i < RPT; ++i) {
                 const int r = row0 + i;
                 const bool ok = r < len;
-                const f32x8 qf = bf16x8_to_f32(ok ? R.q[i] : zero) * p.scale;
+                const f32x8 qf = bf16x8_to_f32(ok ? R.q[i] : zero);
                 const f32x8 kf = bf16x8_to_f32(ok ? R.k[i] : zero);
                 const f32x8 bk = bf16x8_to_f32(R.b[i]) * kf;
                 f32x8 kb, qh, rr, kt;
@@ -626,7 +631,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         if (lds_ld<int>(smem, L::FL) == 0) {
             for (int m = 0; m < 4; ++m) {
                 const int t = 4 + rw + 4 * m;
-                const int i = kTileI[t], j = kTileJ[t];
+                const int i = tile_i(t), j = tile_j(t);
                 const bool isP = t >= 10;
                 const f32x4 x = ap_mask(ap_tile<K, V>(smem, i, j, isP ? qb : L::KB, l16, q4), i == j, isP, l16, q4);
                 if (isP) lds_st<bf16x4>(smem, L::PB + 2 * ((16 * i + l16) * L::CP + 16 * j + 4 * q4), f32x4_to_bf16(x));
@@ -635,45 +640,14 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         } else {
             exact_ap<K, V>(smem, p, ch, c0, len, qb, tid);
         }
-        // prefetch the next chunk (T, WY and phase E of the next iteration
-        // hide the latency)
+        __syncthreads();  // ------------------------------------------ B3
+
+        // the next chunk's g, q, k, beta: issued while the state waves build
+        // T's off-diagonal blocks (the issue stalls until the CU's memory
+        // pipeline has room); T2, WY and phase E1 hide the latency
         if (it + 1 < nc) {
             load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
             load_keys<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
-        }
-        __syncthreads();  // ------------------------------------------ B3
-
-        // ---- T2: block column j = rw of T by fp32 MFMA,
-        // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, i = j+1..3. T_kj (k > j)
-        // stay in registers in the MFMA result layout and feed later
-        // products as B operands (k index 4*q4 + e in step e).
-        if (rw < 3) {
-            const int j = rw;
-            f32x4 Tc[4];
-            for (int i = 1; i < 4; ++i) {
-                if (i <= j) continue;
-                f32x4 X = {0, 0, 0, 0};
-                for (int st = 0; st < 4; ++st) {  // k = j: T_jj from AB
-                    const float a = lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * st + q4));
-                    const float b = lds_ld<float>(smem, L::AB + 4 * ((16 * j + 4 * st + q4) * L::AP + 16 * j + l16));
-                    X = mfma_f32(a, b, X);
-                }
-                for (int kb = 1; kb < 3; ++kb) {
-                    if (kb <= j || kb >= i) continue;
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * kb + 4 * q4 + e));
-                        X = mfma_f32(a, Tc[kb][e], X);
-                    }
-                }
-                f32x4 Y = {0, 0, 0, 0};
-                for (int e = 0; e < 4; ++e) {
-                    const float a = -lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * i + 4 * q4 + e));
-                    Y = mfma_f32(a, X[e], Y);
-                }
-                Tc[i] = Y;
-                for (int e = 0; e < 4; ++e)
-                    lds_st<__bf16>(smem, L::TB + 2 * ((16 * i + 4 * q4 + e) * L::CP + 16 * j + l16), (__bf16)Y[e]);
-            }
         }
         __syncthreads();  // ------------------------------------------ B4
 
@@ -722,6 +696,11 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int it = 0; it < NRT; ++it)
                 for (int jt = 0; jt < NCT; ++jt)
                     for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16];
+            // complete these loads here: left outstanding into the chunk
+            // loop, they make every later write of S wait on the vector
+            // memory counter, which then also waits for the v, w prefetch
+            for (int it = 0; it < NRT; ++it)
+                for (int jt = 0; jt < NCT; ++jt) asm volatile("" ::"v"(S[it][jt]));
         } else {
             for (int it = 0; it < NRT; ++it)
                 for (int jt = 0; jt < NCT; ++jt) S[it][jt] = f32x4{0, 0, 0, 0};
@@ -735,7 +714,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int z = opaque_zero();
         char *smem = smem0 + z;
         const int tid = tid0 + z;
-        const int lane = tid & 63, rw = tid >> 6, rt = tid;
+        const int lane = tid & 63, rw = __builtin_amdgcn_readfirstlane(tid >> 6), rt = tid;
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
         const int64_t c0 = ch.tb + (int64_t)it * CH;
@@ -787,7 +766,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                 if (row < lenp)
                     for (int jt = 0; jt < NCT; ++jt)
                         *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
-                            f32x4_to_bf16(Y[i][jt]);
+                            f32x4_to_bf16(Y[i][jt] * p.scale);
             }
         }
         __syncthreads();  // ------------------------------------------ B1
@@ -821,31 +800,55 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         if (!act) break;
 
         // ---- AP + T1: A's diagonal tile rw, then its block of T
-        f32x4 dblk;
         if (lds_ld<int>(smem, L::FL) == 0) {
             const f32x4 x = ap_mask(ap_tile<K, V>(smem, rw, rw, L::KB, l16, q4), true, false, l16, q4);
             lds_st<f32x4>(smem, L::AB + 4 * ((16 * rw + l16) * L::AP + 16 * rw + 4 * q4), x);
-            dblk = t1_block<K, V>(smem, rw, l16, q4);
         } else {
             exact_ap<K, V>(smem, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
-            dblk = t1_block<K, V>(smem, rw, l16, q4);
         }
-        __syncthreads();  // ------------------------------------------ B3
-
-        // T's diagonal block in bf16, the zero blocks (0,1) and (2,3) that
-        // the WY products read, and w v of this chunk (row-major)
-        for (int e = 0; e < 4; ++e)
-            lds_st<__bf16>(smem, L::TB + 2 * ((16 * rw + 4 * q4 + e) * L::CP + 16 * rw + l16), (__bf16)dblk[e]);
-        if (rw == 0 || rw == 2) {
-            const int rr = lane >> 2, cc = (lane & 3) * 4;
-            lds_st<uint64_t>(smem, L::TB + 2 * ((16 * rw + rr) * L::CP + 16 * rw + 16 + cc), 0ull);
-        }
+        t1_block<K, V>(smem, rw, l16, q4);
+        // w v of this chunk, row-major
         {
             const bf16x8 zero = {};
             for (int i = 0; i < RPTV; ++i) {
                 const int r = emv.row0 + i;
                 const f32x8 wv = bf16x8_to_f32(r < len ? vr[i] : zero) * bf16x8_to_f32(wr[i]);
                 lds_st<bf16x8>(smem, L::WV + 2 * (r * L::VP + emv.c0), f32x8_to_bf16(wv));
+            }
+        }
+        __syncthreads();  // ------------------------------------------ B3
+
+
+        // ---- T2: block column j = rw of T by fp32 MFMA,
+        // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, i = j+1..3. T_kj (k > j)
+        // stay in registers in the MFMA result layout and feed later
+        // products as B operands (k index 4*q4 + e in step e).
+        if (rw < 3) {
+            const int j = rw;
+            f32x4 Tc[4];
+            for (int i = 1; i < 4; ++i) {
+                if (i <= j) continue;
+                f32x4 X = {0, 0, 0, 0};
+                for (int st = 0; st < 4; ++st) {  // k = j: T_jj from AB
+                    const float a = lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * st + q4));
+                    const float b = lds_ld<float>(smem, L::AB + 4 * ((16 * j + 4 * st + q4) * L::AP + 16 * j + l16));
+                    X = mfma_f32(a, b, X);
+                }
+                for (int kb = 1; kb < 3; ++kb) {
+                    if (kb <= j || kb >= i) continue;
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * kb + 4 * q4 + e));
+                        X = mfma_f32(a, Tc[kb][e], X);
+                    }
+                }
+                f32x4 Y = {0, 0, 0, 0};
+                for (int e = 0; e < 4; ++e) {
+                    const float a = -lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * i + 4 * q4 + e));
+                    Y = mfma_f32(a, X[e], Y);
+                }
+                Tc[i] = Y;
+                for (int e = 0; e < 4; ++e)
+                    lds_st<__bf16>(smem, L::TB + 2 * ((16 * i + 4 * q4 + e) * L::CP + 16 * j + l16), (__bf16)Y[e]);
             }
         }
         __syncthreads();  // ------------------------------------------ B4
@@ -899,6 +902,11 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     // P's blocks above the diagonal stay zero for the whole chain (ordered
     // before any use by the first barrier)
     for (int i = tid; i < CH * L::CP / 2; i += NTHR) lds_st<uint32_t>(smem, L::PB + 4 * i, 0u);
+    // T's blocks (0,1) and (2,3), read by the WY products, stay zero too
+    if (tid < 128) {
+        const int b = tid >> 6, rr = (tid >> 2) & 15, cc = (tid & 3) * 4;
+        lds_st<uint64_t>(smem, L::TB + 2 * ((32 * b + rr) * L::CP + 32 * b + 16 + cc), 0ull);
+    }
 
     if (tid >= NROLE) key_role<K, V>(smem, p, ch, tid, nc);
     else state_role<K, V>(smem, p, ch, tid, nc);
