@@ -459,24 +459,28 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
 // ---------------------------------------------------------------- phase T1 --
 // Diagonal block i of T = (I + A)^{-1} by forward substitution,
 // T_rc = delta_rc - sum_{s<r} A_rs T_sc: lane l16 builds column l16 (every
-// lane group redundantly), reading row r of A as a broadcast when it is
-// needed. The block is written over A's block in AB (fp32) and into TB
-// (bf16); lane group q4 writes rows 4 q4 .. 4 q4 + 3.
+// lane group redundantly) from the block's rows read as broadcasts. The
+// block is written over A's block in AB (fp32) and into TB (bf16); lane
+// group q4 writes rows 4 q4 .. 4 q4 + 3.
 template <int K, int V>
 __device__ __forceinline__ void t1_block(char *smem, int i, int l16, int q4)
 {
     using L = Lds<K, V>;
     const int d0 = 16 * i;
+    // the strictly lower triangle first (one wait), then a pure FMA chain
+    float a[16][16];
+    for (int r = 1; r < 16; ++r)
+        for (int s4 = 0; s4 < r; s4 += 4) {
+            const f32x4 x = lds_ld<f32x4>(smem, L::AB + 4 * ((d0 + r) * L::AP + d0 + s4));
+            for (int e = 0; e < 4; ++e) a[r][s4 + e] = x[e];
+        }
     float t[16];
     t[0] = l16 == 0 ? 1.0f : 0.0f;
     for (int r = 1; r < 16; ++r) {
         float acc0 = 0.0f, acc1 = 0.0f;
-        for (int s4 = 0; s4 < r; s4 += 4) {
-            const f32x4 x = lds_ld<f32x4>(smem, L::AB + 4 * ((d0 + r) * L::AP + d0 + s4));
-            for (int e = 0; e < 4 && s4 + e < r; ++e) {
-                if (e & 1) acc1 = fmaf(x[e], t[s4 + e], acc1);
-                else acc0 = fmaf(x[e], t[s4 + e], acc0);
-            }
+        for (int s2 = 0; s2 < r; ++s2) {
+            if (s2 & 1) acc1 = fmaf(a[r][s2], t[s2], acc1);
+            else acc0 = fmaf(a[r][s2], t[s2], acc0);
         }
         t[r] = (r == l16 ? 1.0f : 0.0f) - (acc0 + acc1);
     }
@@ -627,19 +631,14 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             lds_st<f32x4>(smem, L::GAM + 4 * (c0k + 4), f32x4{egl[4], egl[5], egl[6], egl[7]});
         }
 
-        // ---- AP: the 16 tiles that are not A's diagonal, four per key wave
+        // ---- AP + T1: A's diagonal tile rw, then its block of T
         if (lds_ld<int>(smem, L::FL) == 0) {
-            for (int m = 0; m < 4; ++m) {
-                const int t = 4 + rw + 4 * m;
-                const int i = tile_i(t), j = tile_j(t);
-                const bool isP = t >= 10;
-                const f32x4 x = ap_mask(ap_tile<K, V>(smem, i, j, isP ? qb : L::KB, l16, q4), i == j, isP, l16, q4);
-                if (isP) lds_st<bf16x4>(smem, L::PB + 2 * ((16 * i + l16) * L::CP + 16 * j + 4 * q4), f32x4_to_bf16(x));
-                else lds_st<f32x4>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * q4), x);
-            }
+            const f32x4 x = ap_mask(ap_tile<K, V>(smem, rw, rw, L::KB, l16, q4), true, false, l16, q4);
+            lds_st<f32x4>(smem, L::AB + 4 * ((16 * rw + l16) * L::AP + 16 * rw + 4 * q4), x);
         } else {
             exact_ap<K, V>(smem, p, ch, c0, len, qb, tid);
         }
+        t1_block<K, V>(smem, rw, l16, q4);
         __syncthreads();  // ------------------------------------------ B3
 
         // the next chunk's g, q, k, beta: issued while the state waves build
@@ -648,6 +647,8 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         if (it + 1 < nc) {
             load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
             load_keys<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
+        } else {
+            R = RawChunk<RPT>{};  // ends the live range of this chunk's values here
         }
         __syncthreads();  // ------------------------------------------ B4
 
@@ -721,53 +722,28 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const bool act = it < nc;
         const int len = act ? chunk_len(c0, ch.te) : 0;
 
-        // ---- S, first half (chunk it - 1): U = wy_u - wy_w S, then the
-        // output transposed, O^T = S^T QH^T + U^T P^T, stored as 4
-        // consecutive values of an output row per lane
-        bf16x8 Ub[2][NCT];
+        // ---- S, first half (chunk it - 1): U = wy_u - wy_w S. S as bf16
+        // operands: k slab ks holds state rows {32ks + 4q4 + e} then
+        // {32ks + 16 + 4q4 + e}, e = 0..3; LDS operands are read with the
+        // same k order, and U as bf16 operands (Ub) in the same way over
+        // tokens.
+        bf16x8 Ub[2][NCT], Sb[NKS][NCT];
         if (it > 0) {
-            const int64_t cp = c0 - CH;
-            const int lenp = chunk_len(cp, ch.te);
-            const int qbp = L::QH + ((it - 1) & 1) * L::QH_SZ;
-            // S as bf16 operands: k slab ks holds state rows {32ks + 4q4 + e}
-            // then {32ks + 16 + 4q4 + e}, e = 0..3; LDS operands are read
-            // with the same k order.
-            bf16x8 Sb[NKS][NCT];
             for (int ks = 0; ks < NKS; ++ks)
                 for (int jt = 0; jt < NCT; ++jt)
                     Sb[ks][jt] = cat4(f32x4_to_bf16(S[2 * ks][jt]), f32x4_to_bf16(S[2 * ks + 1][jt]));
-            f32x4 Y[4][NCT];
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * i + l16;
-                for (int jt = 0; jt < NCT; ++jt) Y[i][jt] = f32x4{0, 0, 0, 0};
                 for (int ks = 0; ks < NKS; ++ks) {
                     const int cA = 32 * ks + 4 * q4, cB = cA + 16;
                     const bf16x8 aw = cat4(lds_ld<bf16x4>(smem, L::WYW + 2 * (row * L::KP + cA)),
                                            lds_ld<bf16x4>(smem, L::WYW + 2 * (row * L::KP + cB)));
-                    const bf16x8 bq = cat4(lds_ld<bf16x4>(smem, qbp + 2 * (row * L::KP + cA)),
-                                           lds_ld<bf16x4>(smem, qbp + 2 * (row * L::KP + cB)));
-                    for (int jt = 0; jt < NCT; ++jt) {
-                        U[i][jt] = mfma_bf16(aw, Sb[ks][jt], U[i][jt]);
-                        Y[i][jt] = mfma_bf16(Sb[ks][jt], bq, Y[i][jt]);
-                    }
+                    for (int jt = 0; jt < NCT; ++jt) U[i][jt] = mfma_bf16(aw, Sb[ks][jt], U[i][jt]);
                 }
             }
             for (int ks = 0; ks < 2; ++ks)
                 for (int jt = 0; jt < NCT; ++jt)
                     Ub[ks][jt] = cat4(f32x4_to_bf16(U[2 * ks][jt]), f32x4_to_bf16(U[2 * ks + 1][jt]));
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * i + l16;
-                for (int ks = 0; ks <= (i >> 1); ++ks) {
-                    const int cA = 32 * ks + 4 * q4, cB = cA + 16;
-                    const bf16x8 bp = cat4(lds_ld<bf16x4>(smem, L::PB + 2 * (row * L::CP + cA)),
-                                           lds_ld<bf16x4>(smem, L::PB + 2 * (row * L::CP + cB)));
-                    for (int jt = 0; jt < NCT; ++jt) Y[i][jt] = mfma_bf16(Ub[ks][jt], bp, Y[i][jt]);
-                }
-                if (row < lenp)
-                    for (int jt = 0; jt < NCT; ++jt)
-                        *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
-                            f32x4_to_bf16(Y[i][jt] * p.scale);
-            }
         }
         __syncthreads();  // ------------------------------------------ B1
 
@@ -777,10 +753,36 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const EMap<V> emv(rt);
         if (act) load_values<V, RPTV>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0);
 
-        // ---- S, second half: S <- diag(2^G_last) S + KT^T U. KT^T operands
-        // come from transpose reads of the row-major KT, tokens in the same
-        // permuted order as Ub.
+        // ---- S, second half: the output, computed transposed,
+        // O^T = scale (S^T QH^T + U^T P^T), stored as 4 consecutive values
+        // of an output row per lane; then S <- diag(2^G_last) S + KT^T U,
+        // with KT^T operands from transpose reads of the row-major KT
+        // (tokens in the permuted order of Ub).
         if (it > 0) {
+            const int64_t cp = c0 - CH;
+            const int lenp = chunk_len(cp, ch.te);
+            const int qbp = L::QH + ((it - 1) & 1) * L::QH_SZ;
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * i + l16;
+                f32x4 Y[NCT];
+                for (int jt = 0; jt < NCT; ++jt) Y[jt] = f32x4{0, 0, 0, 0};
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int cA = 32 * ks + 4 * q4, cB = cA + 16;
+                    const bf16x8 bq = cat4(lds_ld<bf16x4>(smem, qbp + 2 * (row * L::KP + cA)),
+                                           lds_ld<bf16x4>(smem, qbp + 2 * (row * L::KP + cB)));
+                    for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Sb[ks][jt], bq, Y[jt]);
+                }
+                for (int ks = 0; ks <= (i >> 1); ++ks) {
+                    const int cA = 32 * ks + 4 * q4, cB = cA + 16;
+                    const bf16x8 bp = cat4(lds_ld<bf16x4>(smem, L::PB + 2 * (row * L::CP + cA)),
+                                           lds_ld<bf16x4>(smem, L::PB + 2 * (row * L::CP + cB)));
+                    for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Ub[ks][jt], bp, Y[jt]);
+                }
+                if (row < lenp)
+                    for (int jt = 0; jt < NCT; ++jt)
+                        *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
+                            f32x4_to_bf16(Y[jt] * p.scale);
+            }
             for (int rtile = 0; rtile < NRT; ++rtile) {
                 const f32x4 gam = lds_ld<f32x4>(smem, L::GAM + 4 * (16 * rtile + 4 * q4));
                 bf16x8 ak[2];
@@ -799,14 +801,20 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         __syncthreads();  // ------------------------------------------ B2
         if (!act) break;
 
-        // ---- AP + T1: A's diagonal tile rw, then its block of T
+        // ---- AP: the 16 tiles that are not A's diagonal, four per state wave
         if (lds_ld<int>(smem, L::FL) == 0) {
-            const f32x4 x = ap_mask(ap_tile<K, V>(smem, rw, rw, L::KB, l16, q4), true, false, l16, q4);
-            lds_st<f32x4>(smem, L::AB + 4 * ((16 * rw + l16) * L::AP + 16 * rw + 4 * q4), x);
+            const int qb = L::QH + (it & 1) * L::QH_SZ;
+            for (int m = 0; m < 4; ++m) {
+                const int t = 4 + rw + 4 * m;
+                const int i = tile_i(t), j = tile_j(t);
+                const bool isP = t >= 10;
+                const f32x4 x = ap_mask(ap_tile<K, V>(smem, i, j, isP ? qb : L::KB, l16, q4), i == j, isP, l16, q4);
+                if (isP) lds_st<bf16x4>(smem, L::PB + 2 * ((16 * i + l16) * L::CP + 16 * j + 4 * q4), f32x4_to_bf16(x));
+                else lds_st<f32x4>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * q4), x);
+            }
         } else {
             exact_ap<K, V>(smem, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
         }
-        t1_block<K, V>(smem, rw, l16, q4);
         // w v of this chunk, row-major
         {
             const bf16x8 zero = {};
