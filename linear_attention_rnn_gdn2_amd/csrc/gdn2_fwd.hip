@@ -511,6 +511,10 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         const EMap<K> em(tid & (NROLE - 1));
         load_decay<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hv, em.row0, em.c0);
         load_keys<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hk, ch.hv, em.row0, em.c0);
+        // complete the first chunk's loads before the loop, so that inside
+        // it the vector memory counter only tracks the in-loop prefetch,
+        // issued g first (a wait for g then leaves q, k, beta in flight)
+        for (int i = 0; i < RPT; ++i) asm volatile("" ::"v"(R.q[i]), "v"(R.k[i]), "v"(R.b[i]), "v"(R.g[i][0]), "v"(R.g[i][1]));
     }
 
     char *const smem0 = smem;
@@ -916,7 +920,10 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
         lds_st<uint64_t>(smem, L::TB + 2 * ((32 * b + rr) * L::CP + 32 * b + 16 + cc), 0ull);
     }
 
-    if (tid >= NROLE) key_role<K, V>(smem, p, ch, tid, nc);
+    // a wave-uniform test, so that the two roles are separate branches and
+    // not one exec-masked instruction stream (whose wait-counter analysis
+    // would mix the roles' outstanding loads)
+    if (__builtin_amdgcn_readfirstlane(tid) >= NROLE) key_role<K, V>(smem, p, ch, tid, nc);
     else state_role<K, V>(smem, p, ch, tid, nc);
 }
 
