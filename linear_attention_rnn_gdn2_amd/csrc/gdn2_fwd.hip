@@ -4,27 +4,31 @@
 // chain and walks its 64-token chunks in order. The waves have two roles:
 //
 //   state waves 0-3  hold the K x V float32 state in registers (result layout
-//                    of v_mfma_f32_16x16x32_bf16, V split four ways), invert
-//                    (I + A) and run the sequential state pass;
+//                    of v_mfma_f32_16x16x32_bf16, V split four ways), build
+//                    the off-diagonal A/P tiles and T's off-diagonal blocks,
+//                    and run the sequential state pass;
 //   key waves 4-7    hold the next chunk's raw q, k, beta, g in registers
-//                    (prefetched), build the decay factors and MFMA operands,
-//                    and the pseudo-keys.
+//                    (prefetched; key wave w owns K/4 channels over all 64
+//                    rows), build the decay factors and MFMA operands, A's
+//                    diagonal tiles with their inverses, and the pseudo-keys.
 //
 // Per chunk (rows r, s are positions in the chunk; G = inclusive in-chunk
 // cumulative sum of the log-decay g per key channel, kept in log2 units;
 // S = state entering the chunk):
 //
-//   E   cumulative sum of g (in-thread + wave DPP + LDS exchange of tile
-//       totals), then the operands  KB = beta k 2^G,  QH = q 2^G,
-//       RR = k 2^-G,  KT = k 2^(G_last - G)  (bf16, row-major in LDS)
+//   E   cumulative sum of g over the chunk inside each key wave (in-thread,
+//       DPP row scans, permlane row swaps), then the operands
+//       KB = beta k 2^G,  QH = q 2^G,  RR = k 2^-G,  KT = k 2^(G_last - G)
+//       (bf16, row-major in LDS)
 //   AP  A_rs = sum_c KB_rc RR_sc   (s < r),   P_rs = sum_c QH_rc RR_sc  (s <= r)
 //       on MFMA. 2^G_r 2^-G_s is exp(G_r - G_s) with one reference per
 //       chunk; it is used for every channel whose |G| stays within 2^120.
 //       Channels beyond that (extreme decay) get RR = 0 and their share of
 //       A and P is added by an exact per-pair evaluation of exp(G_r - G_s).
-//   T   T = (I + A)^{-1}, float32: diagonal 16x16 blocks by forward
-//       substitution, then the block columns by fp32 MFMA chains
-//       T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
+//   T   T = (I + A)^{-1} in float32: diagonal 16x16 blocks by forward
+//       substitution, then the block columns
+//       T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj by MFMA on float32 values
+//       split into high and low bf16 parts.
 //   WY  wy_w = T KB,  wy_u = T (w v)                              (bf16 MFMA)
 //   S   U = wy_u - wy_w S;  O = scale (QH S + P U);
 //       S <- diag(2^G_last) S + KT^T U                             (bf16 MFMA)
@@ -106,6 +110,27 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
 }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A float32 4-vector as the sum of two bf16 4-vectors (high part rounded to
+// nearest even, low part the rounded remainder).
+struct Split4 {
+    bf16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(f32x4 x)
+{
+    Split4 r;
+    r.hi = __builtin_convertvector(x, bf16x4);
+    r.lo = __builtin_convertvector(x - __builtin_convertvector(r.hi, f32x4), bf16x4);
+    return r;
+}
+// c + a b for float32 operands given as hi + lo bf16 parts: lo hi + hi lo +
+// hi hi on v_mfma_f32_16x16x16_bf16 (small terms first).
+__device__ __forceinline__ f32x4 mfma3(Split4 a, Split4 b, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+}
+
 // An opaque zero, produced inside a loop body, keeps LDS address arithmetic
 // in that body: without it the compiler hoists dozens of loop-invariant
 // addresses out of the chunk loop and pins a register for each.
@@ -118,7 +143,7 @@ __device__ __forceinline__ int opaque_zero()
 
 // The 20 lower-triangular 16x16 tiles of A (0..9) and P (10..19), each as
 // (row tile i, column tile j). Tiles 0-3 are A's diagonal tiles, taken by
-// the state waves so that each can invert its block at once; the key waves
+// the key waves so that each can invert its block at once; the state waves
 // take tiles 4..19.
 // Packed 2 bits per tile (no memory access, so no wait on the vector
 // memory counter, which also counts the outstanding prefetch):
@@ -155,18 +180,18 @@ struct Lds {
     static constexpr int AB_SZ = cmax(CH * AP * 4, CH * KP * 2);
     static constexpr int PB = AB + AB_SZ;                          // P bf16              [64][CP]  AP -> S
     static constexpr int GAM = PB + CH * CP * 2;                   // 2^G_last fp32       [K]       E -> S
-    static constexpr int TT = GAM + K * 4;                         // tile totals of G    [4][K]
-    static constexpr int TX = TT + 4 * K * 4;                      // tile max |G - G(tile start)| [4][K]
-    static constexpr int XF = TX + 4 * K * 4;                      // exact-channel flags [K] int
+    static constexpr int XF = GAM + K * 4;                         // exact-channel flags [K] int
     static constexpr int XL = XF + K * 4;                          // exact-channel list  [K] int
-    static constexpr int FL = XL + K * 4;                          // chunk flag, exact-channel count
-    static constexpr int TOTAL = FL + 16;
+    static constexpr int FL = XL + K * 4;                          // per key wave: any exact channel [4] int
+    static constexpr int XN = FL + 16;                             // exact-channel count int
+    static constexpr int TOTAL = XN + 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// Phase-E thread map of one role (4 waves over a 64-row x NC-column chunk,
-// 8 columns per thread): wave w owns rows [16w, 16w + 16); inside a wave the
-// row group varies fastest, so that consecutive lanes write consecutive rows.
+// Value-side thread map of the state waves (4 waves over a 64-row x
+// NC-column chunk, 8 columns per thread): wave w owns rows [16w, 16w + 16);
+// inside a wave the row group varies fastest, so that consecutive lanes
+// write consecutive rows.
 template <int NC>
 struct EMap {
     static constexpr int CG = NC / 8;              // column groups
@@ -255,36 +280,76 @@ __device__ __forceinline__ void load_values(bf16x8 *v, bf16x8 *w, const FwdParam
     }
 }
 
-// Reductions over the RGW consecutive lanes of a row group: DPP quad
-// permutes (and a half-row mirror for 8 lanes).
-template <int RGW>
-__device__ __forceinline__ float group_max(float x)
+// Key-wave thread map for phase E: key wave w owns the K/4 channels
+// [w K/4, (w + 1) K/4) over all 64 rows of the chunk, so that the cumulative
+// sum over the chunk stays inside the wave. lane = rg * NCG + cgl: cgl picks
+// 8 channels, rg a group of RPT consecutive rows. Consecutive lanes hold the
+// channel groups of one row, then of the next row group, so that 16-byte
+// stores to a padded row-major tile fall in distinct banks.
+template <int K>
+struct KMap {
+    static constexpr int NCG = K / 32;     // 8-channel groups per wave
+    static constexpr int NRG = 64 / NCG;   // row groups per wave
+    static constexpr int RPT = CH / NRG;   // rows per thread
+    int rg, cgl, row0, c0;
+    __device__ __forceinline__ explicit KMap(int rt)
+    {
+        const int lane = rt & 63, w = rt >> 6;
+        cgl = lane % NCG;
+        rg = lane / NCG;
+        row0 = rg * RPT;
+        c0 = w * (K / 4) + 8 * cgl;
+    }
+};
+
+template <int D>
+__device__ __forceinline__ float dpp_shr(float x)  // row_shr:D, zero shifted in
 {
-    static_assert(RGW == 4 || RGW == 8, "4 or 8 lanes per row group");
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
-    if constexpr (RGW == 8)
-        x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)));
-    return x;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xf, 0xf, false));
+}
+template <int D>
+__device__ __forceinline__ float dpp_ror(float x)  // row_ror:D
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + D, 0xf, 0xf, false));
+}
+template <int D>
+__device__ __forceinline__ void row_scan_steps(float &s, float &t)
+{
+    if constexpr (D < 16) {
+        s += dpp_shr<D>(s);
+        t += dpp_ror<D>(t);
+        row_scan_steps<2 * D>(s, t);
+    }
 }
 
-// Inclusive prefix sum over the RGW consecutive lanes of a row group
-// (rgl = lane index inside the group).
-template <int RGW>
-__device__ __forceinline__ float group_scan(float x, int rgl)
+// Inclusive prefix sum (incl) and total over the row groups of KMap: the
+// lanes with equal lane % NCG form one sequence in lane order. DPP shifts
+// scan inside each 16-lane row while DPP rotates form the row totals; the
+// totals are carried across rows by permlane16 / permlane32 swaps, which
+// hand every lane the values of both rows of its pair (both halves).
+template <int NCG>
+__device__ __forceinline__ void wave_scan(float x, int lane, float &incl, float &total)
 {
-    if constexpr (RGW == 4) {  // DPP row shifts by 1 and 2 lanes
-        const float o1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
-        if (rgl >= 1) x += o1;
-        const float o2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
-        if (rgl >= 2) x += o2;
-    } else {
-        for (int d = 1; d < RGW; d <<= 1) {
-            const float o = __shfl_up(x, d, 64);
-            if (rgl >= d) x += o;
-        }
-    }
-    return x;
+    float s = x, t = x;
+    row_scan_steps<NCG>(s, t);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    const float ev = __uint_as_float(p16[0]), od = __uint_as_float(p16[1]);
+    if (lane & 16) s += ev;
+    const float pair = ev + od;
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair), false, false);
+    const float lo = __uint_as_float(p32[0]), hi = __uint_as_float(p32[1]);
+    if (lane & 32) s += lo;
+    incl = s;
+    total = lo + hi;
+}
+
+// One bit per lane of each KMap channel group (lanes cgl, cgl + NCG, ...).
+template <int NCG>
+__device__ __forceinline__ uint64_t group_lanes(int cgl)
+{
+    uint64_t m = 0;
+    for (int i = 0; i < 64; i += NCG) m |= 1ull << i;
+    return m << cgl;
 }
 
 // ----------------------------------------------------------- chain context --
@@ -310,6 +375,16 @@ __device__ __forceinline__ f32x4 ap_tile(const char *smem, int i, int j, int xb,
         const bf16x8 b = lds_ld<bf16x8>(smem, xb + 2 * ((16 * i + l16) * L::KP + c8));
         acc = mfma_bf16(a, b, acc);
     }
+    return acc;
+}
+
+// The same tile from per-lane base pointers: rrb addresses RR row 16j + l16,
+// xb the X row 16i + l16, both at column 8 q4.
+template <int K>
+__device__ __forceinline__ f32x4 ap_tile_at(const char *rrb, const char *xb)
+{
+    f32x4 acc = {0, 0, 0, 0};
+    for (int ks = 0; ks < K / 32; ++ks) acc = mfma_bf16(lds_ld<bf16x8>(rrb, 64 * ks), lds_ld<bf16x8>(xb, 64 * ks), acc);
     return acc;
 }
 
@@ -349,7 +424,7 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
             if (f) lds_st<int>(smem, L::XL + 4 * (cnt + __popcll(m & ((1ull << lane) - 1))), c);
             cnt += __popcll(m);
         }
-        if (lane == 0) lds_st<int>(smem, L::FL + 4, cnt);
+        if (lane == 0) lds_st<int>(smem, L::XN, cnt);
     }
     f32x4 acc[3];
     for (int m = 0; m < 3; ++m) {
@@ -369,7 +444,7 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
             lds_st<f32x4>(smem, (isP ? L::PF : L::AB) + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * q4), x);
         }
     }
-    const int nx = lds_ld<int>(smem, L::FL + 4);
+    const int nx = lds_ld<int>(smem, L::XN);
     const int r = tid >> 3, sb = tid & 7;
     float accA[8], accP[8];
     for (int u = 0; u < 8; ++u) accA[u] = accP[u] = 0.0f;
@@ -457,58 +532,62 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
 }
 
 // ---------------------------------------------------------------- phase T1 --
-// Diagonal block i of T = (I + A)^{-1} by forward substitution,
-// T_rc = delta_rc - sum_{s<r} A_rs T_sc: lane l16 builds column l16 (every
-// lane group redundantly) from the block's rows read as broadcasts. The
-// block is written over A's block in AB (fp32) and into TB (bf16); lane
-// group q4 writes rows 4 q4 .. 4 q4 + 3.
+// Diagonal block of T = (I + A)^{-1} (blk: the block's first element in AB):
+// lane l16 solves column l16 (every lane group redundantly) by right-looking
+// forward substitution: as soon as t_c is known, its term is folded into
+// every later row's accumulator, so that the dependent chain is one FMA and
+// one subtraction per row. The block's rows are read as broadcasts, all in
+// flight before the first use. The result is written over A's block in AB
+// (fp32, st_ab) and into TB (bf16, st_tb): lane group q4 writes rows
+// 4 q4 .. 4 q4 + 3 of column l16.
 template <int K, int V>
-__device__ __forceinline__ void t1_block(char *smem, int i, int l16, int q4)
+__device__ __forceinline__ void t1_block(const char *blk, char *st_ab, char *st_tb, int l16, int q4)
 {
     using L = Lds<K, V>;
-    const int d0 = 16 * i;
-    // the strictly lower triangle first (one wait), then a pure FMA chain
-    float a[16][16];
+    constexpr int RA = 4 * L::AP, RC = 2 * L::CP;
+    f32x4 a[16][4];
     for (int r = 1; r < 16; ++r)
-        for (int s4 = 0; s4 < r; s4 += 4) {
-            const f32x4 x = lds_ld<f32x4>(smem, L::AB + 4 * ((d0 + r) * L::AP + d0 + s4));
-            for (int e = 0; e < 4; ++e) a[r][s4 + e] = x[e];
-        }
-    float t[16];
-    t[0] = l16 == 0 ? 1.0f : 0.0f;
-    for (int r = 1; r < 16; ++r) {
-        float acc0 = 0.0f, acc1 = 0.0f;
-        for (int s2 = 0; s2 < r; ++s2) {
-            if (s2 & 1) acc1 = fmaf(a[r][s2], t[s2], acc1);
-            else acc0 = fmaf(a[r][s2], t[s2], acc0);
-        }
-        t[r] = (r == l16 ? 1.0f : 0.0f) - (acc0 + acc1);
+        for (int c4 = 0; 4 * c4 < r; ++c4) a[r][c4] = lds_ld<f32x4>(blk, r * RA + 16 * c4);
+    for (int r = 1; r < 16; ++r)
+        for (int c4 = 0; 4 * c4 < r; ++c4) asm volatile("" ::"v"(a[r][c4]));
+    float acc[16], t[16];
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int c = 0; c < 16; ++c) {
+        t[c] = (c == l16 ? 1.0f : 0.0f) - acc[c];
+        for (int r = c + 1; r < 16; ++r) acc[r] = fmaf(a[r][c >> 2][c & 3], t[c], acc[r]);
     }
     f32x4 out;
     for (int e = 0; e < 4; ++e)
         out[e] = q4 == 0 ? t[e] : q4 == 1 ? t[4 + e] : q4 == 2 ? t[8 + e] : t[12 + e];
     for (int e = 0; e < 4; ++e) {
-        lds_st<float>(smem, L::AB + 4 * ((d0 + 4 * q4 + e) * L::AP + d0 + l16), out[e]);
-        lds_st<__bf16>(smem, L::TB + 2 * ((d0 + 4 * q4 + e) * L::CP + d0 + l16), (__bf16)out[e]);
+        lds_st<float>(st_ab, e * RA, out[e]);
+        lds_st<__bf16>(st_tb, e * RC, (__bf16)out[e]);
     }
 }
 
+// Whether any key wave flagged an exact channel in this chunk.
+__device__ __forceinline__ bool any_exact(const char *fl)
+{
+    const i32x4 f = *reinterpret_cast<const i32x4 *>(fl);
+    return (f[0] | f[1] | f[2] | f[3]) != 0;
+}
+
 // ------------------------------------------------------------- key waves --
-// Barrier sequence per iteration (must match state_role): B1, B2, then
-// (exact_ap), B3, B4, B5.
+// Barrier sequence per iteration (must match state_role): B2, then
+// (exact_ap), B3, B4, B5. LDS addressing as in state_role: per-lane bases
+// plus compile-time constants.
 template <int K, int V>
 __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const Chain &ch, int tid, int nc)
 {
     using L = Lds<K, V>;
-    constexpr int CGK = K / 8;              // 8-channel groups along K
-    constexpr int RPT = CH * CGK / NROLE;   // rows per thread
-    constexpr int RGW = 64 / CGK;           // row groups per wave
+    using M = KMap<K>;
+    constexpr int RPT = M::RPT;
     constexpr int NCTK = K / 64;            // -wy_w channel tiles per key wave
-    static_assert(RPT * RGW == 16, "a key wave covers one 16-row tile");
+    constexpr int RK = 2 * L::KP, RC = 2 * L::CP, RA = 4 * L::AP;  // row pitches (bytes)
 
     RawChunk<RPT> R;
     if (nc > 0) {
-        const EMap<K> em(tid & (NROLE - 1));
+        const M em(tid & (NROLE - 1));
         load_decay<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hv, em.row0, em.c0);
         load_keys<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hk, ch.hv, em.row0, em.c0);
         // complete the first chunk's loads before the loop, so that inside
@@ -522,78 +601,67 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
     for (int it = 0; it <= nc; ++it) {
         // lane-derived values are recomputed per chunk (see opaque_zero)
         const int z = opaque_zero();
-        char *smem = smem0 + z;
+        char *const sm = smem0 + z;
         const int tid = tid0 + z;
         const int lane = tid & 63, rw = __builtin_amdgcn_readfirstlane((tid >> 6) & 3), rt = tid & (NROLE - 1);
         const int l16 = lane & 15, q4 = lane >> 4;
-        const EMap<K> em(rt);
-        const int rgl = em.rgl, row0 = em.row0, c0k = em.c0;
+        const M em(rt);
+        const int row0 = em.row0, c0k = em.c0;
+        const int o_e = row0 * RK + 2 * c0k;  // rows row0 + i, channels c0k .. c0k + 7
+        const int o_c = 4 * c0k;              // fp32 per-channel records
         const int64_t c0 = ch.tb + (int64_t)it * CH;
         const bool act = it < nc;
         const int len = act ? chunk_len(c0, ch.te) : 0;
         const int qb = L::QH + (it & 1) * L::QH_SZ;
+        char *const b_c = sm + o_c;
 
-        // ---- E1: tile-local cumulative log2 decay, tile totals and spans
-        float G[RPT][8];
+        // ---- E: cumulative log2 decay over the chunk (in-thread over RPT
+        // rows, then across the wave's row groups), exact-channel flags and
+        // the MFMA operands  KB = beta k 2^G,  QH = q 2^G,  RR = k 2^-G,
+        // KT = k 2^(G_last - G)
+        bf16x8 ktr[RPT];
+        f32x8 egl;
         if (act) {
+            // all of this chunk's raw inputs are complete here: the next
+            // chunk's g is issued below, and a later wait for q, k, beta
+            // would otherwise also wait for it
+            for (int i = 0; i < RPT; ++i) asm volatile("" ::"v"(R.q[i]), "v"(R.k[i]), "v"(R.b[i]), "v"(R.g[i][0]), "v"(R.g[i][1]));
+            float G[RPT][8], glast[8];
             for (int i = 0; i < RPT; ++i)
                 for (int j = 0; j < 8; ++j)
                     G[i][j] = (i ? G[i - 1][j] : 0.0f) +
                               (row0 + i < len ? (j < 4 ? R.g[i][0][j] : R.g[i][1][j - 4]) * LOG2E : 0.0f);
-            float tx[8];
+            // the next chunk's g (this chunk's is consumed): a whole chunk
+            // period ahead of its use
+            if (it + 1 < nc) load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
             for (int j = 0; j < 8; ++j) {
-                const float tot = G[RPT - 1][j];
-                const float excl = group_scan<RGW>(tot, rgl) - tot;
-                float m = 0.0f;
-                for (int i = 0; i < RPT; ++i) {
-                    G[i][j] += excl;
-                    m = fmaxf(m, fabsf(G[i][j]));
-                }
-                tx[j] = group_max<RGW>(m);
+                float incl, tot;
+                wave_scan<M::NCG>(G[RPT - 1][j], lane, incl, tot);
+                const float excl = incl - G[RPT - 1][j];
+                for (int i = 0; i < RPT; ++i) G[i][j] += excl;
+                glast[j] = tot;
             }
-            if (rgl == RGW - 1) {
-                lds_st<f32x4>(smem, L::TT + 4 * (rw * K + c0k), f32x4{G[RPT - 1][0], G[RPT - 1][1], G[RPT - 1][2], G[RPT - 1][3]});
-                lds_st<f32x4>(smem, L::TT + 4 * (rw * K + c0k + 4), f32x4{G[RPT - 1][4], G[RPT - 1][5], G[RPT - 1][6], G[RPT - 1][7]});
+            // a channel is exact if |G| leaves the single-reference range
+            // anywhere in the chunk (NaN counts as extreme)
+            const uint64_t mine = group_lanes<M::NCG>(em.cgl);
+            bool xf[8];
+            uint64_t anyb = 0;
+            for (int j = 0; j < 8; ++j) {
+                bool out = false;
+                for (int i = 0; i < RPT; ++i) out |= !(fabsf(G[i][j]) <= XLIM);
+                const uint64_t b = __ballot(out);
+                xf[j] = (b & mine) != 0;
+                anyb |= b;
             }
-            if (rgl == 0) {
-                lds_st<f32x4>(smem, L::TX + 4 * (rw * K + c0k), f32x4{tx[0], tx[1], tx[2], tx[3]});
-                lds_st<f32x4>(smem, L::TX + 4 * (rw * K + c0k + 4), f32x4{tx[4], tx[5], tx[6], tx[7]});
-            }
-        }
-        __syncthreads();  // ------------------------------------------ B1
-
-        // ---- E3: chunk-relative G, exact-channel flags, operands
-        bf16x8 ktr[RPT];
-        f32x8 egl;
-        if (act) {
-            float base[8], glast[8];
-            bool xf[8], anyx = false;
-            for (int h = 0; h < 2; ++h) {
-                f32x4 acc = {0, 0, 0, 0}, bs = {0, 0, 0, 0}, xm = {0, 0, 0, 0};
-                for (int t = 0; t < 4; ++t) {
-                    const f32x4 tt = lds_ld<f32x4>(smem, L::TT + 4 * (t * K + c0k + 4 * h));
-                    const f32x4 tx = lds_ld<f32x4>(smem, L::TX + 4 * (t * K + c0k + 4 * h));
-                    if (t == rw) bs = acc;
-                    for (int e = 0; e < 4; ++e) xm[e] = fmaxf(xm[e], fabsf(acc[e]) + tx[e]);
-                    acc += tt;
-                }
-                for (int e = 0; e < 4; ++e) {
-                    base[4 * h + e] = bs[e];
-                    glast[4 * h + e] = acc[e];
-                    xf[4 * h + e] = !(xm[e] <= XLIM);  // NaN counts as extreme
-                    anyx |= xf[4 * h + e];
-                }
-            }
-            const bool wx = __any(anyx);  // every key wave covers all K channels
-            if (rw == 0 && lane == 0) lds_st<int>(smem, L::FL, wx ? 1 : 0);
-            if (wx && rw == 0 && rgl == 0) {
-                lds_st<i32x4>(smem, L::XF + 4 * c0k, i32x4{xf[0], xf[1], xf[2], xf[3]});
-                lds_st<i32x4>(smem, L::XF + 4 * (c0k + 4), i32x4{xf[4], xf[5], xf[6], xf[7]});
+            const bool wx = anyb != 0;  // wave-uniform: any exact channel of this wave
+            if (lane == 0) lds_st<int>(sm, L::FL + 4 * rw, wx ? 1 : 0);
+            if (em.rg == 0) {
+                lds_st<i32x4>(b_c, L::XF, i32x4{xf[0], xf[1], xf[2], xf[3]});
+                lds_st<i32x4>(b_c, L::XF + 16, i32x4{xf[4], xf[5], xf[6], xf[7]});
             }
             for (int j = 0; j < 8; ++j) egl[j] = ex2(glast[j]);
-            for (int i = 0; i < RPT; ++i)
-                for (int j = 0; j < 8; ++j) G[i][j] += base[j];
             const bf16x8 zero = {};
+            char *const b_e = sm + o_e;
             for (int i = 0; i < RPT; ++i) {
                 const int r = row0 + i;
                 const bool ok = r < len;
@@ -618,9 +686,9 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                         kt[j] = xf[j] ? kf[j] * ex2(glast[j] - G[i][j]) : rr[j] * egl[j];
                     }
                 }
-                lds_st<bf16x8>(smem, L::KB + 2 * (r * L::KP + c0k), f32x8_to_bf16(kb));
-                lds_st<bf16x8>(smem, L::RR + 2 * (r * L::KP + c0k), f32x8_to_bf16(rr));
-                lds_st<bf16x8>(smem, qb + 2 * (r * L::KP + c0k), f32x8_to_bf16(qh));
+                lds_st<bf16x8>(b_e, L::KB + i * RK, f32x8_to_bf16(kb));
+                lds_st<bf16x8>(b_e, L::RR + i * RK, f32x8_to_bf16(rr));
+                lds_st<bf16x8>(b_e, qb + i * RK, f32x8_to_bf16(qh));
                 ktr[i] = f32x8_to_bf16(kt);
             }
         }
@@ -629,27 +697,32 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
 
         // KT and 2^G_last of this chunk: the state waves read the previous
         // chunk's until B2
-        for (int i = 0; i < RPT; ++i) lds_st<bf16x8>(smem, L::KT + 2 * ((row0 + i) * L::KP + c0k), ktr[i]);
-        if (rw == 0 && rgl == 0) {
-            lds_st<f32x4>(smem, L::GAM + 4 * c0k, f32x4{egl[0], egl[1], egl[2], egl[3]});
-            lds_st<f32x4>(smem, L::GAM + 4 * (c0k + 4), f32x4{egl[4], egl[5], egl[6], egl[7]});
+        {
+            char *const b_e = sm + o_e;
+            for (int i = 0; i < RPT; ++i) lds_st<bf16x8>(b_e, L::KT + i * RK, ktr[i]);
+        }
+        if (em.rg == 0) {
+            lds_st<f32x4>(b_c, L::GAM, f32x4{egl[0], egl[1], egl[2], egl[3]});
+            lds_st<f32x4>(b_c, L::GAM + 16, f32x4{egl[4], egl[5], egl[6], egl[7]});
         }
 
         // ---- AP + T1: A's diagonal tile rw, then its block of T
-        if (lds_ld<int>(smem, L::FL) == 0) {
-            const f32x4 x = ap_mask(ap_tile<K, V>(smem, rw, rw, L::KB, l16, q4), true, false, l16, q4);
-            lds_st<f32x4>(smem, L::AB + 4 * ((16 * rw + l16) * L::AP + 16 * rw + 4 * q4), x);
+        if (!any_exact(sm + L::FL)) {
+            const char *const b_k8 = sm + l16 * RK + 16 * q4 + rw * 16 * RK;  // rows 16 rw + l16, columns 8q4
+            const f32x4 x = ap_mask(ap_tile_at<K>(b_k8 + L::RR, b_k8 + L::KB), true, false, l16, q4);
+            lds_st<f32x4>(sm, L::AB + l16 * RA + 16 * q4 + rw * (16 * RA + 64), x);
         } else {
-            exact_ap<K, V>(smem, p, ch, c0, len, qb, tid);
+            exact_ap<K, V>(sm, p, ch, c0, len, qb, tid);
         }
-        t1_block<K, V>(smem, rw, l16, q4);
+        t1_block<K, V>(sm + L::AB + rw * (16 * RA + 64), sm + L::AB + 4 * q4 * RA + 4 * l16 + rw * (16 * RA + 64),
+                       sm + L::TB + 4 * q4 * RC + 2 * l16 + rw * (16 * RC + 32), l16, q4);
         __syncthreads();  // ------------------------------------------ B3
 
-        // the next chunk's g, q, k, beta: issued while the state waves build
-        // T's off-diagonal blocks (the issue stalls until the CU's memory
-        // pipeline has room); T2, WY and phase E1 hide the latency
+        // the next chunk's q, k, beta (its g went out in phase E): issued
+        // while the state waves build T's off-diagonal blocks (the issue
+        // stalls until the CU's memory pipeline has room); WY and the next
+        // phase E hide the latency
         if (it + 1 < nc) {
-            load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
             load_keys<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
         } else {
             R = RawChunk<RPT>{};  // ends the live range of this chunk's values here
@@ -658,20 +731,22 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
 
         // ---- WY: -wy_w^T = -KB^T T^T for this wave's channel tiles, stored
         // row-major (token, channel) as -wy_w
-        for (int jt = 0; jt < NCTK; ++jt) {
-            const int ct = rw * NCTK + jt;
-            bf16x8 ak[2];
-            for (int ks = 0; ks < 2; ++ks) {
-                const int off = L::KB + 2 * ((32 * ks + 8 * q4 + (l16 >> 2)) * L::KP + 16 * ct + 4 * (l16 & 3));
-                ak[ks] = cat4(lds_tr(smem, off), lds_tr(smem, off + 2 * 4 * L::KP));
-            }
-            for (int i = 0; i < 4; ++i) {
-                f32x4 acc = {0, 0, 0, 0};
-                for (int ks = 0; ks <= (i >> 1); ++ks) {
-                    const bf16x8 b = lds_ld<bf16x8>(smem, L::TB + 2 * ((16 * i + l16) * L::CP + 32 * ks + 8 * q4));
-                    acc = mfma_bf16(ak[ks], b, acc);
+        {
+            const char *const b_kbt = sm + (8 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3) + 32 * rw * NCTK;  // KB transpose reads
+            const char *const b_c8 = sm + l16 * RC + 16 * q4;             // T rows 16i + l16, columns 32ks + 8q4
+            char *const b_wy = sm + l16 * RK + 8 * q4 + 32 * rw * NCTK;    // -wy_w stores
+            for (int jt = 0; jt < NCTK; ++jt) {
+                bf16x8 ak[2];
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int o = L::KB + 32 * ks * RK + 32 * jt;
+                    ak[ks] = cat4(lds_tr(b_kbt, o), lds_tr(b_kbt, o + 4 * RK));
                 }
-                lds_st<bf16x4>(smem, L::WYW + 2 * ((16 * i + l16) * L::KP + 16 * ct + 4 * q4), f32x4_to_bf16(-acc));
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 acc = {0, 0, 0, 0};
+                    for (int ks = 0; ks <= (i >> 1); ++ks)
+                        acc = mfma_bf16(ak[ks], lds_ld<bf16x8>(b_c8, L::TB + 16 * i * RC + 64 * ks), acc);
+                    lds_st<bf16x4>(b_wy, L::WYW + 16 * i * RK + 32 * jt, f32x4_to_bf16(-acc));
+                }
             }
         }
         __syncthreads();  // ------------------------------------------ B5
@@ -679,6 +754,11 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
 }
 
 // ----------------------------------------------------------- state waves --
+// LDS addressing in the chunk loops: every access is (per-lane base) +
+// (compile-time constant). The lane parts are loop invariant; the per-chunk
+// opaque zero is added to a handful of base pointers once per chunk, so the
+// constants fold into the instructions' offset fields (and pairs of reads
+// merge) instead of being hoisted out of the loop one register per address.
 template <int K, int V>
 __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const Chain &ch, int tid, int nc)
 {
@@ -689,42 +769,52 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
     constexpr int NCT = VW / 16;  // 16-column tiles per state wave
     constexpr int NRT = K / 16;   // 16-row tiles of the state
     constexpr int NKS = K / 32;   // 32-deep k slabs over K
+    constexpr int RK = 2 * L::KP, RC = 2 * L::CP, RV = 2 * L::VP, RA = 4 * L::AP;  // row pitches (bytes)
 
     // state: rows 16*it + 4*q4 + e, column vbase + 16*jt + l16
     f32x4 S[NRT][NCT];
-    {
+    if (p.h0) {
         const int lane = tid & 63, rw = tid >> 6;
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
-        if (p.h0) {
-            const float *h0 = p.h0 + ((int64_t)ch.n * p.HV + ch.hv) * K * V;
-            for (int it = 0; it < NRT; ++it)
-                for (int jt = 0; jt < NCT; ++jt)
-                    for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16];
-            // complete these loads here: left outstanding into the chunk
-            // loop, they make every later write of S wait on the vector
-            // memory counter, which then also waits for the v, w prefetch
-            for (int it = 0; it < NRT; ++it)
-                for (int jt = 0; jt < NCT; ++jt) asm volatile("" ::"v"(S[it][jt]));
-        } else {
-            for (int it = 0; it < NRT; ++it)
-                for (int jt = 0; jt < NCT; ++jt) S[it][jt] = f32x4{0, 0, 0, 0};
-        }
+        const float *h0 = p.h0 + ((int64_t)ch.n * p.HV + ch.hv) * K * V;
+        for (int it = 0; it < NRT; ++it)
+            for (int jt = 0; jt < NCT; ++jt)
+                for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16];
+        // complete these loads here: left outstanding into the chunk
+        // loop, they make every later write of S wait on the vector
+        // memory counter, which then also waits for the v, w prefetch
+        for (int it = 0; it < NRT; ++it)
+            for (int jt = 0; jt < NCT; ++jt) asm volatile("" ::"v"(S[it][jt]));
+    } else {
+        for (int it = 0; it < NRT; ++it)
+            for (int jt = 0; jt < NCT; ++jt) S[it][jt] = f32x4{0, 0, 0, 0};
     }
     f32x4 U[4][NCT];  // wy_u, then U, of the chunk in the state pass
 
     char *const smem0 = smem;
     const int tid0 = tid;
     for (int it = 0; it <= nc; ++it) {
+        // lane-derived values are recomputed per chunk from an opaque copy
+        // of the thread id (see opaque_zero)
         const int z = opaque_zero();
-        char *smem = smem0 + z;
+        char *const sm = smem0 + z;
         const int tid = tid0 + z;
-        const int lane = tid & 63, rw = __builtin_amdgcn_readfirstlane(tid >> 6), rt = tid;
+        const int lane = tid & 63, rw = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
+        const EMap<V> emv(tid);
+        // per-lane byte offsets of the access patterns
+        const int o_k4 = l16 * RK + 8 * q4;                           // K-pitched rows 16i + l16, columns 32ks + 4q4 (+16)
+        const int o_c4 = l16 * RC + 8 * q4;                           // the same in a 64-column tile
+        const int o_k8 = l16 * RK + 16 * q4;                          // K-pitched rows, columns 32ks + 8q4
+        const int o_c8 = l16 * RC + 16 * q4;                          // 64-column rows, columns 32ks + 8q4
+        const int o_a4 = l16 * RA + 16 * q4;                          // fp32 tile rows 16i + l16, columns 4q4
         const int64_t c0 = ch.tb + (int64_t)it * CH;
         const bool act = it < nc;
         const int len = act ? chunk_len(c0, ch.te) : 0;
+        const char *const b_k4 = sm + o_k4;
+        const char *const b_c4 = sm + o_c4;
 
         // ---- S, first half (chunk it - 1): U = wy_u - wy_w S. S as bf16
         // operands: k slab ks holds state rows {32ks + 4q4 + e} then
@@ -736,25 +826,20 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int ks = 0; ks < NKS; ++ks)
                 for (int jt = 0; jt < NCT; ++jt)
                     Sb[ks][jt] = cat4(f32x4_to_bf16(S[2 * ks][jt]), f32x4_to_bf16(S[2 * ks + 1][jt]));
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * i + l16;
+            for (int i = 0; i < 4; ++i)
                 for (int ks = 0; ks < NKS; ++ks) {
-                    const int cA = 32 * ks + 4 * q4, cB = cA + 16;
-                    const bf16x8 aw = cat4(lds_ld<bf16x4>(smem, L::WYW + 2 * (row * L::KP + cA)),
-                                           lds_ld<bf16x4>(smem, L::WYW + 2 * (row * L::KP + cB)));
+                    const int o = L::WYW + 16 * i * RK + 64 * ks;
+                    const bf16x8 aw = cat4(lds_ld<bf16x4>(b_k4, o), lds_ld<bf16x4>(b_k4, o + 32));
                     for (int jt = 0; jt < NCT; ++jt) U[i][jt] = mfma_bf16(aw, Sb[ks][jt], U[i][jt]);
                 }
-            }
             for (int ks = 0; ks < 2; ++ks)
                 for (int jt = 0; jt < NCT; ++jt)
                     Ub[ks][jt] = cat4(f32x4_to_bf16(U[2 * ks][jt]), f32x4_to_bf16(U[2 * ks + 1][jt]));
         }
-        __syncthreads();  // ------------------------------------------ B1
 
-        // this chunk's v and w (stored as w v after B3; the latency hides
+        // this chunk's v and w (stored as w v after B2; the latency hides
         // behind the rest of phase S, AP and T1)
         bf16x8 vr[RPTV], wr[RPTV];
-        const EMap<V> emv(rt);
         if (act) load_values<V, RPTV>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0);
 
         // ---- S, second half: the output, computed transposed,
@@ -765,21 +850,19 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         if (it > 0) {
             const int64_t cp = c0 - CH;
             const int lenp = chunk_len(cp, ch.te);
-            const int qbp = L::QH + ((it - 1) & 1) * L::QH_SZ;
+            const char *const b_q = b_k4 + ((it - 1) & 1) * L::QH_SZ;
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * i + l16;
                 f32x4 Y[NCT];
                 for (int jt = 0; jt < NCT; ++jt) Y[jt] = f32x4{0, 0, 0, 0};
                 for (int ks = 0; ks < NKS; ++ks) {
-                    const int cA = 32 * ks + 4 * q4, cB = cA + 16;
-                    const bf16x8 bq = cat4(lds_ld<bf16x4>(smem, qbp + 2 * (row * L::KP + cA)),
-                                           lds_ld<bf16x4>(smem, qbp + 2 * (row * L::KP + cB)));
+                    const int o = L::QH + 16 * i * RK + 64 * ks;
+                    const bf16x8 bq = cat4(lds_ld<bf16x4>(b_q, o), lds_ld<bf16x4>(b_q, o + 32));
                     for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Sb[ks][jt], bq, Y[jt]);
                 }
                 for (int ks = 0; ks <= (i >> 1); ++ks) {
-                    const int cA = 32 * ks + 4 * q4, cB = cA + 16;
-                    const bf16x8 bp = cat4(lds_ld<bf16x4>(smem, L::PB + 2 * (row * L::CP + cA)),
-                                           lds_ld<bf16x4>(smem, L::PB + 2 * (row * L::CP + cB)));
+                    const int o = L::PB + 16 * i * RC + 64 * ks;
+                    const bf16x8 bp = cat4(lds_ld<bf16x4>(b_c4, o), lds_ld<bf16x4>(b_c4, o + 32));
                     for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Ub[ks][jt], bp, Y[jt]);
                 }
                 if (row < lenp)
@@ -787,12 +870,14 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                         *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
                             f32x4_to_bf16(Y[jt] * p.scale);
             }
+            const char *const b_kt = sm + (4 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3);  // KT transpose reads
+            const char *const b_g = sm + 16 * q4;
             for (int rtile = 0; rtile < NRT; ++rtile) {
-                const f32x4 gam = lds_ld<f32x4>(smem, L::GAM + 4 * (16 * rtile + 4 * q4));
+                const f32x4 gam = lds_ld<f32x4>(b_g, L::GAM + 64 * rtile);
                 bf16x8 ak[2];
                 for (int ks = 0; ks < 2; ++ks) {
-                    const int off = L::KT + 2 * ((32 * ks + 4 * q4 + (l16 >> 2)) * L::KP + 16 * rtile + 4 * (l16 & 3));
-                    ak[ks] = cat4(lds_tr(smem, off), lds_tr(smem, off + 2 * 16 * L::KP));
+                    const int o = L::KT + 32 * ks * RK + 32 * rtile;
+                    ak[ks] = cat4(lds_tr(b_kt, o), lds_tr(b_kt, o + 16 * RK));
                 }
                 for (int jt = 0; jt < NCT; ++jt) {
                     f32x4 s = S[rtile][jt] * gam;
@@ -806,93 +891,93 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         if (!act) break;
 
         // ---- AP: the 16 tiles that are not A's diagonal, four per state wave
-        if (lds_ld<int>(smem, L::FL) == 0) {
-            const int qb = L::QH + (it & 1) * L::QH_SZ;
+        if (!any_exact(sm + L::FL)) {
+            const char *const b_k8 = sm + o_k8;
+            const char *const b_x = b_k8 + (it & 1) * L::QH_SZ;  // QH of this chunk for P tiles
             for (int m = 0; m < 4; ++m) {
                 const int t = 4 + rw + 4 * m;
                 const int i = tile_i(t), j = tile_j(t);
                 const bool isP = t >= 10;
-                const f32x4 x = ap_mask(ap_tile<K, V>(smem, i, j, isP ? qb : L::KB, l16, q4), i == j, isP, l16, q4);
-                if (isP) lds_st<bf16x4>(smem, L::PB + 2 * ((16 * i + l16) * L::CP + 16 * j + 4 * q4), f32x4_to_bf16(x));
-                else lds_st<f32x4>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * q4), x);
+                const f32x4 x = ap_mask(ap_tile_at<K>(b_k8 + L::RR + 16 * j * RK, isP ? b_x + L::QH + 16 * i * RK : b_k8 + L::KB + 16 * i * RK),
+                                        i == j, isP, l16, q4);
+                if (isP) lds_st<bf16x4>(sm, L::PB + o_c4 + 16 * i * RC + 32 * j, f32x4_to_bf16(x));
+                else lds_st<f32x4>(sm, L::AB + o_a4 + 16 * i * RA + 64 * j, x);
             }
         } else {
-            exact_ap<K, V>(smem, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
+            exact_ap<K, V>(sm, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
         }
         // w v of this chunk, row-major
         {
             const bf16x8 zero = {};
+            char *const b_wv = sm + emv.row0 * RV + 2 * emv.c0;
             for (int i = 0; i < RPTV; ++i) {
                 const int r = emv.row0 + i;
                 const f32x8 wv = bf16x8_to_f32(r < len ? vr[i] : zero) * bf16x8_to_f32(wr[i]);
-                lds_st<bf16x8>(smem, L::WV + 2 * (r * L::VP + emv.c0), f32x8_to_bf16(wv));
+                lds_st<bf16x8>(b_wv, L::WV + i * RV, f32x8_to_bf16(wv));
             }
         }
         __syncthreads();  // ------------------------------------------ B3
 
-
-        // ---- T2: block column j = rw of T by fp32 MFMA,
-        // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, i = j+1..3. T_kj (k > j)
-        // stay in registers in the MFMA result layout and feed later
-        // products as B operands (k index 4*q4 + e in step e).
+        // ---- T2: block column j = rw of T,
+        // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, i = j+1..3, on bf16 MFMA
+        // with float32 operands split into high and low bf16 parts (three
+        // products; the dropped low x low term is 2^-16 relative). T_kj
+        // (k > j) stay in registers in the MFMA result layout, which is the
+        // B operand layout of the 16x16x16 product.
         if (rw < 3) {
             const int j = rw;
-            f32x4 Tc[4];
+            const char *const b_a4 = sm + o_a4;
+            const char *const b_tc = sm + 4 * q4 * RA + 4 * l16 + j * (16 * RA + 64);  // rows 4q4 + e, column l16
+            f32x4 tjj;
+            for (int e = 0; e < 4; ++e) tjj[e] = lds_ld<float>(b_tc, L::AB + e * RA);
+            const Split4 bjj = split4(tjj);
+            Split4 Tc[4];
+            char *const b_tb = sm + 4 * q4 * RC + 2 * l16 + 32 * j;
             for (int i = 1; i < 4; ++i) {
                 if (i <= j) continue;
                 f32x4 X = {0, 0, 0, 0};
-                for (int st = 0; st < 4; ++st) {  // k = j: T_jj from AB
-                    const float a = lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * j + 4 * st + q4));
-                    const float b = lds_ld<float>(smem, L::AB + 4 * ((16 * j + 4 * st + q4) * L::AP + 16 * j + l16));
-                    X = mfma_f32(a, b, X);
+                for (int kb = 0; kb < 3; ++kb) {
+                    if (kb < j || kb >= i) continue;
+                    X = mfma3(split4(lds_ld<f32x4>(b_a4, L::AB + 16 * i * RA + 64 * kb)), kb == j ? bjj : Tc[kb], X);
                 }
-                for (int kb = 1; kb < 3; ++kb) {
-                    if (kb <= j || kb >= i) continue;
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * kb + 4 * q4 + e));
-                        X = mfma_f32(a, Tc[kb][e], X);
-                    }
-                }
-                f32x4 Y = {0, 0, 0, 0};
-                for (int e = 0; e < 4; ++e) {
-                    const float a = -lds_ld<float>(smem, L::AB + 4 * ((16 * i + l16) * L::AP + 16 * i + 4 * q4 + e));
-                    Y = mfma_f32(a, X[e], Y);
-                }
-                Tc[i] = Y;
-                for (int e = 0; e < 4; ++e)
-                    lds_st<__bf16>(smem, L::TB + 2 * ((16 * i + 4 * q4 + e) * L::CP + 16 * j + l16), (__bf16)Y[e]);
+                const f32x4 Y = mfma3(split4(-lds_ld<f32x4>(b_a4, L::AB + 16 * i * RA + 64 * i)), split4(X), f32x4{0, 0, 0, 0});
+                Tc[i] = split4(Y);
+                for (int e = 0; e < 4; ++e) lds_st<__bf16>(b_tb, L::TB + (16 * i + e) * RC, (__bf16)Y[e]);
             }
         }
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- WY: wy_u = T (w v) for this wave's value columns: U starts here
-        for (int jt = 0; jt < NCT; ++jt) {
-            bf16x8 bv[2];
-            for (int ks = 0; ks < 2; ++ks) {
-                const int off = L::WV + 2 * ((32 * ks + 8 * q4 + (l16 >> 2)) * L::VP + vbase + 16 * jt + 4 * (l16 & 3));
-                bv[ks] = cat4(lds_tr(smem, off), lds_tr(smem, off + 2 * 4 * L::VP));
-            }
-            for (int i = 0; i < 4; ++i) {
-                f32x4 acc = {0, 0, 0, 0};
-                for (int ks = 0; ks <= (i >> 1); ++ks) {
-                    const bf16x8 a = lds_ld<bf16x8>(smem, L::TB + 2 * ((16 * i + l16) * L::CP + 32 * ks + 8 * q4));
-                    acc = mfma_bf16(a, bv[ks], acc);
+        {
+            const char *const b_vt = sm + (8 * q4 + (l16 >> 2)) * RV + 8 * (l16 & 3) + 2 * vbase;  // w v transpose reads
+            const char *const b_c8 = sm + o_c8;
+            for (int jt = 0; jt < NCT; ++jt) {
+                bf16x8 bv[2];
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int o = L::WV + 32 * ks * RV + 32 * jt;
+                    bv[ks] = cat4(lds_tr(b_vt, o), lds_tr(b_vt, o + 4 * RV));
                 }
-                U[i][jt] = acc;
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 acc = {0, 0, 0, 0};
+                    for (int ks = 0; ks <= (i >> 1); ++ks)
+                        acc = mfma_bf16(lds_ld<bf16x8>(b_c8, L::TB + 16 * i * RC + 64 * ks), bv[ks], acc);
+                    U[i][jt] = acc;
+                }
             }
         }
         __syncthreads();  // ------------------------------------------ B5
     }
 
-    const int lane = tid & 63, rw = tid >> 6;
-    const int l16 = lane & 15, q4 = lane >> 4;
-    const int vbase = rw * VW;
-    if (p.ht)
+    if (p.ht) {
+        const int lane = tid & 63, rw = tid >> 6;
+        const int l16 = lane & 15, q4 = lane >> 4;
+        const int vbase = rw * VW;
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
                 for (int e = 0; e < 4; ++e)
                     p.ht[(((int64_t)ch.n * p.HV + ch.hv) * K + 16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16] =
                         S[it][jt][e];
+    }
 }
 
 // ------------------------------------------------------------------ kernel --
