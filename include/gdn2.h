@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 1
+#define GDN2_ABI_VERSION 2
 
 /* Element types a tensor descriptor may carry. */
 typedef enum gdn2_dtype {
@@ -100,8 +100,13 @@ enum {
  *
  * Ownership: the caller owns every buffer. Inputs and initial_state are only
  * read; out and final_state must be preallocated and are fully written. The
- * library keeps no pointer after the call returns and allocates no device
- * memory.
+ * library keeps no pointer after the call returns. When it splits sequences
+ * (see gdn2_chunk_fwd_opts) it takes a stream-ordered workspace of
+ * 3 * N * HV * nseg * K * V * 4 bytes with hipMallocAsync on `stream` and
+ * returns it with hipFreeAsync on the same stream (nseg = segments per
+ * sequence, at most ceil(ceil(T / 64) / segment chunks)); if that
+ * allocation fails it runs the sequences whole instead. Otherwise it
+ * allocates no device memory.
  *
  * Layout: every tensor is row-major contiguous with a 16-byte aligned data
  * pointer (GDN2_ERR_LAYOUT otherwise).
@@ -126,6 +131,52 @@ int gdn2_chunk_fwd(const gdn2_tensor *q, const gdn2_tensor *k,
                    const gdn2_tensor *initial_state,
                    const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
                    const gdn2_tensor *final_state, hipStream_t stream);
+
+/*
+ * Options of gdn2_chunk_fwd_opts. `struct_size` must be at least
+ * sizeof(gdn2_fwd_options) (later versions may append fields).
+ *
+ * seq_split_chunks selects how a sequence is walked:
+ *    0  automatic: gdn2_split_plan() for this shape and the current
+ *       device's compute-unit count decides (what gdn2_chunk_fwd does);
+ *   -1  never split: one workgroup walks each (sequence, value head);
+ *  > 0  split every sequence into segments of this many 64-token chunks.
+ *
+ * A split run is the same computation in another order (the chunked WY form
+ * is affine in the entering state): a transition pass gives every segment's
+ * end state from a zero start and its K x K state transition, a combine
+ * chains them into each segment's entering state, and an output pass runs
+ * all segments at once. It pays when there are few (sequence, value head)
+ * chains for the compute units and they are long (the parallel scan over
+ * the sequence that the FlashInfer docs' output_state note alludes to when
+ * it speaks of one sequence split across CTAs).
+ */
+typedef struct gdn2_fwd_options {
+    int32_t struct_size;
+    int32_t seq_split_chunks;
+} gdn2_fwd_options;
+
+/*
+ * gdn2_chunk_fwd_opts -- gdn2_chunk_fwd with options (NULL opts = defaults).
+ * Same arguments, contract and errors as gdn2_chunk_fwd, plus
+ * GDN2_ERR_SHAPE for a bad options struct (struct_size too small,
+ * seq_split_chunks < -1).
+ */
+int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
+                        const gdn2_tensor *v, const gdn2_tensor *g,
+                        const gdn2_tensor *beta, const gdn2_tensor *w,
+                        float scale, const gdn2_tensor *initial_state,
+                        const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
+                        const gdn2_tensor *final_state,
+                        const gdn2_fwd_options *opts, hipStream_t stream);
+
+/*
+ * gdn2_split_plan -- the automatic choice of seq_split_chunks for T packed
+ * tokens in N sequences with HV value heads on a device with num_cu compute
+ * units: 0 (run whole sequences) or the segment length in chunks. Pure host
+ * arithmetic (assumes equal sequence lengths); needs no GPU.
+ */
+int gdn2_split_plan(int64_t T, int32_t N, int32_t HV, int32_t num_cu);
 
 /*
  * gdn2_chunk_fwd_check -- the host-side argument validation of

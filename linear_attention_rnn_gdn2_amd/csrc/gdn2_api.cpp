@@ -11,6 +11,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "gdn2_internal.h"
@@ -167,6 +168,33 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     return GDN2_OK;
 }
 
+int read_options(const gdn2_fwd_options *opts, int32_t *split)
+{
+    *split = 0;
+    if (!opts) return GDN2_OK;
+    if (opts->struct_size < (int32_t)sizeof(gdn2_fwd_options))
+        return fail(GDN2_ERR_SHAPE, "options: struct_size %d is smaller than %d", opts->struct_size,
+                    (int)sizeof(gdn2_fwd_options));
+    if (opts->seq_split_chunks < -1)
+        return fail(GDN2_ERR_SHAPE, "options: seq_split_chunks must be -1, 0 or positive (got %d)",
+                    opts->seq_split_chunks);
+    *split = opts->seq_split_chunks;
+    return GDN2_OK;
+}
+
+// Compute-unit count per device, looked up once.
+int cu_count(int dev)
+{
+    static std::atomic<int> cache[64];
+    if (dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,13 +214,81 @@ int gdn2_chunk_fwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
                    const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens,
                    const gdn2_tensor *out, const gdn2_tensor *final_state, hipStream_t stream)
 {
+    return gdn2_chunk_fwd_opts(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state,
+                               nullptr, stream);
+}
+
+int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
+                        const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                        const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens,
+                        const gdn2_tensor *out, const gdn2_tensor *final_state,
+                        const gdn2_fwd_options *opts, hipStream_t stream)
+{
     gdn2::FwdParams p;
     int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p);
     if (rc != GDN2_OK) return rc;
+    int32_t split = 0;
+    if ((rc = read_options(opts, &split)) != GDN2_OK) return rc;
+    p.seg_chunks = 0;
+    p.nseg = 1;
+    p.pass = gdn2::PASS_OUTPUT;
+    p.wb = p.wm = p.ws = nullptr;
+    if (split == 0) {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) == hipSuccess) ncu = cu_count(dev);
+        split = gdn2_split_plan(p.T, p.N, p.HV, ncu);
+    }
+    const int64_t chunks = (p.T + 63) / 64;
+    const int64_t nseg = split > 0 ? (chunks + split - 1) / split : 1;
+    if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
+        // sequence split: transition pass, combine, output pass, all on
+        // `stream`, with a stream-ordered workspace
+        const size_t state = (size_t)p.K * p.V * sizeof(float);
+        const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
+        void *ws = nullptr;
+        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && hipMallocAsync(&ws, 3 * one, stream) == hipSuccess) {
+            p.seg_chunks = split;
+            p.nseg = (int32_t)nseg;
+            p.wb = static_cast<float *>(ws);
+            p.wm = reinterpret_cast<float *>(static_cast<char *>(ws) + one);
+            p.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * one);
+            gdn2::FwdParams pt = p;
+            pt.pass = gdn2::PASS_TRANSITION;
+            hipError_t e = gdn2::launch_chunk_fwd(pt, stream);
+            if (e == hipSuccess) e = gdn2::launch_seg_combine(p, stream);
+            if (e == hipSuccess) e = gdn2::launch_chunk_fwd(p, stream);
+            const hipError_t ef = hipFreeAsync(ws, stream);
+            if (e != hipSuccess)
+                return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+            if (ef != hipSuccess)
+                return fail(GDN2_ERR_HIP, "workspace release failed: %s", hipGetErrorString(ef));
+            return GDN2_OK;
+        }
+        (void)hipGetLastError();  // no workspace: run the sequences whole instead
+    }
     hipError_t e = gdn2::launch_chunk_fwd(p, stream);
     if (e != hipSuccess)
         return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN2_OK;
+}
+
+int gdn2_split_plan(int64_t T, int32_t N, int32_t HV, int32_t num_cu)
+{
+    // Split only when the (sequence, head) chains leave at least half of
+    // the compute units idle and are long (32 chunks or more). Segments of
+    // about sqrt(chunks per sequence) chunks balance the two serial parts of
+    // a split run, the segment walk (L chunk steps) and the combine (one
+    // step per segment, P = chunks / L); at least 8 chunks, so that
+    // per-workgroup start-up and the composition of segment maps stay small.
+    // (Measured on MI355X: 16 chains x 64 chunks are fastest at 8, 32
+    // chains x 1024 chunks at 32.)
+    if (T <= 0 || N <= 0 || HV <= 0 || num_cu <= 0) return 0;
+    const int64_t chains = (int64_t)N * HV;
+    const int64_t avg = ((T + 63) / 64 + N - 1) / N;
+    if (2 * chains > num_cu || avg < 32) return 0;
+    int64_t L = (int64_t)llround(sqrt((double)avg));
+    if (L < 8) L = 8;
+    return (int)L;
 }
 
 const char *gdn2_last_error(void) { return g_last_error.c_str(); }

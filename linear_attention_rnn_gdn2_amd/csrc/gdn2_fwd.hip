@@ -227,6 +227,7 @@ struct RawChunk {
 __device__ __attribute__((aligned(16))) uint16_t kOnesBf16[8] = {0x3f80, 0x3f80, 0x3f80, 0x3f80,
                                                                0x3f80, 0x3f80, 0x3f80, 0x3f80};
 __device__ __attribute__((aligned(16))) float kZerosF32[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+__device__ __attribute__((aligned(16))) uint16_t kZerosBf16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
 // Straight-line loads: rows past the chunk end read the last valid row (the
 // consumer masks them); omitted gates read the stand-in row.
@@ -267,15 +268,16 @@ __device__ __forceinline__ void load_keys(RawChunk<RPT> &R, const FwdParams &p, 
 // consumer).
 template <int V, int RPTV>
 __device__ __forceinline__ void load_values(bf16x8 *v, bf16x8 *w, const FwdParams &p, int64_t c0, int len, int hv,
-                                            int row0, int c0v)
+                                            int row0, int c0v, bool zero_v)
 {
-    const uint16_t *vb = p.v + (c0 * p.HV + hv) * V;
-    const uint16_t *wb = p.w ? p.w + (c0 * p.HV + hv) * V : kOnesBf16;
-    const int svw = p.HV * V, sw = p.w ? svw : 0, cw = p.w ? c0v : 0;
+    const uint16_t *vb = zero_v ? kZerosBf16 : p.v + (c0 * p.HV + hv) * V;
+    const uint16_t *wb = p.w && !zero_v ? p.w + (c0 * p.HV + hv) * V : kOnesBf16;
+    const int sv = zero_v ? 0 : p.HV * V, cv = zero_v ? 0 : c0v;
+    const int sw = p.w && !zero_v ? p.HV * V : 0, cw = p.w && !zero_v ? c0v : 0;
     for (int i = 0; i < RPTV; ++i) {
         const int r = row0 + i;
         const int rc = r < len ? r : len - 1;
-        v[i] = ldg_bf16x8(vb + (uint32_t)(rc * svw + c0v));
+        v[i] = ldg_bf16x8(vb + (uint32_t)(rc * sv + cv));
         w[i] = ldg_bf16x8(wb + (uint32_t)(rc * sw + cw));
     }
 }
@@ -353,9 +355,16 @@ __device__ __forceinline__ uint64_t group_lanes(int cgl)
 }
 
 // ----------------------------------------------------------- chain context --
+// What one workgroup does: a token range of one sequence and value head,
+// where its state starts and ends, and whether it writes the output.
 struct Chain {
     int n, hv, hk;
-    int64_t tb, te;  // token range of the sequence
+    int64_t tb, te;   // token range (the sequence, or one segment of it)
+    const float *s0;  // entering state [K][V] (nullptr: zero)
+    float *s1;        // destination of the leaving state [K][V] (nullptr: none)
+    bool ident;       // entering state is the identity (transition pass, K == V)
+    bool zero_v;      // values taken as zero (transition pass)
+    bool out;         // write the output rows
 };
 
 __device__ __forceinline__ int chunk_len(int64_t c0, int64_t te) { return (int)((te - c0) < CH ? (te - c0) : CH); }
@@ -773,11 +782,18 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
 
     // state: rows 16*it + 4*q4 + e, column vbase + 16*jt + l16
     f32x4 S[NRT][NCT];
-    if (p.h0) {
+    if (ch.ident) {
         const int lane = tid & 63, rw = tid >> 6;
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
-        const float *h0 = p.h0 + ((int64_t)ch.n * p.HV + ch.hv) * K * V;
+        for (int it = 0; it < NRT; ++it)
+            for (int jt = 0; jt < NCT; ++jt)
+                for (int e = 0; e < 4; ++e) S[it][jt][e] = 16 * it + 4 * q4 + e == vbase + 16 * jt + l16 ? 1.0f : 0.0f;
+    } else if (ch.s0) {
+        const int lane = tid & 63, rw = tid >> 6;
+        const int l16 = lane & 15, q4 = lane >> 4;
+        const int vbase = rw * VW;
+        const float *h0 = ch.s0;
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
                 for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16];
@@ -840,7 +856,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         // this chunk's v and w (stored as w v after B2; the latency hides
         // behind the rest of phase S, AP and T1)
         bf16x8 vr[RPTV], wr[RPTV];
-        if (act) load_values<V, RPTV>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0);
+        if (act) load_values<V, RPTV>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0, ch.zero_v);
 
         // ---- S, second half: the output, computed transposed,
         // O^T = scale (S^T QH^T + U^T P^T), stored as 4 consecutive values
@@ -851,24 +867,26 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             const int64_t cp = c0 - CH;
             const int lenp = chunk_len(cp, ch.te);
             const char *const b_q = b_k4 + ((it - 1) & 1) * L::QH_SZ;
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * i + l16;
-                f32x4 Y[NCT];
-                for (int jt = 0; jt < NCT; ++jt) Y[jt] = f32x4{0, 0, 0, 0};
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int o = L::QH + 16 * i * RK + 64 * ks;
-                    const bf16x8 bq = cat4(lds_ld<bf16x4>(b_q, o), lds_ld<bf16x4>(b_q, o + 32));
-                    for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Sb[ks][jt], bq, Y[jt]);
+            if (ch.out) {
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * i + l16;
+                    f32x4 Y[NCT];
+                    for (int jt = 0; jt < NCT; ++jt) Y[jt] = f32x4{0, 0, 0, 0};
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int o = L::QH + 16 * i * RK + 64 * ks;
+                        const bf16x8 bq = cat4(lds_ld<bf16x4>(b_q, o), lds_ld<bf16x4>(b_q, o + 32));
+                        for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Sb[ks][jt], bq, Y[jt]);
+                    }
+                    for (int ks = 0; ks <= (i >> 1); ++ks) {
+                        const int o = L::PB + 16 * i * RC + 64 * ks;
+                        const bf16x8 bp = cat4(lds_ld<bf16x4>(b_c4, o), lds_ld<bf16x4>(b_c4, o + 32));
+                        for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Ub[ks][jt], bp, Y[jt]);
+                    }
+                    if (row < lenp)
+                        for (int jt = 0; jt < NCT; ++jt)
+                            *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
+                                f32x4_to_bf16(Y[jt] * p.scale);
                 }
-                for (int ks = 0; ks <= (i >> 1); ++ks) {
-                    const int o = L::PB + 16 * i * RC + 64 * ks;
-                    const bf16x8 bp = cat4(lds_ld<bf16x4>(b_c4, o), lds_ld<bf16x4>(b_c4, o + 32));
-                    for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Ub[ks][jt], bp, Y[jt]);
-                }
-                if (row < lenp)
-                    for (int jt = 0; jt < NCT; ++jt)
-                        *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
-                            f32x4_to_bf16(Y[jt] * p.scale);
             }
             const char *const b_kt = sm + (4 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3);  // KT transpose reads
             const char *const b_g = sm + 16 * q4;
@@ -968,15 +986,13 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         __syncthreads();  // ------------------------------------------ B5
     }
 
-    if (p.ht) {
+    if (ch.s1) {
         const int lane = tid & 63, rw = tid >> 6;
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e)
-                    p.ht[(((int64_t)ch.n * p.HV + ch.hv) * K + 16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16] =
-                        S[it][jt][e];
+                for (int e = 0; e < 4; ++e) ch.s1[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16] = S[it][jt][e];
     }
 }
 
@@ -988,12 +1004,52 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
     const int tid = threadIdx.x;
 
+    // work item: (sequence, value head), times the segment and, in the
+    // transition pass, the kind (0: end state from the segment's entering
+    // state or zero, 1: transition map from the identity with zero values)
+    int item = blockIdx.x;
+    const int kind = p.pass == PASS_TRANSITION ? item & 1 : 0;
+    if (p.pass == PASS_TRANSITION) item >>= 1;
+    const int seg = p.seg_chunks ? item % p.nseg : 0;
+    if (p.seg_chunks) item /= p.nseg;
     Chain ch;
-    ch.n = blockIdx.x / p.HV;
-    ch.hv = blockIdx.x - ch.n * p.HV;
+    ch.n = item / p.HV;
+    ch.hv = item - ch.n * p.HV;
     ch.hk = ch.hv / (p.HV / p.H);
-    ch.tb = p.cu ? (int64_t)p.cu[ch.n] : 0;
-    ch.te = p.cu ? (int64_t)p.cu[ch.n + 1] : p.T;
+    const int64_t sb = p.cu ? (int64_t)p.cu[ch.n] : 0;
+    const int64_t se = p.cu ? (int64_t)p.cu[ch.n + 1] : p.T;
+    const int64_t shead = ((int64_t)ch.n * p.HV + ch.hv) * K * V;  // [N, HV, K, V] states
+    ch.tb = sb;
+    ch.te = se;
+    ch.s0 = p.h0 ? p.h0 + shead : nullptr;
+    ch.s1 = p.ht ? p.ht + shead : nullptr;
+    ch.ident = ch.zero_v = false;
+    ch.out = true;
+    if (p.seg_chunks) {
+        const int64_t nch = (se - sb + CH - 1) / CH;
+        const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;
+        if (seg > last) return;  // past the end of this sequence
+        const int64_t span = (int64_t)p.seg_chunks * CH;
+        ch.tb = sb + seg * span;
+        ch.te = se < ch.tb + span ? se : ch.tb + span;
+        const int64_t sseg = (((int64_t)ch.n * p.HV + ch.hv) * p.nseg + seg) * K * V;  // [N, HV, nseg, K, V]
+        if (p.pass == PASS_TRANSITION) {
+            // nothing follows the last segment; the first one's map is not needed
+            if (seg >= last || (kind == 1 && seg == 0)) return;
+            ch.out = false;
+            if (kind == 0) {
+                if (seg > 0) ch.s0 = nullptr;
+                ch.s1 = p.wb + sseg;
+            } else {
+                ch.s0 = nullptr;
+                ch.ident = ch.zero_v = true;
+                ch.s1 = p.wm + sseg;
+            }
+        } else {
+            if (seg > 0) ch.s0 = p.ws + sseg;
+            if (seg < last) ch.s1 = nullptr;
+        }
+    }
     const int nc = (int)((ch.te - ch.tb + CH - 1) / CH);
 
     // P's blocks above the diagonal stay zero for the whole chain (ordered
@@ -1012,11 +1068,78 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     else state_role<K, V>(smem, p, ch, tid, nc);
 }
 
+// ------------------------------------------------------ segment combine --
+// The state pass is affine in the entering state, so a sequence cut into
+// segments j = 0 .. last has S_{j+1} = M_j S_j + B_j, with B_j the end state
+// of segment j from a zero start (from the true initial state for j = 0) and
+// M_j its K x K transition. One workgroup per (sequence, value head, 4
+// columns) applies the recurrence in float32 and stores every entering state
+// S_j (j >= 1) for the output pass.
+constexpr int CMB_COLS = 4;  // state columns per workgroup; two per thread
+
+template <int K>
+constexpr int cmb_threads() { return K * CMB_COLS / 2; }
+
+template <int K, int V>
+__global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams p)
+{
+    __shared__ __attribute__((aligned(16))) float Sl[K][CMB_COLS];
+    const int ncb = V / CMB_COLS;
+    const int chain = blockIdx.x / ncb, cb = blockIdx.x - chain * ncb;
+    const int n = chain / p.HV;
+    const int64_t sb = p.cu ? (int64_t)p.cu[n] : 0;
+    const int64_t se = p.cu ? (int64_t)p.cu[n + 1] : p.T;
+    const int64_t nch = (se - sb + CH - 1) / CH;
+    const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;
+    if (last == 0) return;
+    const int t = threadIdx.x, r = t >> 1, c = CMB_COLS / 2 * (t & 1);
+    const int64_t seg0 = (int64_t)chain * p.nseg * K * V;  // chain = n * HV + hv
+    const int col = cb * CMB_COLS + c;
+    float s0 = p.wb[seg0 + r * V + col], s1 = p.wb[seg0 + r * V + col + 1];
+    p.ws[seg0 + (int64_t)K * V + r * V + col] = s0;
+    p.ws[seg0 + (int64_t)K * V + r * V + col + 1] = s1;
+    for (int j = 1; j < last; ++j) {
+        // row r of M_j and this thread's entries of B_j, all loads in flight
+        // together (one memory round trip per step)
+        const int64_t sj = seg0 + (int64_t)j * K * V;
+        const float *m = p.wm + sj + (int64_t)r * K;
+        f32x4 mr[K / 4];
+        for (int k4 = 0; k4 < K / 4; ++k4) mr[k4] = *reinterpret_cast<const f32x4 *>(m + 4 * k4);
+        float a0 = p.wb[sj + r * V + col], a1 = p.wb[sj + r * V + col + 1];
+        __syncthreads();  // the previous step's reads of Sl are done
+        Sl[r][c] = s0;
+        Sl[r][c + 1] = s1;
+        __syncthreads();
+        for (int k4 = 0; k4 < K / 4; ++k4)
+            for (int e = 0; e < 4; ++e) {
+                a0 = fmaf(mr[k4][e], Sl[4 * k4 + e][c], a0);
+                a1 = fmaf(mr[k4][e], Sl[4 * k4 + e][c + 1], a1);
+            }
+        s0 = a0;
+        s1 = a1;
+        p.ws[sj + (int64_t)K * V + r * V + col] = s0;
+        p.ws[sj + (int64_t)K * V + r * V + col + 1] = s1;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.N * p.HV * (p.V / CMB_COLS)));
+    if (p.K == 128 && p.V == 128)
+        hipLaunchKernelGGL((seg_combine_kernel<128, 128>), grid, dim3(cmb_threads<128>()), 0, stream, p);
+    else if (p.K == 64 && p.V == 64)
+        hipLaunchKernelGGL((seg_combine_kernel<64, 64>), grid, dim3(cmb_threads<64>()), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(p.N * p.HV)), block(NTHR);
+    const int64_t items = (int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1) * (p.pass == PASS_TRANSITION ? 2 : 1);
+    const dim3 grid((unsigned)items), block(NTHR);
     if (p.K == 128 && p.V == 128)
         hipLaunchKernelGGL((chunk_fwd_kernel<128, 128>), grid, block, 0, stream, p);
     else if (p.K == 64 && p.V == 64)

@@ -24,9 +24,24 @@ struct FwdParams {
     int64_t T;
     int32_t N, H, HV, K, V;
     float scale;           // already resolved (never 0)
+    // Sequence split (0: one workgroup walks each whole sequence). With
+    // seg_chunks > 0 every sequence is cut into segments of seg_chunks
+    // chunks (nseg per sequence at most) and the launch is one of:
+    int32_t seg_chunks;
+    int32_t nseg;
+    int32_t pass;          // PASS_OUTPUT or PASS_TRANSITION
+    float *wb;             // [N, HV, nseg, K, V] segment end state from a zero start (segment 0: from h0)
+    float *wm;             // [N, HV, nseg, K, K] segment transition (state map S_in -> S_out minus wb)
+    float *ws;             // [N, HV, nseg, K, V] entering state of segment j >= 1
 };
 
-// Enqueue the fused chunked forward on `stream`. Returns the launch status.
+enum { PASS_OUTPUT = 0, PASS_TRANSITION = 1 };
+
+// Enqueue the fused chunked forward on `stream` (one pass, as p describes).
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);
+
+// Enqueue the segment combine of a split forward: ws[j + 1] = wm[j] ws[j] +
+// wb[j] in segment order, with ws[1] = wb[0].
+hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream);
 
 }  // namespace gdn2

@@ -22,13 +22,19 @@ _DTYPES = {torch.bfloat16: GDN2_DTYPE_BF16, torch.float32: GDN2_DTYPE_F32, torch
 STATUS = {0: "OK", -1: "NULL_ARG", -2: "DTYPE", -3: "SHAPE", -4: "HEADS",
           -5: "UNSUPPORTED", -6: "LAYOUT", -7: "ALIAS", -8: "HIP"}
 
-EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_check", "gdn2_last_error", "gdn2_abi_version"]
+EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_opts", "gdn2_chunk_fwd_check", "gdn2_split_plan",
+            "gdn2_last_error", "gdn2_abi_version"]
 
 
 class Gdn2Tensor(ctypes.Structure):
     """Mirror of ``gdn2_tensor``."""
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class Gdn2FwdOptions(ctypes.Structure):
+    """Mirror of ``gdn2_fwd_options``."""
+    _fields_ = [("struct_size", ctypes.c_int32), ("seq_split_chunks", ctypes.c_int32)]
 
 
 class Gdn2Error(RuntimeError):
@@ -52,6 +58,11 @@ def load_library():
         P = ctypes.POINTER(Gdn2Tensor)
         lib.gdn2_chunk_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
         lib.gdn2_chunk_fwd.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_opts.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P,
+                                            ctypes.POINTER(Gdn2FwdOptions), ctypes.c_void_p]
+        lib.gdn2_chunk_fwd_opts.restype = ctypes.c_int
+        lib.gdn2_split_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        lib.gdn2_split_plan.restype = ctypes.c_int
         lib.gdn2_chunk_fwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
         lib.gdn2_chunk_fwd_check.restype = ctypes.c_int
         lib.gdn2_last_error.argtypes = []
@@ -101,8 +112,15 @@ def check(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
                                     *[_ptr(d) for d in rest])
 
 
+def split_plan(T, N, HV, num_cu):
+    """The library's automatic segment length (0 = whole sequences) for T
+    tokens in N sequences with HV value heads on ``num_cu`` compute units."""
+    return load_library().gdn2_split_plan(int(T), int(N), int(HV), int(num_cu))
+
+
 def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
-              cu_seqlens=None, output_final_state=True, out=None, final_state=None):
+              cu_seqlens=None, output_final_state=True, out=None, final_state=None,
+              seq_split=None):
     """GDN-2 chunked prefill forward on the current HIP stream.
 
     q, k [T, H, K] bf16; v, w [T, HV, V] bf16; g [T, HV, K] float32;
@@ -110,6 +128,8 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
     cu_seqlens [N + 1] int32 (None: one sequence). ``scale`` None or 0 means
     1/sqrt(K). Returns (out [T, HV, V] bf16, final_state or None).
     Preallocated ``out`` / ``final_state`` are written in place.
+    ``seq_split``: None or 0 automatic, -1 never split sequences, n > 0
+    split every sequence into segments of n 64-token chunks.
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w),
@@ -126,8 +146,13 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
     descs = [describe(x) for x in (q, k, v, g, beta, w)]
     rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
     stream = torch.cuda.current_stream(v.device).cuda_stream
-    rc = lib.gdn2_chunk_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
-                            *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
+    if seq_split is None:
+        rc = lib.gdn2_chunk_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
+                                *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
+    else:
+        opts = Gdn2FwdOptions(ctypes.sizeof(Gdn2FwdOptions), int(seq_split))
+        rc = lib.gdn2_chunk_fwd_opts(*[_ptr(d) for d in descs], _scale_arg(scale),
+                                     *[_ptr(d) for d in rest], ctypes.byref(opts), ctypes.c_void_p(stream))
     if rc != 0:
         raise Gdn2Error(rc, last_error())
     return out, final_state

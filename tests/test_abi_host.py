@@ -133,3 +133,38 @@ def test_no_cpu_path(gdn2):
     c = case()
     with pytest.raises(ValueError):
         gdn2.chunk_fwd(c["q"], c["k"], c["v"])
+
+
+def test_options_rejected_before_any_device_work(gdn2):
+    """A bad options struct is rejected (SHAPE) after the tensor checks pass
+    and before anything touches a device (host tensors here)."""
+    import ctypes
+    lib = gdn2.load_library()
+    t = case()
+    P = lambda x: None if x is None else ctypes.byref(x)
+    for size, split in ((4, 0), (ctypes.sizeof(gdn2.Gdn2FwdOptions), -2)):
+        opts = gdn2.Gdn2FwdOptions(size, split)
+        descs = [gdn2.describe(t[n]) for n in ("q", "k", "v", "g", "beta", "w")]
+        rest = [gdn2.describe(t[n]) for n in ("initial_state", "cu_seqlens", "out", "final_state")]
+        rc = lib.gdn2_chunk_fwd_opts(*[P(x) for x in descs], 0.0, *[P(x) for x in rest],
+                                     ctypes.byref(opts), None)
+        assert rc == -3, (size, split, rc)
+        assert "options" in gdn2.last_error()
+
+
+def test_split_plan(gdn2):
+    """The automatic split: whole sequences when the chains fill at least
+    half the CUs or are short (under 32 chunks); otherwise segments of about
+    sqrt(chunks per sequence), at least 8 chunks."""
+    plan = gdn2.split_plan
+    assert plan(4096, 1, 16, 256) == 8          # 16 chains x 64 chunks
+    assert plan(131072, 2, 16, 256) == 32       # 32 chains x 1024 chunks
+    assert plan(65536, 4, 48, 256) == 0         # 192 chains: no split
+    assert plan(37517, 8, 32, 256) == 0         # 256 chains
+    assert plan(256, 1, 2, 256) == 0            # 4 chunks per chain
+    assert plan(31 * 64, 1, 1, 256) == 0 and plan(32 * 64, 1, 1, 256) == 8
+    assert plan(0, 1, 1, 256) == 0 and plan(4096, 1, 1, 0) == 0
+    for T, N, HV in ((8192, 1, 1), (65536, 1, 4), (1 << 20, 2, 8), (50000, 3, 7)):
+        L = plan(T, N, HV, 256)
+        avg = -(-(-(-T // 64)) // N)
+        assert L >= 8 and abs(L - avg ** 0.5) <= max(1.0, 8 - avg ** 0.5)
