@@ -171,6 +171,38 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
                         const gdn2_fwd_options *opts, hipStream_t stream);
 
 /*
+ * gdn2_recurrent_fwd -- the same operation evaluated token by token: for
+ * decode (one new token per sequence) and short spans (a few tokens per
+ * sequence, e.g. speculative or chunk-remainder steps), where the WY chunk
+ * machinery would waste most of a 64-token chunk. Same tensors, dtypes,
+ * defaults, varlen packing and errors as gdn2_chunk_fwd, with one
+ * difference: final_state may be the very buffer of initial_state (same
+ * data pointer) to update the state in place; any other overlap is
+ * GDN2_ERR_ALIAS. The arithmetic is the recurrence step by step in float32
+ * (state, gates, products); only the output is rounded to bf16.
+ *
+ * Cost: every (sequence, value head) state is read and written once per
+ * call (2 * K * V * 4 bytes), plus the tokens' vectors; one workgroup per
+ * (sequence, value head, 32 value columns) walks the span in order, so long
+ * sequences belong on gdn2_chunk_fwd. Allocates nothing.
+ */
+int gdn2_recurrent_fwd(const gdn2_tensor *q, const gdn2_tensor *k,
+                       const gdn2_tensor *v, const gdn2_tensor *g,
+                       const gdn2_tensor *beta, const gdn2_tensor *w,
+                       float scale, const gdn2_tensor *initial_state,
+                       const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
+                       const gdn2_tensor *final_state, hipStream_t stream);
+
+/* The host-side validation of gdn2_recurrent_fwd alone (no device work). */
+int gdn2_recurrent_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
+                             const gdn2_tensor *v, const gdn2_tensor *g,
+                             const gdn2_tensor *beta, const gdn2_tensor *w,
+                             float scale, const gdn2_tensor *initial_state,
+                             const gdn2_tensor *cu_seqlens,
+                             const gdn2_tensor *out,
+                             const gdn2_tensor *final_state);
+
+/*
  * gdn2_split_plan -- the automatic choice of seq_split_chunks for T packed
  * tokens in N sequences with HV value heads on a device with num_cu compute
  * units: 0 (run whole sequences) or the segment length in chunks. Pure host

@@ -95,7 +95,7 @@ bool overlaps(const gdn2_tensor *a, const gdn2_tensor *b)
 int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
              const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
              const gdn2_tensor *h0, const gdn2_tensor *cu, const gdn2_tensor *out,
-             const gdn2_tensor *ht, gdn2::FwdParams *p)
+             const gdn2_tensor *ht, gdn2::FwdParams *p, bool allow_inplace_state = false)
 {
     g_last_error.clear();
     if (!q) return fail(GDN2_ERR_NULL_ARG, "q is NULL");
@@ -138,10 +138,13 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
 
     const gdn2_tensor *inputs[] = {q, k, v, g, beta, w, h0, cu};
     const char *in_names[] = {"q", "k", "v", "g", "beta", "w", "initial_state", "cu_seqlens"};
+    // final_state may be initial_state itself (same buffer) where the kernel
+    // reads every state element before writing it (the recurrent path)
+    const bool inplace = allow_inplace_state && h0 && ht && h0->data == ht->data;
     for (int i = 0; i < 8; ++i) {
         if (overlaps(out, inputs[i]))
             return fail(GDN2_ERR_ALIAS, "out overlaps %s", in_names[i]);
-        if (overlaps(ht, inputs[i]))
+        if (overlaps(ht, inputs[i]) && !(inplace && inputs[i] == h0))
             return fail(GDN2_ERR_ALIAS, "final_state overlaps %s", in_names[i]);
     }
     if (overlaps(out, ht)) return fail(GDN2_ERR_ALIAS, "out overlaps final_state");
@@ -270,6 +273,33 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_t
     if (e != hipSuccess)
         return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN2_OK;
+}
+
+int gdn2_recurrent_fwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
+                       const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                       const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens,
+                       const gdn2_tensor *out, const gdn2_tensor *final_state, hipStream_t stream)
+{
+    gdn2::FwdParams p;
+    int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p, true);
+    if (rc != GDN2_OK) return rc;
+    p.seg_chunks = 0;
+    p.nseg = 1;
+    p.pass = gdn2::PASS_OUTPUT;
+    p.wb = p.wm = p.ws = nullptr;
+    hipError_t e = gdn2::launch_recurrent_fwd(p, stream);
+    if (e != hipSuccess)
+        return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN2_OK;
+}
+
+int gdn2_recurrent_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
+                             const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w,
+                             float scale, const gdn2_tensor *initial_state,
+                             const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
+                             const gdn2_tensor *final_state)
+{
+    return validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, nullptr, true);
 }
 
 int gdn2_split_plan(int64_t T, int32_t N, int32_t HV, int32_t num_cu)

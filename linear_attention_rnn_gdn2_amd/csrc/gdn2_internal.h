@@ -40,6 +40,10 @@ enum { PASS_OUTPUT = 0, PASS_TRANSITION = 1 };
 // Enqueue the fused chunked forward on `stream` (one pass, as p describes).
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);
 
+// Enqueue the token-by-token forward (decode and short spans): one
+// workgroup per (sequence, value head, 32 value columns).
+hipError_t launch_recurrent_fwd(const FwdParams &p, hipStream_t stream);
+
 // Enqueue the segment combine of a split forward: ws[j + 1] = wm[j] ws[j] +
 // wb[j] in segment order, with ws[1] = wb[0].
 hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream);

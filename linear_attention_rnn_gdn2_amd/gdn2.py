@@ -23,7 +23,7 @@ STATUS = {0: "OK", -1: "NULL_ARG", -2: "DTYPE", -3: "SHAPE", -4: "HEADS",
           -5: "UNSUPPORTED", -6: "LAYOUT", -7: "ALIAS", -8: "HIP"}
 
 EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_opts", "gdn2_chunk_fwd_check", "gdn2_split_plan",
-            "gdn2_last_error", "gdn2_abi_version"]
+            "gdn2_recurrent_fwd", "gdn2_recurrent_fwd_check", "gdn2_last_error", "gdn2_abi_version"]
 
 
 class Gdn2Tensor(ctypes.Structure):
@@ -61,6 +61,10 @@ def load_library():
         lib.gdn2_chunk_fwd_opts.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P,
                                             ctypes.POINTER(Gdn2FwdOptions), ctypes.c_void_p]
         lib.gdn2_chunk_fwd_opts.restype = ctypes.c_int
+        lib.gdn2_recurrent_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
+        lib.gdn2_recurrent_fwd.restype = ctypes.c_int
+        lib.gdn2_recurrent_fwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
+        lib.gdn2_recurrent_fwd_check.restype = ctypes.c_int
         lib.gdn2_split_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         lib.gdn2_split_plan.restype = ctypes.c_int
         lib.gdn2_chunk_fwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
@@ -153,6 +157,35 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
         opts = Gdn2FwdOptions(ctypes.sizeof(Gdn2FwdOptions), int(seq_split))
         rc = lib.gdn2_chunk_fwd_opts(*[_ptr(d) for d in descs], _scale_arg(scale),
                                      *[_ptr(d) for d in rest], ctypes.byref(opts), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise Gdn2Error(rc, last_error())
+    return out, final_state
+
+
+def recurrent_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
+                  cu_seqlens=None, output_final_state=True, out=None, final_state=None):
+    """The same forward evaluated token by token (decode and short spans).
+
+    Tensors as in :func:`chunk_fwd`. ``final_state`` may be ``initial_state``
+    itself to update the state in place.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w),
+                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    T, HV, V = v.shape
+    K = q.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
+    descs = [describe(x) for x in (q, k, v, g, beta, w)]
+    rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
+    stream = torch.cuda.current_stream(v.device).cuda_stream
+    rc = lib.gdn2_recurrent_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
+                                *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
     if rc != 0:
         raise Gdn2Error(rc, last_error())
     return out, final_state

@@ -168,3 +168,27 @@ def test_split_plan(gdn2):
         L = plan(T, N, HV, 256)
         avg = -(-(-(-T // 64)) // N)
         assert L >= 8 and abs(L - avg ** 0.5) <= max(1.0, 8 - avg ** 0.5)
+
+
+def test_recurrent_allows_in_place_state_only(gdn2):
+    """gdn2_recurrent_fwd accepts final_state == initial_state (same
+    buffer); a partial overlap, and the in-place pair on the chunked entry,
+    are ALIAS."""
+    import ctypes
+    lib = gdn2.load_library()
+    t = case()
+    P = lambda x: None if x is None else ctypes.byref(x)
+
+    def call(fn, init, final):
+        descs = [gdn2.describe(t[n]) for n in ("q", "k", "v", "g", "beta", "w")]
+        rest = [gdn2.describe(x) for x in (init, t["cu_seqlens"], t["out"], final)]
+        return fn(*[P(x) for x in descs], 0.0, *[P(x) for x in rest])
+
+    s0 = t["initial_state"]
+    assert call(lib.gdn2_recurrent_fwd_check, s0, s0) == 0
+    assert call(lib.gdn2_chunk_fwd_check, s0, s0) == -7
+    big = torch.zeros(2 * s0.numel() + 64)
+    a = big[:s0.numel()].view(s0.shape)
+    b = big[16:16 + s0.numel()].view(s0.shape)  # shifted by 64 bytes: overlaps a
+    assert call(lib.gdn2_recurrent_fwd_check, a, b) == -7
+    assert "final_state overlaps initial_state" in gdn2.last_error()
