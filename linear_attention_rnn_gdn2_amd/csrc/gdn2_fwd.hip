@@ -123,12 +123,13 @@ __device__ __forceinline__ Split4 split4(f32x4 x)
     return r;
 }
 // c + a b for float32 operands given as hi + lo bf16 parts: lo hi + hi lo +
-// hi hi on v_mfma_f32_16x16x16_bf16 (small terms first).
+// hi hi on v_mfma_f32_16x16x16_bf16, as two independent chains.
 __device__ __forceinline__ f32x4 mfma3(Split4 a, Split4 b, f32x4 c)
 {
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+    f32x4 d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, f32x4{0, 0, 0, 0}, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);  // independent of d
+    d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, d, 0, 0, 0);
+    return c + d;
 }
 
 // An opaque zero, produced inside a loop body, keeps LDS address arithmetic
@@ -219,29 +220,39 @@ struct RawChunk {
     f32x4 g[RPT][2];
 };
 
-// Stand-ins for omitted gates: one row of ones (beta, w) or zeros (g), read
-// with row stride 0. They live in global memory (not the constant address
-// space) so that a pointer that may be either an input or a stand-in stays a
-// global pointer: a flat load would also count against the LDS wait counter,
-// and every later LDS wait would then wait for the HBM prefetch as well.
+// Chunk loads are buffer loads: a scalar resource per (chunk, tensor) whose
+// base is the chunk's first row of this head and whose range ends at the
+// sequence's last row, plus 32-bit per-lane byte offsets. Rows past the end
+// of the sequence read as zero in hardware (q = k = v = 0, g = 0: identity
+// steps), so the consumers need no row masks. An omitted gate reads a
+// 16-byte row of ones with row stride 0 (beta, w = 1; on padded rows k and v
+// are zero); an omitted g, or values taken as zero, is a resource of length
+// zero.
 __device__ __attribute__((aligned(16))) uint16_t kOnesBf16[8] = {0x3f80, 0x3f80, 0x3f80, 0x3f80,
                                                                0x3f80, 0x3f80, 0x3f80, 0x3f80};
-__device__ __attribute__((aligned(16))) float kZerosF32[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-__device__ __attribute__((aligned(16))) uint16_t kZerosBf16[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
-// Straight-line loads: rows past the chunk end read the last valid row (the
-// consumer masks them); omitted gates read the stand-in row.
+constexpr int BUF_DWORD3 = 0x00020000;  // raw (unformatted) buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, BUF_DWORD3);
+}
+template <typename T>
+__device__ __forceinline__ T buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 template <int K, int RPT>
 __device__ __forceinline__ void load_decay(RawChunk<RPT> &R, const FwdParams &p, int64_t c0, int len, int hv,
                                            int row0, int c0k)
 {
-    const float *gb = p.g ? p.g + (c0 * p.HV + hv) * K : kZerosF32;
-    const int sg = p.g ? p.HV * K : 0, cgg = p.g ? c0k : 0;
+    const int rs = p.HV * K * 4;  // row stride (bytes)
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(p.g ? p.g + (c0 * p.HV + hv) * K : nullptr, p.g ? len * rs : 0);
     for (int i = 0; i < RPT; ++i) {
-        const int r = row0 + i;
-        const int rc = r < len ? r : len - 1;
-        R.g[i][0] = ldg_f32x4(gb + (uint32_t)(rc * sg + cgg));
-        R.g[i][1] = ldg_f32x4(gb + (uint32_t)(rc * sg + cgg) + 4);
+        const uint32_t o = (uint32_t)((row0 + i) * rs + 4 * c0k);
+        R.g[i][0] = buf_ld16<f32x4>(rg, o);
+        R.g[i][1] = buf_ld16<f32x4>(rg, o + 16);
     }
 }
 
@@ -249,36 +260,33 @@ template <int K, int RPT>
 __device__ __forceinline__ void load_keys(RawChunk<RPT> &R, const FwdParams &p, int64_t c0, int len, int hk,
                                           int hv, int row0, int c0k)
 {
-    // wave-uniform chunk bases + 32-bit per-lane offsets
-    const uint16_t *qb = p.q + (c0 * p.H + hk) * K;
-    const uint16_t *kb = p.k + (c0 * p.H + hk) * K;
-    const uint16_t *bb = p.beta ? p.beta + (c0 * p.HV + hv) * K : kOnesBf16;
-    const int sqk = p.H * K, sb = p.beta ? p.HV * K : 0, cb = p.beta ? c0k : 0;
+    const int rqk = p.H * K * 2, rb = p.HV * K * 2;  // row strides (bytes)
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(p.q + (c0 * p.H + hk) * K, len * rqk);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(p.k + (c0 * p.H + hk) * K, len * rqk);
+    const __amdgpu_buffer_rsrc_t rbb = p.beta ? buf_rsrc(p.beta + (c0 * p.HV + hv) * K, len * rb) : buf_rsrc(kOnesBf16, 16);
+    const int sb = p.beta ? rb : 0, cb = p.beta ? 2 * c0k : 0;
     for (int i = 0; i < RPT; ++i) {
         const int r = row0 + i;
-        const int rc = r < len ? r : len - 1;
-        R.q[i] = ldg_bf16x8(qb + (uint32_t)(rc * sqk + c0k));
-        R.k[i] = ldg_bf16x8(kb + (uint32_t)(rc * sqk + c0k));
-        R.b[i] = ldg_bf16x8(bb + (uint32_t)(rc * sb + cb));
+        R.q[i] = buf_ld16<bf16x8>(rq, (uint32_t)(r * rqk + 2 * c0k));
+        R.k[i] = buf_ld16<bf16x8>(rk, (uint32_t)(r * rqk + 2 * c0k));
+        R.b[i] = buf_ld16<bf16x8>(rbb, (uint32_t)(r * sb + cb));
     }
 }
 
 // Value-side rows of one chunk (state waves): v and w, rows row0 + i,
-// columns c0 .. c0 + 7; rows past the end repeat the last row (masked by the
-// consumer).
+// columns c0 .. c0 + 7 (zero past the end of the sequence).
 template <int V, int RPTV>
 __device__ __forceinline__ void load_values(bf16x8 *v, bf16x8 *w, const FwdParams &p, int64_t c0, int len, int hv,
                                             int row0, int c0v, bool zero_v)
 {
-    const uint16_t *vb = zero_v ? kZerosBf16 : p.v + (c0 * p.HV + hv) * V;
-    const uint16_t *wb = p.w && !zero_v ? p.w + (c0 * p.HV + hv) * V : kOnesBf16;
-    const int sv = zero_v ? 0 : p.HV * V, cv = zero_v ? 0 : c0v;
-    const int sw = p.w && !zero_v ? p.HV * V : 0, cw = p.w && !zero_v ? c0v : 0;
+    const int rs = p.HV * V * 2;
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(p.v + (c0 * p.HV + hv) * V, zero_v ? 0 : len * rs);
+    const __amdgpu_buffer_rsrc_t rw = p.w ? buf_rsrc(p.w + (c0 * p.HV + hv) * V, len * rs) : buf_rsrc(kOnesBf16, 16);
+    const int sw = p.w ? rs : 0, cw = p.w ? 2 * c0v : 0;
     for (int i = 0; i < RPTV; ++i) {
         const int r = row0 + i;
-        const int rc = r < len ? r : len - 1;
-        v[i] = ldg_bf16x8(vb + (uint32_t)(rc * sv + cv));
-        w[i] = ldg_bf16x8(wb + (uint32_t)(rc * sw + cw));
+        v[i] = buf_ld16<bf16x8>(rv, (uint32_t)(r * rs + 2 * c0v));
+        w[i] = buf_ld16<bf16x8>(rw, (uint32_t)(r * sw + cw));
     }
 }
 
@@ -541,16 +549,16 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
 }
 
 // ---------------------------------------------------------------- phase T1 --
-// Diagonal block of T = (I + A)^{-1} (blk: the block's first element in AB):
-// lane l16 solves column l16 (every lane group redundantly) by right-looking
-// forward substitution: as soon as t_c is known, its term is folded into
-// every later row's accumulator, so that the dependent chain is one FMA and
-// one subtraction per row. The block's rows are read as broadcasts, all in
-// flight before the first use. The result is written over A's block in AB
-// (fp32, st_ab) and into TB (bf16, st_tb): lane group q4 writes rows
-// 4 q4 .. 4 q4 + 3 of column l16.
+// Diagonal block of T = (I + A)^{-1} (blk: the block's first element in AB),
+// solved by lanes 0-15 of one wave: lane l16 solves column l16 by
+// right-looking forward substitution (as soon as t_c is known, its term is
+// folded into every later row's accumulator, so that the dependent chain is
+// one FMA and one subtraction per row). The block's rows are read as
+// broadcasts, all in flight before the first use; with one lane group active
+// they cost a quarter of the LDS bandwidth. Column l16 is written over A's
+// block in AB (fp32, st_ab: row 0 of the column) and into TB (bf16, st_tb).
 template <int K, int V>
-__device__ __forceinline__ void t1_block(const char *blk, char *st_ab, char *st_tb, int l16, int q4)
+__device__ __forceinline__ void t1_block(const char *blk, char *st_ab, char *st_tb, int l16)
 {
     using L = Lds<K, V>;
     constexpr int RA = 4 * L::AP, RC = 2 * L::CP;
@@ -565,12 +573,32 @@ __device__ __forceinline__ void t1_block(const char *blk, char *st_ab, char *st_
         t[c] = (c == l16 ? 1.0f : 0.0f) - acc[c];
         for (int r = c + 1; r < 16; ++r) acc[r] = fmaf(a[r][c >> 2][c & 3], t[c], acc[r]);
     }
-    f32x4 out;
-    for (int e = 0; e < 4; ++e)
-        out[e] = q4 == 0 ? t[e] : q4 == 1 ? t[4 + e] : q4 == 2 ? t[8 + e] : t[12 + e];
-    for (int e = 0; e < 4; ++e) {
-        lds_st<float>(st_ab, e * RA, out[e]);
-        lds_st<__bf16>(st_tb, e * RC, (__bf16)out[e]);
+    for (int r = 0; r < 16; ++r) {
+        lds_st<float>(st_ab, r * RA, t[r]);
+        lds_st<__bf16>(st_tb, r * RC, (__bf16)t[r]);
+    }
+}
+
+// One 16-channel tile ct of the pseudo-keys, stored negated and row-major
+// (token, channel) as -wy_w: -wy_w^T = -KB^T T^T, with KB^T operands from
+// transpose reads of the row-major KB.
+template <int K, int V>
+__device__ __forceinline__ void wyw_tile(char *sm, int ct, int l16, int q4)
+{
+    using L = Lds<K, V>;
+    constexpr int RK = 2 * L::KP, RC = 2 * L::CP;
+    const char *const b_kbt = sm + (8 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3) + 32 * ct;  // KB transpose reads
+    const char *const b_c8 = sm + l16 * RC + 16 * q4;              // T rows 16i + l16, columns 32ks + 8q4
+    char *const b_wy = sm + l16 * RK + 8 * q4 + 32 * ct;           // -wy_w stores
+    bf16x8 ak[2];
+    for (int ks = 0; ks < 2; ++ks) {
+        const int o = L::KB + 32 * ks * RK;
+        ak[ks] = cat4(lds_tr(b_kbt, o), lds_tr(b_kbt, o + 4 * RK));
+    }
+    for (int i = 0; i < 4; ++i) {
+        f32x4 acc = {0, 0, 0, 0};
+        for (int ks = 0; ks <= (i >> 1); ++ks) acc = mfma_bf16(ak[ks], lds_ld<bf16x8>(b_c8, L::TB + 16 * i * RC + 64 * ks), acc);
+        lds_st<bf16x4>(b_wy, L::WYW + 16 * i * RK, f32x4_to_bf16(-acc));
     }
 }
 
@@ -592,6 +620,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
     using M = KMap<K>;
     constexpr int RPT = M::RPT;
     constexpr int NCTK = K / 64;            // -wy_w channel tiles per key wave
+    constexpr int NCTK_KEY = NCTK > 1 ? NCTK - 1 : NCTK;  // of which the key wave computes
     constexpr int RK = 2 * L::KP, RC = 2 * L::CP, RA = 4 * L::AP;  // row pitches (bytes)
 
     RawChunk<RPT> R;
@@ -638,8 +667,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             float G[RPT][8], glast[8];
             for (int i = 0; i < RPT; ++i)
                 for (int j = 0; j < 8; ++j)
-                    G[i][j] = (i ? G[i - 1][j] : 0.0f) +
-                              (row0 + i < len ? (j < 4 ? R.g[i][0][j] : R.g[i][1][j - 4]) * LOG2E : 0.0f);
+                    G[i][j] = (i ? G[i - 1][j] : 0.0f) + (j < 4 ? R.g[i][0][j] : R.g[i][1][j - 4]) * LOG2E;
             // the next chunk's g (this chunk's is consumed): a whole chunk
             // period ahead of its use
             if (it + 1 < nc) load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
@@ -669,13 +697,10 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                 lds_st<i32x4>(b_c, L::XF + 16, i32x4{xf[4], xf[5], xf[6], xf[7]});
             }
             for (int j = 0; j < 8; ++j) egl[j] = ex2(glast[j]);
-            const bf16x8 zero = {};
             char *const b_e = sm + o_e;
             for (int i = 0; i < RPT; ++i) {
-                const int r = row0 + i;
-                const bool ok = r < len;
-                const f32x8 qf = bf16x8_to_f32(ok ? R.q[i] : zero);
-                const f32x8 kf = bf16x8_to_f32(ok ? R.k[i] : zero);
+                const f32x8 qf = bf16x8_to_f32(R.q[i]);
+                const f32x8 kf = bf16x8_to_f32(R.k[i]);
                 const f32x8 bk = bf16x8_to_f32(R.b[i]) * kf;
                 f32x8 kb, qh, rr, kt;
                 if (!wx) {
@@ -723,8 +748,9 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         } else {
             exact_ap<K, V>(sm, p, ch, c0, len, qb, tid);
         }
-        t1_block<K, V>(sm + L::AB + rw * (16 * RA + 64), sm + L::AB + 4 * q4 * RA + 4 * l16 + rw * (16 * RA + 64),
-                       sm + L::TB + 4 * q4 * RC + 2 * l16 + rw * (16 * RC + 32), l16, q4);
+        if (q4 == 0)
+            t1_block<K, V>(sm + L::AB + rw * (16 * RA + 64), sm + L::AB + 4 * l16 + rw * (16 * RA + 64),
+                           sm + L::TB + 2 * l16 + rw * (16 * RC + 32), l16);
         __syncthreads();  // ------------------------------------------ B3
 
         // the next chunk's q, k, beta (its g went out in phase E): issued
@@ -738,26 +764,9 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         }
         __syncthreads();  // ------------------------------------------ B4
 
-        // ---- WY: -wy_w^T = -KB^T T^T for this wave's channel tiles, stored
-        // row-major (token, channel) as -wy_w
-        {
-            const char *const b_kbt = sm + (8 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3) + 32 * rw * NCTK;  // KB transpose reads
-            const char *const b_c8 = sm + l16 * RC + 16 * q4;             // T rows 16i + l16, columns 32ks + 8q4
-            char *const b_wy = sm + l16 * RK + 8 * q4 + 32 * rw * NCTK;    // -wy_w stores
-            for (int jt = 0; jt < NCTK; ++jt) {
-                bf16x8 ak[2];
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int o = L::KB + 32 * ks * RK + 32 * jt;
-                    ak[ks] = cat4(lds_tr(b_kbt, o), lds_tr(b_kbt, o + 4 * RK));
-                }
-                for (int i = 0; i < 4; ++i) {
-                    f32x4 acc = {0, 0, 0, 0};
-                    for (int ks = 0; ks <= (i >> 1); ++ks)
-                        acc = mfma_bf16(ak[ks], lds_ld<bf16x8>(b_c8, L::TB + 16 * i * RC + 64 * ks), acc);
-                    lds_st<bf16x4>(b_wy, L::WYW + 16 * i * RK + 32 * jt, f32x4_to_bf16(-acc));
-                }
-            }
-        }
+        // ---- WY: -wy_w for this wave's channel tiles but the last when there
+        // are two (that one goes to a state wave, which has the time)
+        for (int jt = 0; jt < NCTK_KEY; ++jt) wyw_tile<K, V>(sm, rw * NCTK + jt, l16, q4);
         __syncthreads();  // ------------------------------------------ B5
     }
 }
@@ -926,11 +935,9 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         }
         // w v of this chunk, row-major
         {
-            const bf16x8 zero = {};
             char *const b_wv = sm + emv.row0 * RV + 2 * emv.c0;
             for (int i = 0; i < RPTV; ++i) {
-                const int r = emv.row0 + i;
-                const f32x8 wv = bf16x8_to_f32(r < len ? vr[i] : zero) * bf16x8_to_f32(wr[i]);
+                const f32x8 wv = bf16x8_to_f32(vr[i]) * bf16x8_to_f32(wr[i]);
                 lds_st<bf16x8>(b_wv, L::WV + i * RV, f32x8_to_bf16(wv));
             }
         }
@@ -965,7 +972,9 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         }
         __syncthreads();  // ------------------------------------------ B4
 
-        // ---- WY: wy_u = T (w v) for this wave's value columns: U starts here
+        // ---- WY: the last -wy_w channel tile of key wave rw (K = 128), then
+        // wy_u = T (w v) for this wave's value columns: U starts here
+        if constexpr (K / 64 > 1) wyw_tile<K, V>(sm, rw * (K / 64) + K / 64 - 1, l16, q4);
         {
             const char *const b_vt = sm + (8 * q4 + (l16 >> 2)) * RV + 8 * (l16 & 3) + 2 * vbase;  // w v transpose reads
             const char *const b_c8 = sm + o_c8;
