@@ -29,13 +29,15 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 2
+#define GDN2_ABI_VERSION 3
 
 /* Element types a tensor descriptor may carry. */
 typedef enum gdn2_dtype {
     GDN2_DTYPE_BF16 = 1, /* bfloat16 */
     GDN2_DTYPE_F32 = 2,  /* IEEE float32 */
-    GDN2_DTYPE_I32 = 3   /* int32 */
+    GDN2_DTYPE_I32 = 3,  /* int32 */
+    GDN2_DTYPE_F16 = 4,  /* IEEE float16 */
+    GDN2_DTYPE_I64 = 5   /* int64 */
 } gdn2_dtype;
 
 /*
@@ -60,7 +62,7 @@ enum {
     GDN2_ERR_SHAPE = -3,       /* ranks or extents disagree */
     GDN2_ERR_HEADS = -4,       /* HV is not a positive multiple of H */
     GDN2_ERR_UNSUPPORTED = -5, /* (K, V) not in {(64,64), (128,128)} */
-    GDN2_ERR_LAYOUT = -6,      /* a tensor is not row-major contiguous */
+    GDN2_ERR_LAYOUT = -6,      /* a tensor's strides or alignment are not accepted */
     GDN2_ERR_ALIAS = -7,       /* an output overlaps an input */
     GDN2_ERR_HIP = -8          /* the HIP runtime reported an error */
 };
@@ -69,19 +71,27 @@ enum {
  * gdn2_chunk_fwd -- enqueue the GDN-2 chunked prefill forward on `stream`.
  *
  * Tensors (T = total packed tokens, N = number of sequences, H = q/k heads,
- * HV = value heads, K = key dim, V = value dim), all row-major contiguous:
- *   q, k           [T, H, K]       bf16
- *   v, w           [T, HV, V]      bf16
- *   g              [T, HV, K]      float32, natural-log decay, each value <= 0
- *                                  and finite (precondition, not checked)
- *   beta           [T, HV, K]      bf16 (erase gate, taken as given, e.g. in
- *                                  [0, 1] or [0, 2]; not clamped)
- *   initial_state  [N, HV, K, V]   float32, K-major (V innermost)
- *   cu_seqlens     [N + 1]         int32, device memory; cu[0] = 0,
+ * HV = value heads, K = key dim, V = value dim):
+ *   q, k           [T, H, K]       bf16 or float16 (the io type: q's type,
+ *                                  which k, v, beta, w and out must share)
+ *   v, w           [T, HV, V]      io type
+ *   g              [T, HV, K]      float32, bf16 or float16, natural-log
+ *                                  decay, each value <= 0 and finite
+ *                                  (precondition, not checked)
+ *   beta           [T, HV, K]      io type (erase gate, taken as given, e.g.
+ *                                  in [0, 1] or [0, 2]; not clamped)
+ *   initial_state  [N, HV, K, V]   float32, K-major (V innermost); V-major
+ *                                  [N, HV, V, K] with the state_layout option
+ *   cu_seqlens     [N + 1]         int32 or int64, device memory; cu[0] = 0,
  *                                  non-decreasing, cu[N] = T (precondition,
  *                                  not checked on the device)
- *   out            [T, HV, V]      bf16, written for every token
- *   final_state    [N, HV, K, V]   float32
+ *   out            [T, HV, V]      io type, written for every token
+ *   final_state    [N, HV, K, V]   float32, layout as initial_state
+ *
+ * The FlashInfer parameter list names these element types (q, k, v at
+ * float16 or bfloat16, beta and w read at q's type, g at float32, bfloat16
+ * or float16, int32 or int64 cu_seqlens). Arithmetic is float32 throughout;
+ * the MFMA operands are bf16 for either io type.
  *
  * Value head hv reads q/k head hv / (HV / H) (contiguous groups of value
  * heads share one q/k head).
@@ -108,8 +118,16 @@ enum {
  * allocation fails it runs the sequences whole instead. Otherwise it
  * allocates no device memory.
  *
- * Layout: every tensor is row-major contiguous with a 16-byte aligned data
- * pointer (GDN2_ERR_LAYOUT otherwise).
+ * Layout (GDN2_ERR_LAYOUT otherwise; strides are in elements, as the
+ * FlashInfer parameter list has it, only the innermost dimension needs to be
+ * contiguous):
+ *   q, k, v, g, beta, w, out: the K or V elements of each (token, head) row
+ *     contiguous; the token and head strides free, non-negative and
+ *     multiples of 16 bytes, with the token stride at least one row (K or V
+ *     elements) and under 2^31 / 64 bytes; e.g. q, k, v as views of one
+ *     fused [T, 3, H, D] projection. The rows of out must not overlap.
+ *   initial_state, final_state, cu_seqlens: row-major contiguous.
+ *   Every data pointer is 16-byte aligned.
  *
  * Aliasing: neither output (out, final_state) may overlap any input or the
  * other output; in particular final_state may not alias initial_state
@@ -132,9 +150,17 @@ int gdn2_chunk_fwd(const gdn2_tensor *q, const gdn2_tensor *k,
                    const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
                    const gdn2_tensor *final_state, hipStream_t stream);
 
+/* State layouts (gdn2_fwd_options.state_layout). */
+enum {
+    GDN2_STATE_KV = 0, /* [N, HV, K, V]: V innermost (default) */
+    GDN2_STATE_VK = 1  /* [N, HV, V, K]: K innermost, the FlashInfer layout */
+};
+
 /*
- * Options of gdn2_chunk_fwd_opts. `struct_size` must be at least
- * sizeof(gdn2_fwd_options) (later versions may append fields).
+ * Options of gdn2_chunk_fwd_opts and gdn2_recurrent_fwd_opts. Set
+ * `struct_size` to sizeof(gdn2_fwd_options); fields that lie past a smaller
+ * struct_size (a caller built against an earlier version; at least the
+ * first two fields) take their defaults (0).
  *
  * seq_split_chunks selects how a sequence is walked:
  *    0  automatic: gdn2_split_plan() for this shape and the current
@@ -153,14 +179,23 @@ int gdn2_chunk_fwd(const gdn2_tensor *q, const gdn2_tensor *k,
  */
 typedef struct gdn2_fwd_options {
     int32_t struct_size;
-    int32_t seq_split_chunks;
+    int32_t seq_split_chunks; /* chunked entry only; ignored by the recurrent one */
+    /* GDN2_STATE_KV or GDN2_STATE_VK: the layout of initial_state and
+     * final_state (FlashInfer parameter list: its states are V-major) */
+    int32_t state_layout;
+    /* 1: normalise every (token, head) row of q and of k to unit L2 norm
+     * inside the kernel, x / max(||x||_2, 1e-12) in float32 from the stored
+     * values (the FlashInfer use_qk_l2norm_in_kernel flag; the normalisation
+     * is that of the Flash-GDN-2 quick start's torch normalize call); 0: q
+     * and k are used as given */
+    int32_t qk_l2norm;
 } gdn2_fwd_options;
 
 /*
  * gdn2_chunk_fwd_opts -- gdn2_chunk_fwd with options (NULL opts = defaults).
  * Same arguments, contract and errors as gdn2_chunk_fwd, plus
- * GDN2_ERR_SHAPE for a bad options struct (struct_size too small,
- * seq_split_chunks < -1).
+ * GDN2_ERR_SHAPE for a bad options struct (struct_size under 8,
+ * seq_split_chunks < -1, state_layout or qk_l2norm out of range).
  */
 int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
                         const gdn2_tensor *v, const gdn2_tensor *g,
@@ -179,7 +214,7 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
  * difference: final_state may be the very buffer of initial_state (same
  * data pointer) to update the state in place; any other overlap is
  * GDN2_ERR_ALIAS. The arithmetic is the recurrence step by step in float32
- * (state, gates, products); only the output is rounded to bf16.
+ * (state, gates, products); only the output is rounded to the io type.
  *
  * Cost: every (sequence, value head) state is read and written once per
  * call (2 * K * V * 4 bytes), plus the tokens' vectors; one workgroup per
@@ -192,6 +227,20 @@ int gdn2_recurrent_fwd(const gdn2_tensor *q, const gdn2_tensor *k,
                        float scale, const gdn2_tensor *initial_state,
                        const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
                        const gdn2_tensor *final_state, hipStream_t stream);
+
+/*
+ * gdn2_recurrent_fwd_opts -- gdn2_recurrent_fwd with options (NULL opts =
+ * defaults): state_layout and qk_l2norm as for gdn2_chunk_fwd_opts;
+ * seq_split_chunks is ignored. Errors as gdn2_chunk_fwd_opts.
+ */
+int gdn2_recurrent_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
+                            const gdn2_tensor *v, const gdn2_tensor *g,
+                            const gdn2_tensor *beta, const gdn2_tensor *w,
+                            float scale, const gdn2_tensor *initial_state,
+                            const gdn2_tensor *cu_seqlens,
+                            const gdn2_tensor *out,
+                            const gdn2_tensor *final_state,
+                            const gdn2_fwd_options *opts, hipStream_t stream);
 
 /* The host-side validation of gdn2_recurrent_fwd alone (no device work). */
 int gdn2_recurrent_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,

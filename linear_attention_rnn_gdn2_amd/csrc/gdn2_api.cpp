@@ -11,8 +11,11 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <stddef.h>
+
 #include <atomic>
 #include <string>
+#include <utility>
 
 #include "gdn2_internal.h"
 
@@ -37,11 +40,21 @@ const char *dtype_name(int32_t d)
     case GDN2_DTYPE_BF16: return "bf16";
     case GDN2_DTYPE_F32: return "float32";
     case GDN2_DTYPE_I32: return "int32";
+    case GDN2_DTYPE_F16: return "float16";
+    case GDN2_DTYPE_I64: return "int64";
     default: return "unknown";
     }
 }
 
-int64_t elem_size(int32_t d) { return d == GDN2_DTYPE_BF16 ? 2 : 4; }
+int64_t elem_size(int32_t d)
+{
+    switch (d) {
+    case GDN2_DTYPE_BF16:
+    case GDN2_DTYPE_F16: return 2;
+    case GDN2_DTYPE_I64: return 8;
+    default: return 4;
+    }
+}
 
 int64_t numel(const gdn2_tensor *t)
 {
@@ -50,16 +63,28 @@ int64_t numel(const gdn2_tensor *t)
     return n;
 }
 
-// Rank, dtype, extents (-1 = any), non-negative extents, row-major
-// contiguity, non-NULL data when non-empty, 16-byte alignment.
-int check_tensor(const gdn2_tensor *t, const char *name, int32_t dtype, int ndim,
-                 const int64_t *want)
+// How a tensor may be laid out in memory.
+enum Layout {
+    DENSE,  // row-major contiguous
+    ROWS    // [tokens, heads, D]: the D elements of a row contiguous, token
+            // and head strides free (non-negative, multiples of 16 bytes,
+            // the token stride at least one row), rows 16-byte aligned
+};
+
+// Rank, dtype (one of two accepted: dtype2 < 0 for one), extents (-1 = any),
+// non-negative extents, layout, non-NULL data when non-empty, 16-byte
+// alignment.
+int check_tensor(const gdn2_tensor *t, const char *name, int32_t dtype, int32_t dtype2, int ndim,
+                 const int64_t *want, Layout layout = DENSE)
 {
     if (t->ndim != ndim)
         return fail(GDN2_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
-    if (t->dtype != dtype)
-        return fail(GDN2_ERR_DTYPE, "%s: expected %s, got %s", name, dtype_name(dtype),
-                    dtype_name(t->dtype));
+    if (t->dtype != dtype && t->dtype != dtype2) {
+        if (dtype2 >= 0)
+            return fail(GDN2_ERR_DTYPE, "%s: expected %s or %s, got %s", name, dtype_name(dtype), dtype_name(dtype2),
+                        dtype_name(t->dtype));
+        return fail(GDN2_ERR_DTYPE, "%s: expected %s, got %s", name, dtype_name(dtype), dtype_name(t->dtype));
+    }
     for (int d = 0; d < ndim; ++d) {
         if (t->shape[d] < 0)
             return fail(GDN2_ERR_SHAPE, "%s: negative extent in dimension %d", name, d);
@@ -67,12 +92,34 @@ int check_tensor(const gdn2_tensor *t, const char *name, int32_t dtype, int ndim
             return fail(GDN2_ERR_SHAPE, "%s: dimension %d is %lld, expected %lld", name, d,
                         (long long)t->shape[d], (long long)want[d]);
     }
-    int64_t expect = 1;
-    for (int d = ndim - 1; d >= 0; --d) {
-        if (t->shape[d] > 1 && t->stride[d] != expect)
-            return fail(GDN2_ERR_LAYOUT, "%s: not row-major contiguous (dimension %d stride %lld, expected %lld)",
-                        name, d, (long long)t->stride[d], (long long)expect);
-        expect *= t->shape[d];
+    const int64_t es = elem_size(t->dtype);
+    if (layout == ROWS) {
+        const int64_t D = t->shape[2];
+        if (D > 1 && t->stride[2] != 1)
+            return fail(GDN2_ERR_LAYOUT, "%s: the last dimension must be contiguous (stride %lld)", name,
+                        (long long)t->stride[2]);
+        for (int d = 0; d < 2; ++d) {
+            if (t->shape[d] <= 1) continue;
+            if (t->stride[d] < 0 || (t->stride[d] * es) % 16 != 0)
+                return fail(GDN2_ERR_LAYOUT, "%s: dimension %d stride %lld must be non-negative and a multiple of 16 bytes",
+                            name, d, (long long)t->stride[d]);
+        }
+        if (t->shape[0] > 1) {
+            if (t->stride[0] < D)
+                return fail(GDN2_ERR_LAYOUT, "%s: token stride %lld is shorter than a row (%lld elements)", name,
+                            (long long)t->stride[0], (long long)D);
+            if (t->stride[0] * es * 64 > INT32_MAX)
+                return fail(GDN2_ERR_LAYOUT, "%s: token stride %lld is too large (64 rows must span under 2 GiB)",
+                            name, (long long)t->stride[0]);
+        }
+    } else {
+        int64_t expect = 1;
+        for (int d = ndim - 1; d >= 0; --d) {
+            if (t->shape[d] > 1 && t->stride[d] != expect)
+                return fail(GDN2_ERR_LAYOUT, "%s: not row-major contiguous (dimension %d stride %lld, expected %lld)",
+                            name, d, (long long)t->stride[d], (long long)expect);
+            expect *= t->shape[d];
+        }
     }
     if (numel(t) > 0) {
         if (!t->data)
@@ -83,10 +130,39 @@ int check_tensor(const gdn2_tensor *t, const char *name, int32_t dtype, int ndim
     return GDN2_OK;
 }
 
+// Whether the [tokens, heads, D] rows of a ROWS tensor are pairwise disjoint:
+// with the token and head dimensions taken in order of increasing stride,
+// each stride must reach past everything the smaller ones span.
+bool rows_disjoint(const gdn2_tensor *t)
+{
+    int64_t st[2] = {t->stride[0], t->stride[1]}, ex[2] = {t->shape[0], t->shape[1]};
+    if (st[0] > st[1]) {
+        std::swap(st[0], st[1]);
+        std::swap(ex[0], ex[1]);
+    }
+    int64_t span = t->shape[2];  // elements one row covers
+    for (int d = 0; d < 2; ++d) {
+        if (ex[d] <= 1) continue;
+        if (st[d] < span) return false;
+        span += (ex[d] - 1) * st[d];
+    }
+    return true;
+}
+
+// Bytes from the first to one past the last element (strided tensors: the
+// whole span, which is conservative for interleaved views).
+int64_t span_bytes(const gdn2_tensor *t)
+{
+    if (numel(t) == 0) return 0;
+    int64_t last = 0;
+    for (int d = 0; d < t->ndim; ++d) last += (t->shape[d] - 1) * t->stride[d];
+    return (last + 1) * elem_size(t->dtype);
+}
+
 bool overlaps(const gdn2_tensor *a, const gdn2_tensor *b)
 {
     if (!a || !b || !a->data || !b->data) return false;
-    const int64_t na = numel(a) * elem_size(a->dtype), nb = numel(b) * elem_size(b->dtype);
+    const int64_t na = span_bytes(a), nb = span_bytes(b);
     if (na == 0 || nb == 0) return false;
     const uintptr_t pa = reinterpret_cast<uintptr_t>(a->data), pb = reinterpret_cast<uintptr_t>(b->data);
     return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
@@ -103,12 +179,13 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     if (!v) return fail(GDN2_ERR_NULL_ARG, "v is NULL");
     if (!out) return fail(GDN2_ERR_NULL_ARG, "out is NULL");
     int rc;
-    if ((rc = check_tensor(q, "q", GDN2_DTYPE_BF16, 3, nullptr))) return rc;
+    if ((rc = check_tensor(q, "q", GDN2_DTYPE_BF16, GDN2_DTYPE_F16, 3, nullptr, ROWS))) return rc;
+    const int32_t io = q->dtype;  // q, k, v, beta, w and out share one 16-bit type
     const int64_t T = q->shape[0], H = q->shape[1], K = q->shape[2];
     const int64_t qs[3] = {T, H, K};
-    if ((rc = check_tensor(k, "k", GDN2_DTYPE_BF16, 3, qs))) return rc;
+    if ((rc = check_tensor(k, "k", io, -1, 3, qs, ROWS))) return rc;
     const int64_t vs_any[3] = {T, -1, -1};
-    if ((rc = check_tensor(v, "v", GDN2_DTYPE_BF16, 3, vs_any))) return rc;
+    if ((rc = check_tensor(v, "v", io, -1, 3, vs_any, ROWS))) return rc;
     const int64_t HV = v->shape[1], V = v->shape[2];
     if (H < 1 || HV < H || HV % H != 0)
         return fail(GDN2_ERR_HEADS, "value heads (%lld) must be a positive multiple of q/k heads (%lld)",
@@ -119,13 +196,18 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     if (T > INT32_MAX)
         return fail(GDN2_ERR_SHAPE, "T = %lld exceeds the int32 range of cu_seqlens", (long long)T);
     const int64_t vs[3] = {T, HV, V}, gs[3] = {T, HV, K};
-    if (w && (rc = check_tensor(w, "w", GDN2_DTYPE_BF16, 3, vs))) return rc;
-    if (g && (rc = check_tensor(g, "g", GDN2_DTYPE_F32, 3, gs))) return rc;
-    if (beta && (rc = check_tensor(beta, "beta", GDN2_DTYPE_BF16, 3, gs))) return rc;
-    if ((rc = check_tensor(out, "out", GDN2_DTYPE_BF16, 3, vs))) return rc;
+    if (w && (rc = check_tensor(w, "w", io, -1, 3, vs, ROWS))) return rc;
+    if (g) {
+        if (g->dtype != GDN2_DTYPE_F32 && g->dtype != GDN2_DTYPE_BF16 && g->dtype != GDN2_DTYPE_F16)
+            return fail(GDN2_ERR_DTYPE, "g: expected float32, bf16 or float16, got %s", dtype_name(g->dtype));
+        if ((rc = check_tensor(g, "g", g->dtype, -1, 3, gs, ROWS))) return rc;
+    }
+    if (beta && (rc = check_tensor(beta, "beta", io, -1, 3, gs, ROWS))) return rc;
+    if ((rc = check_tensor(out, "out", io, -1, 3, vs, ROWS))) return rc;
+    if (!rows_disjoint(out)) return fail(GDN2_ERR_LAYOUT, "out: rows overlap each other");
     int64_t N = 1;
     if (cu) {
-        if ((rc = check_tensor(cu, "cu_seqlens", GDN2_DTYPE_I32, 1, nullptr))) return rc;
+        if ((rc = check_tensor(cu, "cu_seqlens", GDN2_DTYPE_I32, GDN2_DTYPE_I64, 1, nullptr))) return rc;
         N = cu->shape[0] - 1;
         if (N < 1) return fail(GDN2_ERR_SHAPE, "cu_seqlens needs at least 2 entries (N >= 1)");
         if (!cu->data) return fail(GDN2_ERR_NULL_ARG, "cu_seqlens: data is NULL");
@@ -133,8 +215,8 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     if (N * HV > INT32_MAX)
         return fail(GDN2_ERR_SHAPE, "N * HV = %lld exceeds the grid limit", (long long)(N * HV));
     const int64_t ss[4] = {N, HV, K, V};
-    if (h0 && (rc = check_tensor(h0, "initial_state", GDN2_DTYPE_F32, 4, ss))) return rc;
-    if (ht && (rc = check_tensor(ht, "final_state", GDN2_DTYPE_F32, 4, ss))) return rc;
+    if (h0 && (rc = check_tensor(h0, "initial_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
+    if (ht && (rc = check_tensor(ht, "final_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
 
     const gdn2_tensor *inputs[] = {q, k, v, g, beta, w, h0, cu};
     const char *in_names[] = {"q", "k", "v", "g", "beta", "w", "initial_state", "cu_seqlens"};
@@ -153,11 +235,11 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
         p->q = static_cast<const uint16_t *>(q->data);
         p->k = static_cast<const uint16_t *>(k->data);
         p->v = static_cast<const uint16_t *>(v->data);
-        p->g = g ? static_cast<const float *>(g->data) : nullptr;
+        p->g = g ? g->data : nullptr;
         p->beta = beta ? static_cast<const uint16_t *>(beta->data) : nullptr;
         p->w = w ? static_cast<const uint16_t *>(w->data) : nullptr;
         p->h0 = h0 ? static_cast<const float *>(h0->data) : nullptr;
-        p->cu = cu ? static_cast<const int32_t *>(cu->data) : nullptr;
+        p->cu = cu ? cu->data : nullptr;
         p->out = static_cast<uint16_t *>(out->data);
         p->ht = ht ? static_cast<float *>(ht->data) : nullptr;
         p->T = T;
@@ -167,21 +249,65 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
         p->K = (int32_t)K;
         p->V = (int32_t)V;
         p->scale = scale == 0.0f ? (float)(1.0 / sqrt((double)K)) : scale;
+        p->io = io == GDN2_DTYPE_F16 ? gdn2::IO_F16 : gdn2::IO_BF16;
+        p->gtype = !g || g->dtype == GDN2_DTYPE_F32 ? gdn2::G_F32
+                   : g->dtype == GDN2_DTYPE_BF16    ? gdn2::G_BF16
+                                                    : gdn2::G_F16;
+        p->cu64 = cu && cu->dtype == GDN2_DTYPE_I64;
+        // token and head strides (elements). A dimension of extent one is
+        // only ever indexed at 0; its token stride is then taken as one row,
+        // which keeps the kernels' chunk ranges (rows x token stride) whole.
+        // An omitted tensor is never addressed.
+        auto st = [](const gdn2_tensor *t, int d) { return t && t->shape[d] > 1 ? t->stride[d] : 0; };
+        auto tok = [](const gdn2_tensor *t) { return !t ? 0 : t->shape[0] > 1 ? t->stride[0] : t->shape[2]; };
+        p->sq = tok(q);
+        p->sk = tok(k);
+        p->sv = tok(v);
+        p->sw = tok(w);
+        p->sg = tok(g);
+        p->sb = tok(beta);
+        p->so = tok(out);
+        p->hsq = st(q, 1);
+        p->hsk = st(k, 1);
+        p->hsv = st(v, 1);
+        p->hsw = st(w, 1);
+        p->hsg = st(g, 1);
+        p->hsb = st(beta, 1);
+        p->hso = st(out, 1);
+        p->state_vmajor = 0;
+        p->qk_l2norm = 0;
     }
     return GDN2_OK;
 }
 
-int read_options(const gdn2_fwd_options *opts, int32_t *split)
+// Options: fields past struct_size keep their defaults, so that callers
+// built against an older, shorter struct keep working.
+struct Options {
+    int32_t split = 0, vmajor = 0, l2norm = 0;
+};
+
+int read_options(const gdn2_fwd_options *opts, Options *o)
 {
-    *split = 0;
+    *o = Options{};
     if (!opts) return GDN2_OK;
-    if (opts->struct_size < (int32_t)sizeof(gdn2_fwd_options))
-        return fail(GDN2_ERR_SHAPE, "options: struct_size %d is smaller than %d", opts->struct_size,
-                    (int)sizeof(gdn2_fwd_options));
+    const int32_t sz = opts->struct_size;
+    if (sz < (int32_t)(2 * sizeof(int32_t)))
+        return fail(GDN2_ERR_SHAPE, "options: struct_size %d is smaller than %d", sz, (int)(2 * sizeof(int32_t)));
     if (opts->seq_split_chunks < -1)
         return fail(GDN2_ERR_SHAPE, "options: seq_split_chunks must be -1, 0 or positive (got %d)",
                     opts->seq_split_chunks);
-    *split = opts->seq_split_chunks;
+    o->split = opts->seq_split_chunks;
+    if (sz >= (int32_t)(offsetof(gdn2_fwd_options, state_layout) + sizeof(int32_t))) {
+        if (opts->state_layout != GDN2_STATE_KV && opts->state_layout != GDN2_STATE_VK)
+            return fail(GDN2_ERR_SHAPE, "options: state_layout must be GDN2_STATE_KV or GDN2_STATE_VK (got %d)",
+                        opts->state_layout);
+        o->vmajor = opts->state_layout == GDN2_STATE_VK;
+    }
+    if (sz >= (int32_t)(offsetof(gdn2_fwd_options, qk_l2norm) + sizeof(int32_t))) {
+        if (opts->qk_l2norm != 0 && opts->qk_l2norm != 1)
+            return fail(GDN2_ERR_SHAPE, "options: qk_l2norm must be 0 or 1 (got %d)", opts->qk_l2norm);
+        o->l2norm = opts->qk_l2norm;
+    }
     return GDN2_OK;
 }
 
@@ -230,8 +356,11 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_t
     gdn2::FwdParams p;
     int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p);
     if (rc != GDN2_OK) return rc;
-    int32_t split = 0;
-    if ((rc = read_options(opts, &split)) != GDN2_OK) return rc;
+    Options o;
+    if ((rc = read_options(opts, &o)) != GDN2_OK) return rc;
+    int32_t split = o.split;
+    p.state_vmajor = o.vmajor;
+    p.qk_l2norm = o.l2norm;
     p.seg_chunks = 0;
     p.nseg = 1;
     p.pass = gdn2::PASS_OUTPUT;
@@ -280,9 +409,23 @@ int gdn2_recurrent_fwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_te
                        const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens,
                        const gdn2_tensor *out, const gdn2_tensor *final_state, hipStream_t stream)
 {
+    return gdn2_recurrent_fwd_opts(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state,
+                                   nullptr, stream);
+}
+
+int gdn2_recurrent_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
+                            const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                            const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens,
+                            const gdn2_tensor *out, const gdn2_tensor *final_state,
+                            const gdn2_fwd_options *opts, hipStream_t stream)
+{
     gdn2::FwdParams p;
     int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p, true);
     if (rc != GDN2_OK) return rc;
+    Options o;
+    if ((rc = read_options(opts, &o)) != GDN2_OK) return rc;
+    p.state_vmajor = o.vmajor;
+    p.qk_l2norm = o.l2norm;
     p.seg_chunks = 0;
     p.nseg = 1;
     p.pass = gdn2::PASS_OUTPUT;

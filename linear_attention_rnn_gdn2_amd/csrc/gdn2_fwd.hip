@@ -62,6 +62,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;       // chunk length
@@ -75,13 +78,34 @@ constexpr float XLIM = 120.0f;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------- helpers --
-__device__ __forceinline__ f32x8 bf16x8_to_f32(bf16x8 x) { return __builtin_convertvector(x, f32x8); }
 __device__ __forceinline__ bf16x8 f32x8_to_bf16(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 __device__ __forceinline__ bf16x4 f32x4_to_bf16(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 
-__device__ __forceinline__ bf16x8 ldg_bf16x8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-__device__ __forceinline__ f32x4 ldg_f32x4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Element type of q, k, v, beta, w and out: bf16 (IO_BF16) or fp16 (IO_F16).
+// Values are widened to float32 on load; the MFMA operands built from them
+// are bf16 either way.
+template <int IO>
+struct IoT;
+template <>
+struct IoT<IO_BF16> {
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+};
+template <>
+struct IoT<IO_F16> {
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+};
+template <int IO>
+__device__ __forceinline__ float io_bits_to_f32(uint16_t b)
+{
+    if constexpr (IO == IO_F16) return (float)__builtin_bit_cast(_Float16, b);
+    else return bf16_bits_to_f32(b);
+}
+template <typename T8>
+__device__ __forceinline__ f32x8 to_f32x8(T8 x) { return __builtin_convertvector(x, f32x8); }
 
 template <typename T>
 __device__ __forceinline__ T lds_ld(const char *base, int off) { return *reinterpret_cast<const T *>(base + off); }
@@ -103,10 +127,6 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) { return __builtin_sh
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -185,7 +205,9 @@ struct Lds {
     static constexpr int XL = XF + K * 4;                          // exact-channel list  [K] int
     static constexpr int FL = XL + K * 4;                          // per key wave: any exact channel [4] int
     static constexpr int XN = FL + 16;                             // exact-channel count int
-    static constexpr int TOTAL = XN + 16;
+    static constexpr int NP = XN + 16;                             // q/k L2 norms: per key wave partial sums of squares [4][64] (q, k) fp32
+    static constexpr int NRM = NP + 4 * CH * 8;                    // q/k L2 norms: reciprocal norms [64] (q, k) fp32  E -> exact AP
+    static constexpr int TOTAL = NRM + CH * 8;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -214,10 +236,10 @@ struct EMap {
 // end of the sequence hold a copy of its last row; the consumer zeroes them,
 // so that no instruction touches the registers while the loads are in
 // flight (a select right after a load would wait for it).
-template <int RPT>
+template <int RPT, int IO>
 struct RawChunk {
-    bf16x8 q[RPT], k[RPT], b[RPT];
-    f32x4 g[RPT][2];
+    typename IoT<IO>::v8 q[RPT], k[RPT], b[RPT];
+    f32x4 g[RPT][2];  // float32 g: 8 values; 16-bit g: the 8 values in g[i][0]
 };
 
 // Chunk loads are buffer loads: a scalar resource per (chunk, tensor) whose
@@ -228,8 +250,9 @@ struct RawChunk {
 // 16-byte row of ones with row stride 0 (beta, w = 1; on padded rows k and v
 // are zero); an omitted g, or values taken as zero, is a resource of length
 // zero.
-__device__ __attribute__((aligned(16))) uint16_t kOnesBf16[8] = {0x3f80, 0x3f80, 0x3f80, 0x3f80,
-                                                               0x3f80, 0x3f80, 0x3f80, 0x3f80};
+__device__ __attribute__((aligned(16))) uint16_t kOnes16[2][8] = {
+    {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80},   // bf16 1.0
+    {0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00}};  // fp16 1.0
 
 constexpr int BUF_DWORD3 = 0x00020000;  // raw (unformatted) buffer, gfx9 family
 
@@ -243,50 +266,67 @@ __device__ __forceinline__ T buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int K, int RPT>
-__device__ __forceinline__ void load_decay(RawChunk<RPT> &R, const FwdParams &p, int64_t c0, int len, int hv,
+template <int K, int RPT, int IO, bool G16>
+__device__ __forceinline__ void load_decay(RawChunk<RPT, IO> &R, const FwdParams &p, int64_t c0, int len, int hv,
                                            int row0, int c0k)
 {
-    const int rs = p.HV * K * 4;  // row stride (bytes)
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(p.g ? p.g + (c0 * p.HV + hv) * K : nullptr, p.g ? len * rs : 0);
+    constexpr int ES = G16 ? 2 : 4;  // bytes per g element
+    const int rs = (int)p.sg * ES;  // token stride (bytes)
+    const char *gb = static_cast<const char *>(p.g);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gb ? gb + (c0 * p.sg + hv * p.hsg) * ES : nullptr, gb ? len * rs : 0);
     for (int i = 0; i < RPT; ++i) {
-        const uint32_t o = (uint32_t)((row0 + i) * rs + 4 * c0k);
+        const uint32_t o = (uint32_t)((row0 + i) * rs + ES * c0k);
         R.g[i][0] = buf_ld16<f32x4>(rg, o);
-        R.g[i][1] = buf_ld16<f32x4>(rg, o + 16);
+        if constexpr (!G16) R.g[i][1] = buf_ld16<f32x4>(rg, o + 16);
     }
 }
 
-template <int K, int RPT>
-__device__ __forceinline__ void load_keys(RawChunk<RPT> &R, const FwdParams &p, int64_t c0, int len, int hk,
+// g of row i of a RawChunk as float32 (natural-log units)
+template <int RPT, int IO, bool G16>
+__device__ __forceinline__ f32x8 decay_row(const RawChunk<RPT, IO> &R, int i, bool g_f16)
+{
+    if constexpr (G16) {
+        return g_f16 ? to_f32x8(__builtin_bit_cast(f16x8, R.g[i][0])) : to_f32x8(__builtin_bit_cast(bf16x8, R.g[i][0]));
+    } else {
+        return __builtin_shufflevector(R.g[i][0], R.g[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+template <int K, int RPT, int IO>
+__device__ __forceinline__ void load_keys(RawChunk<RPT, IO> &R, const FwdParams &p, int64_t c0, int len, int hk,
                                           int hv, int row0, int c0k)
 {
-    const int rqk = p.H * K * 2, rb = p.HV * K * 2;  // row strides (bytes)
-    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(p.q + (c0 * p.H + hk) * K, len * rqk);
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(p.k + (c0 * p.H + hk) * K, len * rqk);
-    const __amdgpu_buffer_rsrc_t rbb = p.beta ? buf_rsrc(p.beta + (c0 * p.HV + hv) * K, len * rb) : buf_rsrc(kOnesBf16, 16);
+    typedef typename IoT<IO>::v8 T8;
+    const int rq = (int)p.sq * 2, rk = (int)p.sk * 2, rb = (int)p.sb * 2;  // token strides (bytes)
+    const __amdgpu_buffer_rsrc_t bq = buf_rsrc(p.q + c0 * p.sq + hk * p.hsq, len * rq);
+    const __amdgpu_buffer_rsrc_t bk = buf_rsrc(p.k + c0 * p.sk + hk * p.hsk, len * rk);
+    const __amdgpu_buffer_rsrc_t rbb =
+        p.beta ? buf_rsrc(p.beta + c0 * p.sb + hv * p.hsb, len * rb) : buf_rsrc(kOnes16[IO], 16);
     const int sb = p.beta ? rb : 0, cb = p.beta ? 2 * c0k : 0;
     for (int i = 0; i < RPT; ++i) {
         const int r = row0 + i;
-        R.q[i] = buf_ld16<bf16x8>(rq, (uint32_t)(r * rqk + 2 * c0k));
-        R.k[i] = buf_ld16<bf16x8>(rk, (uint32_t)(r * rqk + 2 * c0k));
-        R.b[i] = buf_ld16<bf16x8>(rbb, (uint32_t)(r * sb + cb));
+        R.q[i] = buf_ld16<T8>(bq, (uint32_t)(r * rq + 2 * c0k));
+        R.k[i] = buf_ld16<T8>(bk, (uint32_t)(r * rk + 2 * c0k));
+        R.b[i] = buf_ld16<T8>(rbb, (uint32_t)(r * sb + cb));
     }
 }
 
 // Value-side rows of one chunk (state waves): v and w, rows row0 + i,
 // columns c0 .. c0 + 7 (zero past the end of the sequence).
-template <int V, int RPTV>
-__device__ __forceinline__ void load_values(bf16x8 *v, bf16x8 *w, const FwdParams &p, int64_t c0, int len, int hv,
-                                            int row0, int c0v, bool zero_v)
+template <int V, int RPTV, int IO>
+__device__ __forceinline__ void load_values(typename IoT<IO>::v8 *v, typename IoT<IO>::v8 *w, const FwdParams &p,
+                                            int64_t c0, int len, int hv, int row0, int c0v, bool zero_v)
 {
-    const int rs = p.HV * V * 2;
-    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(p.v + (c0 * p.HV + hv) * V, zero_v ? 0 : len * rs);
-    const __amdgpu_buffer_rsrc_t rw = p.w ? buf_rsrc(p.w + (c0 * p.HV + hv) * V, len * rs) : buf_rsrc(kOnesBf16, 16);
-    const int sw = p.w ? rs : 0, cw = p.w ? 2 * c0v : 0;
+    typedef typename IoT<IO>::v8 T8;
+    const int rs = (int)p.sv * 2, rsw = (int)p.sw * 2;  // token strides (bytes)
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(p.v + c0 * p.sv + hv * p.hsv, zero_v ? 0 : len * rs);
+    const __amdgpu_buffer_rsrc_t rw =
+        p.w ? buf_rsrc(p.w + c0 * p.sw + hv * p.hsw, len * rsw) : buf_rsrc(kOnes16[IO], 16);
+    const int sw = p.w ? rsw : 0, cw = p.w ? 2 * c0v : 0;
     for (int i = 0; i < RPTV; ++i) {
         const int r = row0 + i;
-        v[i] = buf_ld16<bf16x8>(rv, (uint32_t)(r * rs + 2 * c0v));
-        w[i] = buf_ld16<bf16x8>(rw, (uint32_t)(r * sw + cw));
+        v[i] = buf_ld16<T8>(rv, (uint32_t)(r * rs + 2 * c0v));
+        w[i] = buf_ld16<T8>(rw, (uint32_t)(r * sw + cw));
     }
 }
 
@@ -370,6 +410,7 @@ struct Chain {
     int64_t tb, te;   // token range (the sequence, or one segment of it)
     const float *s0;  // entering state [K][V] (nullptr: zero)
     float *s1;        // destination of the leaving state [K][V] (nullptr: none)
+    bool s0_vm, s1_vm; // s0 / s1 stored V-major ([V][K]): the caller's states with that option
     bool ident;       // entering state is the identity (transition pass, K == V)
     bool zero_v;      // values taken as zero (transition pass)
     bool out;         // write the output rows
@@ -422,7 +463,7 @@ __device__ __forceinline__ f32x4 ap_mask(f32x4 x, bool diag, bool isP, int l16, 
 // bounded |G| (RR is zero on the others); every exact channel then adds
 // beta_r k_r k_s exp(G_r - G_s) and q_r k_s exp(G_r - G_s) per pair,
 // NXB channels per batch, with G rebuilt from g in float32.
-template <int K, int V>
+template <int K, int V, int IO, bool G16, bool L2N>
 __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_t c0, int len, int qb, int tid)
 {
     using L = Lds<K, V>;
@@ -465,10 +506,13 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
     const int r = tid >> 3, sb = tid & 7;
     float accA[8], accP[8];
     for (int u = 0; u < 8; ++u) accA[u] = accP[u] = 0.0f;
-    const float *gp = p.g ? p.g + (c0 * p.HV + ch.hv) * K : nullptr;
-    const uint16_t *qp = p.q + (c0 * p.H + ch.hk) * K;
-    const uint16_t *kp = p.k + (c0 * p.H + ch.hk) * K;
-    const uint16_t *bp = p.beta ? p.beta + (c0 * p.HV + ch.hv) * K : nullptr;
+    const int64_t goff = c0 * p.sg + ch.hv * p.hsg;
+    const float *gp = p.g ? static_cast<const float *>(p.g) + goff : nullptr;          // float32 g
+    const uint16_t *gh = p.g ? static_cast<const uint16_t *>(p.g) + goff : nullptr;    // 16-bit g
+    const bool g_f16 = p.gtype == G_F16;
+    const uint16_t *qp = p.q + c0 * p.sq + ch.hk * p.hsq;
+    const uint16_t *kp = p.k + c0 * p.sk + ch.hk * p.hsk;
+    const uint16_t *bp = p.beta ? p.beta + c0 * p.sb + ch.hv * p.hsb : nullptr;
     for (int b0 = 0; b0 < nx; b0 += NXB) {
         const int nb = nx - b0 < NXB ? nx - b0 : NXB;
         __syncthreads();  // the previous batch is consumed
@@ -481,10 +525,20 @@ __device__ void exact_ap(char *smem, const FwdParams &p, const Chain &ch, int64_
                 const int rr = ti * RPX + u;
                 const bool ok = x < nb && rr < len;
                 const int64_t t = ok ? rr : 0;
-                const float gv = ok && gp ? gp[t * p.HV * K + c] * LOG2E : 0.0f;
-                const float qv = ok ? bf16_bits_to_f32(qp[t * p.H * K + c]) : 0.0f;
-                const float kk = ok ? bf16_bits_to_f32(kp[t * p.H * K + c]) : 0.0f;
-                const float bv = ok && bp ? bf16_bits_to_f32(bp[t * p.HV * K + c]) : 1.0f;
+                float gv = 0.0f;
+                if (ok && gp) {
+                    if constexpr (G16) gv = (g_f16 ? io_bits_to_f32<IO_F16>(gh[t * p.sg + c])
+                                                   : io_bits_to_f32<IO_BF16>(gh[t * p.sg + c])) * LOG2E;
+                    else gv = gp[t * p.sg + c] * LOG2E;
+                }
+                float qv = ok ? io_bits_to_f32<IO>(qp[t * p.sq + c]) : 0.0f;
+                float kk = ok ? io_bits_to_f32<IO>(kp[t * p.sk + c]) : 0.0f;
+                const float bv = ok && bp ? io_bits_to_f32<IO>(bp[t * p.sb + c]) : 1.0f;
+                if constexpr (L2N) {
+                    const f32x2 nr = lds_ld<f32x2>(smem, L::NRM + 8 * (int)t);
+                    qv *= nr[0];
+                    kk *= nr[1];
+                }
                 run += gv;
                 gs[u] = run;
                 bk[u] = bv * kk;
@@ -609,11 +663,48 @@ __device__ __forceinline__ bool any_exact(const char *fl)
     return (f[0] | f[1] | f[2] | f[3]) != 0;
 }
 
+// Wait for a chunk's raw inputs (the asm consumes the registers).
+template <int RPT, int IO, bool G16>
+__device__ __forceinline__ void await_raw(const RawChunk<RPT, IO> &R)
+{
+    for (int i = 0; i < RPT; ++i) {
+        if constexpr (G16) asm volatile("" ::"v"(R.q[i]), "v"(R.k[i]), "v"(R.b[i]), "v"(R.g[i][0]));
+        else asm volatile("" ::"v"(R.q[i]), "v"(R.k[i]), "v"(R.b[i]), "v"(R.g[i][0]), "v"(R.g[i][1]));
+    }
+}
+
+// In-kernel q/k L2 normalisation, first half: the sums of squares of q and
+// k over this lane's 8 channels of each of its rows, added over the lanes of
+// the row group (the wave's K/4 channels) and stored per key wave,
+// NP[wave][row] = (sum q^2, sum k^2). Phase E of the chunk adds the four
+// waves' parts.
+template <int K, int V, int RPT, int IO>
+__device__ __forceinline__ void norm_partials(const RawChunk<RPT, IO> &R, char *sm, int rt)
+{
+    using L = Lds<K, V>;
+    using M = KMap<K>;
+    const M em(rt);
+    const int w = rt >> 6;
+    for (int i = 0; i < RPT; ++i) {
+        const f32x8 qf = to_f32x8(R.q[i]), kf = to_f32x8(R.k[i]);
+        float sq = 0.0f, sk = 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            sq = fmaf(qf[j], qf[j], sq);
+            sk = fmaf(kf[j], kf[j], sk);
+        }
+        for (int d = 1; d < M::NCG; d <<= 1) {
+            sq += __shfl_xor(sq, d);
+            sk += __shfl_xor(sk, d);
+        }
+        if (em.cgl == 0) lds_st<f32x2>(sm, L::NP + 8 * (w * CH + em.row0 + i), f32x2{sq, sk});
+    }
+}
+
 // ------------------------------------------------------------- key waves --
 // Barrier sequence per iteration (must match state_role): B2, then
 // (exact_ap), B3, B4, B5. LDS addressing as in state_role: per-lane bases
 // plus compile-time constants.
-template <int K, int V>
+template <int K, int V, int IO, bool G16, bool L2N>
 __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const Chain &ch, int tid, int nc)
 {
     using L = Lds<K, V>;
@@ -623,16 +714,19 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
     constexpr int NCTK_KEY = NCTK > 1 ? NCTK - 1 : NCTK;  // of which the key wave computes
     constexpr int RK = 2 * L::KP, RC = 2 * L::CP, RA = 4 * L::AP;  // row pitches (bytes)
 
-    RawChunk<RPT> R;
+    const bool g_f16 = p.gtype == G_F16;
+    RawChunk<RPT, IO> R;
     if (nc > 0) {
         const M em(tid & (NROLE - 1));
-        load_decay<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hv, em.row0, em.c0);
-        load_keys<K, RPT>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hk, ch.hv, em.row0, em.c0);
+        load_decay<K, RPT, IO, G16>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hv, em.row0, em.c0);
+        load_keys<K, RPT, IO>(R, p, ch.tb, chunk_len(ch.tb, ch.te), ch.hk, ch.hv, em.row0, em.c0);
         // complete the first chunk's loads before the loop, so that inside
         // it the vector memory counter only tracks the in-loop prefetch,
         // issued g first (a wait for g then leaves q, k, beta in flight)
-        for (int i = 0; i < RPT; ++i) asm volatile("" ::"v"(R.q[i]), "v"(R.k[i]), "v"(R.b[i]), "v"(R.g[i][0]), "v"(R.g[i][1]));
+        await_raw<RPT, IO, G16>(R);
+        if constexpr (L2N) norm_partials<K, V, RPT, IO>(R, smem, tid & (NROLE - 1));
     }
+    if constexpr (L2N) __syncthreads();  // ------------------- the first chunk's norms
 
     char *const smem0 = smem;
     const int tid0 = tid;
@@ -663,14 +757,15 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             // all of this chunk's raw inputs are complete here: the next
             // chunk's g is issued below, and a later wait for q, k, beta
             // would otherwise also wait for it
-            for (int i = 0; i < RPT; ++i) asm volatile("" ::"v"(R.q[i]), "v"(R.k[i]), "v"(R.b[i]), "v"(R.g[i][0]), "v"(R.g[i][1]));
+            await_raw<RPT, IO, G16>(R);
             float G[RPT][8], glast[8];
-            for (int i = 0; i < RPT; ++i)
-                for (int j = 0; j < 8; ++j)
-                    G[i][j] = (i ? G[i - 1][j] : 0.0f) + (j < 4 ? R.g[i][0][j] : R.g[i][1][j - 4]) * LOG2E;
+            for (int i = 0; i < RPT; ++i) {
+                const f32x8 gi = decay_row<RPT, IO, G16>(R, i, g_f16);
+                for (int j = 0; j < 8; ++j) G[i][j] = (i ? G[i - 1][j] : 0.0f) + gi[j] * LOG2E;
+            }
             // the next chunk's g (this chunk's is consumed): a whole chunk
             // period ahead of its use
-            if (it + 1 < nc) load_decay<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
+            if (it + 1 < nc) load_decay<K, RPT, IO, G16>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
             for (int j = 0; j < 8; ++j) {
                 float incl, tot;
                 wave_scan<M::NCG>(G[RPT - 1][j], lane, incl, tot);
@@ -697,11 +792,28 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                 lds_st<i32x4>(b_c, L::XF + 16, i32x4{xf[4], xf[5], xf[6], xf[7]});
             }
             for (int j = 0; j < 8; ++j) egl[j] = ex2(glast[j]);
+            // in-kernel L2 normalisation: the reciprocal norms of this
+            // lane's rows from the key waves' partial sums (x / max(|x|, eps))
+            float nq[RPT], nk[RPT];
+            if constexpr (L2N) {
+                for (int i = 0; i < RPT; ++i) {
+                    const int o = L::NP + 8 * (row0 + i);
+                    const f32x2 ss = lds_ld<f32x2>(sm, o) + lds_ld<f32x2>(sm, o + 8 * CH) +
+                                     lds_ld<f32x2>(sm, o + 16 * CH) + lds_ld<f32x2>(sm, o + 24 * CH);
+                    nq[i] = 1.0f / fmaxf(sqrtf(ss[0]), 1e-12f);
+                    nk[i] = 1.0f / fmaxf(sqrtf(ss[1]), 1e-12f);
+                    if (rw == 0 && em.cgl == 0) lds_st<f32x2>(sm, L::NRM + 8 * (row0 + i), f32x2{nq[i], nk[i]});
+                }
+            }
             char *const b_e = sm + o_e;
             for (int i = 0; i < RPT; ++i) {
-                const f32x8 qf = bf16x8_to_f32(R.q[i]);
-                const f32x8 kf = bf16x8_to_f32(R.k[i]);
-                const f32x8 bk = bf16x8_to_f32(R.b[i]) * kf;
+                f32x8 qf = to_f32x8(R.q[i]);
+                f32x8 kf = to_f32x8(R.k[i]);
+                if constexpr (L2N) {
+                    qf *= nq[i];
+                    kf *= nk[i];
+                }
+                const f32x8 bk = to_f32x8(R.b[i]) * kf;
                 f32x8 kb, qh, rr, kt;
                 if (!wx) {
                     for (int j = 0; j < 8; ++j) {
@@ -746,7 +858,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             const f32x4 x = ap_mask(ap_tile_at<K>(b_k8 + L::RR, b_k8 + L::KB), true, false, l16, q4);
             lds_st<f32x4>(sm, L::AB + l16 * RA + 16 * q4 + rw * (16 * RA + 64), x);
         } else {
-            exact_ap<K, V>(sm, p, ch, c0, len, qb, tid);
+            exact_ap<K, V, IO, G16, L2N>(sm, p, ch, c0, len, qb, tid);
         }
         if (q4 == 0)
             t1_block<K, V>(sm + L::AB + rw * (16 * RA + 64), sm + L::AB + 4 * l16 + rw * (16 * RA + 64),
@@ -758,15 +870,19 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // stalls until the CU's memory pipeline has room); WY and the next
         // phase E hide the latency
         if (it + 1 < nc) {
-            load_keys<K, RPT>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
+            load_keys<K, RPT, IO>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
         } else {
-            R = RawChunk<RPT>{};  // ends the live range of this chunk's values here
+            R = RawChunk<RPT, IO>{};  // ends the live range of this chunk's values here
         }
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- WY: -wy_w for this wave's channel tiles but the last when there
         // are two (that one goes to a state wave, which has the time)
         for (int jt = 0; jt < NCTK_KEY; ++jt) wyw_tile<K, V>(sm, rw * NCTK + jt, l16, q4);
+        // the next chunk's norm partials (its q, k arrive here; phase E of
+        // this chunk has read the previous ones)
+        if constexpr (L2N)
+            if (it + 1 < nc) norm_partials<K, V, RPT, IO>(R, sm, rt);
         __syncthreads();  // ------------------------------------------ B5
     }
 }
@@ -777,7 +893,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
 // opaque zero is added to a handful of base pointers once per chunk, so the
 // constants fold into the instructions' offset fields (and pairs of reads
 // merge) instead of being hoisted out of the loop one register per address.
-template <int K, int V>
+template <int K, int V, int IO, bool G16, bool L2N>
 __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const Chain &ch, int tid, int nc)
 {
     using L = Lds<K, V>;
@@ -803,9 +919,10 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int l16 = lane & 15, q4 = lane >> 4;
         const int vbase = rw * VW;
         const float *h0 = ch.s0;
+        const int sr = ch.s0_vm ? 1 : V, sc = ch.s0_vm ? K : 1;  // strides of (state row, column)
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16];
+                for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * sr + (vbase + 16 * jt + l16) * sc];
         // complete these loads here: left outstanding into the chunk
         // loop, they make every later write of S wait on the vector
         // memory counter, which then also waits for the v, w prefetch
@@ -816,6 +933,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int jt = 0; jt < NCT; ++jt) S[it][jt] = f32x4{0, 0, 0, 0};
     }
     f32x4 U[4][NCT];  // wy_u, then U, of the chunk in the state pass
+    if constexpr (L2N) __syncthreads();  // ------------------- the first chunk's norms (key waves)
 
     char *const smem0 = smem;
     const int tid0 = tid;
@@ -864,8 +982,8 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
 
         // this chunk's v and w (stored as w v after B2; the latency hides
         // behind the rest of phase S, AP and T1)
-        bf16x8 vr[RPTV], wr[RPTV];
-        if (act) load_values<V, RPTV>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0, ch.zero_v);
+        typename IoT<IO>::v8 vr[RPTV], wr[RPTV];
+        if (act) load_values<V, RPTV, IO>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0, ch.zero_v);
 
         // ---- S, second half: the output, computed transposed,
         // O^T = scale (S^T QH^T + U^T P^T), stored as 4 consecutive values
@@ -893,8 +1011,9 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                     }
                     if (row < lenp)
                         for (int jt = 0; jt < NCT; ++jt)
-                            *reinterpret_cast<bf16x4 *>(p.out + ((cp + row) * p.HV + ch.hv) * V + vbase + 16 * jt + 4 * q4) =
-                                f32x4_to_bf16(Y[jt] * p.scale);
+                            *reinterpret_cast<typename IoT<IO>::v4 *>(p.out + (cp + row) * p.so + ch.hv * p.hso + vbase +
+                                                                      16 * jt + 4 * q4) =
+                                __builtin_convertvector(Y[jt] * p.scale, typename IoT<IO>::v4);
                 }
             }
             const char *const b_kt = sm + (4 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3);  // KT transpose reads
@@ -931,13 +1050,13 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                 else lds_st<f32x4>(sm, L::AB + o_a4 + 16 * i * RA + 64 * j, x);
             }
         } else {
-            exact_ap<K, V>(sm, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
+            exact_ap<K, V, IO, G16, L2N>(sm, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
         }
         // w v of this chunk, row-major
         {
             char *const b_wv = sm + emv.row0 * RV + 2 * emv.c0;
             for (int i = 0; i < RPTV; ++i) {
-                const f32x8 wv = bf16x8_to_f32(vr[i]) * bf16x8_to_f32(wr[i]);
+                const f32x8 wv = to_f32x8(vr[i]) * to_f32x8(wr[i]);
                 lds_st<bf16x8>(b_wv, L::WV + i * RV, f32x8_to_bf16(wv));
             }
         }
@@ -1001,12 +1120,14 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int vbase = rw * VW;
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e) ch.s1[(16 * it + 4 * q4 + e) * V + vbase + 16 * jt + l16] = S[it][jt][e];
+                for (int e = 0; e < 4; ++e)
+                    ch.s1[(16 * it + 4 * q4 + e) * (ch.s1_vm ? 1 : V) + (vbase + 16 * jt + l16) * (ch.s1_vm ? K : 1)] =
+                        S[it][jt][e];
     }
 }
 
 // ------------------------------------------------------------------ kernel --
-template <int K, int V>
+template <int K, int V, int IO, bool G16, bool L2N>
 __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
 {
     using L = Lds<K, V>;
@@ -1025,13 +1146,14 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     ch.n = item / p.HV;
     ch.hv = item - ch.n * p.HV;
     ch.hk = ch.hv / (p.HV / p.H);
-    const int64_t sb = p.cu ? (int64_t)p.cu[ch.n] : 0;
-    const int64_t se = p.cu ? (int64_t)p.cu[ch.n + 1] : p.T;
+    const int64_t sb = p.cu ? cu_at(p, ch.n) : 0;
+    const int64_t se = p.cu ? cu_at(p, ch.n + 1) : p.T;
     const int64_t shead = ((int64_t)ch.n * p.HV + ch.hv) * K * V;  // [N, HV, K, V] states
     ch.tb = sb;
     ch.te = se;
     ch.s0 = p.h0 ? p.h0 + shead : nullptr;
     ch.s1 = p.ht ? p.ht + shead : nullptr;
+    ch.s0_vm = ch.s1_vm = p.state_vmajor != 0;
     ch.ident = ch.zero_v = false;
     ch.out = true;
     if (p.seg_chunks) {
@@ -1046,6 +1168,7 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
             // nothing follows the last segment; the first one's map is not needed
             if (seg >= last || (kind == 1 && seg == 0)) return;
             ch.out = false;
+            ch.s1_vm = false;  // the workspace is K-major
             if (kind == 0) {
                 if (seg > 0) ch.s0 = nullptr;
                 ch.s1 = p.wb + sseg;
@@ -1055,7 +1178,10 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
                 ch.s1 = p.wm + sseg;
             }
         } else {
-            if (seg > 0) ch.s0 = p.ws + sseg;
+            if (seg > 0) {
+                ch.s0 = p.ws + sseg;
+                ch.s0_vm = false;
+            }
             if (seg < last) ch.s1 = nullptr;
         }
     }
@@ -1073,8 +1199,8 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     // a wave-uniform test, so that the two roles are separate branches and
     // not one exec-masked instruction stream (whose wait-counter analysis
     // would mix the roles' outstanding loads)
-    if (__builtin_amdgcn_readfirstlane(tid) >= NROLE) key_role<K, V>(smem, p, ch, tid, nc);
-    else state_role<K, V>(smem, p, ch, tid, nc);
+    if (__builtin_amdgcn_readfirstlane(tid) >= NROLE) key_role<K, V, IO, G16, L2N>(smem, p, ch, tid, nc);
+    else state_role<K, V, IO, G16, L2N>(smem, p, ch, tid, nc);
 }
 
 // ------------------------------------------------------ segment combine --
@@ -1096,8 +1222,8 @@ __global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams
     const int ncb = V / CMB_COLS;
     const int chain = blockIdx.x / ncb, cb = blockIdx.x - chain * ncb;
     const int n = chain / p.HV;
-    const int64_t sb = p.cu ? (int64_t)p.cu[n] : 0;
-    const int64_t se = p.cu ? (int64_t)p.cu[n + 1] : p.T;
+    const int64_t sb = p.cu ? cu_at(p, n) : 0;
+    const int64_t se = p.cu ? cu_at(p, n + 1) : p.T;
     const int64_t nch = (se - sb + CH - 1) / CH;
     const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;
     if (last == 0) return;
@@ -1145,14 +1271,36 @@ hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+namespace {
+// one instantiation per (K, V, io type, 16-bit g, L2 normalisation)
+template <int K, int V, int IO, bool G16>
+void launch_chunk_l2(const FwdParams &p, dim3 grid, hipStream_t stream)
+{
+    if (p.qk_l2norm) hipLaunchKernelGGL((chunk_fwd_kernel<K, V, IO, G16, true>), grid, dim3(NTHR), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_fwd_kernel<K, V, IO, G16, false>), grid, dim3(NTHR), 0, stream, p);
+}
+template <int K, int V>
+void launch_chunk_typed(const FwdParams &p, dim3 grid, hipStream_t stream)
+{
+    const bool g16 = p.gtype != G_F32;
+    if (p.io == IO_F16) {
+        if (g16) launch_chunk_l2<K, V, IO_F16, true>(p, grid, stream);
+        else launch_chunk_l2<K, V, IO_F16, false>(p, grid, stream);
+    } else {
+        if (g16) launch_chunk_l2<K, V, IO_BF16, true>(p, grid, stream);
+        else launch_chunk_l2<K, V, IO_BF16, false>(p, grid, stream);
+    }
+}
+}  // namespace
+
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
 {
     const int64_t items = (int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1) * (p.pass == PASS_TRANSITION ? 2 : 1);
-    const dim3 grid((unsigned)items), block(NTHR);
+    const dim3 grid((unsigned)items);
     if (p.K == 128 && p.V == 128)
-        hipLaunchKernelGGL((chunk_fwd_kernel<128, 128>), grid, block, 0, stream, p);
+        launch_chunk_typed<128, 128>(p, grid, stream);
     else if (p.K == 64 && p.V == 64)
-        hipLaunchKernelGGL((chunk_fwd_kernel<64, 64>), grid, block, 0, stream, p);
+        launch_chunk_typed<64, 64>(p, grid, stream);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

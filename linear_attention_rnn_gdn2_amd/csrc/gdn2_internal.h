@@ -11,19 +11,30 @@ namespace gdn2 {
 // Validated, resolved arguments of one forward call. Pointers are device
 // pointers; optional ones are nullptr when omitted.
 struct FwdParams {
-    const uint16_t *q;     // [T, H, K] bf16
-    const uint16_t *k;     // [T, H, K] bf16
-    const uint16_t *v;     // [T, HV, V] bf16
-    const float *g;        // [T, HV, K] or nullptr (= 0)
-    const uint16_t *beta;  // [T, HV, K] bf16 or nullptr (= 1)
-    const uint16_t *w;     // [T, HV, V] bf16 or nullptr (= 1)
-    const float *h0;       // [N, HV, K, V] or nullptr (= 0)
-    const int32_t *cu;     // [N + 1] or nullptr (one sequence of T tokens)
-    uint16_t *out;         // [T, HV, V] bf16
-    float *ht;             // [N, HV, K, V] or nullptr (not written)
+    // Element types: the io type (q, k, v, beta, w, out) is bf16 or fp16
+    // (IO_BF16 / IO_F16); g is fp32, bf16 or fp16 (G_F32 / G_BF16 / G_F16).
+    const uint16_t *q;     // [T, H, K] io
+    const uint16_t *k;     // [T, H, K] io
+    const uint16_t *v;     // [T, HV, V] io
+    const void *g;         // [T, HV, K] g type, or nullptr (= 0)
+    const uint16_t *beta;  // [T, HV, K] io, or nullptr (= 1)
+    const uint16_t *w;     // [T, HV, V] io, or nullptr (= 1)
+    const float *h0;       // [N, HV, K, V] (or [N, HV, V, K]) or nullptr (= 0)
+    const void *cu;        // [N + 1] int32 or int64, or nullptr (one sequence of T tokens)
+    uint16_t *out;         // [T, HV, V] io
+    float *ht;             // [N, HV, K, V] (or [N, HV, V, K]) or nullptr (not written)
     int64_t T;
     int32_t N, H, HV, K, V;
     float scale;           // already resolved (never 0)
+    int32_t io;            // IO_BF16 or IO_F16
+    int32_t gtype;         // G_F32, G_BF16 or G_F16
+    int32_t cu64;          // cu_seqlens is int64
+    // element strides of the token and head dimensions; the K or V
+    // elements of one (token, head) row are contiguous
+    int64_t sq, sk, sv, sw, sg, sb, so;          // per token
+    int64_t hsq, hsk, hsv, hsw, hsg, hsb, hso;   // per head
+    int32_t state_vmajor;  // initial/final state stored [N, HV, V, K]
+    int32_t qk_l2norm;     // normalise q and k rows in the kernel
     // Sequence split (0: one workgroup walks each whole sequence). With
     // seg_chunks > 0 every sequence is cut into segments of seg_chunks
     // chunks (nseg per sequence at most) and the launch is one of:
@@ -36,6 +47,14 @@ struct FwdParams {
 };
 
 enum { PASS_OUTPUT = 0, PASS_TRANSITION = 1 };
+enum { IO_BF16 = 0, IO_F16 = 1 };
+enum { G_F32 = 0, G_BF16 = 1, G_F16 = 2 };
+
+// cu_seqlens[i] as int64 (either stored type)
+__host__ __device__ inline int64_t cu_at(const FwdParams &p, int64_t i)
+{
+    return p.cu64 ? static_cast<const int64_t *>(p.cu)[i] : (int64_t) static_cast<const int32_t *>(p.cu)[i];
+}
 
 // Enqueue the fused chunked forward on `stream` (one pass, as p describes).
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);

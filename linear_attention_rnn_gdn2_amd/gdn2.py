@@ -16,14 +16,18 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn2.so")
 
-GDN2_DTYPE_BF16, GDN2_DTYPE_F32, GDN2_DTYPE_I32 = 1, 2, 3
-_DTYPES = {torch.bfloat16: GDN2_DTYPE_BF16, torch.float32: GDN2_DTYPE_F32, torch.int32: GDN2_DTYPE_I32}
+GDN2_DTYPE_BF16, GDN2_DTYPE_F32, GDN2_DTYPE_I32, GDN2_DTYPE_F16, GDN2_DTYPE_I64 = 1, 2, 3, 4, 5
+_DTYPES = {torch.bfloat16: GDN2_DTYPE_BF16, torch.float32: GDN2_DTYPE_F32, torch.int32: GDN2_DTYPE_I32,
+           torch.float16: GDN2_DTYPE_F16, torch.int64: GDN2_DTYPE_I64}
+GDN2_STATE_KV, GDN2_STATE_VK = 0, 1
+_LAYOUTS = {"kv": GDN2_STATE_KV, "vk": GDN2_STATE_VK}
 
 STATUS = {0: "OK", -1: "NULL_ARG", -2: "DTYPE", -3: "SHAPE", -4: "HEADS",
           -5: "UNSUPPORTED", -6: "LAYOUT", -7: "ALIAS", -8: "HIP"}
 
 EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_opts", "gdn2_chunk_fwd_check", "gdn2_split_plan",
-            "gdn2_recurrent_fwd", "gdn2_recurrent_fwd_check", "gdn2_last_error", "gdn2_abi_version"]
+            "gdn2_recurrent_fwd", "gdn2_recurrent_fwd_opts", "gdn2_recurrent_fwd_check", "gdn2_last_error",
+            "gdn2_abi_version"]
 
 
 class Gdn2Tensor(ctypes.Structure):
@@ -34,7 +38,17 @@ class Gdn2Tensor(ctypes.Structure):
 
 class Gdn2FwdOptions(ctypes.Structure):
     """Mirror of ``gdn2_fwd_options``."""
-    _fields_ = [("struct_size", ctypes.c_int32), ("seq_split_chunks", ctypes.c_int32)]
+    _fields_ = [("struct_size", ctypes.c_int32), ("seq_split_chunks", ctypes.c_int32),
+                ("state_layout", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32)]
+
+
+def make_options(seq_split=0, state_layout="kv", qk_l2norm=False):
+    """A filled ``gdn2_fwd_options`` (state_layout "kv": [N, HV, K, V],
+    "vk": [N, HV, V, K])."""
+    if state_layout not in _LAYOUTS:
+        raise ValueError(f"state_layout must be 'kv' or 'vk', not {state_layout!r}")
+    return Gdn2FwdOptions(ctypes.sizeof(Gdn2FwdOptions), int(seq_split or 0), _LAYOUTS[state_layout],
+                          1 if qk_l2norm else 0)
 
 
 class Gdn2Error(RuntimeError):
@@ -63,6 +77,9 @@ def load_library():
         lib.gdn2_chunk_fwd_opts.restype = ctypes.c_int
         lib.gdn2_recurrent_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
         lib.gdn2_recurrent_fwd.restype = ctypes.c_int
+        lib.gdn2_recurrent_fwd_opts.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P,
+                                                ctypes.POINTER(Gdn2FwdOptions), ctypes.c_void_p]
+        lib.gdn2_recurrent_fwd_opts.restype = ctypes.c_int
         lib.gdn2_recurrent_fwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
         lib.gdn2_recurrent_fwd_check.restype = ctypes.c_int
         lib.gdn2_split_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
@@ -122,20 +139,7 @@ def split_plan(T, N, HV, num_cu):
     return load_library().gdn2_split_plan(int(T), int(N), int(HV), int(num_cu))
 
 
-def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
-              cu_seqlens=None, output_final_state=True, out=None, final_state=None,
-              seq_split=None):
-    """GDN-2 chunked prefill forward on the current HIP stream.
-
-    q, k [T, H, K] bf16; v, w [T, HV, V] bf16; g [T, HV, K] float32;
-    beta [T, HV, K] bf16; initial_state [N, HV, K, V] float32;
-    cu_seqlens [N + 1] int32 (None: one sequence). ``scale`` None or 0 means
-    1/sqrt(K). Returns (out [T, HV, V] bf16, final_state or None).
-    Preallocated ``out`` / ``final_state`` are written in place.
-    ``seq_split``: None or 0 automatic, -1 never split sequences, n > 0
-    split every sequence into segments of n 64-token chunks.
-    """
-    lib = load_library()
+def _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out, final_state, g, beta, w):
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w),
                     ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
         if t is not None and not t.is_cuda:
@@ -144,17 +148,39 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
     K = q.shape[2]
     N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
     if out is None:
-        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
+        out = torch.empty((T, HV, V), dtype=q.dtype, device=v.device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
     descs = [describe(x) for x in (q, k, v, g, beta, w)]
     rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
+    return out, final_state, descs, rest
+
+
+def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
+              cu_seqlens=None, output_final_state=True, out=None, final_state=None,
+              seq_split=None, state_layout="kv", qk_l2norm=False):
+    """GDN-2 chunked prefill forward on the current HIP stream.
+
+    q, k [T, H, K] and v, w [T, HV, V], beta [T, HV, K], out: bf16 or
+    float16 (q's type); g [T, HV, K] float32, bf16 or float16;
+    initial_state [N, HV, K, V] float32 ([N, HV, V, K] with
+    ``state_layout="vk"``); cu_seqlens [N + 1] int32 or int64 (None: one
+    sequence). Strided views are accepted where the rows are contiguous.
+    ``scale`` None or 0 means 1/sqrt(K). Returns (out [T, HV, V],
+    final_state or None); preallocated ``out`` / ``final_state`` are written
+    in place. ``seq_split``: None or 0 automatic, -1 never split sequences,
+    n > 0 split every sequence into segments of n 64-token chunks.
+    ``qk_l2norm``: normalise q and k rows in the kernel.
+    """
+    lib = load_library()
+    out, final_state, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out,
+                                             final_state, g, beta, w)
     stream = torch.cuda.current_stream(v.device).cuda_stream
-    if seq_split is None:
+    if seq_split is None and state_layout == "kv" and not qk_l2norm:
         rc = lib.gdn2_chunk_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
                                 *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
     else:
-        opts = Gdn2FwdOptions(ctypes.sizeof(Gdn2FwdOptions), int(seq_split))
+        opts = make_options(seq_split, state_layout, qk_l2norm)
         rc = lib.gdn2_chunk_fwd_opts(*[_ptr(d) for d in descs], _scale_arg(scale),
                                      *[_ptr(d) for d in rest], ctypes.byref(opts), ctypes.c_void_p(stream))
     if rc != 0:
@@ -163,29 +189,24 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
 
 
 def recurrent_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
-                  cu_seqlens=None, output_final_state=True, out=None, final_state=None):
+                  cu_seqlens=None, output_final_state=True, out=None, final_state=None,
+                  state_layout="kv", qk_l2norm=False):
     """The same forward evaluated token by token (decode and short spans).
 
-    Tensors as in :func:`chunk_fwd`. ``final_state`` may be ``initial_state``
-    itself to update the state in place.
+    Tensors and options as in :func:`chunk_fwd`. ``final_state`` may be
+    ``initial_state`` itself to update the state in place.
     """
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w),
-                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
-        if t is not None and not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
-    T, HV, V = v.shape
-    K = q.shape[2]
-    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
-    if out is None:
-        out = torch.empty((T, HV, V), dtype=torch.bfloat16, device=v.device)
-    if final_state is None and output_final_state:
-        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
-    descs = [describe(x) for x in (q, k, v, g, beta, w)]
-    rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
+    out, final_state, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out,
+                                             final_state, g, beta, w)
     stream = torch.cuda.current_stream(v.device).cuda_stream
-    rc = lib.gdn2_recurrent_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
-                                *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
+    if state_layout == "kv" and not qk_l2norm:
+        rc = lib.gdn2_recurrent_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
+                                    *[_ptr(d) for d in rest], ctypes.c_void_p(stream))
+    else:
+        opts = make_options(0, state_layout, qk_l2norm)
+        rc = lib.gdn2_recurrent_fwd_opts(*[_ptr(d) for d in descs], _scale_arg(scale),
+                                         *[_ptr(d) for d in rest], ctypes.byref(opts), ctypes.c_void_p(stream))
     if rc != 0:
         raise Gdn2Error(rc, last_error())
     return out, final_state

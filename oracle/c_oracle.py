@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 from .build import LIB
-from .recurrence import resolve_scale
+from .recurrence import l2_normalize_rows, resolve_scale
 
 _F64, _F32, _BF16 = 0, 1, 2
 _lib = None
@@ -66,9 +66,13 @@ def max_threads() -> int:
 
 
 def gdn2_recurrence_c(q, k, v, g=None, beta=None, w=None, scale=None,
-                      initial_state=None, cu_seqlens=None, heads=None):
-    """Same contract as :func:`oracle.recurrence.gdn2_recurrence`."""
+                      initial_state=None, cu_seqlens=None, heads=None, qk_l2norm=False):
+    """Same contract as :func:`oracle.recurrence.gdn2_recurrence` (with
+    ``qk_l2norm`` the rows of q and k are normalised in float64 first, by the
+    same reading, and the C loop runs on them)."""
     lib = _load()
+    if qk_l2norm:
+        q, k = l2_normalize_rows(q), l2_normalize_rows(k)
     qa, qd = _arr(q)
     ka, kd = _arr(k)
     va, vd = _arr(v)

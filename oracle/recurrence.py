@@ -26,6 +26,12 @@ Readings taken where the pages leave a step open:
 * Varlen packing: tokens of all sequences end to end, sequence n spans
   ``cu_seqlens[n] .. cu_seqlens[n+1]`` (FlashInfer docs, description and
   ``cu_seqlens`` parameter). Each sequence starts from its own initial state.
+* ``qk_l2norm`` (FlashInfer docs, ``use_qk_l2norm_in_kernel``: the q/k L2
+  normalisation moved into the kernel instead of pre-normalised inputs): the
+  pages do not spell the normalisation out; the one they use to make the
+  pre-normalised inputs is the Flash-GDN-2 README quick start's torch
+  ``normalize`` over the head dimension, x / max(||x||_2, 1e-12), applied
+  here to every (token, head) row of q and of k before the recurrence.
 """
 
 from __future__ import annotations
@@ -43,7 +49,21 @@ def resolve_scale(scale, K: int) -> float:
 
 
 def _f64(x):
-    return None if x is None else np.asarray(x, dtype=np.float64)
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor (e.g. bf16, which numpy lacks)
+        import torch
+        return x.detach().cpu().to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def l2_normalize_rows(x, eps: float = 1e-12):
+    """Each row along the last (head) axis divided by max(its L2 norm, eps),
+    in float64: the reading of the in-kernel q/k normalisation (module
+    docstring)."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
 
 
 def gdn2_sequence(q, k, v, g, beta, w, scale, S0):
@@ -73,7 +93,7 @@ def gdn2_sequence(q, k, v, g, beta, w, scale, S0):
 
 
 def gdn2_recurrence(q, k, v, g=None, beta=None, w=None, scale=None,
-                    initial_state=None, cu_seqlens=None, heads=None):
+                    initial_state=None, cu_seqlens=None, heads=None, qk_l2norm=False):
     """FP64 oracle of the GDN-2 forward over packed (varlen) sequences.
 
     Arguments follow the boundary's layout (any float dtype; upcast to float64
@@ -83,10 +103,13 @@ def gdn2_recurrence(q, k, v, g=None, beta=None, w=None, scale=None,
       sequence of T tokens).
     ``heads``: optional list of value-head indices to evaluate (each head is an
     independent recurrence); outputs then carry only those heads, in order.
+    ``qk_l2norm``: normalise every (token, head) row of q and k first.
 
     Returns (out [T, nH, V] float64, final_state [N, nH, K, V] float64).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
+    if qk_l2norm:
+        q, k = l2_normalize_rows(q), l2_normalize_rows(k)
     T, H, K = q.shape
     HV, V = v.shape[1], v.shape[2]
     if HV % H != 0:

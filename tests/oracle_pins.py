@@ -303,7 +303,41 @@ def pin_varlen(fn):
     _close(S[1], S0[1], 0.0, "empty sequence keeps its state")
 
 
+# --------------------------------------------------------------------------- #
+# In-kernel q/k L2 normalisation (FlashInfer docs, use_qk_l2norm_in_kernel).
+# Facts that hold for any correct normalisation of each (token, head) row
+# over the head dimension, whatever the raw norms:
+#  * retrieval: q_t = c_t k_t, beta = 1 returns sign(c_t) scale w v exactly;
+#  * invariance: positive per-row rescaling of q or k changes nothing;
+#  * unit rows: the option is the identity;
+#  * a zero row of q gives a zero output row (no division by zero).
+# --------------------------------------------------------------------------- #
+def pin_qk_l2norm(fn):
+    r = _rng(31)
+    T, H, K, V = 16, 2, 6, 5
+    q, k, v, g, beta, w, S0 = _rand_case(31, T=T, H=H, HV=2 * H, K=K, V=V, g_max=1.0)
+    raw_k = k * r.uniform(0.3, 4.0, size=(T, H, 1))
+    c = r.uniform(0.2, 3.0, size=(T, H, 1)) * np.where(r.random((T, H, 1)) < 0.3, -1.0, 1.0)
+    ones = np.ones_like(beta)
+    o, _ = fn(c * raw_k, raw_k, v, g, ones, w, 0.7, S0, qk_l2norm=True)
+    sgn = np.repeat(np.sign(c), 2, axis=1)  # value heads 2h, 2h + 1 read q/k head h
+    _close(o, 0.7 * sgn * w * v, TOL, "l2norm retrieval")
+    o1, s1 = fn(q, k, v, g, beta, w, 0.9, S0, qk_l2norm=True)
+    a = r.uniform(0.1, 5.0, size=(T, H, 1))
+    b = r.uniform(0.1, 5.0, size=(T, H, 1))
+    o2, s2 = fn(a * q, b * k, v, g, beta, w, 0.9, S0, qk_l2norm=True)
+    _close(o2, o1, TOL, "l2norm invariance (output)")
+    _close(s2, s1, TOL, "l2norm invariance (state)")
+    o3, s3 = fn(q, k, v, g, beta, w, 0.9, S0)
+    _close(o1, o3, TOL, "l2norm on unit rows (output)")
+    _close(s1, s3, TOL, "l2norm on unit rows (state)")
+    qz = q.copy()
+    qz[5] = 0.0
+    o4, _ = fn(qz, k, v, g, beta, w, 0.9, S0, qk_l2norm=True)
+    assert np.all(np.isfinite(o4)) and np.all(o4[5] == 0.0), "l2norm zero row"
+
+
 ALL_PINS = [pin_hand_worked, pin_matrix_form, pin_retrieval, pin_linear_attention,
             pin_gated_linear_attention, pin_scalar_gdn, pin_wy_solve, pin_split_carry,
             pin_linearity, pin_key_permutation, pin_value_permutation, pin_heads_and_gva,
-            pin_single_token, pin_defaults, pin_varlen]
+            pin_single_token, pin_defaults, pin_varlen, pin_qk_l2norm]

@@ -46,8 +46,8 @@ def test_abi_version_matches_header(gdn2):
 
 def test_status_codes_match_header(gdn2):
     src = open(HEADER).read()
-    codes = dict((int(v), k) for k, v in re.findall(r"GDN2_(?:ERR_)?(\w+) = (-?\d+)", src)
-                 if k not in ("DTYPE_BF16", "DTYPE_F32", "DTYPE_I32", "ABI_VERSION"))
+    codes = dict((int(v), k) for k, ok, v in re.findall(r"GDN2_(?:ERR_(\w+)|(OK)) = (-?\d+)", src)
+                 for k in [k or ok])
     assert codes == gdn2.STATUS
 
 
@@ -86,9 +86,16 @@ def test_valid_calls(gdn2):
     (lambda c: c.update(v=None), "NULL_ARG"),
     (lambda c: c.update(out=None), "NULL_ARG"),
     (lambda c: c.update(q=c["q"].float()), "DTYPE"),
-    (lambda c: c.update(g=c["g"].bfloat16()), "DTYPE"),
+    (lambda c: c.update(g=c["g"].double()), "DTYPE"),
+    (lambda c: c.update(g=c["g"].int()), "DTYPE"),
+    (lambda c: c.update(k=c["k"].half()), "DTYPE"),                     # io types disagree
+    (lambda c: c.update(beta=c["beta"].half()), "DTYPE"),
+    (lambda c: c.update(out=c["out"].half()), "DTYPE"),
+    (lambda c: c.update(q=c["q"].half(), k=c["k"].half(), v=c["v"].half(), beta=c["beta"].half(),
+                        w=c["w"].half()), "DTYPE"),                       # out left bf16
     (lambda c: c.update(initial_state=c["initial_state"].bfloat16()), "DTYPE"),
-    (lambda c: c.update(cu_seqlens=c["cu_seqlens"].long()), "DTYPE"),
+    (lambda c: c.update(cu_seqlens=c["cu_seqlens"].float()), "DTYPE"),
+    (lambda c: c.update(cu_seqlens=c["cu_seqlens"].short()), "DTYPE"),
     (lambda c: c.update(out=c["out"].float()), "DTYPE"),
     (lambda c: c.update(k=c["k"][:60]), "SHAPE"),
     (lambda c: c.update(beta=c["beta"][:, :2]), "SHAPE"),
@@ -102,6 +109,16 @@ def test_valid_calls(gdn2):
     (lambda c: c.update(v=torch.zeros(70, 4, 128, dtype=torch.bfloat16)), "UNSUPPORTED"),
     (lambda c: c.update(v=torch.zeros(70, 64, 4, dtype=torch.bfloat16).transpose(1, 2)), "LAYOUT"),
     (lambda c: c.update(q=torch.zeros(70 * 2 * 64 + 1, dtype=torch.bfloat16)[1:].view(70, 2, 64)), "LAYOUT"),
+    # head stride of 68 elements: rows not 16-byte aligned
+    (lambda c: c.update(q=torch.zeros(70, 2, 68, dtype=torch.bfloat16)[:, :, :64]), "LAYOUT"),
+    # token stride shorter than a row (rows of one head overlap)
+    (lambda c: c.update(k=torch.zeros(2 * 70 * 64, dtype=torch.bfloat16).as_strided((70, 2, 64), (8, 64 * 70, 1))),
+     "LAYOUT"),
+    # a broadcast (stride 0) token dimension: shorter than a row
+    (lambda c: c.update(v=torch.zeros(1, 4, 64, dtype=torch.bfloat16).expand(70, 4, 64)), "LAYOUT"),
+    # out rows overlapping each other (two heads at one address)
+    (lambda c: c.update(out=torch.zeros(70, 1, 64, dtype=torch.bfloat16).expand(70, 4, 64)), "LAYOUT"),
+    (lambda c: c.update(initial_state=c["initial_state"].transpose(2, 3)), "LAYOUT"),
 ])
 def test_rejections(gdn2, mutate, expect):
     c = case()
@@ -109,6 +126,39 @@ def test_rejections(gdn2, mutate, expect):
     code, msg = status(gdn2, **c)
     assert code == expect, (code, msg)
     assert msg
+
+
+def test_accepted_types_and_strides(gdn2):
+    """fp16 io, 16-bit g, int64 cu_seqlens, and strided views whose rows are
+    contiguous (FlashInfer parameter list: strides honoured, innermost
+    dimension contiguous) pass validation."""
+    c = case()
+    for n in ("q", "k", "v", "beta", "w", "out"):
+        c[n] = c[n].half()
+    assert status(gdn2, **c) == ("OK", "")
+    for gt in (torch.bfloat16, torch.float16):
+        c = case()
+        c["g"] = c["g"].to(gt)
+        assert status(gdn2, **c)[0] == "OK"
+    c = case()
+    c["cu_seqlens"] = c["cu_seqlens"].long()
+    assert status(gdn2, **c)[0] == "OK"
+    # q, k, v as views of one fused [T, 3, H, D] projection (H = HV here)
+    c = case(H=4)
+    qkv = torch.zeros(70, 3, 4, 64, dtype=torch.bfloat16)
+    c["q"], c["k"], c["v"] = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    assert status(gdn2, **c) == ("OK", "")
+    # head-major storage [H, T, D] seen as [T, H, D]; padded token rows
+    c = case()
+    c["q"] = torch.zeros(2, 70, 64, dtype=torch.bfloat16).transpose(0, 1)
+    c["g"] = torch.zeros(70, 4, 72)[:, :, :64]
+    c["out"] = torch.zeros(4, 70, 64, dtype=torch.bfloat16).transpose(0, 1)
+    assert status(gdn2, **c) == ("OK", "")
+    # one token: its token stride is never used
+    c = case(T=1)
+    c["cu_seqlens"] = torch.tensor([0, 1, 1], dtype=torch.int32)
+    c["q"] = torch.zeros(1, 2, 64, dtype=torch.bfloat16).as_strided((1, 2, 64), (3, 64, 1))
+    assert status(gdn2, **c) == ("OK", "")
 
 
 def test_alias_rules(gdn2):

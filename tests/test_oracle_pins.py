@@ -128,3 +128,26 @@ def test_wrong_gva_mapping_is_caught():
                                initial_state, cu_seqlens, heads)
     with pytest.raises(AssertionError):
         pins.pin_heads_and_gva(wrong)
+
+
+def _wrong_norm(kind):
+    def norm(x, eps=1e-12):
+        x = rec._f64(x)
+        if kind == "none":
+            return x
+        if kind == "head_axis":  # over the heads instead of the head dimension
+            return x / np.maximum(np.sqrt(np.sum(x * x, axis=-2, keepdims=True)), eps)
+        if kind == "squared":  # divided by the squared norm
+            return x / np.maximum(np.sum(x * x, axis=-1, keepdims=True), eps)
+        if kind == "abs":  # sign dropped
+            return np.abs(x) / np.maximum(np.sqrt(np.sum(x * x, axis=-1, keepdims=True)), eps)
+        raise ValueError(kind)
+    return norm
+
+
+@pytest.mark.parametrize("kind", ["none", "head_axis", "squared", "abs"])
+def test_planted_l2norm_mistake_is_caught(kind, monkeypatch):
+    """A wrong in-kernel normalisation in the oracle fails the l2norm pin."""
+    monkeypatch.setattr(rec, "l2_normalize_rows", _wrong_norm(kind))
+    with pytest.raises(AssertionError):
+        pins.pin_qk_l2norm(rec.gdn2_recurrence)
