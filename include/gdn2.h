@@ -80,18 +80,21 @@ enum {
  *                                  (precondition, not checked)
  *   beta           [T, HV, K]      io type (erase gate, taken as given, e.g.
  *                                  in [0, 1] or [0, 2]; not clamped)
- *   initial_state  [N, HV, K, V]   float32, K-major (V innermost); V-major
- *                                  [N, HV, V, K] with the state_layout option
+ *   initial_state  [N, HV, K, V]   float32 or bf16, K-major (V innermost);
+ *                                  V-major [N, HV, V, K] with the
+ *                                  state_layout option
  *   cu_seqlens     [N + 1]         int32 or int64, device memory; cu[0] = 0,
  *                                  non-decreasing, cu[N] = T (precondition,
  *                                  not checked on the device)
  *   out            [T, HV, V]      io type, written for every token
- *   final_state    [N, HV, K, V]   float32, layout as initial_state
+ *   final_state    [N, HV, K, V]   float32 or bf16 (rounded to nearest
+ *                                  even), layout as initial_state
  *
  * The FlashInfer parameter list names these element types (q, k, v at
  * float16 or bfloat16, beta and w read at q's type, g at float32, bfloat16
- * or float16, int32 or int64 cu_seqlens). Arithmetic is float32 throughout;
- * the MFMA operands are bf16 for either io type.
+ * or float16, states at float32 or bfloat16, int32 or int64 cu_seqlens).
+ * Arithmetic is float32 throughout (a bf16 state is widened on load and
+ * carried in float32); the MFMA operands are bf16 for either io type.
  *
  * Value head hv reads q/k head hv / (HV / H) (contiguous groups of value
  * heads share one q/k head).
@@ -212,9 +215,10 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
  * machinery would waste most of a 64-token chunk. Same tensors, dtypes,
  * defaults, varlen packing and errors as gdn2_chunk_fwd, with one
  * difference: final_state may be the very buffer of initial_state (same
- * data pointer) to update the state in place; any other overlap is
- * GDN2_ERR_ALIAS. The arithmetic is the recurrence step by step in float32
- * (state, gates, products); only the output is rounded to the io type.
+ * data pointer and element type) to update the state in place; any other
+ * overlap is GDN2_ERR_ALIAS. The arithmetic is the recurrence step by step
+ * in float32 (state, gates, products); only the output (and a bf16 final
+ * state) is rounded.
  *
  * Cost: every (sequence, value head) state is read and written once per
  * call (2 * K * V * 4 bytes), plus the tokens' vectors; one workgroup per

@@ -215,14 +215,14 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     if (N * HV > INT32_MAX)
         return fail(GDN2_ERR_SHAPE, "N * HV = %lld exceeds the grid limit", (long long)(N * HV));
     const int64_t ss[4] = {N, HV, K, V};
-    if (h0 && (rc = check_tensor(h0, "initial_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
-    if (ht && (rc = check_tensor(ht, "final_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
+    if (h0 && (rc = check_tensor(h0, "initial_state", GDN2_DTYPE_F32, GDN2_DTYPE_BF16, 4, ss))) return rc;
+    if (ht && (rc = check_tensor(ht, "final_state", GDN2_DTYPE_F32, GDN2_DTYPE_BF16, 4, ss))) return rc;
 
     const gdn2_tensor *inputs[] = {q, k, v, g, beta, w, h0, cu};
     const char *in_names[] = {"q", "k", "v", "g", "beta", "w", "initial_state", "cu_seqlens"};
     // final_state may be initial_state itself (same buffer) where the kernel
     // reads every state element before writing it (the recurrent path)
-    const bool inplace = allow_inplace_state && h0 && ht && h0->data == ht->data;
+    const bool inplace = allow_inplace_state && h0 && ht && h0->data == ht->data && h0->dtype == ht->dtype;
     for (int i = 0; i < 8; ++i) {
         if (overlaps(out, inputs[i]))
             return fail(GDN2_ERR_ALIAS, "out overlaps %s", in_names[i]);
@@ -254,6 +254,8 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
                    : g->dtype == GDN2_DTYPE_BF16    ? gdn2::G_BF16
                                                     : gdn2::G_F16;
         p->cu64 = cu && cu->dtype == GDN2_DTYPE_I64;
+        p->h0_bf16 = h0 && h0->dtype == GDN2_DTYPE_BF16;
+        p->ht_bf16 = ht && ht->dtype == GDN2_DTYPE_BF16;
         // token and head strides (elements). A dimension of extent one is
         // only ever indexed at 0; its token stride is then taken as one row,
         // which keeps the kernels' chunk ranges (rows x token stride) whole.

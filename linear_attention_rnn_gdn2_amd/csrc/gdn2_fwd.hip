@@ -411,6 +411,7 @@ struct Chain {
     const float *s0;  // entering state [K][V] (nullptr: zero)
     float *s1;        // destination of the leaving state [K][V] (nullptr: none)
     bool s0_vm, s1_vm; // s0 / s1 stored V-major ([V][K]): the caller's states with that option
+    bool s0_b16, s1_b16; // s0 / s1 hold bf16 elements (the caller's states may)
     bool ident;       // entering state is the identity (transition pass, K == V)
     bool zero_v;      // values taken as zero (transition pass)
     bool out;         // write the output rows
@@ -922,7 +923,8 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int sr = ch.s0_vm ? 1 : V, sc = ch.s0_vm ? K : 1;  // strides of (state row, column)
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e) S[it][jt][e] = h0[(16 * it + 4 * q4 + e) * sr + (vbase + 16 * jt + l16) * sc];
+                for (int e = 0; e < 4; ++e)
+                    S[it][jt][e] = state_ld(h0, ch.s0_b16, (16 * it + 4 * q4 + e) * sr + (vbase + 16 * jt + l16) * sc);
         // complete these loads here: left outstanding into the chunk
         // loop, they make every later write of S wait on the vector
         // memory counter, which then also waits for the v, w prefetch
@@ -1121,8 +1123,9 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
                 for (int e = 0; e < 4; ++e)
-                    ch.s1[(16 * it + 4 * q4 + e) * (ch.s1_vm ? 1 : V) + (vbase + 16 * jt + l16) * (ch.s1_vm ? K : 1)] =
-                        S[it][jt][e];
+                    state_st(ch.s1, ch.s1_b16,
+                             (16 * it + 4 * q4 + e) * (ch.s1_vm ? 1 : V) + (vbase + 16 * jt + l16) * (ch.s1_vm ? K : 1),
+                             S[it][jt][e]);
     }
 }
 
@@ -1151,9 +1154,11 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     const int64_t shead = ((int64_t)ch.n * p.HV + ch.hv) * K * V;  // [N, HV, K, V] states
     ch.tb = sb;
     ch.te = se;
-    ch.s0 = p.h0 ? p.h0 + shead : nullptr;
-    ch.s1 = p.ht ? p.ht + shead : nullptr;
+    ch.s0 = p.h0 ? state_at(p.h0, p.h0_bf16, shead) : nullptr;
+    ch.s1 = p.ht ? state_at(p.ht, p.ht_bf16, shead) : nullptr;
     ch.s0_vm = ch.s1_vm = p.state_vmajor != 0;
+    ch.s0_b16 = p.h0_bf16 != 0;
+    ch.s1_b16 = p.ht_bf16 != 0;
     ch.ident = ch.zero_v = false;
     ch.out = true;
     if (p.seg_chunks) {
@@ -1168,7 +1173,7 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
             // nothing follows the last segment; the first one's map is not needed
             if (seg >= last || (kind == 1 && seg == 0)) return;
             ch.out = false;
-            ch.s1_vm = false;  // the workspace is K-major
+            ch.s1_vm = ch.s1_b16 = false;  // the workspace is K-major float32
             if (kind == 0) {
                 if (seg > 0) ch.s0 = nullptr;
                 ch.s1 = p.wb + sseg;
@@ -1180,7 +1185,7 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
         } else {
             if (seg > 0) {
                 ch.s0 = p.ws + sseg;
-                ch.s0_vm = false;
+                ch.s0_vm = ch.s0_b16 = false;
             }
             if (seg < last) ch.s1 = nullptr;
         }

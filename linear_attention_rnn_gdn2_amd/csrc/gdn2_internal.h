@@ -19,16 +19,17 @@ struct FwdParams {
     const void *g;         // [T, HV, K] g type, or nullptr (= 0)
     const uint16_t *beta;  // [T, HV, K] io, or nullptr (= 1)
     const uint16_t *w;     // [T, HV, V] io, or nullptr (= 1)
-    const float *h0;       // [N, HV, K, V] (or [N, HV, V, K]) or nullptr (= 0)
+    const float *h0;       // [N, HV, K, V] (or [N, HV, V, K]) float32 or bf16, or nullptr (= 0)
     const void *cu;        // [N + 1] int32 or int64, or nullptr (one sequence of T tokens)
     uint16_t *out;         // [T, HV, V] io
-    float *ht;             // [N, HV, K, V] (or [N, HV, V, K]) or nullptr (not written)
+    float *ht;             // [N, HV, K, V] (or [N, HV, V, K]) float32 or bf16, or nullptr (not written)
     int64_t T;
     int32_t N, H, HV, K, V;
     float scale;           // already resolved (never 0)
     int32_t io;            // IO_BF16 or IO_F16
     int32_t gtype;         // G_F32, G_BF16 or G_F16
     int32_t cu64;          // cu_seqlens is int64
+    int32_t h0_bf16, ht_bf16;  // initial / final state stored as bf16 (element offsets count bf16s)
     // element strides of the token and head dimensions; the K or V
     // elements of one (token, head) row are contiguous
     int64_t sq, sk, sv, sw, sg, sb, so;          // per token
@@ -49,6 +50,26 @@ struct FwdParams {
 enum { PASS_OUTPUT = 0, PASS_TRANSITION = 1 };
 enum { IO_BF16 = 0, IO_F16 = 1 };
 enum { G_F32 = 0, G_BF16 = 1, G_F16 = 2 };
+
+// State buffers hold float32 or bf16 elements: the element at offset e, a
+// pointer to it, and a store rounding to nearest even.
+__host__ __device__ inline const float *state_at(const float *s, bool b16, int64_t e)
+{
+    return b16 ? reinterpret_cast<const float *>(reinterpret_cast<const uint16_t *>(s) + e) : s + e;
+}
+__host__ __device__ inline float *state_at(float *s, bool b16, int64_t e)
+{
+    return b16 ? reinterpret_cast<float *>(reinterpret_cast<uint16_t *>(s) + e) : s + e;
+}
+__device__ inline float state_ld(const float *s, bool b16, int64_t e)
+{
+    return b16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(s)[e] << 16) : s[e];
+}
+__device__ inline void state_st(float *s, bool b16, int64_t e, float x)
+{
+    if (b16) reinterpret_cast<__bf16 *>(s)[e] = (__bf16)x;
+    else s[e] = x;
+}
 
 // cu_seqlens[i] as int64 (either stored type)
 __host__ __device__ inline int64_t cu_at(const FwdParams &p, int64_t i)

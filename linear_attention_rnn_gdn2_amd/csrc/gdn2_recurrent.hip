@@ -91,7 +91,7 @@ __global__ __launch_bounds__(RB_THR) void recurrent_fwd_kernel(FwdParams p)
     const int sr = p.state_vmajor ? 1 : V, sc = p.state_vmajor ? K : 1;
     float S[RPG];
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) S[i] = p.h0 ? p.h0[shead + (int64_t)(r0 + i) * sr + col * sc] : 0.0f;
+    for (int i = 0; i < RPG; ++i) S[i] = p.h0 ? state_ld(p.h0, p.h0_bf16, shead + (int64_t)(r0 + i) * sr + col * sc) : 0.0f;
 
     for (int64_t tok = tb; tok < te; ++tok) {
         // this token's q, k, beta, g on the group's rows (16-byte loads; every
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(RB_THR) void recurrent_fwd_kernel(FwdParams p)
     }
     if (p.ht)
 #pragma unroll
-        for (int i = 0; i < RPG; ++i) p.ht[shead + (int64_t)(r0 + i) * sr + col * sc] = S[i];
+        for (int i = 0; i < RPG; ++i) state_st(p.ht, p.ht_bf16, shead + (int64_t)(r0 + i) * sr + col * sc, S[i]);
 }
 
 template <int K, int V, int IO, bool G16>

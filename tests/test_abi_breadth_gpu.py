@@ -200,3 +200,33 @@ def test_everything_together(lib, c_oracle, path):
     ro, rs = oracle(c_oracle, d, qk_l2norm=True)
     assert_parity(f"everything {path}", out, fin.transpose(-1, -2), ro, rs)
     assert torch.all(big[:, :, D:] == 5.0)
+
+
+@pytest.mark.parametrize("path", ["chunk", "split", "rec"])
+@pytest.mark.parametrize("h0_t,ht_t", [(torch.bfloat16, torch.bfloat16), (torch.bfloat16, torch.float32),
+                                       (torch.float32, torch.bfloat16)])
+def test_bf16_states(lib, c_oracle, path, h0_t, ht_t):
+    """Initial and final states in bf16 (FlashInfer parameter list: float32
+    or bfloat16), K-major and V-major; the oracle starts from the same
+    rounded state, and a bf16 final state is the float32 one rounded."""
+    d = synth(LENS if path != "rec" else [1, 5, 0, 33], 2, 4, 128, 128, seed=209, init_std=0.05, beta_max=2.0)
+    d["initial_state"] = d["initial_state"].to(h0_t)
+    ro, rs = oracle(c_oracle, d)
+    N, HV, K, V = d["initial_state"].shape
+    for layout in ("kv", "vk"):
+        s0 = d["initial_state"] if layout == "kv" else d["initial_state"].transpose(-1, -2).contiguous()
+        fin = torch.empty((N, HV, K, V), dtype=ht_t, device=DEV)
+        out, fin = call(lib, path, dev(d), d, initial_state=s0, final_state=fin, state_layout=layout)
+        f = fin if layout == "kv" else fin.transpose(-1, -2)
+        assert_parity(f"states {h0_t}->{ht_t} {layout} {path}", out, f.float(), ro, rs)
+        if ht_t == torch.bfloat16:
+            # the float32 final state of the same call, rounded once
+            f32 = torch.empty((N, HV, K, V), dtype=torch.float32, device=DEV)
+            _, f32 = call(lib, path, dev(d), d, initial_state=s0, final_state=f32, state_layout=layout)
+            assert torch.equal(fin, f32.to(torch.bfloat16))
+    if path == "rec" and h0_t == ht_t:  # in place, bf16
+        s = d["initial_state"].to(DEV)
+        out3, _ = lib.recurrent_fwd(**dev(d), scale=d["scale"], initial_state=s, cu_seqlens=d["cu_seqlens"].to(DEV),
+                                    final_state=s)
+        torch.cuda.synchronize()
+        assert_parity("states in place bf16", out3, s.float(), ro, rs)

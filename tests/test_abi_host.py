@@ -93,7 +93,8 @@ def test_valid_calls(gdn2):
     (lambda c: c.update(out=c["out"].half()), "DTYPE"),
     (lambda c: c.update(q=c["q"].half(), k=c["k"].half(), v=c["v"].half(), beta=c["beta"].half(),
                         w=c["w"].half()), "DTYPE"),                       # out left bf16
-    (lambda c: c.update(initial_state=c["initial_state"].bfloat16()), "DTYPE"),
+    (lambda c: c.update(initial_state=c["initial_state"].half()), "DTYPE"),
+    (lambda c: c.update(final_state=c["final_state"].double()), "DTYPE"),
     (lambda c: c.update(cu_seqlens=c["cu_seqlens"].float()), "DTYPE"),
     (lambda c: c.update(cu_seqlens=c["cu_seqlens"].short()), "DTYPE"),
     (lambda c: c.update(out=c["out"].float()), "DTYPE"),
@@ -142,6 +143,10 @@ def test_accepted_types_and_strides(gdn2):
         assert status(gdn2, **c)[0] == "OK"
     c = case()
     c["cu_seqlens"] = c["cu_seqlens"].long()
+    assert status(gdn2, **c)[0] == "OK"
+    c = case()
+    c["initial_state"] = c["initial_state"].bfloat16()
+    c["final_state"] = c["final_state"].bfloat16()
     assert status(gdn2, **c)[0] == "OK"
     # q, k, v as views of one fused [T, 3, H, D] projection (H = HV here)
     c = case(H=4)
