@@ -1038,16 +1038,32 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         __syncthreads();  // ------------------------------------------ B2
         if (!act) break;
 
-        // ---- AP: the 16 tiles that are not A's diagonal, four per state wave
+        // ---- AP: the 16 tiles that are not A's diagonal, four per state
+        // wave. Every operand read of the four tiles is issued before the
+        // first product, so that their LDS round trips overlap and the four
+        // accumulation chains interleave.
         if (!any_exact(sm + L::FL)) {
             const char *const b_k8 = sm + o_k8;
-            const char *const b_x = b_k8 + (it & 1) * L::QH_SZ;  // QH of this chunk for P tiles
+            const int xq = L::QH + (it & 1) * L::QH_SZ;  // QH of this chunk for P tiles
+            bf16x8 ra[4][K / 32], xa[4][K / 32];
+            for (int m = 0; m < 4; ++m) {
+                const int t = 4 + rw + 4 * m;
+                const int i = tile_i(t), j = tile_j(t);
+                const int xo = (t >= 10 ? xq : L::KB) + 16 * i * RK;
+                for (int ks = 0; ks < K / 32; ++ks) {
+                    ra[m][ks] = lds_ld<bf16x8>(b_k8, L::RR + 16 * j * RK + 64 * ks);
+                    xa[m][ks] = lds_ld<bf16x8>(b_k8, xo + 64 * ks);
+                }
+            }
+            f32x4 acc[4];
+            for (int m = 0; m < 4; ++m) acc[m] = f32x4{0, 0, 0, 0};
+            for (int ks = 0; ks < K / 32; ++ks)
+                for (int m = 0; m < 4; ++m) acc[m] = mfma_bf16(ra[m][ks], xa[m][ks], acc[m]);
             for (int m = 0; m < 4; ++m) {
                 const int t = 4 + rw + 4 * m;
                 const int i = tile_i(t), j = tile_j(t);
                 const bool isP = t >= 10;
-                const f32x4 x = ap_mask(ap_tile_at<K>(b_k8 + L::RR + 16 * j * RK, isP ? b_x + L::QH + 16 * i * RK : b_k8 + L::KB + 16 * i * RK),
-                                        i == j, isP, l16, q4);
+                const f32x4 x = ap_mask(acc[m], i == j, isP, l16, q4);
                 if (isP) lds_st<bf16x4>(sm, L::PB + o_c4 + 16 * i * RC + 32 * j, f32x4_to_bf16(x));
                 else lds_st<f32x4>(sm, L::AB + o_a4 + 16 * i * RA + 64 * j, x);
             }
