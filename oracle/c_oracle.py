@@ -32,6 +32,12 @@ def _load():
                                         vp, i32, vp, vp]
         lib.gdn2_oracle_fwd.restype = ctypes.c_int
         lib.gdn2_oracle_max_threads.restype = ctypes.c_int
+        lib.gdn2_oracle_bwd.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int,
+                                        vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int,
+                                        dbl, vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int,
+                                        vp, i32, i64, i32, i32, i32, i32, i32,
+                                        vp, vp, vp, vp, vp, vp, vp]
+        lib.gdn2_oracle_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -59,6 +65,9 @@ def _arr(x):
     if a.dtype == np.float32:
         return a, _F32
     return np.ascontiguousarray(a, dtype=np.float64), _F64
+
+
+load = _load
 
 
 def max_threads() -> int:
@@ -101,3 +110,45 @@ def gdn2_recurrence_c(q, k, v, g=None, beta=None, w=None, scale=None,
     if rc != 0:
         raise RuntimeError("C oracle rejected its arguments")
     return out, final
+
+
+def gdn2_recurrence_bwd_c(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, d_out,
+                          d_final_state=None, block=64):
+    """Same contract as :func:`oracle.recurrence_bwd.gdn2_recurrence_bwd`;
+    ``block`` is the recompute block length of the C loop (it changes where
+    states are recomputed, not the result)."""
+    lib = _load()
+    qa, qd = _arr(q)
+    ka, kd = _arr(k)
+    va, vd = _arr(v)
+    ga, gd = _arr(g)
+    ba, bd = _arr(beta)
+    wa, wd = _arr(w)
+    sa, sd = _arr(initial_state)
+    da, dd = _arr(d_out)
+    fa, fd = _arr(d_final_state)
+    T, H, K = qa.shape
+    HV, V = va.shape[1], va.shape[2]
+    if cu_seqlens is None:
+        cu, N = None, 1
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).astype(np.int32))
+        N = len(cu) - 1
+    dq = np.zeros((T, HV, K))
+    dk = np.zeros((T, HV, K))
+    dv = np.zeros((T, HV, V))
+    dw = np.zeros((T, HV, V))
+    dg = np.zeros((T, HV, K))
+    db = np.zeros((T, HV, K))
+    ds0 = np.zeros((N, HV, K, V))
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.gdn2_oracle_bwd(ptr(qa), qd, ptr(ka), kd, ptr(va), vd, ptr(ga), gd, ptr(ba), bd,
+                             ptr(wa), wd, resolve_scale(scale, K), ptr(sa), sd, ptr(da), dd,
+                             ptr(fa), fd, ptr(cu), N, T, H, HV, K, V, int(block),
+                             dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, dw.ctypes.data,
+                             dg.ctypes.data, db.ctypes.data, ds0.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("C oracle rejected its arguments")
+    m = HV // H
+    return {"dq": dq.reshape(T, H, m, K).sum(axis=2), "dk": dk.reshape(T, H, m, K).sum(axis=2),
+            "dv": dv, "dw": dw, "dg": dg, "dbeta": db, "d_initial_state": ds0}
