@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 3
+#define GDN2_ABI_VERSION 4
 
 /* Element types a tensor descriptor may carry. */
 typedef enum gdn2_dtype {
@@ -275,6 +275,80 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
                          float scale, const gdn2_tensor *initial_state,
                          const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
                          const gdn2_tensor *final_state);
+
+/*
+ * gdn2_chunk_bwd -- enqueue the backward of gdn2_chunk_fwd on `stream`: the
+ * gradients of a scalar loss with respect to q, k, v, g, beta, w and the
+ * initial state, given its gradients d_out with respect to the output and
+ * d_final_state with respect to the final state. It differentiates the same
+ * recurrence (FlashInfer chunk_gated_delta_rule2 docs, recurrence display
+ * equation) through the same 64-token chunked WY form, so a training step
+ * can pair the two calls.
+ *
+ * Tensors (every one dense, row-major; shapes and roles as in
+ * gdn2_chunk_fwd):
+ *   q, k [T, H, K], v, w [T, HV, V], beta [T, HV, K]      bf16 (required)
+ *   g [T, HV, K]                                           float32 (required)
+ *   initial_state [N, HV, K, V]                            float32, K-major, or NULL (zero)
+ *   cu_seqlens [N + 1]                                     int32 or int64, or NULL (one sequence)
+ *   d_out [T, HV, V]                                       bf16 (required)
+ *   d_final_state [N, HV, K, V]                            float32, or NULL (zero)
+ * Outputs (caller-allocated, fully written):
+ *   dq, dk [T, H, K]                                       bf16: sums over the value heads that
+ *                                                          read each q/k head
+ *   dv, dw [T, HV, V], dbeta [T, HV, K]                    bf16
+ *   dg [T, HV, K]                                          float32 (gradient of the natural-log g)
+ *   d_initial_state [N, HV, K, V]                          float32, or NULL (not written)
+ * scale == 0 means 1/sqrt(K). Supported sizes as gdn2_chunk_fwd.
+ *
+ * Decay bound: in every 64-token chunk the running in-chunk sum of g of
+ * every key channel must stay within 120 ln 2 (about 83) in magnitude;
+ * the gradients of a chunk beyond it, and every state gradient reaching
+ * back through it, are NaN (not silently wrong). Inputs whose g stays in
+ * [-1.3, 0] per token always satisfy it.
+ *
+ * Evaluation: the forward runs again and keeps the float32 state entering
+ * every chunk; a chunk-parallel pass builds each chunk's WY quantities; one
+ * workgroup per (sequence, value head) carries the state gradient over the
+ * chunks in reverse; a chunk-parallel pass forms every gradient; a last pass
+ * sums dq and dk over grouped value heads. Arithmetic is float32 with bf16
+ * MFMA operands, as in the forward.
+ *
+ * Ownership and memory: the caller owns every buffer; inputs are only read.
+ * A stream-ordered workspace (hipMallocAsync / hipFreeAsync on `stream`) of
+ *   (T / 64 + N) * HV * (2 * K * V * 4 + 6 * 64 * K + 8192 + 4 * K)
+ *   + 2 * T * HV * K * 4 bytes
+ * (rounded up per part) holds the checkpoints and partial gradients; if it
+ * cannot be allocated the call fails with GDN2_ERR_HIP and enqueues nothing.
+ *
+ * Errors as gdn2_chunk_fwd: NULL_ARG for a missing required tensor, DTYPE,
+ * SHAPE, HEADS, UNSUPPORTED, LAYOUT for a non-dense tensor, ALIAS when an
+ * output overlaps an input or another output. Asynchronous, deterministic
+ * (no atomics), reentrant.
+ */
+int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k,
+                   const gdn2_tensor *v, const gdn2_tensor *g,
+                   const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                   const gdn2_tensor *initial_state,
+                   const gdn2_tensor *cu_seqlens, const gdn2_tensor *d_out,
+                   const gdn2_tensor *d_final_state, const gdn2_tensor *dq,
+                   const gdn2_tensor *dk, const gdn2_tensor *dv,
+                   const gdn2_tensor *dg, const gdn2_tensor *dbeta,
+                   const gdn2_tensor *dw, const gdn2_tensor *d_initial_state,
+                   hipStream_t stream);
+
+/* The host-side validation of gdn2_chunk_bwd alone (no device work). */
+int gdn2_chunk_bwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
+                         const gdn2_tensor *v, const gdn2_tensor *g,
+                         const gdn2_tensor *beta, const gdn2_tensor *w,
+                         float scale, const gdn2_tensor *initial_state,
+                         const gdn2_tensor *cu_seqlens,
+                         const gdn2_tensor *d_out,
+                         const gdn2_tensor *d_final_state,
+                         const gdn2_tensor *dq, const gdn2_tensor *dk,
+                         const gdn2_tensor *dv, const gdn2_tensor *dg,
+                         const gdn2_tensor *dbeta, const gdn2_tensor *dw,
+                         const gdn2_tensor *d_initial_state);
 
 /* Message describing the last failure on the calling thread ("" if none).
  * The string stays valid until the next call on the same thread. */

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdn2.so")
 SOURCES = [os.path.join(HERE, "csrc", "gdn2_api.cpp"), os.path.join(HERE, "csrc", "gdn2_fwd.hip"),
-           os.path.join(HERE, "csrc", "gdn2_recurrent.hip")]
+           os.path.join(HERE, "csrc", "gdn2_recurrent.hip"), os.path.join(HERE, "csrc", "gdn2_bwd.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -278,6 +278,7 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
         p->hso = st(out, 1);
         p->state_vmajor = 0;
         p->qk_l2norm = 0;
+        p->ckpt = nullptr;
     }
     return GDN2_OK;
 }
@@ -326,9 +327,192 @@ int cu_count(int dev)
     return n;
 }
 
+// Validation of a backward call: every tensor dense and row-major, bf16
+// except g, dg and the states (float32). Fills the backward's parameters and
+// the forward's (for the checkpoint pass) when p is given.
+int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v, const gdn2_tensor *g,
+                 const gdn2_tensor *beta, const gdn2_tensor *w, float scale, const gdn2_tensor *h0,
+                 const gdn2_tensor *cu, const gdn2_tensor *dout, const gdn2_tensor *dht, const gdn2_tensor *dq,
+                 const gdn2_tensor *dk, const gdn2_tensor *dv, const gdn2_tensor *dg, const gdn2_tensor *dbeta,
+                 const gdn2_tensor *dw, const gdn2_tensor *dh0, gdn2::BwdParams *p, gdn2::FwdParams *pf)
+{
+    g_last_error.clear();
+    const gdn2_tensor *req[] = {q, k, v, g, beta, w, dout, dq, dk, dv, dg, dbeta, dw};
+    const char *req_names[] = {"q", "k", "v", "g", "beta", "w", "d_out", "dq", "dk", "dv", "dg", "dbeta", "dw"};
+    for (int i = 0; i < 13; ++i)
+        if (!req[i]) return fail(GDN2_ERR_NULL_ARG, "%s is NULL (required by the backward)", req_names[i]);
+    int rc;
+    if ((rc = check_tensor(q, "q", GDN2_DTYPE_BF16, -1, 3, nullptr))) return rc;
+    const int64_t T = q->shape[0], H = q->shape[1], K = q->shape[2];
+    if ((rc = check_tensor(v, "v", GDN2_DTYPE_BF16, -1, 3, nullptr))) return rc;
+    if (v->shape[0] != T) return fail(GDN2_ERR_SHAPE, "v: dimension 0 is %lld, expected %lld", (long long)v->shape[0], (long long)T);
+    const int64_t HV = v->shape[1], V = v->shape[2];
+    if (H < 1 || HV < H || HV % H != 0)
+        return fail(GDN2_ERR_HEADS, "value heads (%lld) must be a positive multiple of q/k heads (%lld)",
+                    (long long)HV, (long long)H);
+    if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
+        return fail(GDN2_ERR_UNSUPPORTED, "(K, V) = (%lld, %lld) not supported; use (64, 64) or (128, 128)",
+                    (long long)K, (long long)V);
+    if (T > INT32_MAX) return fail(GDN2_ERR_SHAPE, "T = %lld exceeds the int32 range", (long long)T);
+    const int64_t qs[3] = {T, H, K}, vs[3] = {T, HV, V}, gs[3] = {T, HV, K};
+    if ((rc = check_tensor(k, "k", GDN2_DTYPE_BF16, -1, 3, qs))) return rc;
+    if ((rc = check_tensor(w, "w", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(g, "g", GDN2_DTYPE_F32, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(beta, "beta", GDN2_DTYPE_BF16, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(dout, "d_out", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(dq, "dq", GDN2_DTYPE_BF16, -1, 3, qs))) return rc;
+    if ((rc = check_tensor(dk, "dk", GDN2_DTYPE_BF16, -1, 3, qs))) return rc;
+    if ((rc = check_tensor(dv, "dv", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(dw, "dw", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(dg, "dg", GDN2_DTYPE_F32, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(dbeta, "dbeta", GDN2_DTYPE_BF16, -1, 3, gs))) return rc;
+    int64_t N = 1;
+    if (cu) {
+        if ((rc = check_tensor(cu, "cu_seqlens", GDN2_DTYPE_I32, GDN2_DTYPE_I64, 1, nullptr))) return rc;
+        N = cu->shape[0] - 1;
+        if (N < 1) return fail(GDN2_ERR_SHAPE, "cu_seqlens needs at least 2 entries (N >= 1)");
+        if (!cu->data) return fail(GDN2_ERR_NULL_ARG, "cu_seqlens: data is NULL");
+    }
+    const int64_t nslots = T / 64 + N;
+    if (N * HV > INT32_MAX || nslots * HV > INT32_MAX)
+        return fail(GDN2_ERR_SHAPE, "N * HV or the chunk count times HV exceeds the grid limit");
+    const int64_t ss[4] = {N, HV, K, V};
+    if (h0 && (rc = check_tensor(h0, "initial_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
+    if (dht && (rc = check_tensor(dht, "d_final_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
+    if (dh0 && (rc = check_tensor(dh0, "d_initial_state", GDN2_DTYPE_F32, -1, 4, ss))) return rc;
+
+    const gdn2_tensor *ins[] = {q, k, v, g, beta, w, h0, cu, dout, dht};
+    const char *in_names[] = {"q", "k", "v", "g", "beta", "w", "initial_state", "cu_seqlens", "d_out", "d_final_state"};
+    const gdn2_tensor *outs[] = {dq, dk, dv, dg, dbeta, dw, dh0};
+    const char *out_names[] = {"dq", "dk", "dv", "dg", "dbeta", "dw", "d_initial_state"};
+    for (int o = 0; o < 7; ++o) {
+        for (int i = 0; i < 10; ++i)
+            if (overlaps(outs[o], ins[i])) return fail(GDN2_ERR_ALIAS, "%s overlaps %s", out_names[o], in_names[i]);
+        for (int o2 = o + 1; o2 < 7; ++o2)
+            if (overlaps(outs[o], outs[o2])) return fail(GDN2_ERR_ALIAS, "%s overlaps %s", out_names[o], out_names[o2]);
+    }
+
+    if (p) {
+        *p = gdn2::BwdParams{};
+        p->q = static_cast<const uint16_t *>(q->data);
+        p->k = static_cast<const uint16_t *>(k->data);
+        p->v = static_cast<const uint16_t *>(v->data);
+        p->w = static_cast<const uint16_t *>(w->data);
+        p->g = static_cast<const float *>(g->data);
+        p->beta = static_cast<const uint16_t *>(beta->data);
+        p->dout = static_cast<const uint16_t *>(dout->data);
+        p->cu = cu ? cu->data : nullptr;
+        p->cu64 = cu && cu->dtype == GDN2_DTYPE_I64;
+        p->dht = dht ? static_cast<const float *>(dht->data) : nullptr;
+        p->dh0 = dh0 ? static_cast<float *>(dh0->data) : nullptr;
+        p->dq = static_cast<uint16_t *>(dq->data);
+        p->dk = static_cast<uint16_t *>(dk->data);
+        p->dv = static_cast<uint16_t *>(dv->data);
+        p->dw = static_cast<uint16_t *>(dw->data);
+        p->dbeta = static_cast<uint16_t *>(dbeta->data);
+        p->dg = static_cast<float *>(dg->data);
+        p->T = T;
+        p->N = (int32_t)N;
+        p->H = (int32_t)H;
+        p->HV = (int32_t)HV;
+        p->K = (int32_t)K;
+        p->V = (int32_t)V;
+        p->nslots = (int32_t)nslots;
+        p->scale = scale == 0.0f ? (float)(1.0 / sqrt((double)K)) : scale;
+    }
+    if (pf) {
+        *pf = gdn2::FwdParams{};
+        pf->q = static_cast<const uint16_t *>(q->data);
+        pf->k = static_cast<const uint16_t *>(k->data);
+        pf->v = static_cast<const uint16_t *>(v->data);
+        pf->g = g->data;
+        pf->beta = static_cast<const uint16_t *>(beta->data);
+        pf->w = static_cast<const uint16_t *>(w->data);
+        pf->h0 = h0 ? static_cast<const float *>(h0->data) : nullptr;
+        pf->cu = cu ? cu->data : nullptr;
+        pf->cu64 = cu && cu->dtype == GDN2_DTYPE_I64;
+        pf->T = T;
+        pf->N = (int32_t)N;
+        pf->H = (int32_t)H;
+        pf->HV = (int32_t)HV;
+        pf->K = (int32_t)K;
+        pf->V = (int32_t)V;
+        pf->scale = scale == 0.0f ? (float)(1.0 / sqrt((double)K)) : scale;
+        pf->io = gdn2::IO_BF16;
+        pf->gtype = gdn2::G_F32;
+        // dense row-major strides (elements)
+        pf->sq = pf->sk = H * K;
+        pf->hsq = pf->hsk = K;
+        pf->sv = pf->sw = pf->so = HV * V;
+        pf->hsv = pf->hsw = pf->hso = V;
+        pf->sg = pf->sb = HV * K;
+        pf->hsg = pf->hsb = K;
+        pf->nseg = 1;
+        pf->pass = gdn2::PASS_OUTPUT;
+    }
+    return GDN2_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gdn2_chunk_bwd_check(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v, const gdn2_tensor *g,
+                         const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                         const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens, const gdn2_tensor *d_out,
+                         const gdn2_tensor *d_final_state, const gdn2_tensor *dq, const gdn2_tensor *dk,
+                         const gdn2_tensor *dv, const gdn2_tensor *dg, const gdn2_tensor *dbeta,
+                         const gdn2_tensor *dw, const gdn2_tensor *d_initial_state)
+{
+    return validate_bwd(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, d_out, d_final_state, dq, dk, dv, dg,
+                        dbeta, dw, d_initial_state, nullptr, nullptr);
+}
+
+int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v, const gdn2_tensor *g,
+                   const gdn2_tensor *beta, const gdn2_tensor *w, float scale, const gdn2_tensor *initial_state,
+                   const gdn2_tensor *cu_seqlens, const gdn2_tensor *d_out, const gdn2_tensor *d_final_state,
+                   const gdn2_tensor *dq, const gdn2_tensor *dk, const gdn2_tensor *dv, const gdn2_tensor *dg,
+                   const gdn2_tensor *dbeta, const gdn2_tensor *dw, const gdn2_tensor *d_initial_state,
+                   hipStream_t stream)
+{
+    gdn2::BwdParams p;
+    gdn2::FwdParams pf;
+    int rc = validate_bwd(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, d_out, d_final_state, dq, dk, dv,
+                          dg, dbeta, dw, d_initial_state, &p, &pf);
+    if (rc != GDN2_OK) return rc;
+    // stream-ordered workspace: forward checkpoints, state-gradient
+    // checkpoints, prep records, per-value-head dq and dk
+    const size_t state = (size_t)p.K * p.V * sizeof(float);
+    const size_t chunks = (size_t)p.nslots * (size_t)p.HV;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t sz_ck = up(chunks * state);
+    const size_t sz_prep = up(chunks * (size_t)gdn2::bwd_prep_bytes(p.K));
+    const size_t sz_qk = up((size_t)p.T * p.HV * p.K * sizeof(float));
+    const size_t total = 2 * sz_ck + sz_prep + 2 * sz_qk;
+    void *ws = nullptr;
+    if (total > 0 && hipMallocAsync(&ws, total, stream) != hipSuccess)
+        return fail(GDN2_ERR_HIP, "backward workspace of %zu bytes could not be allocated", total);
+    char *b = static_cast<char *>(ws);
+    float *s_ckpt = reinterpret_cast<float *>(b);
+    p.s_ckpt = s_ckpt;
+    p.ds_ckpt = reinterpret_cast<float *>(b + sz_ck);
+    p.prep = b + 2 * sz_ck;
+    p.dq_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep);
+    p.dk_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep + sz_qk);
+    pf.ckpt = s_ckpt;
+    hipError_t e = hipSuccess;
+    if (p.T > 0) {
+        e = gdn2::launch_chunk_fwd(pf, stream);
+        if (e == hipSuccess) e = gdn2::launch_bwd_chunk(p, 0, stream);
+    }
+    if (e == hipSuccess) e = gdn2::launch_bwd_state(p, stream);
+    if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, 1, stream);
+    if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_reduce(p, stream);
+    const hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+    if (e != hipSuccess) return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    if (ef != hipSuccess) return fail(GDN2_ERR_HIP, "workspace release failed: %s", hipGetErrorString(ef));
+    return GDN2_OK;
+}
 
 int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
                          const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w,

@@ -1,0 +1,733 @@
+// Backward of the GDN-2 chunked forward for CDNA4 (gfx950).
+//
+// Gradients of a scalar loss with respect to q, k, v, g, beta, w and the
+// initial state, given the gradients of the output and of the final state.
+// The chain rule is taken through the chunked WY form of the forward (per
+// 64-token chunk, rows r, s; G = in-chunk cumulative sum of g per key
+// channel; S_in the state entering the chunk, S_out the one leaving it):
+//
+//   QH = q e^G, KB = beta k e^G, RR = k e^-G, gamma = e^G_last, WV = w v
+//   A = strict_tril(KB RR^T), P = tril(QH RR^T), T = (I + A)^-1
+//   wy_w = T KB, wy_u = T WV, U = wy_u - wy_w S_in
+//   O = scale (QH S_in + P U),  S_out = gamma S_in + (RR gamma)^T U
+//
+// (the chunked evaluation of the FlashInfer chunk_gated_delta_rule2
+// recurrence display equation that the FlashRT card's 64-token WY chain and
+// the burn-gdn2 README's "Fused CUDA kernels" section describe). Reversed:
+//
+//   dU    = scale P^T dO + RR (gamma dS_out)
+//   dS_in = gamma dS_out + scale QH^T dO - wy_w^T dU
+//   dQH   = scale dO S_in^T + dP RR,       dP = scale tril(dO U^T)
+//   dKH   = U dS_out^T,  dgamma = rowsum(S_in dS_out) + colsum(dKH RR)
+//   dwy_w = -dU S_in^T,  dT = dU WV^T + dwy_w KB^T,  dWV = T^T dU
+//   dKB   = T^T dwy_w + dA RR,  dA = -strict_tril(T^T dT T^T)
+//   dRR   = dA^T KB + dP^T QH + gamma dKH
+//
+// then through the decay factors to dq, dk, dbeta, dg (a reverse cumulative
+// sum over the chunk) and through WV to dv, dw. Four launches follow the
+// forward with per-chunk state checkpoints:
+//
+//   prep   (chunk-parallel)  QH, RR, wy_w, P, gamma of every chunk
+//   state  (one workgroup per (sequence, value head), chunks in reverse)
+//          the dS_in recurrence on MFMA, saving dS_out of every chunk
+//   grads  (chunk-parallel)  every gradient of the chunk from the forward
+//          checkpoint S_in, the saved dS_out and dO
+//   reduce dq, dk summed over the value heads of each q/k head
+//
+// Bounded decay: as in the forward's single-reference factorisation, every
+// |G| (log2 units) of a chunk must stay within 2^120; a chunk beyond it has
+// its gradients (and, through gamma, the state gradient) set to NaN.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "gdn2_device.h"
+#include "gdn2_internal.h"
+
+namespace gdn2 {
+namespace {
+
+using namespace dev;
+
+constexpr int BT = 256;  // threads per workgroup (4 waves)
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float XLIM = 120.0f;
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+__device__ __forceinline__ int64_t cu_of(const BwdParams &p, int64_t i)
+{
+    if (!p.cu) return i == 0 ? 0 : p.T;
+    return p.cu64 ? static_cast<const int64_t *>(p.cu)[i] : (int64_t) static_cast<const int32_t *>(p.cu)[i];
+}
+__device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
+__device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float rbf(float x) { return (float)(__bf16)x; }  // rounded to bf16 and back
+
+// One 16x16 tile Z[m0 + 4 q4 + e][n0 + l16] (element e of the result) of
+// acc + X Y over k in [0, kd), X and Y bf16 in LDS at byte offsets xo, yo:
+//   X[m][k] at xo + 2 (m lx + k)   (XT false: k contiguous)
+//             xo + 2 (k lx + m)   (XT true: read with transpose reads)
+//   Y[k][n] at yo + 2 (n ly + k)   (YT false: k contiguous)
+//             yo + 2 (k ly + n)   (YT true: transpose reads)
+template <bool XT, bool YT>
+__device__ __forceinline__ f32x4 tile_mm(const char *sm, int xo, int lx, int yo, int ly, int m0, int n0, int kd,
+                                         f32x4 acc, int l16, int q4)
+{
+    for (int k0 = 0; k0 < kd; k0 += 32) {
+        bf16x8 a, b;
+        if constexpr (!XT) {
+            a = lds_ld<bf16x8>(sm, xo + 2 * ((m0 + l16) * lx + k0 + 8 * q4));
+        } else {
+            const int o = xo + 2 * ((k0 + 8 * q4 + (l16 >> 2)) * lx + m0 + 4 * (l16 & 3));
+            a = cat4(lds_tr(sm, o), lds_tr(sm, o + 8 * lx));
+        }
+        if constexpr (!YT) {
+            b = lds_ld<bf16x8>(sm, yo + 2 * ((n0 + l16) * ly + k0 + 8 * q4));
+        } else {
+            const int o = yo + 2 * ((k0 + 8 * q4 + (l16 >> 2)) * ly + n0 + 4 * (l16 & 3));
+            b = cat4(lds_tr(sm, o), lds_tr(sm, o + 8 * ly));
+        }
+        acc = mfma_bf16(a, b, acc);
+    }
+    return acc;
+}
+
+// MFMA operands from a float32 row-major [D][D] matrix M in global memory:
+//   col_frag: M[r0 + j][c] for j = 0..7 (8 rows of one column; a Y operand
+//             whose k runs down the rows)
+//   row_frag: M[r][c0 .. c0 + 7] (8 consecutive elements of one row)
+__device__ __forceinline__ bf16x8 col_frag(const float *M, int ld, int r0, int c, const float *scl)
+{
+    f32x8 x;
+    for (int j = 0; j < 8; ++j) x[j] = M[(int64_t)(r0 + j) * ld + c] * (scl ? scl[r0 + j] : 1.0f);
+    return f32x8_to_bf16(x);
+}
+__device__ __forceinline__ bf16x8 row_frag(const float *M, int ld, int r, int c0)
+{
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(M + (int64_t)r * ld + c0);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(M + (int64_t)r * ld + c0 + 4);
+    return f32x8_to_bf16(__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Store a tile (result layout) to an LDS matrix Z[m][n] at zo with pitch lz
+// (bf16 or float32), each element scaled by s.
+__device__ __forceinline__ void st_tile_bf(char *sm, int zo, int lz, int m0, int n0, f32x4 x, int l16, int q4)
+{
+    for (int e = 0; e < 4; ++e) lds_st<__bf16>(sm, zo + 2 * ((m0 + 4 * q4 + e) * lz + n0 + l16), (__bf16)x[e]);
+}
+__device__ __forceinline__ void st_tile_f32(char *sm, int zo, int lz, int m0, int n0, f32x4 x, int l16, int q4)
+{
+    for (int e = 0; e < 4; ++e) lds_st<float>(sm, zo + 4 * ((m0 + 4 * q4 + e) * lz + n0 + l16), x[e]);
+}
+
+// Keep entries with n < m (strict) or n <= m of a tile (m0, n0).
+__device__ __forceinline__ f32x4 tril_mask(f32x4 x, int m0, int n0, bool strict, int l16, int q4)
+{
+    for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 4 * q4 + e, n = n0 + l16;
+        x[e] = (strict ? n < m : n <= m) ? x[e] : 0.0f;
+    }
+    return x;
+}
+
+// ------------------------------------------------------------ LDS layout --
+// Regions of the chunk kernels (K = V = D); lifetimes by phase noted.
+template <int D>
+struct BL {
+    static constexpr int RK = D + 8;   // bf16 pitch of [64][D]
+    static constexpr int RC = 64 + 8;  // bf16 pitch of [64][64]
+    static constexpr int RA = 64 + 4;  // float32 pitch of [64][64]
+    static constexpr int RF = D + 4;   // float32 pitch of [64][D]
+    static constexpr int TK = 64 * RK * 2, TC = 64 * RC * 2, TA = 64 * RA * 4;
+    static constexpr int QH = 0, KB = QH + TK, RR = KB + TK;  // all phases
+    static constexpr int RGA = RR + TK;           // A -> T (float32); U; WV again; Y
+    static constexpr int RGB = RGA + cmax(TA, TK);  // WV; dO; dT, then dA
+    static constexpr int RGC = RGB + cmax(TK, TC);  // G (float32, with RGD); wy_w; dU
+    static constexpr int RGD = RGC + TK;          // dwy_w
+    static constexpr int PB = RGD + TK;           // P; dP
+    static constexpr int TB = PB + TC;            // T (bf16)
+    static constexpr int GAM = TB + TC;           // e^G_last [D] float32
+    static constexpr int DGM = GAM + 4 * D;       // rowsum(S_in dS_out) [D] float32
+    static constexpr int XS = DGM + 4 * D;        // T blocks: three 16x16 float32 scratch blocks
+    static constexpr int FLG = XS + 3 * 1024;     // int: chunk beyond the decay bound
+    static constexpr int TOTAL = FLG + 16;
+    static constexpr int EF = 64 * RF * 4;        // epilogue: dQH, dKB, dRR, dKH float32 [64][RF]
+    static constexpr int SIZE = cmax(TOTAL, 4 * EF);
+    static_assert(2 * TK >= 64 * D * 4, "G scratch");
+    static_assert(SIZE <= 160 * 1024, "LDS budget");
+};
+
+// The 20 lower tiles (i >= j) of A (0..9) and P (10..19) of a chunk.
+__device__ __forceinline__ void lower_tile(int t, int &i, int &j)
+{
+    const int u = t % 10;  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+    i = u >= 6 ? 3 : u >= 3 ? 2 : u >= 1 ? 1 : 0;
+    j = u - i * (i + 1) / 2;
+}
+
+// ----------------------------------------------------- chunk-parallel kernel --
+// MODE 0: prep record of every chunk (for the state-gradient pass).
+// MODE 1: every gradient of the chunk.
+template <int D, int MODE>
+__global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
+{
+    using L = BL<D>;
+    constexpr int RK = L::RK, RC = L::RC, RA = L::RA;
+    constexpr int NTD = D / 16;  // 16-wide tiles across D
+    constexpr int NTW = NTD / 4; // of them per wave
+    __shared__ __attribute__((aligned(16))) char sm[L::SIZE];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+
+    // work item: (checkpoint slot, value head); the slot's sequence is the
+    // last one whose first slot is not past it
+    const int hv = blockIdx.x % p.HV;
+    const int64_t slot = blockIdx.x / p.HV;
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_slot(cu_of(p, mid), mid, 0) <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    const int64_t sb = cu_of(p, n), se = cu_of(p, n + 1);
+    const int64_t c = slot - chunk_slot(sb, n, 0);
+    if (c * 64 >= se - sb) return;  // no chunk in this slot
+    const int64_t t0 = sb + c * 64;
+    const int len = (int)(se - t0 < 64 ? se - t0 : 64);
+    const int hk = hv / (p.HV / p.H);
+    const int64_t kd_off = (int64_t)(slot * p.HV + hv) * D * D;  // checkpoint of this chunk
+
+    // ---- G = cumsum(g) log2(e) per channel (float32 scratch [64][D] over RGC, RGD)
+    if (tid == 0) lds_st<int>(sm, L::FLG, 0);
+    __syncthreads();
+    if (tid < D) {
+        float run = 0.0f;
+        bool out = false;
+        for (int r = 0; r < 64; ++r) {
+            run = fmaf(r < len ? p.g[((t0 + r) * p.HV + hv) * D + tid] : 0.0f, LOG2E, run);
+            out |= !(fabsf(run) <= XLIM);
+            lds_st<float>(sm, L::RGC + 4 * (r * D + tid), run);
+        }
+        lds_st<float>(sm, L::GAM + 4 * tid, ex2(run));
+        if (out) lds_st<int>(sm, L::FLG, 1);
+    }
+    __syncthreads();
+    const bool poison = lds_ld<int>(sm, L::FLG) != 0;
+
+    // ---- QH, KB, RR, WV (bf16, row-major [token][D]); rows past the end are zero
+    for (int e = tid; e < 64 * D / 8; e += BT) {
+        const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
+        f32x8 qf = {}, kf = {}, bb = {}, vf = {}, wf = {};
+        if (r < len) {
+            const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
+            const bf16x8 qr = *reinterpret_cast<const bf16x8 *>(p.q + tk);
+            const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(p.k + tk);
+            const bf16x8 br = *reinterpret_cast<const bf16x8 *>(p.beta + tv);
+            const bf16x8 vr = *reinterpret_cast<const bf16x8 *>(p.v + tv);
+            const bf16x8 wr = *reinterpret_cast<const bf16x8 *>(p.w + tv);
+            qf = __builtin_convertvector(qr, f32x8);
+            kf = __builtin_convertvector(kr, f32x8);
+            bb = __builtin_convertvector(br, f32x8);
+            vf = __builtin_convertvector(vr, f32x8);
+            wf = __builtin_convertvector(wr, f32x8);
+        }
+        f32x8 qh, kb, rr;
+        for (int j = 0; j < 8; ++j) {
+            const float G = lds_ld<float>(sm, L::RGC + 4 * (r * D + c0 + j));
+            const float eg = ex2(G), ie = ex2(-G);
+            qh[j] = qf[j] * eg;
+            kb[j] = bb[j] * kf[j] * eg;
+            rr[j] = kf[j] * ie;
+        }
+        const int o = 2 * (r * RK + c0);
+        lds_st<bf16x8>(sm, L::QH + o, f32x8_to_bf16(qh));
+        lds_st<bf16x8>(sm, L::KB + o, f32x8_to_bf16(kb));
+        lds_st<bf16x8>(sm, L::RR + o, f32x8_to_bf16(rr));
+        lds_st<bf16x8>(sm, L::RGB + o, f32x8_to_bf16(vf * wf));
+    }
+    // the blocks above the diagonal of P and T stay zero
+    for (int e = tid; e < 6 * 256; e += BT) {
+        const int b = e >> 8, x = e & 255;
+        const int bi = b < 3 ? 0 : b < 5 ? 1 : 2, bj = b < 3 ? b + 1 : b < 5 ? b - 1 : 3;  // (0,1)(0,2)(0,3)(1,2)(1,3)(2,3)
+        const int r = 16 * bi + (x >> 4), s = 16 * bj + (x & 15);
+        lds_st<__bf16>(sm, L::PB + 2 * (r * RC + s), (__bf16)0.0f);
+        lds_st<__bf16>(sm, L::TB + 2 * (r * RC + s), (__bf16)0.0f);
+    }
+    __syncthreads();
+
+    // ---- A (float32) and P (bf16): 20 lower tiles, 5 per wave
+    for (int t = wv; t < 20; t += 4) {
+        int i, j;
+        lower_tile(t, i, j);
+        const bool isP = t >= 10;
+        const f32x4 x = tril_mask(tile_mm<false, false>(sm, isP ? L::QH : L::KB, RK, L::RR, RK, 16 * i, 16 * j, D,
+                                                        f32x4{0, 0, 0, 0}, l16, q4),
+                                  16 * i, 16 * j, !isP, l16, q4);
+        if (isP) st_tile_bf(sm, L::PB, RC, 16 * i, 16 * j, x, l16, q4);
+        else st_tile_f32(sm, L::RGA, RA, 16 * i, 16 * j, x, l16, q4);
+    }
+    __syncthreads();
+
+    // ---- T = (I + A)^-1 in float32, in place over A. Diagonal blocks by
+    // forward substitution (wave i, lane l16 solves column l16 of block i)
+    if (q4 == 0) {
+        const int bo = L::RGA + 4 * (16 * wv * RA + 16 * wv);
+        float a[16][16];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+            for (int cc = 0; cc < r; ++cc) a[r][cc] = lds_ld<float>(sm, bo + 4 * (r * RA + cc));
+        float acc[16], t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+            t[cc] = (cc == l16 ? 1.0f : 0.0f) - acc[cc];
+#pragma unroll
+            for (int r = cc + 1; r < 16; ++r) acc[r] = fmaf(a[r][cc], t[cc], acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lds_st<float>(sm, bo + 4 * (r * RA + l16), t[r]);
+    }
+    __syncthreads();
+    // block rows i = 1..3: X_ij = sum_{k=j}^{i-1} A_ik T_kj, then T_ij = -T_ii X_ij
+    for (int i = 1; i < 4; ++i) {
+        const int r = tid >> 4, cc = tid & 15;
+        for (int j = 0; j < i; ++j) {
+            float x = 0.0f;
+            for (int kb = j; kb < i; ++kb)
+                for (int u = 0; u < 16; ++u)
+                    x = fmaf(lds_ld<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * kb + u)),
+                             lds_ld<float>(sm, L::RGA + 4 * ((16 * kb + u) * RA + 16 * j + cc)), x);
+            lds_st<float>(sm, L::XS + 4 * (256 * j + tid), x);
+        }
+        __syncthreads();
+        for (int j = 0; j < i; ++j) {
+            float x = 0.0f;
+            for (int u = 0; u < 16; ++u)
+                x = fmaf(lds_ld<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * i + u)),
+                         lds_ld<float>(sm, L::XS + 4 * (256 * j + 16 * u + cc)), x);
+            lds_st<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * j + cc), -x);
+        }
+        __syncthreads();
+    }
+    // T as bf16 (lower blocks; the upper ones are zero)
+    for (int e = tid; e < 10 * 256; e += BT) {
+        int i, j;
+        lower_tile(e >> 8, i, j);
+        const int r = 16 * i + ((e & 255) >> 4), s = 16 * j + (e & 15);
+        lds_st<__bf16>(sm, L::TB + 2 * (r * RC + s), (__bf16)lds_ld<float>(sm, L::RGA + 4 * (r * RA + s)));
+    }
+    __syncthreads();
+
+    // ---- wy_w = T KB (bf16 [token][D] in RGC)
+    for (int t = wv; t < 4 * NTD; t += 4) {
+        const int mi = t & 3, ni = t >> 2;
+        const f32x4 x = tile_mm<false, true>(sm, L::TB, RC, L::KB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+        st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * ni, x, l16, q4);
+    }
+    __syncthreads();
+
+    if constexpr (MODE == 0) {
+        // prep record: QH, RR, wy_w [64][D] bf16, P [64][64] bf16, gamma [D]
+        char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
+        const int srcs[3] = {L::QH, L::RR, L::RGC};
+        for (int m = 0; m < 3; ++m)
+            for (int e = tid; e < 64 * D / 8; e += BT) {
+                const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                *reinterpret_cast<bf16x8 *>(rec + m * 128 * D + 2 * (r * D + c0)) =
+                    lds_ld<bf16x8>(sm, srcs[m] + 2 * (r * RK + c0));
+            }
+        for (int e = tid; e < 64 * 8; e += BT) {
+            const int r = e >> 3, c0 = 8 * (e & 7);
+            *reinterpret_cast<bf16x8 *>(rec + 3 * 128 * D + 2 * (r * 64 + c0)) = lds_ld<bf16x8>(sm, L::PB + 2 * (r * RC + c0));
+        }
+        if (tid < D)
+            *reinterpret_cast<float *>(rec + 3 * 128 * D + 64 * 64 * 2 + 4 * tid) =
+                poison ? __builtin_nanf("") : lds_ld<float>(sm, L::GAM + 4 * tid);
+        return;
+    } else {
+        const float *Sin = p.s_ckpt + kd_off;
+        const float *dSo = p.ds_ckpt + kd_off;
+        const float *gam = reinterpret_cast<const float *>(sm + L::GAM);
+
+        // ---- U = T WV - wy_w S_in (bf16 [token][D] in RGA); wave wv takes
+        // the column tiles wv, wv + 4, ... and all four row tiles
+        for (int nn = 0; nn < NTW; ++nn) {
+            const int ni = wv + 4 * nn;
+            f32x4 wu[4], ws[4];
+            for (int mi = 0; mi < 4; ++mi) {
+                wu[mi] = tile_mm<false, true>(sm, L::TB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+                ws[mi] = f32x4{0, 0, 0, 0};
+            }
+            for (int k0 = 0; k0 < D; k0 += 32) {
+                const bf16x8 b = col_frag(Sin, D, k0 + 8 * q4, 16 * ni + l16, nullptr);
+                for (int mi = 0; mi < 4; ++mi)
+                    ws[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + 2 * ((16 * mi + l16) * RK + k0 + 8 * q4)), b, ws[mi]);
+            }
+            for (int mi = 0; mi < 4; ++mi) st_tile_bf(sm, L::RGA, RK, 16 * mi, 16 * ni, wu[mi] - ws[mi], l16, q4);
+        }
+        __syncthreads();
+
+        // ---- dO (bf16 [token][D] in RGB; rows past the end zero) and
+        // dgamma's direct part rowsum(S_in dS_out)
+        for (int e = tid; e < 64 * D / 8; e += BT) {
+            const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            bf16x8 x = {};
+            if (r < len) x = *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0);
+            lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), x);
+        }
+        if (tid < D) {
+            float s = 0.0f;
+            for (int v = 0; v < D; v += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(Sin + tid * D + v);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(dSo + tid * D + v);
+                s += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+            }
+            lds_st<float>(sm, L::DGM + 4 * tid, s);
+        }
+        __syncthreads();
+
+        // ---- dU = scale P^T dO + RR (gamma dS_out) (bf16 in RGC), and
+        // dKH = U dS_out^T (registers, tiles (mi, wv + 4 nn))
+        f32x4 dKH[4][NTW], dQH[4][NTW], dKB[4][NTW], dRR[4][NTW];
+        for (int nn = 0; nn < NTW; ++nn) {
+            const int ni = wv + 4 * nn;
+            f32x4 acc[4];
+            for (int mi = 0; mi < 4; ++mi)
+                acc[mi] = tile_mm<true, true>(sm, L::PB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4) *
+                          p.scale;
+            for (int k0 = 0; k0 < D; k0 += 32) {
+                const bf16x8 b = col_frag(dSo, D, k0 + 8 * q4, 16 * ni + l16, gam);
+                for (int mi = 0; mi < 4; ++mi)
+                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RR + 2 * ((16 * mi + l16) * RK + k0 + 8 * q4)), b, acc[mi]);
+            }
+            for (int mi = 0; mi < 4; ++mi) st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * ni, acc[mi], l16, q4);
+            // dKH[r][c] = sum_v U[r][v] dS_out[c][v]
+            for (int mi = 0; mi < 4; ++mi) dKH[mi][nn] = f32x4{0, 0, 0, 0};
+            for (int k0 = 0; k0 < D; k0 += 32) {
+                const bf16x8 b = row_frag(dSo, D, 16 * ni + l16, k0 + 8 * q4);
+                for (int mi = 0; mi < 4; ++mi)
+                    dKH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGA + 2 * ((16 * mi + l16) * RK + k0 + 8 * q4)), b, dKH[mi][nn]);
+            }
+        }
+        __syncthreads();
+
+        // ---- dQH = scale dO S_in^T (registers), dwy_w = -dU S_in^T (bf16 in RGD)
+        for (int nn = 0; nn < NTW; ++nn) {
+            const int ni = wv + 4 * nn;
+            f32x4 acc[4];
+            for (int mi = 0; mi < 4; ++mi) dQH[mi][nn] = acc[mi] = f32x4{0, 0, 0, 0};
+            for (int k0 = 0; k0 < D; k0 += 32) {
+                const bf16x8 b = row_frag(Sin, D, 16 * ni + l16, k0 + 8 * q4);
+                for (int mi = 0; mi < 4; ++mi) {
+                    const int o = 2 * ((16 * mi + l16) * RK + k0 + 8 * q4);
+                    dQH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), b, dQH[mi][nn]);
+                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), b, acc[mi]);
+                }
+            }
+            for (int mi = 0; mi < 4; ++mi) {
+                dQH[mi][nn] *= p.scale;
+                st_tile_bf(sm, L::RGD, RK, 16 * mi, 16 * ni, -acc[mi], l16, q4);
+            }
+        }
+        __syncthreads();
+
+        // ---- dP = scale tril(dO U^T) (bf16 over P)
+        for (int t = wv; t < 10; t += 4) {
+            int i, j;
+            lower_tile(t, i, j);
+            const f32x4 x = tile_mm<false, false>(sm, L::RGB, RK, L::RGA, RK, 16 * i, 16 * j, D, f32x4{0, 0, 0, 0}, l16, q4);
+            st_tile_bf(sm, L::PB, RC, 16 * i, 16 * j, tril_mask(x, 16 * i, 16 * j, false, l16, q4) * p.scale, l16, q4);
+        }
+        __syncthreads();
+
+        // ---- WV again (bf16 in RGA)
+        for (int e = tid; e < 64 * D / 8; e += BT) {
+            const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            f32x8 x = {};
+            if (r < len) {
+                const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
+                x = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.v + tv), f32x8) *
+                    __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.w + tv), f32x8);
+            }
+            lds_st<bf16x8>(sm, L::RGA + 2 * (r * RK + c0), f32x8_to_bf16(x));
+        }
+        __syncthreads();
+
+        // ---- dT = strict_tril(dU WV^T + dwy_w KB^T) (bf16 in RGB, all 16 tiles)
+        for (int t = wv; t < 16; t += 4) {
+            const int i = t >> 2, j = t & 3;
+            f32x4 x = tile_mm<false, false>(sm, L::RGC, RK, L::RGA, RK, 16 * i, 16 * j, D, f32x4{0, 0, 0, 0}, l16, q4);
+            x = tile_mm<false, false>(sm, L::RGD, RK, L::KB, RK, 16 * i, 16 * j, D, x, l16, q4);
+            st_tile_bf(sm, L::RGB, RC, 16 * i, 16 * j, tril_mask(x, 16 * i, 16 * j, true, l16, q4), l16, q4);
+        }
+        // ---- dWV = T^T dU -> dv = dWV w, dw = dWV v; dKB = T^T dwy_w
+        for (int nn = 0; nn < NTW; ++nn) {
+            const int ni = wv + 4 * nn;
+            for (int mi = 0; mi < 4; ++mi) {
+                const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGC, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 16 * mi + 4 * q4 + e;
+                    if (s < len) {
+                        const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
+                        const float pn = poison ? __builtin_nanf("") : 1.0f;
+                        p.dv[o] = to_bf(x[e] * bf(p.w[o]) * pn);
+                        p.dw[o] = to_bf(x[e] * bf(p.v[o]) * pn);
+                    }
+                }
+                dKB[mi][nn] = tile_mm<true, true>(sm, L::TB, RC, L::RGD, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+            }
+        }
+        __syncthreads();
+
+        // ---- Y = T^T dT (bf16 in RGA), then dA = -strict_tril(Y T^T) (bf16 in RGB)
+        for (int t = wv; t < 16; t += 4) {
+            const int i = t >> 2, j = t & 3;
+            const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGB, RC, 16 * i, 16 * j, 64, f32x4{0, 0, 0, 0}, l16, q4);
+            st_tile_bf(sm, L::RGA, RC, 16 * i, 16 * j, x, l16, q4);
+        }
+        __syncthreads();
+        for (int t = wv; t < 16; t += 4) {
+            const int i = t >> 2, j = t & 3;
+            const f32x4 x = tile_mm<false, false>(sm, L::RGA, RC, L::TB, RC, 16 * i, 16 * j, 64, f32x4{0, 0, 0, 0}, l16, q4);
+            st_tile_bf(sm, L::RGB, RC, 16 * i, 16 * j, -tril_mask(x, 16 * i, 16 * j, true, l16, q4), l16, q4);
+        }
+        __syncthreads();
+
+        // ---- dKB += dA RR; dRR = dA^T KB + dP^T QH; dQH += dP RR
+        for (int nn = 0; nn < NTW; ++nn) {
+            const int ni = wv + 4 * nn;
+            for (int mi = 0; mi < 4; ++mi) {
+                dKB[mi][nn] = tile_mm<false, true>(sm, L::RGB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dKB[mi][nn], l16, q4);
+                f32x4 x = tile_mm<true, true>(sm, L::RGB, RC, L::KB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+                dRR[mi][nn] = tile_mm<true, true>(sm, L::PB, RC, L::QH, RK, 16 * mi, 16 * ni, 64, x, l16, q4);
+                dQH[mi][nn] = tile_mm<false, true>(sm, L::PB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dQH[mi][nn], l16, q4);
+            }
+        }
+        __syncthreads();
+
+        // ---- epilogue: the four K-side gradients as float32 [64][D] in LDS,
+        // then one thread per channel through the decay factors
+        constexpr int RF = L::RF, EF = L::EF;
+        const float dgm = tid < D ? lds_ld<float>(sm, L::DGM + 4 * tid) : 0.0f;
+        __syncthreads();  // the last LDS reads of the regions below are done
+        for (int nn = 0; nn < NTW; ++nn)
+            for (int mi = 0; mi < 4; ++mi) {
+                const int ni = wv + 4 * nn;
+                st_tile_f32(sm, 0 * EF, RF, 16 * mi, 16 * ni, dQH[mi][nn], l16, q4);
+                st_tile_f32(sm, 1 * EF, RF, 16 * mi, 16 * ni, dKB[mi][nn], l16, q4);
+                st_tile_f32(sm, 2 * EF, RF, 16 * mi, 16 * ni, dRR[mi][nn], l16, q4);
+                st_tile_f32(sm, 3 * EF, RF, 16 * mi, 16 * ni, dKH[mi][nn], l16, q4);
+            }
+        __syncthreads();
+        if (tid < D) {
+            const int ch = tid;
+            float G[64];
+            float run = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 64; ++r) {
+                run = fmaf(r < len ? p.g[((t0 + r) * p.HV + hv) * D + ch] : 0.0f, LOG2E, run);  // as in the prep phase
+                G[r] = run;
+            }
+            const float gm = ex2(G[63]);
+            // The decay factors' share of dG pairs each product's gradient
+            // with the very bf16 factors that product used (rounded as in the
+            // prep phase, from the same float32 values): a pair (r, s) adds
+            // to dG_r and subtracts from dG_s the same amount, and with
+            // mismatched roundings these would no longer cancel in the
+            // reverse cumulative sum under strong decay.
+            // dgamma = rowsum(S_in dS_out) + sum_r dKH[r] RR[r]
+            float dgam = dgm;
+#pragma unroll
+            for (int r = 0; r < 64; ++r) {
+                if (r >= len) continue;
+                const float kv = bf(p.k[((t0 + r) * p.H + hk) * D + ch]);
+                dgam += lds_ld<float>(sm, 3 * EF + 4 * (r * RF + ch)) * rbf(kv * ex2(-G[r]));
+            }
+            const float pn = poison ? __builtin_nanf("") : 1.0f;
+            float acc = dgam * gm;  // dG of the last row (G_last)
+#pragma unroll
+            for (int r = 63; r >= 0; --r) {
+                if (r >= len) continue;  // padded rows: zero inputs, zero dG
+                const int64_t tk = ((t0 + r) * p.H + hk) * D + ch, tv = ((t0 + r) * p.HV + hv) * D + ch;
+                const float qv = bf(p.q[tk]), kv = bf(p.k[tk]), bv = bf(p.beta[tv]);
+                const float eg = ex2(G[r]), ie = ex2(-G[r]);
+                const int o = 4 * (r * RF + ch);
+                const float gq = lds_ld<float>(sm, 0 * EF + o), gkb = lds_ld<float>(sm, 1 * EF + o);
+                const float grr = lds_ld<float>(sm, 2 * EF + o) + gm * lds_ld<float>(sm, 3 * EF + o);
+                acc += gq * rbf(qv * eg) + gkb * rbf(bv * kv * eg) - grr * rbf(kv * ie);
+                p.dq_ws[tv] = gq * eg * pn;
+                p.dk_ws[tv] = (gkb * bv * eg + grr * ie) * pn;
+                p.dbeta[tv] = to_bf(gkb * kv * eg * pn);
+                p.dg[tv] = acc * pn;
+            }
+        }
+    }
+}
+
+// -------------------------------------------------- state-gradient pass --
+// One workgroup per (sequence, value head): dS (float32 [D][D], the result
+// layout of 16x16 tiles, wave wv owning columns [wv D/4, (wv + 1) D/4))
+// walks the chunks in reverse; dS entering a chunk's step is the gradient
+// of that chunk's S_out and is saved.
+template <int D>
+struct SL {
+    static constexpr int RK = D + 8, RC = 64 + 8;
+    static constexpr int TK = 64 * RK * 2, TC = 64 * RC * 2;
+    static constexpr int QH = 0, RR = TK, WY = 2 * TK, DO = 3 * TK, PB = 4 * TK, GAM = 4 * TK + TC;
+    static constexpr int SIZE = GAM + 4 * D;
+};
+
+template <int D>
+__global__ __launch_bounds__(BT) void bwd_state_kernel(BwdParams p)
+{
+    using L = SL<D>;
+    constexpr int RK = L::RK, RC = L::RC;
+    constexpr int NRT = D / 16, VW = D / 4, NCT = VW / 16, NKS = D / 32;
+    __shared__ __attribute__((aligned(16))) char sm[L::SIZE];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+    const int n = blockIdx.x / p.HV, hv = blockIdx.x % p.HV;
+    const int64_t sb = cu_of(p, n), se = cu_of(p, n + 1);
+    const int nc = (int)((se - sb + 63) / 64);
+    const int vbase = wv * VW;
+    const int64_t head = ((int64_t)n * p.HV + hv) * D * D;
+
+    f32x4 dS[NRT][NCT];
+    for (int rt = 0; rt < NRT; ++rt)
+        for (int jt = 0; jt < NCT; ++jt)
+            for (int e = 0; e < 4; ++e)
+                dS[rt][jt][e] = p.dht ? p.dht[head + (16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] : 0.0f;
+
+    for (int c = nc - 1; c >= 0; --c) {
+        const int64_t slot = chunk_slot(sb, n, c), t0 = sb + 64 * (int64_t)c;
+        const int len = (int)(se - t0 < 64 ? se - t0 : 64);
+        const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
+        __syncthreads();  // the previous chunk's reads are done
+        for (int e = tid; e < 64 * D / 8; e += BT) {
+            const int r = e / (D / 8), c0 = 8 * (e % (D / 8)), o = 2 * (r * RK + c0);
+            lds_st<bf16x8>(sm, L::QH + o, *reinterpret_cast<const bf16x8 *>(rec + 2 * (r * D + c0)));
+            lds_st<bf16x8>(sm, L::RR + o, *reinterpret_cast<const bf16x8 *>(rec + 128 * D + 2 * (r * D + c0)));
+            lds_st<bf16x8>(sm, L::WY + o, *reinterpret_cast<const bf16x8 *>(rec + 256 * D + 2 * (r * D + c0)));
+            bf16x8 x = {};
+            if (r < len) x = *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0);
+            lds_st<bf16x8>(sm, L::DO + o, x);
+        }
+        for (int e = tid; e < 64 * 8; e += BT) {
+            const int r = e >> 3, c0 = 8 * (e & 7);
+            lds_st<bf16x8>(sm, L::PB + 2 * (r * RC + c0), *reinterpret_cast<const bf16x8 *>(rec + 384 * D + 2 * (r * 64 + c0)));
+        }
+        if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, *reinterpret_cast<const float *>(rec + 384 * D + 8192 + 4 * tid));
+        // the gradient of this chunk's S_out
+        float *dso = p.ds_ckpt + (slot * p.HV + hv) * D * D;
+        for (int rt = 0; rt < NRT; ++rt)
+            for (int jt = 0; jt < NCT; ++jt)
+                for (int e = 0; e < 4; ++e) dso[(16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
+        __syncthreads();
+
+        // dU = scale P^T dO + RR (gamma dS): tokens x this wave's columns.
+        // gamma dS as bf16 operands: k slab ks holds channels
+        // {32 ks + 4 q4 + e} then {32 ks + 16 + 4 q4 + e}; RR is read in
+        // the same channel order.
+        bf16x8 gS[NKS][NCT];
+        for (int ks = 0; ks < NKS; ++ks) {
+            const f32x4 g0 = lds_ld<f32x4>(sm, L::GAM + 4 * (32 * ks + 4 * q4));
+            const f32x4 g1 = lds_ld<f32x4>(sm, L::GAM + 4 * (32 * ks + 16 + 4 * q4));
+            for (int jt = 0; jt < NCT; ++jt)
+                gS[ks][jt] = cat4(f32x4_to_bf16(dS[2 * ks][jt] * g0), f32x4_to_bf16(dS[2 * ks + 1][jt] * g1));
+        }
+        f32x4 dU[4][NCT];
+        for (int mi = 0; mi < 4; ++mi)
+            for (int jt = 0; jt < NCT; ++jt) {
+                f32x4 acc = tile_mm<true, true>(sm, L::PB, RC, L::DO, RK, 16 * mi, vbase + 16 * jt, 64, f32x4{0, 0, 0, 0},
+                                                l16, q4) * p.scale;
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int o = L::RR + 2 * ((16 * mi + l16) * RK + 32 * ks + 4 * q4);
+                    acc = mfma_bf16(cat4(lds_ld<bf16x4>(sm, o), lds_ld<bf16x4>(sm, o + 32)), gS[ks][jt], acc);
+                }
+                dU[mi][jt] = acc;
+            }
+        // dS <- gamma dS + scale QH^T dO - wy_w^T dU; dU as bf16 operands:
+        // k slab ks holds tokens {32 ks + 4 q4 + e} then {32 ks + 16 + 4 q4 + e}
+        bf16x8 dUb[2][NCT];
+        for (int ks = 0; ks < 2; ++ks)
+            for (int jt = 0; jt < NCT; ++jt)
+                dUb[ks][jt] = cat4(f32x4_to_bf16(dU[2 * ks][jt]), f32x4_to_bf16(dU[2 * ks + 1][jt]));
+        for (int rt = 0; rt < NRT; ++rt) {
+            const f32x4 gr = lds_ld<f32x4>(sm, L::GAM + 4 * (16 * rt + 4 * q4));
+            for (int jt = 0; jt < NCT; ++jt) {
+                f32x4 acc = tile_mm<true, true>(sm, L::QH, RK, L::DO, RK, 16 * rt, vbase + 16 * jt, 64, f32x4{0, 0, 0, 0},
+                                                l16, q4) * p.scale;
+                f32x4 neg = {0, 0, 0, 0};
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int o = L::WY + 2 * ((32 * ks + 4 * q4 + (l16 >> 2)) * RK + 16 * rt + 4 * (l16 & 3));
+                    neg = mfma_bf16(cat4(lds_tr(sm, o), lds_tr(sm, o + 32 * RK)), dUb[ks][jt], neg);
+                }
+                dS[rt][jt] = dS[rt][jt] * gr + acc - neg;
+            }
+        }
+    }
+    if (p.dh0)
+        for (int rt = 0; rt < NRT; ++rt)
+            for (int jt = 0; jt < NCT; ++jt)
+                for (int e = 0; e < 4; ++e) p.dh0[head + (16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
+}
+
+// ------------------------------------------------------------- reduce --
+// dq, dk of q/k head h: the sums over its value heads h m .. h m + m - 1.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p)
+{
+    const int m = p.HV / p.H;
+    const int64_t total = p.T * p.H * p.K;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t c = i % p.K, th = i / p.K, h = th % p.H, t = th / p.H;
+        float sq = 0.0f, sk = 0.0f;
+        for (int j = 0; j < m; ++j) {
+            const int64_t o = (t * p.HV + h * m + j) * p.K + c;
+            sq += p.dq_ws[o];
+            sk += p.dk_ws[o];
+        }
+        p.dq[i] = to_bf(sq);
+        p.dk[i] = to_bf(sk);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunk(const BwdParams &p, int mode, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((int64_t)p.nslots * p.HV));
+    if (grid.x == 0) return hipSuccess;
+    if (p.K == 128) {
+        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<128, 0>), grid, dim3(BT), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<128, 1>), grid, dim3(BT), 0, stream, p);
+    } else if (p.K == 64) {
+        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<64, 0>), grid, dim3(BT), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<64, 1>), grid, dim3(BT), 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((int64_t)p.N * p.HV));
+    if (grid.x == 0) return hipSuccess;
+    if (p.K == 128) hipLaunchKernelGGL((bwd_state_kernel<128>), grid, dim3(BT), 0, stream, p);
+    else if (p.K == 64) hipLaunchKernelGGL((bwd_state_kernel<64>), grid, dim3(BT), 0, stream, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const BwdParams &p, hipStream_t stream)
+{
+    const int64_t total = p.T * p.H * p.K;
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn2

@@ -52,22 +52,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gdn2_device.h"
 #include "gdn2_internal.h"
 
 namespace gdn2 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+using namespace dev;
 
-constexpr int CH = 64;       // chunk length
 constexpr int NTHR = 512;    // threads per workgroup (8 waves)
 constexpr int NROLE = 256;   // threads per role (4 waves)
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -78,11 +70,6 @@ constexpr float XLIM = 120.0f;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------- helpers --
-__device__ __forceinline__ bf16x8 f32x8_to_bf16(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
-__device__ __forceinline__ bf16x4 f32x4_to_bf16(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // Element type of q, k, v, beta, w and out: bf16 (IO_BF16) or fp16 (IO_F16).
 // Values are widened to float32 on load; the MFMA operands built from them
 // are bf16 either way.
@@ -106,29 +93,6 @@ __device__ __forceinline__ float io_bits_to_f32(uint16_t b)
 }
 template <typename T8>
 __device__ __forceinline__ f32x8 to_f32x8(T8 x) { return __builtin_convertvector(x, f32x8); }
-
-template <typename T>
-__device__ __forceinline__ T lds_ld(const char *base, int off) { return *reinterpret_cast<const T *>(base + off); }
-template <typename T>
-__device__ __forceinline__ void lds_st(char *base, int off, T v) { *reinterpret_cast<T *>(base + off) = v; }
-
-// LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each group of 16
-// lanes, lane s supplies the address of 4 consecutive bf16 of row k0 + s/4,
-// columns c0 + 4 (s % 4); lane s receives column c0 + s of rows k0 .. k0 + 3.
-__device__ __forceinline__ bf16x4 lds_tr(const char *base, int off)
-{
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + off));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
-__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
-
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A float32 4-vector as the sum of two bf16 4-vectors (high part rounded to
 // nearest even, low part the rounded remainder).
@@ -253,18 +217,6 @@ struct RawChunk {
 __device__ __attribute__((aligned(16))) uint16_t kOnes16[2][8] = {
     {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80},   // bf16 1.0
     {0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00, 0x3c00}};  // fp16 1.0
-
-constexpr int BUF_DWORD3 = 0x00020000;  // raw (unformatted) buffer, gfx9 family
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, BUF_DWORD3);
-}
-template <typename T>
-__device__ __forceinline__ T buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 template <int K, int RPT, int IO, bool G16>
 __device__ __forceinline__ void load_decay(RawChunk<RPT, IO> &R, const FwdParams &p, int64_t c0, int len, int hv,
@@ -415,6 +367,7 @@ struct Chain {
     bool ident;       // entering state is the identity (transition pass, K == V)
     bool zero_v;      // values taken as zero (transition pass)
     bool out;         // write the output rows
+    float *ckpt;      // the state entering each chunk, chunk c at ckpt + c * HV * K * V (nullptr: none)
 };
 
 __device__ __forceinline__ int chunk_len(int64_t c0, int64_t te) { return (int)((te - c0) < CH ? (te - c0) : CH); }
@@ -967,6 +920,13 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         // same k order, and U as bf16 operands (Ub) in the same way over
         // tokens.
         bf16x8 Ub[2][NCT], Sb[NKS][NCT];
+        if (it > 0 && ch.ckpt) {
+            // the float32 state entering chunk it - 1 (for the backward)
+            float *const dst = ch.ckpt + (int64_t)(it - 1) * p.HV * (K * V) + vbase + l16;
+            for (int rt = 0; rt < NRT; ++rt)
+                for (int jt = 0; jt < NCT; ++jt)
+                    for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * q4 + e) * V + 16 * jt] = S[rt][jt][e];
+        }
         if (it > 0) {
             for (int ks = 0; ks < NKS; ++ks)
                 for (int jt = 0; jt < NCT; ++jt)
@@ -1176,7 +1136,8 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     ch.s0_b16 = p.h0_bf16 != 0;
     ch.s1_b16 = p.ht_bf16 != 0;
     ch.ident = ch.zero_v = false;
-    ch.out = true;
+    ch.out = p.out != nullptr;
+    ch.ckpt = p.ckpt ? p.ckpt + (chunk_slot(sb, ch.n, 0) * p.HV + ch.hv) * (int64_t)(K * V) : nullptr;
     if (p.seg_chunks) {
         const int64_t nch = (se - sb + CH - 1) / CH;
         const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI layer (gdn2_api.cpp) and the gfx950
-// kernels (gdn2_fwd.hip). Not installed, not part of the ABI.
+// kernels (gdn2_fwd.hip, gdn2_recurrent.hip, gdn2_bwd.hip). Not installed, not
+// part of the ABI.
 #pragma once
 
 #include <stdint.h>
@@ -45,7 +46,45 @@ struct FwdParams {
     float *wb;             // [N, HV, nseg, K, V] segment end state from a zero start (segment 0: from h0)
     float *wm;             // [N, HV, nseg, K, K] segment transition (state map S_in -> S_out minus wb)
     float *ws;             // [N, HV, nseg, K, V] entering state of segment j >= 1
+    // Optional: the float32 K-major state entering every chunk, written to
+    // ckpt[slot][hv] with slot = cu[n] / 64 + n + c for chunk c of sequence
+    // n (whole-sequence path only; out may then be nullptr: no output)
+    float *ckpt;
 };
+
+// Checkpoint slot of chunk c of sequence n that starts at token cu_n: unique
+// over all chunks of a packed batch and below T / 64 + N.
+__host__ __device__ inline int64_t chunk_slot(int64_t cu_n, int64_t n, int64_t c) { return cu_n / 64 + n + c; }
+
+// Arguments of the backward kernels (all tensors dense, row-major).
+struct BwdParams {
+    const uint16_t *q, *k;       // [T, H, K] bf16
+    const uint16_t *v, *w;       // [T, HV, V] bf16
+    const float *g;              // [T, HV, K] float32
+    const uint16_t *beta;        // [T, HV, K] bf16
+    const uint16_t *dout;        // [T, HV, V] bf16
+    const void *cu;              // [N + 1] int32 or int64, or nullptr
+    int32_t cu64;
+    const float *dht;            // [N, HV, K, V] gradient of the final state, or nullptr (zero)
+    float *dh0;                  // [N, HV, K, V] gradient of the initial state, or nullptr
+    uint16_t *dq, *dk;           // [T, H, K] bf16
+    uint16_t *dv, *dw;           // [T, HV, V] bf16
+    uint16_t *dbeta;             // [T, HV, K] bf16
+    float *dg;                   // [T, HV, K] float32
+    // workspace
+    float *dq_ws, *dk_ws;        // [T, HV, K] per value head
+    const float *s_ckpt;         // [nslots, HV, K, V] state entering each chunk
+    float *ds_ckpt;              // [nslots, HV, K, V] gradient of the state leaving each chunk
+    char *prep;                  // [nslots, HV] x bwd_prep_bytes(K): QH, RR, wy_w, P, gamma of each chunk
+    int64_t T;
+    int32_t N, H, HV, K, V;
+    int32_t nslots;
+    float scale;
+};
+
+// Bytes of one chunk's record in BwdParams::prep (K = V): QH, RR and wy_w
+// as bf16 [64][K], P as bf16 [64][64], 2^G_last as float32 [K].
+__host__ __device__ inline int64_t bwd_prep_bytes(int K) { return 3 * 64 * K * 2 + 64 * 64 * 2 + K * 4; }
 
 enum { PASS_OUTPUT = 0, PASS_TRANSITION = 1 };
 enum { IO_BF16 = 0, IO_F16 = 1 };
@@ -83,6 +122,13 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);
 // Enqueue the token-by-token forward (decode and short spans): one
 // workgroup per (sequence, value head, 32 value columns).
 hipError_t launch_recurrent_fwd(const FwdParams &p, hipStream_t stream);
+
+// The backward: chunk-parallel prep (mode 0) and gradients (mode 1), the
+// sequential pass of the state gradient over chunks in reverse, and the sum
+// of dq, dk over the value heads of each q/k head.
+hipError_t launch_bwd_chunk(const BwdParams &p, int mode, hipStream_t stream);
+hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream);
+hipError_t launch_bwd_reduce(const BwdParams &p, hipStream_t stream);
 
 // Enqueue the segment combine of a split forward: ws[j + 1] = wm[j] ws[j] +
 // wb[j] in segment order, with ws[1] = wb[0].

@@ -26,8 +26,8 @@ STATUS = {0: "OK", -1: "NULL_ARG", -2: "DTYPE", -3: "SHAPE", -4: "HEADS",
           -5: "UNSUPPORTED", -6: "LAYOUT", -7: "ALIAS", -8: "HIP"}
 
 EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_opts", "gdn2_chunk_fwd_check", "gdn2_split_plan",
-            "gdn2_recurrent_fwd", "gdn2_recurrent_fwd_opts", "gdn2_recurrent_fwd_check", "gdn2_last_error",
-            "gdn2_abi_version"]
+            "gdn2_recurrent_fwd", "gdn2_recurrent_fwd_opts", "gdn2_recurrent_fwd_check",
+            "gdn2_chunk_bwd", "gdn2_chunk_bwd_check", "gdn2_last_error", "gdn2_abi_version"]
 
 
 class Gdn2Tensor(ctypes.Structure):
@@ -86,6 +86,11 @@ def load_library():
         lib.gdn2_split_plan.restype = ctypes.c_int
         lib.gdn2_chunk_fwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P]
         lib.gdn2_chunk_fwd_check.restype = ctypes.c_int
+        lib.gdn2_chunk_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, P,
+                                       ctypes.c_void_p]
+        lib.gdn2_chunk_bwd.restype = ctypes.c_int
+        lib.gdn2_chunk_bwd_check.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, P]
+        lib.gdn2_chunk_bwd_check.restype = ctypes.c_int
         lib.gdn2_last_error.argtypes = []
         lib.gdn2_last_error.restype = ctypes.c_char_p
         lib.gdn2_abi_version.restype = ctypes.c_int
@@ -210,3 +215,60 @@ def recurrent_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=
     if rc != 0:
         raise Gdn2Error(rc, last_error())
     return out, final_state
+
+
+BWD_GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dw", "d_initial_state")
+
+
+def _bwd_descs(q, k, v, g, beta, w, initial_state, cu_seqlens, d_out, d_final_state, grads):
+    ins = [describe(x) for x in (q, k, v, g, beta, w)]
+    mid = [describe(x) for x in (initial_state, cu_seqlens, d_out, d_final_state)]
+    outs = [describe(grads.get(n)) for n in BWD_GRADS]
+    return ins, mid, outs
+
+
+def chunk_bwd(q, k, v, g, beta, w, d_out, scale=None, initial_state=None, cu_seqlens=None,
+              d_final_state=None, need_d_initial_state=True, grads=None):
+    """Backward of :func:`chunk_fwd` on the current HIP stream.
+
+    q, k [T, H, K], v, w [T, HV, V], beta [T, HV, K], d_out [T, HV, V]: bf16;
+    g [T, HV, K], initial_state and d_final_state [N, HV, K, V]: float32 (the
+    states may be None: zero). Returns a dict with dq, dk (bf16 [T, H, K]),
+    dv, dw (bf16 [T, HV, V]), dbeta (bf16 [T, HV, K]), dg (float32
+    [T, HV, K]) and d_initial_state (float32 [N, HV, K, V], or None when not
+    requested). Tensors given in ``grads`` are written in place.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w), ("d_out", d_out),
+                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens), ("d_final_state", d_final_state)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    T, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    dev = v.device
+    out = dict(grads or {})
+    shapes = {"dq": ((T, H, K), torch.bfloat16), "dk": ((T, H, K), torch.bfloat16),
+              "dv": ((T, HV, V), torch.bfloat16), "dw": ((T, HV, V), torch.bfloat16),
+              "dbeta": ((T, HV, K), torch.bfloat16), "dg": ((T, HV, K), torch.float32),
+              "d_initial_state": ((N, HV, K, V), torch.float32)}
+    for n, (shp, dt) in shapes.items():
+        if out.get(n) is None and (n != "d_initial_state" or need_d_initial_state):
+            out[n] = torch.empty(shp, dtype=dt, device=dev)
+    out.setdefault("d_initial_state", None)
+    ins, mid, outs = _bwd_descs(q, k, v, g, beta, w, initial_state, cu_seqlens, d_out, d_final_state, out)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.gdn2_chunk_bwd(*[_ptr(d) for d in ins], _scale_arg(scale), *[_ptr(d) for d in mid],
+                            *[_ptr(d) for d in outs], ctypes.c_void_p(stream))
+    if rc != 0:
+        raise Gdn2Error(rc, last_error())
+    return out
+
+
+def check_bwd(q, k, v, g, beta, w, d_out, scale=None, initial_state=None, cu_seqlens=None,
+              d_final_state=None, grads=None):
+    """The library's host-side validation of a backward call only (no GPU needed)."""
+    lib = load_library()
+    ins, mid, outs = _bwd_descs(q, k, v, g, beta, w, initial_state, cu_seqlens, d_out, d_final_state, grads or {})
+    return lib.gdn2_chunk_bwd_check(*[_ptr(d) for d in ins], _scale_arg(scale), *[_ptr(d) for d in mid],
+                                    *[_ptr(d) for d in outs])

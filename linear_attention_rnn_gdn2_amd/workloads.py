@@ -143,3 +143,14 @@ def total_tokens(config_id: int, seed: int | None = None) -> int:
     lens = torch.randint(wl.len_range[0], wl.len_range[1] + 1, (wl.n_seqs,), generator=gen)
     return int(lens.sum())
 
+
+
+def synth_cotangents(T, N, HV, K, V, seed, *, d_final=True):
+    """Incoming gradients for a backward call: d_out [T, HV, V] ~ N(0, 1) as
+    bf16 and d_final_state [N, HV, K, V] ~ N(0, 1) as float32 (None when
+    ``d_final`` is false), from their own generator seeded with ``seed``."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed) + 7919)
+    d_out = torch.randn((T, HV, V), generator=gen).to(torch.bfloat16)
+    dht = torch.randn((N, HV, K, V), generator=gen) if d_final else None
+    return d_out, dht

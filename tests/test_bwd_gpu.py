@@ -1,0 +1,140 @@
+"""GPU parity of the backward (gdn2_chunk_bwd through the C ABI) against the
+plain-C FP64 backward oracle, on identical bf16-quantised seeded inputs.
+
+Bar, per gradient tensor: relative L2 error <= BWD_REL_L2 and max abs error
+<= BWD_MAX_ABS times the tensor's largest reference magnitude. The bound is
+looser than the forward's 5e-3 because a gradient passes through up to four
+chained bf16-operand products (the forward's output through two) and the
+bf16-rounded dq, dk, dv, dw, dbeta themselves carry 2^-9 relative rounding;
+errors of independent bf16 roundings add in quadrature, so four products at
+the forward's measured ~2.5e-3 each give ~5e-3, doubled for margin.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_rnn_gdn2_amd.workloads import synth, synth_cotangents
+
+pytestmark = pytest.mark.gpu
+
+BWD_REL_L2 = 1e-2
+BWD_MAX_ABS = 5e-2
+GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dw", "d_initial_state")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from linear_attention_rnn_gdn2_amd import gdn2
+    gdn2.load_library()
+    return gdn2
+
+
+@pytest.fixture(scope="module")
+def c_oracle():
+    import os
+    from oracle.build import LIB, build_c_oracle
+    if not os.path.exists(LIB):
+        build_c_oracle()
+    from oracle.c_oracle import gdn2_recurrence_bwd_c
+    return gdn2_recurrence_bwd_c
+
+
+def case(lengths, H, HV, D, seed, init_std=0.02, g_max=0.1, beta_max=1.0, d_final=True):
+    d = synth(list(lengths), H, HV, D, D, seed, init_std=init_std, g_max=g_max, beta_max=beta_max)
+    T, N = sum(lengths), len(lengths)
+    d["d_out"], d["d_final_state"] = synth_cotangents(T, N, HV, D, D, seed, d_final=d_final)
+    return d
+
+
+def run_both(gdn2, c_oracle, d, tag):
+    dev = torch.device("cuda:0")
+    g = {n: d[n].to(dev) for n in ("q", "k", "v", "g", "beta", "w", "d_out")}
+    s0 = None if d["initial_state"] is None else d["initial_state"].to(dev)
+    dht = None if d["d_final_state"] is None else d["d_final_state"].to(dev)
+    say(f"[bwd] {tag}: GPU")
+    got = gdn2.chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], g["w"], g["d_out"], scale=d["scale"],
+                         initial_state=s0, cu_seqlens=d["cu_seqlens"].to(dev), d_final_state=dht)
+    torch.cuda.synchronize()
+    say(f"[bwd] {tag}: oracle")
+    ref = c_oracle(d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["scale"], d["initial_state"],
+                   d["cu_seqlens"].numpy(), d["d_out"], d["d_final_state"])
+    return {n: got[n].float().cpu().double().numpy() for n in GRADS}, ref
+
+
+def errors(got, ref):
+    res = {}
+    for n in GRADS:
+        a, b = got[n], ref[n]
+        nb = np.linalg.norm(b)
+        rel = np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
+        mx = np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30) if b.size else 0.0
+        res[n] = (rel, mx)
+    return res
+
+
+def assert_parity(got, ref, tag):
+    errs = errors(got, ref)
+    say(f"[bwd] {tag}: " + ", ".join(f"{n} rel-L2 {r:.2e} max {m:.2e}" for n, (r, m) in errs.items()))
+    for n, (r, m) in errs.items():
+        assert np.isfinite(got[n]).all(), f"{tag}: {n} not finite"
+        assert r <= BWD_REL_L2, f"{tag}: {n} rel-L2 {r:.3e}"
+        assert m <= BWD_MAX_ABS, f"{tag}: {n} max-abs/ref-max {m:.3e}"
+
+
+@pytest.mark.parametrize("lengths,H,HV,D", [
+    ((256,), 2, 2, 64),                          # one sequence, whole chunks
+    ((65, 0, 1, 130, 64, 63), 2, 4, 128),        # ragged varlen, empty and 1-token sequences, grouped heads
+    ((200, 77), 1, 3, 64),                       # three value heads per q/k head
+    ((1000,), 4, 4, 128),                        # 16 chunks with a ragged tail
+])
+def test_bwd_matches_oracle(lib, c_oracle, lengths, H, HV, D):
+    d = case(lengths, H, HV, D, seed=sum(lengths) + D)
+    got, ref = run_both(lib, c_oracle, d, f"lengths {lengths} H {H} HV {HV} D {D}")
+    assert_parity(got, ref, f"{lengths}")
+
+
+def test_bwd_defaults_and_strong_gates(lib, c_oracle):
+    """Zero initial state and no final-state gradient; beta up to 2 and
+    stronger decay (g = -U(0, 1) per token)."""
+    d = case((190, 70), 2, 2, 128, seed=5, init_std=None, g_max=1.0, beta_max=2.0, d_final=False)
+    got, ref = run_both(lib, c_oracle, d, "defaults, strong gates")
+    assert_parity(got, ref, "defaults, strong gates")
+
+
+def test_bwd_deterministic(lib):
+    d = case((300,), 2, 2, 64, seed=9)
+    dev = torch.device("cuda:0")
+    args = [d[n].to(dev) for n in ("q", "k", "v", "g", "beta", "w", "d_out")]
+    kw = dict(scale=d["scale"], initial_state=d["initial_state"].to(dev), cu_seqlens=d["cu_seqlens"].to(dev),
+              d_final_state=d["d_final_state"].to(dev))
+    a = lib.chunk_bwd(*args, **kw)
+    b = lib.chunk_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_bwd_decay_beyond_bound_is_nan(lib):
+    """A chunk whose in-chunk decay sum leaves the bound gets NaN gradients
+    (loud), while a sequence whose chunks all stay inside gets finite ones."""
+    d = case((64, 64), 1, 1, 64, seed=13)
+    d["g"][:64] = -3.0  # 64 tokens x -3: |G| = 192 > 120 ln 2 in the first sequence's chunk
+    dev = torch.device("cuda:0")
+    got = lib.chunk_bwd(*[d[n].to(dev) for n in ("q", "k", "v", "g", "beta", "w", "d_out")], scale=d["scale"],
+                        initial_state=d["initial_state"].to(dev), cu_seqlens=d["cu_seqlens"].to(dev),
+                        d_final_state=d["d_final_state"].to(dev))
+    torch.cuda.synchronize()
+    assert torch.isnan(got["dg"][:64].float()).all()
+    assert torch.isnan(got["d_initial_state"][0]).all()
+    assert torch.isfinite(got["dg"][64:].float()).all()
+    assert torch.isfinite(got["d_initial_state"][1]).all()
