@@ -12,6 +12,7 @@ kernel (algorithmic bytes per launch / mean launch time from HIP events on
 the launch stream) and the FP64 oracle timed on the host as a CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ID]
+       python bench.py --mode bwd [--workload ID]   (the backward, its own JSON line)
 """
 
 from __future__ import annotations
@@ -36,13 +37,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+FWD_KERNEL_SOURCES = ("gdn2_device.h", "gdn2_fwd.hip", "gdn2_internal.h")
+
+
 def kernel_source_hash() -> str:
+    """sha256 (first 16 hex) over the sources the forward kernel is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_rnn_gdn2_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in FWD_KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -109,7 +113,7 @@ def summarize_profiles(outdir: str, tag: str):
     src_hash = kernel_source_hash()
     stats = _csv_rows(_find(os.path.join(outdir, "kt"), "_kernel_stats.csv"))
     lines = [f"# rocprofv3 kernel-trace statistics: GDN-2 forward, {tag}", "",
-             f"kernel source hash (sha256 over csrc/*.hip, *.cpp, *.h, first 16 hex): {src_hash}",
+             f"kernel source hash (sha256 over csrc/{', '.join(FWD_KERNEL_SOURCES)}, first 16 hex): {src_hash}",
              "command (from the repository root):", "  " + profile_command("kt"), "",
              f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
     for r in stats:
@@ -156,6 +160,84 @@ def summarize_profiles(outdir: str, tag: str):
     log("\n".join(lines))
 
 
+BWD_METRIC = "GDN-2 chunk backward tokens/s (H32 D128 bf16); % of HBM roofline"
+
+
+def bwd_algorithmic_bytes(T, N, H, HV, K, V, has_init: bool, has_final: bool) -> int:
+    """Bytes the backward must move once: q, k, dq, dk (bf16, per q/k head),
+    v, w, d_out, dv, dw (bf16), beta, dbeta (bf16) and g, dg (float32) per
+    value head, the initial state and its gradient, the final state's
+    gradient."""
+    per_token = 4 * K * H * 2 + HV * (5 * 2 * V + 2 * 2 * K + 2 * 4 * K)
+    state = N * HV * K * V * 4
+    return T * per_token + (2 * state if has_init else state) + (state if has_final else 0)
+
+
+def bwd_mfma_flop(T, N, HV, K) -> int:
+    """Dense MFMA work of the backward's products per (64-token chunk, value
+    head) at K = V = D, counted as issued (the forward recompute, the prep
+    and gradient passes' 16x16 tiles, the state-gradient pass), times the
+    chunk count (an upper bound of ceil(T / 64) + N chunks per head)."""
+    D = K
+    mm = lambda m, n, k: 2 * m * n * k
+    fwd = 64 * (2 * (32 * (3 * D + 2 * D) + 3 * D * D))
+    prep = 2 * 10 * mm(16, 16, D) + mm(64, D, 64)
+    state = mm(64, D, 64) + 3 * mm(64, D, D)
+    grads = (prep + mm(64, D, 64) + mm(64, D, D) + mm(64, D, 64) + mm(64, D, D) + 2 * mm(64, D, D)
+             + mm(64, D, D) + 10 * mm(16, 16, D) + 2 * mm(64, 64, D) + 2 * mm(64, D, 64)
+             + 2 * mm(64, 64, 64) + 4 * mm(64, D, 64))
+    return (T // 64 + N) * HV * (fwd + prep + state + grads)
+
+
+def bench_bwd(args, d, gdn2, dev):
+    """Time gdn2.chunk_bwd (all of its launches, workspace included) over the
+    workload and print one JSON line."""
+    import torch
+    from linear_attention_rnn_gdn2_amd.workloads import synth_cotangents
+    wl = d["workload"]
+    T, N = int(d["cu_seqlens"][-1]), len(d["lengths"])
+    d_out, dht = synth_cotangents(T, N, wl.HV, wl.K, wl.V, args.workload)
+    g = {n: d[n].to(dev) for n in ("q", "k", "v", "g", "beta", "w")}
+    s0 = None if d["initial_state"] is None else d["initial_state"].to(dev)
+    cu, do, dh = d["cu_seqlens"].to(dev), d_out.to(dev), dht.to(dev)
+    grads = gdn2.chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], g["w"], do, scale=d["scale"],
+                           initial_state=s0, cu_seqlens=cu, d_final_state=dh)
+
+    def step():
+        gdn2.chunk_bwd(g["q"], g["k"], g["v"], g["g"], g["beta"], g["w"], do, scale=d["scale"],
+                       initial_state=s0, cu_seqlens=cu, d_final_state=dh, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_s = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
+    algo = bwd_algorithmic_bytes(T, N, wl.H, wl.HV, wl.K, wl.V, s0 is not None, True)
+    flop = bwd_mfma_flop(T, N, wl.HV, wl.K)
+    achieved = algo / mean_s / 1e9
+    rec = {"metric": BWD_METRIC, "value": T / (wall / args.steps), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{wl.name} backward: {N} sequences, {T} tokens, H={wl.H} HV={wl.HV} "
+                                  f"K={wl.K} V={wl.V}, chunk 64, seed {args.workload}",
+                      "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_call": algo,
+                        "mean_call_ms": mean_s * 1e3, "mfma_tflops": flop / mean_s / 1e12,
+                        "mfma_frac_of_2500": flop / mean_s / 2.5e15}}
+    log(f"backward: mean call {mean_s*1e3:.3f} ms, {T / mean_s / 1e6:.2f} M tokens/s, {achieved:.0f} GB/s "
+        f"algorithmic ({achieved / HBM_PEAK_GBS * 100:.1f}% of HBM peak), {flop / mean_s / 1e12:.1f} TFLOP/s MFMA")
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(d, workload, min_seconds: float = 10.0):
     """The FP64 oracle on the host: whole passes over the same workload,
     repeated until about ``min_seconds`` of wall time (at least one)."""
@@ -182,6 +264,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: the chunked prefill forward (the headline); bwd: its backward "
+                         "(gradients of every input and of the initial state)")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="host only: write the committed profile summaries from the rocprofv3 CSVs "
                          "of the runs printed by --print-profile-commands, found under DIR")
@@ -221,6 +306,9 @@ def main():
     gdn2.load_library()
     log(f"drawing workload {args.workload}")
     d = make_inputs(args.workload)
+    if args.mode == "bwd":
+        bench_bwd(args, d, gdn2, dev)
+        return
     wl = d["workload"]
     T = int(d["cu_seqlens"][-1])
     N = len(d["lengths"])

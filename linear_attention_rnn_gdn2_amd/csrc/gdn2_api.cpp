@@ -487,7 +487,8 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t sz_ck = up(chunks * state);
     const size_t sz_prep = up(chunks * (size_t)gdn2::bwd_prep_bytes(p.K));
-    const size_t sz_qk = up((size_t)p.T * p.HV * p.K * sizeof(float));
+    // per-value-head dq, dk only with grouped heads (otherwise written directly)
+    const size_t sz_qk = p.H != p.HV ? up((size_t)p.T * p.HV * p.K * sizeof(float)) : 0;
     const size_t total = 2 * sz_ck + sz_prep + 2 * sz_qk;
     void *ws = nullptr;
     if (total > 0 && hipMallocAsync(&ws, total, stream) != hipSuccess)
@@ -507,7 +508,7 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     }
     if (e == hipSuccess) e = gdn2::launch_bwd_state(p, stream);
     if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, 1, stream);
-    if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_reduce(p, stream);
+    if (e == hipSuccess && p.T > 0 && p.H != p.HV) e = gdn2::launch_bwd_reduce(p, stream);
     const hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
     if (e != hipSuccess) return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     if (ef != hipSuccess) return fail(GDN2_ERR_HIP, "workspace release failed: %s", hipGetErrorString(ef));

@@ -131,6 +131,33 @@ __device__ __forceinline__ f32x4 tril_mask(f32x4 x, int m0, int n0, bool strict,
     return x;
 }
 
+// G = cumsum(g) log2(e) of a chunk per key channel, float32 [64][D] (pitch
+// D) at LDS offset go: g is staged with coalesced 16-byte loads (rows past
+// the end of the sequence are zero), then thread c < D scans channel c in
+// place. Returns, for thread c, whether |G| leaves the single-reference
+// bound anywhere in the chunk. The caller synchronises before reading G.
+template <int D>
+__device__ __forceinline__ bool stage_cumsum(char *sm, int go, const BwdParams &p, int64_t t0, int len, int hv, int tid)
+{
+    for (int e = tid; e < 64 * D / 4; e += 256) {
+        const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
+        f32x4 x = {0, 0, 0, 0};
+        if (r < len) x = *reinterpret_cast<const f32x4 *>(p.g + ((t0 + r) * p.HV + hv) * D + c0);
+        lds_st<f32x4>(sm, go + 4 * (r * D + c0), x);
+    }
+    __syncthreads();
+    bool out = false;
+    if (tid < D) {
+        float run = 0.0f;
+        for (int r = 0; r < 64; ++r) {
+            run = fmaf(lds_ld<float>(sm, go + 4 * (r * D + tid)), LOG2E, run);
+            out |= !(fabsf(run) <= XLIM);
+            lds_st<float>(sm, go + 4 * (r * D + tid), run);
+        }
+    }
+    return out;
+}
+
 // ------------------------------------------------------------ LDS layout --
 // Regions of the chunk kernels (K = V = D); lifetimes by phase noted.
 template <int D>
@@ -201,17 +228,8 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
     // ---- G = cumsum(g) log2(e) per channel (float32 scratch [64][D] over RGC, RGD)
     if (tid == 0) lds_st<int>(sm, L::FLG, 0);
     __syncthreads();
-    if (tid < D) {
-        float run = 0.0f;
-        bool out = false;
-        for (int r = 0; r < 64; ++r) {
-            run = fmaf(r < len ? p.g[((t0 + r) * p.HV + hv) * D + tid] : 0.0f, LOG2E, run);
-            out |= !(fabsf(run) <= XLIM);
-            lds_st<float>(sm, L::RGC + 4 * (r * D + tid), run);
-        }
-        lds_st<float>(sm, L::GAM + 4 * tid, ex2(run));
-        if (out) lds_st<int>(sm, L::FLG, 1);
-    }
+    if (stage_cumsum<D>(sm, L::RGC, p, t0, len, hv, tid)) lds_st<int>(sm, L::FLG, 1);
+    if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, ex2(lds_ld<float>(sm, L::RGC + 4 * (63 * D + tid))));
     __syncthreads();
     const bool poison = lds_ld<int>(sm, L::FLG) != 0;
 
@@ -508,61 +526,92 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         }
         __syncthreads();
 
-        // ---- epilogue: the four K-side gradients as float32 [64][D] in LDS,
-        // then one thread per channel through the decay factors
+        // ---- epilogue. dKH enters as K-hat = RR gamma: dRR += gamma dKH and
+        // dgamma += colsum(dKH RR), the latter reduced over the wave's rows
+        // (each channel column belongs to one wave) onto rowsum(S_in dS_out).
+        // The decay factors' share of dG pairs each product's gradient with
+        // the very bf16 factors that product used (rounded as in the prep
+        // phase, from the same float32 values): a pair (r, s) adds to dG_r
+        // and subtracts from dG_s the same amount, and with mismatched
+        // roundings these would no longer cancel in the reverse cumulative
+        // sum under strong decay.
+        for (int nn = 0; nn < NTW; ++nn) {
+            const int col = 16 * (wv + 4 * nn) + l16;
+            const float gc = lds_ld<float>(sm, L::GAM + 4 * col);
+            float part = 0.0f;
+            for (int mi = 0; mi < 4; ++mi)
+                for (int e = 0; e < 4; ++e) {
+                    part += dKH[mi][nn][e] * (float)lds_ld<__bf16>(sm, L::RR + 2 * ((16 * mi + 4 * q4 + e) * RK + col));
+                    dRR[mi][nn][e] += gc * dKH[mi][nn][e];
+                }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (q4 == 0) lds_st<float>(sm, L::DGM + 4 * col, lds_ld<float>(sm, L::DGM + 4 * col) + part);
+        }
         constexpr int RF = L::RF, EF = L::EF;
-        const float dgm = tid < D ? lds_ld<float>(sm, L::DGM + 4 * tid) : 0.0f;
-        __syncthreads();  // the last LDS reads of the regions below are done
+        __syncthreads();  // every read of the regions below is done
         for (int nn = 0; nn < NTW; ++nn)
             for (int mi = 0; mi < 4; ++mi) {
                 const int ni = wv + 4 * nn;
                 st_tile_f32(sm, 0 * EF, RF, 16 * mi, 16 * ni, dQH[mi][nn], l16, q4);
                 st_tile_f32(sm, 1 * EF, RF, 16 * mi, 16 * ni, dKB[mi][nn], l16, q4);
                 st_tile_f32(sm, 2 * EF, RF, 16 * mi, 16 * ni, dRR[mi][nn], l16, q4);
-                st_tile_f32(sm, 3 * EF, RF, 16 * mi, 16 * ni, dKH[mi][nn], l16, q4);
             }
+        stage_cumsum<D>(sm, 3 * EF, p, t0, len, hv, tid);
         __syncthreads();
+        // row-parallel: dq, dk, dbeta, and dG (over dQH)
+        const float pn = poison ? __builtin_nanf("") : 1.0f;
+        const bool direct = p.H == p.HV;  // no grouped heads: dq, dk written here
+        for (int e = tid; e < 64 * D / 8; e += BT) {
+            const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int o = 4 * (r * RF + c0);
+            f32x8 dG = {};
+            if (r < len) {
+                const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
+                const f32x8 qf = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.q + tk), f32x8);
+                const f32x8 kf = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.k + tk), f32x8);
+                const f32x8 bb = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.beta + tv), f32x8);
+                f32x8 dq, dk, db;
+                for (int j = 0; j < 8; ++j) {
+                    const float G = lds_ld<float>(sm, 3 * EF + 4 * (r * D + c0 + j));
+                    const float eg = ex2(G), ie = ex2(-G);
+                    const float gq = lds_ld<float>(sm, 0 * EF + o + 4 * j), gkb = lds_ld<float>(sm, 1 * EF + o + 4 * j);
+                    const float grr = lds_ld<float>(sm, 2 * EF + o + 4 * j);
+                    dq[j] = gq * eg * pn;
+                    dk[j] = (gkb * bb[j] * eg + grr * ie) * pn;
+                    db[j] = gkb * kf[j] * eg * pn;
+                    dG[j] = gq * rbf(qf[j] * eg) + gkb * rbf(bb[j] * kf[j] * eg) - grr * rbf(kf[j] * ie);
+                }
+                if (direct) {
+                    *reinterpret_cast<bf16x8 *>(p.dq + tk) = f32x8_to_bf16(dq);
+                    *reinterpret_cast<bf16x8 *>(p.dk + tk) = f32x8_to_bf16(dk);
+                } else {
+                    *reinterpret_cast<f32x4 *>(p.dq_ws + tv) = __builtin_shufflevector(dq, dq, 0, 1, 2, 3);
+                    *reinterpret_cast<f32x4 *>(p.dq_ws + tv + 4) = __builtin_shufflevector(dq, dq, 4, 5, 6, 7);
+                    *reinterpret_cast<f32x4 *>(p.dk_ws + tv) = __builtin_shufflevector(dk, dk, 0, 1, 2, 3);
+                    *reinterpret_cast<f32x4 *>(p.dk_ws + tv + 4) = __builtin_shufflevector(dk, dk, 4, 5, 6, 7);
+                }
+                *reinterpret_cast<bf16x8 *>(p.dbeta + tv) = f32x8_to_bf16(db);
+            }
+            lds_st<f32x4>(sm, o, __builtin_shufflevector(dG, dG, 0, 1, 2, 3));
+            lds_st<f32x4>(sm, o + 16, __builtin_shufflevector(dG, dG, 4, 5, 6, 7));
+        }
+        __syncthreads();
+        // dg = reverse cumulative sum of dG over the chunk; G_last's share
+        // dgamma gamma reaches every row
         if (tid < D) {
-            const int ch = tid;
-            float G[64];
-            float run = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 64; ++r) {
-                run = fmaf(r < len ? p.g[((t0 + r) * p.HV + hv) * D + ch] : 0.0f, LOG2E, run);  // as in the prep phase
-                G[r] = run;
-            }
-            const float gm = ex2(G[63]);
-            // The decay factors' share of dG pairs each product's gradient
-            // with the very bf16 factors that product used (rounded as in the
-            // prep phase, from the same float32 values): a pair (r, s) adds
-            // to dG_r and subtracts from dG_s the same amount, and with
-            // mismatched roundings these would no longer cancel in the
-            // reverse cumulative sum under strong decay.
-            // dgamma = rowsum(S_in dS_out) + sum_r dKH[r] RR[r]
-            float dgam = dgm;
-#pragma unroll
-            for (int r = 0; r < 64; ++r) {
-                if (r >= len) continue;
-                const float kv = bf(p.k[((t0 + r) * p.H + hk) * D + ch]);
-                dgam += lds_ld<float>(sm, 3 * EF + 4 * (r * RF + ch)) * rbf(kv * ex2(-G[r]));
-            }
-            const float pn = poison ? __builtin_nanf("") : 1.0f;
-            float acc = dgam * gm;  // dG of the last row (G_last)
-#pragma unroll
+            float acc = lds_ld<float>(sm, L::DGM + 4 * tid) * lds_ld<float>(sm, L::GAM + 4 * tid);
             for (int r = 63; r >= 0; --r) {
-                if (r >= len) continue;  // padded rows: zero inputs, zero dG
-                const int64_t tk = ((t0 + r) * p.H + hk) * D + ch, tv = ((t0 + r) * p.HV + hv) * D + ch;
-                const float qv = bf(p.q[tk]), kv = bf(p.k[tk]), bv = bf(p.beta[tv]);
-                const float eg = ex2(G[r]), ie = ex2(-G[r]);
-                const int o = 4 * (r * RF + ch);
-                const float gq = lds_ld<float>(sm, 0 * EF + o), gkb = lds_ld<float>(sm, 1 * EF + o);
-                const float grr = lds_ld<float>(sm, 2 * EF + o) + gm * lds_ld<float>(sm, 3 * EF + o);
-                acc += gq * rbf(qv * eg) + gkb * rbf(bv * kv * eg) - grr * rbf(kv * ie);
-                p.dq_ws[tv] = gq * eg * pn;
-                p.dk_ws[tv] = (gkb * bv * eg + grr * ie) * pn;
-                p.dbeta[tv] = to_bf(gkb * kv * eg * pn);
-                p.dg[tv] = acc * pn;
+                acc += lds_ld<float>(sm, 4 * (r * RF + tid));
+                lds_st<float>(sm, 4 * (r * RF + tid), acc);
             }
+        }
+        __syncthreads();
+        for (int e = tid; e < 64 * D / 4; e += BT) {
+            const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
+            if (r < len)
+                *reinterpret_cast<f32x4 *>(p.dg + ((t0 + r) * p.HV + hv) * D + c0) =
+                    lds_ld<f32x4>(sm, 4 * (r * RF + c0)) * pn;
         }
     }
 }

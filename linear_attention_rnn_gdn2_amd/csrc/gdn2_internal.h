@@ -72,7 +72,7 @@ struct BwdParams {
     uint16_t *dbeta;             // [T, HV, K] bf16
     float *dg;                   // [T, HV, K] float32
     // workspace
-    float *dq_ws, *dk_ws;        // [T, HV, K] per value head
+    float *dq_ws, *dk_ws;        // [T, HV, K] per value head (grouped heads only)
     const float *s_ckpt;         // [nslots, HV, K, V] state entering each chunk
     float *ds_ckpt;              // [nslots, HV, K, V] gradient of the state leaving each chunk
     char *prep;                  // [nslots, HV] x bwd_prep_bytes(K): QH, RR, wy_w, P, gamma of each chunk

@@ -247,3 +247,89 @@ def test_recurrent_allows_in_place_state_only(gdn2):
     b = big[16:16 + s0.numel()].view(s0.shape)  # shifted by 64 bytes: overlaps a
     assert call(lib.gdn2_recurrent_fwd_check, a, b) == -7
     assert "final_state overlaps initial_state" in gdn2.last_error()
+
+
+# ------------------------------------------------------------------ backward --
+def bwd_case(T=70, N=2, H=2, HV=4, D=64):
+    bf = torch.bfloat16
+    c = dict(q=torch.zeros(T, H, D, dtype=bf), k=torch.zeros(T, H, D, dtype=bf),
+             v=torch.zeros(T, HV, D, dtype=bf), g=torch.zeros(T, HV, D), beta=torch.zeros(T, HV, D, dtype=bf),
+             w=torch.zeros(T, HV, D, dtype=bf), d_out=torch.zeros(T, HV, D, dtype=bf),
+             initial_state=torch.zeros(N, HV, D, D), d_final_state=torch.zeros(N, HV, D, D),
+             cu_seqlens=torch.tensor([0, 30, T][: N + 1] if N == 2 else [0, T], dtype=torch.int32))
+    grads = dict(dq=torch.zeros(T, H, D, dtype=bf), dk=torch.zeros(T, H, D, dtype=bf),
+                 dv=torch.zeros(T, HV, D, dtype=bf), dw=torch.zeros(T, HV, D, dtype=bf),
+                 dbeta=torch.zeros(T, HV, D, dtype=bf), dg=torch.zeros(T, HV, D),
+                 d_initial_state=torch.zeros(N, HV, D, D))
+    return c, grads
+
+
+def bwd_status(gdn2, c, grads):
+    rc = gdn2.check_bwd(c["q"], c["k"], c["v"], c["g"], c["beta"], c["w"], c["d_out"],
+                        initial_state=c["initial_state"], cu_seqlens=c["cu_seqlens"],
+                        d_final_state=c["d_final_state"], grads=grads)
+    return gdn2.STATUS[rc], gdn2.last_error()
+
+
+def test_bwd_valid_calls(gdn2):
+    c, gr = bwd_case()
+    assert bwd_status(gdn2, c, gr) == ("OK", "")
+    c, gr = bwd_case(D=128)
+    assert bwd_status(gdn2, c, gr)[0] == "OK"
+    for opt in ("initial_state", "d_final_state"):
+        c, gr = bwd_case()
+        c[opt] = None
+        assert bwd_status(gdn2, c, gr)[0] == "OK", opt
+    c, gr = bwd_case()
+    gr["d_initial_state"] = None
+    assert bwd_status(gdn2, c, gr)[0] == "OK"
+    c, gr = bwd_case(T=0)
+    assert bwd_status(gdn2, c, gr)[0] == "OK"
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda c, g: c.update(g=None), "NULL_ARG"),          # the backward needs every gate
+    (lambda c, g: c.update(beta=None), "NULL_ARG"),
+    (lambda c, g: c.update(w=None), "NULL_ARG"),
+    (lambda c, g: c.update(d_out=None), "NULL_ARG"),
+    (lambda c, g: g.update(dq=None), "NULL_ARG"),
+    (lambda c, g: g.update(dg=None), "NULL_ARG"),
+    (lambda c, g: c.update(q=c["q"].half()), "DTYPE"),     # bf16 only
+    (lambda c, g: c.update(g=c["g"].bfloat16()), "DTYPE"),  # float32 g only
+    (lambda c, g: c.update(d_out=c["d_out"].float()), "DTYPE"),
+    (lambda c, g: g.update(dg=g["dg"].bfloat16()), "DTYPE"),
+    (lambda c, g: g.update(dbeta=g["dbeta"].float()), "DTYPE"),
+    (lambda c, g: c.update(initial_state=c["initial_state"].bfloat16()), "DTYPE"),
+    (lambda c, g: c.update(d_out=c["d_out"][:60]), "SHAPE"),
+    (lambda c, g: g.update(dq=torch.zeros(70, 4, 64, dtype=torch.bfloat16)), "SHAPE"),
+    (lambda c, g: g.update(d_initial_state=torch.zeros(3, 4, 64, 64)), "SHAPE"),
+    (lambda c, g: c.update(v=torch.zeros(70, 3, 64, dtype=torch.bfloat16)), "HEADS"),
+    (lambda c, g: c.update(q=torch.zeros(70, 2, 96, dtype=torch.bfloat16)), "UNSUPPORTED"),
+    # strided views are forward-only: the backward takes dense tensors
+    (lambda c, g: c.update(q=torch.zeros(70, 2, 128, dtype=torch.bfloat16)[:, :, :64]), "LAYOUT"),
+    (lambda c, g: g.update(dv=torch.zeros(70, 64, 4, dtype=torch.bfloat16).transpose(1, 2)), "LAYOUT"),
+])
+def test_bwd_rejections(gdn2, mutate, expect):
+    c, gr = bwd_case()
+    mutate(c, gr)
+    code, msg = bwd_status(gdn2, c, gr)
+    assert code == expect, (code, msg)
+    assert msg
+
+
+def test_bwd_alias_rules(gdn2):
+    c, gr = bwd_case()
+    gr["dv"] = c["d_out"]
+    assert bwd_status(gdn2, c, gr)[0] == "ALIAS"
+    c, gr = bwd_case()
+    gr["dw"] = gr["dv"]
+    assert bwd_status(gdn2, c, gr)[0] == "ALIAS"
+    c, gr = bwd_case()
+    gr["d_initial_state"] = c["initial_state"]
+    assert bwd_status(gdn2, c, gr)[0] == "ALIAS"
+
+
+def test_bwd_no_cpu_path(gdn2):
+    c, _ = bwd_case()
+    with pytest.raises(ValueError):
+        gdn2.chunk_bwd(c["q"], c["k"], c["v"], c["g"], c["beta"], c["w"], c["d_out"])

@@ -138,3 +138,19 @@ def test_bwd_decay_beyond_bound_is_nan(lib):
     assert torch.isnan(got["d_initial_state"][0]).all()
     assert torch.isfinite(got["dg"][64:].float()).all()
     assert torch.isfinite(got["d_initial_state"][1]).all()
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_bwd_full_size_workloads(lib, c_oracle, wid):
+    """The single-sequence (H16), varlen (H32, the headline shape) and
+    grouped-value-head (HV48) workloads at full size, every element against
+    the plain-C oracle. (The long-context workload's extreme-decay channels
+    are beyond the backward's decay bound: its gradients are NaN by
+    contract, which test_bwd_decay_beyond_bound_is_nan covers.)"""
+    from linear_attention_rnn_gdn2_amd.workloads import make_inputs
+    d = make_inputs(wid)
+    T, N = int(d["cu_seqlens"][-1]), len(d["lengths"])
+    wl = d["workload"]
+    d["d_out"], d["d_final_state"] = synth_cotangents(T, N, wl.HV, wl.K, wl.V, wid)
+    got, ref = run_both(lib, c_oracle, d, f"workload {wl.name}")
+    assert_parity(got, ref, wl.name)
