@@ -79,6 +79,7 @@ PROFILE_STEPS = {
     "pmc_write": ("--pmc WRITE_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline"),
     "cal_fetch": ("--pmc FETCH_SIZE", "--copy-probe-mib 1024"),
     "cal_write": ("--pmc WRITE_SIZE", "--copy-probe-mib 1024"),
+    "bkt": ("--kernel-trace --stats", "--mode bwd --steps 5 --warmup 1"),
 }
 KERNEL_TAG = "chunk_fwd_kernel"
 
@@ -158,6 +159,18 @@ def summarize_profiles(outdir: str, tag: str):
                   f, indent=1)
         f.write("\n")
     log("\n".join(lines))
+    bdir = os.path.join(outdir, "bkt")
+    if os.path.isdir(bdir):
+        rows = _csv_rows(_find(bdir, "_kernel_stats.csv"))
+        bl = [f"# rocprofv3 kernel-trace statistics: GDN-2 backward (gdn2_chunk_bwd), {tag}", "",
+              "command (from the repository root):", "  " + profile_command("bkt"), "",
+              f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
+        for r in rows:
+            bl.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
+                      f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {r['Name']}")
+        with open(os.path.join(ROOT, "profiles", f"bwd_kernels_{tag}.txt"), "w") as f:
+            f.write("\n".join(bl) + "\n")
+        log("\n".join(bl))
 
 
 BWD_METRIC = "GDN-2 chunk backward tokens/s (H32 D128 bf16); % of HBM roofline"
