@@ -139,11 +139,17 @@ __device__ __forceinline__ f32x4 tril_mask(f32x4 x, int m0, int n0, bool strict,
 template <int D>
 __device__ __forceinline__ bool stage_cumsum(char *sm, int go, const BwdParams &p, int64_t t0, int len, int hv, int tid)
 {
-    for (int e = tid; e < 64 * D / 4; e += 256) {
-        const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
-        f32x4 x = {0, 0, 0, 0};
-        if (r < len) x = *reinterpret_cast<const f32x4 *>(p.g + ((t0 + r) * p.HV + hv) * D + c0);
-        lds_st<f32x4>(sm, go + 4 * (r * D + c0), x);
+    constexpr int NU = 64 * D / 4 / 256;  // 16-byte pieces per thread, all loads in flight together
+    f32x4 x[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int e = tid + 256 * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+        x[u] = r < len ? *reinterpret_cast<const f32x4 *>(p.g + ((t0 + r) * p.HV + hv) * D + c0) : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int e = tid + 256 * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+        lds_st<f32x4>(sm, go + 4 * (r * D + c0), x[u]);
     }
     __syncthreads();
     bool out = false;
@@ -233,36 +239,44 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
     __syncthreads();
     const bool poison = lds_ld<int>(sm, L::FLG) != 0;
 
-    // ---- QH, KB, RR, WV (bf16, row-major [token][D]); rows past the end are zero
-    for (int e = tid; e < 64 * D / 8; e += BT) {
-        const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
-        f32x8 qf = {}, kf = {}, bb = {}, vf = {}, wf = {};
-        if (r < len) {
+    // ---- QH, KB, RR, WV (bf16, row-major [token][D]); rows past the end are
+    // zero. Every load of a thread is issued before the first use.
+    constexpr int NU8 = 64 * D / 8 / BT;  // 16-byte row pieces per thread
+    {
+        bf16x8 qr[NU8], kr[NU8], br[NU8], vr[NU8], wr[NU8];
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-            const bf16x8 qr = *reinterpret_cast<const bf16x8 *>(p.q + tk);
-            const bf16x8 kr = *reinterpret_cast<const bf16x8 *>(p.k + tk);
-            const bf16x8 br = *reinterpret_cast<const bf16x8 *>(p.beta + tv);
-            const bf16x8 vr = *reinterpret_cast<const bf16x8 *>(p.v + tv);
-            const bf16x8 wr = *reinterpret_cast<const bf16x8 *>(p.w + tv);
-            qf = __builtin_convertvector(qr, f32x8);
-            kf = __builtin_convertvector(kr, f32x8);
-            bb = __builtin_convertvector(br, f32x8);
-            vf = __builtin_convertvector(vr, f32x8);
-            wf = __builtin_convertvector(wr, f32x8);
+            const bool ok = r < len;
+            const bf16x8 z = {};
+            qr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : z;
+            kr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : z;
+            br[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : z;
+            vr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : z;
+            wr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : z;
         }
-        f32x8 qh, kb, rr;
-        for (int j = 0; j < 8; ++j) {
-            const float G = lds_ld<float>(sm, L::RGC + 4 * (r * D + c0 + j));
-            const float eg = ex2(G), ie = ex2(-G);
-            qh[j] = qf[j] * eg;
-            kb[j] = bb[j] * kf[j] * eg;
-            rr[j] = kf[j] * ie;
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const f32x8 qf = __builtin_convertvector(qr[u], f32x8), kf = __builtin_convertvector(kr[u], f32x8);
+            const f32x8 bb = __builtin_convertvector(br[u], f32x8);
+            f32x8 qh, kb, rr;
+            for (int j = 0; j < 8; ++j) {
+                const float G = lds_ld<float>(sm, L::RGC + 4 * (r * D + c0 + j));
+                const float eg = ex2(G), ie = ex2(-G);
+                qh[j] = qf[j] * eg;
+                kb[j] = bb[j] * kf[j] * eg;
+                rr[j] = kf[j] * ie;
+            }
+            const int o = 2 * (r * RK + c0);
+            lds_st<bf16x8>(sm, L::QH + o, f32x8_to_bf16(qh));
+            lds_st<bf16x8>(sm, L::KB + o, f32x8_to_bf16(kb));
+            lds_st<bf16x8>(sm, L::RR + o, f32x8_to_bf16(rr));
+            if constexpr (MODE == 1)
+                lds_st<bf16x8>(sm, L::RGB + o,
+                               f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
         }
-        const int o = 2 * (r * RK + c0);
-        lds_st<bf16x8>(sm, L::QH + o, f32x8_to_bf16(qh));
-        lds_st<bf16x8>(sm, L::KB + o, f32x8_to_bf16(kb));
-        lds_st<bf16x8>(sm, L::RR + o, f32x8_to_bf16(rr));
-        lds_st<bf16x8>(sm, L::RGB + o, f32x8_to_bf16(vf * wf));
     }
     // the blocks above the diagonal of P and T stay zero
     for (int e = tid; e < 6 * 256; e += BT) {
@@ -379,31 +393,47 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
                 wu[mi] = tile_mm<false, true>(sm, L::TB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
                 ws[mi] = f32x4{0, 0, 0, 0};
             }
-            for (int k0 = 0; k0 < D; k0 += 32) {
-                const bf16x8 b = col_frag(Sin, D, k0 + 8 * q4, 16 * ni + l16, nullptr);
+            bf16x8 fr[D / 32];
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) fr[ks] = col_frag(Sin, D, 32 * ks + 8 * q4, 16 * ni + l16, nullptr);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
                 for (int mi = 0; mi < 4; ++mi)
-                    ws[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + 2 * ((16 * mi + l16) * RK + k0 + 8 * q4)), b, ws[mi]);
-            }
+                    ws[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fr[ks], ws[mi]);
             for (int mi = 0; mi < 4; ++mi) st_tile_bf(sm, L::RGA, RK, 16 * mi, 16 * ni, wu[mi] - ws[mi], l16, q4);
         }
         __syncthreads();
 
         // ---- dO (bf16 [token][D] in RGB; rows past the end zero) and
         // dgamma's direct part rowsum(S_in dS_out)
-        for (int e = tid; e < 64 * D / 8; e += BT) {
-            const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            bf16x8 x = {};
-            if (r < len) x = *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0);
-            lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), x);
-        }
-        if (tid < D) {
-            float s = 0.0f;
-            for (int v = 0; v < D; v += 4) {
-                const f32x4 a = *reinterpret_cast<const f32x4 *>(Sin + tid * D + v);
-                const f32x4 b = *reinterpret_cast<const f32x4 *>(dSo + tid * D + v);
-                s += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+        {
+            bf16x8 x[NU8];
+#pragma unroll
+            for (int u = 0; u < NU8; ++u) {
+                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                x[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : bf16x8{};
             }
-            lds_st<float>(sm, L::DGM + 4 * tid, s);
+            // rowsum(S_in dS_out): BT / D threads per channel, each over a
+            // contiguous part of the row
+            constexpr int TPC = BT / D, PART = D / TPC;
+            const int ch = tid / TPC, p0 = (tid % TPC) * PART;
+            f32x4 a[PART / 4], b[PART / 4];
+#pragma unroll
+            for (int u = 0; u < PART / 4; ++u) {
+                a[u] = *reinterpret_cast<const f32x4 *>(Sin + ch * D + p0 + 4 * u);
+                b[u] = *reinterpret_cast<const f32x4 *>(dSo + ch * D + p0 + 4 * u);
+            }
+#pragma unroll
+            for (int u = 0; u < NU8; ++u) {
+                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), x[u]);
+            }
+            float sdot = 0.0f;
+#pragma unroll
+            for (int u = 0; u < PART / 4; ++u)
+                sdot += a[u][0] * b[u][0] + a[u][1] * b[u][1] + a[u][2] * b[u][2] + a[u][3] * b[u][3];
+            for (int d = 1; d < TPC; d <<= 1) sdot += __shfl_xor(sdot, d);
+            if (tid % TPC == 0) lds_st<float>(sm, L::DGM + 4 * ch, sdot);
         }
         __syncthreads();
 
@@ -412,23 +442,28 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         f32x4 dKH[4][NTW], dQH[4][NTW], dKB[4][NTW], dRR[4][NTW];
         for (int nn = 0; nn < NTW; ++nn) {
             const int ni = wv + 4 * nn;
+            bf16x8 fr[D / 32], fc[D / 32];
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gam);
+                fc[ks] = row_frag(dSo, D, 16 * ni + l16, 32 * ks + 8 * q4);
+            }
             f32x4 acc[4];
             for (int mi = 0; mi < 4; ++mi)
                 acc[mi] = tile_mm<true, true>(sm, L::PB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4) *
                           p.scale;
-            for (int k0 = 0; k0 < D; k0 += 32) {
-                const bf16x8 b = col_frag(dSo, D, k0 + 8 * q4, 16 * ni + l16, gam);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
                 for (int mi = 0; mi < 4; ++mi)
-                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RR + 2 * ((16 * mi + l16) * RK + k0 + 8 * q4)), b, acc[mi]);
-            }
+                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RR + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fr[ks], acc[mi]);
             for (int mi = 0; mi < 4; ++mi) st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * ni, acc[mi], l16, q4);
             // dKH[r][c] = sum_v U[r][v] dS_out[c][v]
             for (int mi = 0; mi < 4; ++mi) dKH[mi][nn] = f32x4{0, 0, 0, 0};
-            for (int k0 = 0; k0 < D; k0 += 32) {
-                const bf16x8 b = row_frag(dSo, D, 16 * ni + l16, k0 + 8 * q4);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
                 for (int mi = 0; mi < 4; ++mi)
-                    dKH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGA + 2 * ((16 * mi + l16) * RK + k0 + 8 * q4)), b, dKH[mi][nn]);
-            }
+                    dKH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGA + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fc[ks],
+                                            dKH[mi][nn]);
         }
         __syncthreads();
 
@@ -437,14 +472,16 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
             const int ni = wv + 4 * nn;
             f32x4 acc[4];
             for (int mi = 0; mi < 4; ++mi) dQH[mi][nn] = acc[mi] = f32x4{0, 0, 0, 0};
-            for (int k0 = 0; k0 < D; k0 += 32) {
-                const bf16x8 b = row_frag(Sin, D, 16 * ni + l16, k0 + 8 * q4);
+            bf16x8 fr[D / 32];
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) fr[ks] = row_frag(Sin, D, 16 * ni + l16, 32 * ks + 8 * q4);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
                 for (int mi = 0; mi < 4; ++mi) {
-                    const int o = 2 * ((16 * mi + l16) * RK + k0 + 8 * q4);
-                    dQH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), b, dQH[mi][nn]);
-                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), b, acc[mi]);
+                    const int o = 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4);
+                    dQH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), fr[ks], dQH[mi][nn]);
+                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), fr[ks], acc[mi]);
                 }
-            }
             for (int mi = 0; mi < 4; ++mi) {
                 dQH[mi][nn] *= p.scale;
                 st_tile_bf(sm, L::RGD, RK, 16 * mi, 16 * ni, -acc[mi], l16, q4);
@@ -462,15 +499,21 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         __syncthreads();
 
         // ---- WV again (bf16 in RGA)
-        for (int e = tid; e < 64 * D / 8; e += BT) {
-            const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            f32x8 x = {};
-            if (r < len) {
+        {
+            bf16x8 vr[NU8], wr[NU8];
+#pragma unroll
+            for (int u = 0; u < NU8; ++u) {
+                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
-                x = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.v + tv), f32x8) *
-                    __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.w + tv), f32x8);
+                vr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
+                wr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
             }
-            lds_st<bf16x8>(sm, L::RGA + 2 * (r * RK + c0), f32x8_to_bf16(x));
+#pragma unroll
+            for (int u = 0; u < NU8; ++u) {
+                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                lds_st<bf16x8>(sm, L::RGA + 2 * (r * RK + c0),
+                               f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
+            }
         }
         __syncthreads();
 
@@ -484,15 +527,28 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         // ---- dWV = T^T dU -> dv = dWV w, dw = dWV v; dKB = T^T dwy_w
         for (int nn = 0; nn < NTW; ++nn) {
             const int ni = wv + 4 * nn;
+            // v and w of the lane's 16 elements, all in flight before use
+            uint16_t wl[4][4], vl[4][4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 16 * mi + 4 * q4 + e;
+                    const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
+                    wl[mi][e] = s < len ? p.w[o] : (uint16_t)0;
+                    vl[mi][e] = s < len ? p.v[o] : (uint16_t)0;
+                }
+            const float pn = poison ? __builtin_nanf("") : 1.0f;
+#pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGC, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = 16 * mi + 4 * q4 + e;
                     if (s < len) {
                         const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
-                        const float pn = poison ? __builtin_nanf("") : 1.0f;
-                        p.dv[o] = to_bf(x[e] * bf(p.w[o]) * pn);
-                        p.dw[o] = to_bf(x[e] * bf(p.v[o]) * pn);
+                        p.dv[o] = to_bf(x[e] * bf(wl[mi][e]) * pn);
+                        p.dw[o] = to_bf(x[e] * bf(vl[mi][e]) * pn);
                     }
                 }
                 dKB[mi][nn] = tile_mm<true, true>(sm, L::TB, RC, L::RGD, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
@@ -562,15 +618,25 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         // row-parallel: dq, dk, dbeta, and dG (over dQH)
         const float pn = poison ? __builtin_nanf("") : 1.0f;
         const bool direct = p.H == p.HV;  // no grouped heads: dq, dk written here
-        for (int e = tid; e < 64 * D / 8; e += BT) {
-            const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
+        bf16x8 eq[NU8], ek[NU8], eb[NU8];
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
+            eq[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : bf16x8{};
+            ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
+            eb[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : bf16x8{};
+        }
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int o = 4 * (r * RF + c0);
             f32x8 dG = {};
             if (r < len) {
                 const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-                const f32x8 qf = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.q + tk), f32x8);
-                const f32x8 kf = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.k + tk), f32x8);
-                const f32x8 bb = __builtin_convertvector(*reinterpret_cast<const bf16x8 *>(p.beta + tv), f32x8);
+                const f32x8 qf = __builtin_convertvector(eq[u], f32x8);
+                const f32x8 kf = __builtin_convertvector(ek[u], f32x8);
+                const f32x8 bb = __builtin_convertvector(eb[u], f32x8);
                 f32x8 dq, dk, db;
                 for (int j = 0; j < 8; ++j) {
                     const float G = lds_ld<float>(sm, 3 * EF + 4 * (r * D + c0 + j));
@@ -653,21 +719,38 @@ __global__ __launch_bounds__(BT) void bwd_state_kernel(BwdParams p)
         const int64_t slot = chunk_slot(sb, n, c), t0 = sb + 64 * (int64_t)c;
         const int len = (int)(se - t0 < 64 ? se - t0 : 64);
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
+        // every load of the chunk's operands in flight before the first store
+        constexpr int NU8 = 64 * D / 8 / BT, NUP = 64 * 8 / BT;
+        bf16x8 xq[NU8], xr[NU8], xw[NU8], xo[NU8], xp[NUP];
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            xq[u] = *reinterpret_cast<const bf16x8 *>(rec + 2 * (r * D + c0));
+            xr[u] = *reinterpret_cast<const bf16x8 *>(rec + 128 * D + 2 * (r * D + c0));
+            xw[u] = *reinterpret_cast<const bf16x8 *>(rec + 256 * D + 2 * (r * D + c0));
+            xo[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : bf16x8{};
+        }
+#pragma unroll
+        for (int u = 0; u < NUP; ++u) {
+            const int e = tid + BT * u, r = e >> 3, c0 = 8 * (e & 7);
+            xp[u] = *reinterpret_cast<const bf16x8 *>(rec + 384 * D + 2 * (r * 64 + c0));
+        }
+        const float xg = tid < D ? *reinterpret_cast<const float *>(rec + 384 * D + 8192 + 4 * tid) : 0.0f;
         __syncthreads();  // the previous chunk's reads are done
-        for (int e = tid; e < 64 * D / 8; e += BT) {
-            const int r = e / (D / 8), c0 = 8 * (e % (D / 8)), o = 2 * (r * RK + c0);
-            lds_st<bf16x8>(sm, L::QH + o, *reinterpret_cast<const bf16x8 *>(rec + 2 * (r * D + c0)));
-            lds_st<bf16x8>(sm, L::RR + o, *reinterpret_cast<const bf16x8 *>(rec + 128 * D + 2 * (r * D + c0)));
-            lds_st<bf16x8>(sm, L::WY + o, *reinterpret_cast<const bf16x8 *>(rec + 256 * D + 2 * (r * D + c0)));
-            bf16x8 x = {};
-            if (r < len) x = *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0);
-            lds_st<bf16x8>(sm, L::DO + o, x);
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8)), o = 2 * (r * RK + c0);
+            lds_st<bf16x8>(sm, L::QH + o, xq[u]);
+            lds_st<bf16x8>(sm, L::RR + o, xr[u]);
+            lds_st<bf16x8>(sm, L::WY + o, xw[u]);
+            lds_st<bf16x8>(sm, L::DO + o, xo[u]);
         }
-        for (int e = tid; e < 64 * 8; e += BT) {
-            const int r = e >> 3, c0 = 8 * (e & 7);
-            lds_st<bf16x8>(sm, L::PB + 2 * (r * RC + c0), *reinterpret_cast<const bf16x8 *>(rec + 384 * D + 2 * (r * 64 + c0)));
+#pragma unroll
+        for (int u = 0; u < NUP; ++u) {
+            const int e = tid + BT * u, r = e >> 3, c0 = 8 * (e & 7);
+            lds_st<bf16x8>(sm, L::PB + 2 * (r * RC + c0), xp[u]);
         }
-        if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, *reinterpret_cast<const float *>(rec + 384 * D + 8192 + 4 * tid));
+        if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, xg);
         // the gradient of this chunk's S_out
         float *dso = p.ds_ckpt + (slot * p.HV + hv) * D * D;
         for (int rt = 0; rt < NRT; ++rt)
