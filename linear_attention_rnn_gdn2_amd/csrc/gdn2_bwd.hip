@@ -49,7 +49,9 @@ namespace {
 
 using namespace dev;
 
-constexpr int BT = 256;  // threads per workgroup (4 waves)
+constexpr int BT = 256;  // threads per workgroup of the state-gradient pass (4 waves)
+constexpr int CT = 512;  // threads per workgroup of the chunk-parallel kernels (8 waves)
+constexpr int NW = CT / 64;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float XLIM = 120.0f;
 
@@ -136,19 +138,19 @@ __device__ __forceinline__ f32x4 tril_mask(f32x4 x, int m0, int n0, bool strict,
 // the end of the sequence are zero), then thread c < D scans channel c in
 // place. Returns, for thread c, whether |G| leaves the single-reference
 // bound anywhere in the chunk. The caller synchronises before reading G.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ bool stage_cumsum(char *sm, int go, const BwdParams &p, int64_t t0, int len, int hv, int tid)
 {
-    constexpr int NU = 64 * D / 4 / 256;  // 16-byte pieces per thread, all loads in flight together
+    constexpr int NU = 64 * D / 4 / NT;  // 16-byte pieces per thread, all loads in flight together
     f32x4 x[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int e = tid + 256 * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+        const int e = tid + NT * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
         x[u] = r < len ? *reinterpret_cast<const f32x4 *>(p.g + ((t0 + r) * p.HV + hv) * D + c0) : f32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int e = tid + 256 * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
+        const int e = tid + NT * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
         lds_st<f32x4>(sm, go + 4 * (r * D + c0), x[u]);
     }
     __syncthreads();
@@ -182,7 +184,8 @@ struct BL {
     static constexpr int TB = PB + TC;            // T (bf16)
     static constexpr int GAM = TB + TC;           // e^G_last [D] float32
     static constexpr int DGM = GAM + 4 * D;       // rowsum(S_in dS_out) [D] float32
-    static constexpr int XS = DGM + 4 * D;        // T blocks: three 16x16 float32 scratch blocks
+    static constexpr int DGP = DGM + 4 * D;       // colsum(dKH RR) per row group [2][D] float32
+    static constexpr int XS = DGP + 8 * D;        // T blocks: three 16x16 float32 scratch blocks
     static constexpr int FLG = XS + 3 * 1024;     // int: chunk beyond the decay bound
     static constexpr int TOTAL = FLG + 16;
     static constexpr int EF = 64 * RF * 4;        // epilogue: dQH, dKB, dRR, dKH float32 [64][RF]
@@ -203,14 +206,19 @@ __device__ __forceinline__ void lower_tile(int t, int &i, int &j)
 // MODE 0: prep record of every chunk (for the state-gradient pass).
 // MODE 1: every gradient of the chunk.
 template <int D, int MODE>
-__global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
+__global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 {
     using L = BL<D>;
     constexpr int RK = L::RK, RC = L::RC, RA = L::RA;
-    constexpr int NTD = D / 16;  // 16-wide tiles across D
-    constexpr int NTW = NTD / 4; // of them per wave
+    constexpr int NTD = D / 16;      // 16-wide tiles across D
+    constexpr int NMG = NW / NTD;    // waves per column tile
+    constexpr int MPW = 4 / NMG;     // row tiles per wave
+    static_assert(NW % NTD == 0 && 4 % NMG == 0, "tile split");
     __shared__ __attribute__((aligned(16))) char sm[L::SIZE];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+    // the [64][D] products' tiles of this wave: column tile ni, row tiles
+    // mg, mg + NMG, ...
+    const int ni = wv % NTD, mg = wv / NTD;
 
     // work item: (checkpoint slot, value head); the slot's sequence is the
     // last one whose first slot is not past it
@@ -234,19 +242,19 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
     // ---- G = cumsum(g) log2(e) per channel (float32 scratch [64][D] over RGC, RGD)
     if (tid == 0) lds_st<int>(sm, L::FLG, 0);
     __syncthreads();
-    if (stage_cumsum<D>(sm, L::RGC, p, t0, len, hv, tid)) lds_st<int>(sm, L::FLG, 1);
+    if (stage_cumsum<D, CT>(sm, L::RGC, p, t0, len, hv, tid)) lds_st<int>(sm, L::FLG, 1);
     if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, ex2(lds_ld<float>(sm, L::RGC + 4 * (63 * D + tid))));
     __syncthreads();
     const bool poison = lds_ld<int>(sm, L::FLG) != 0;
 
     // ---- QH, KB, RR, WV (bf16, row-major [token][D]); rows past the end are
     // zero. Every load of a thread is issued before the first use.
-    constexpr int NU8 = 64 * D / 8 / BT;  // 16-byte row pieces per thread
+    constexpr int NU8 = 64 * D / 8 / CT;  // 16-byte row pieces per thread
     {
         bf16x8 qr[NU8], kr[NU8], br[NU8], vr[NU8], wr[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
-            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
             const bool ok = r < len;
             const bf16x8 z = {};
@@ -258,7 +266,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         }
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
-            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const f32x8 qf = __builtin_convertvector(qr[u], f32x8), kf = __builtin_convertvector(kr[u], f32x8);
             const f32x8 bb = __builtin_convertvector(br[u], f32x8);
             f32x8 qh, kb, rr;
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         }
     }
     // the blocks above the diagonal of P and T stay zero
-    for (int e = tid; e < 6 * 256; e += BT) {
+    for (int e = tid; e < 6 * 256; e += CT) {
         const int b = e >> 8, x = e & 255;
         const int bi = b < 3 ? 0 : b < 5 ? 1 : 2, bj = b < 3 ? b + 1 : b < 5 ? b - 1 : 3;  // (0,1)(0,2)(0,3)(1,2)(1,3)(2,3)
         const int r = 16 * bi + (x >> 4), s = 16 * bj + (x & 15);
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
     __syncthreads();
 
     // ---- A (float32) and P (bf16): 20 lower tiles, 5 per wave
-    for (int t = wv; t < 20; t += 4) {
+    for (int t = wv; t < 20; t += NW) {
         int i, j;
         lower_tile(t, i, j);
         const bool isP = t >= 10;
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
 
     // ---- T = (I + A)^-1 in float32, in place over A. Diagonal blocks by
     // forward substitution (wave i, lane l16 solves column l16 of block i)
-    if (q4 == 0) {
+    if (wv < 4 && q4 == 0) {
         const int bo = L::RGA + 4 * (16 * wv * RA + 16 * wv);
         float a[16][16];
 #pragma unroll
@@ -325,17 +333,18 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
     __syncthreads();
     // block rows i = 1..3: X_ij = sum_{k=j}^{i-1} A_ik T_kj, then T_ij = -T_ii X_ij
     for (int i = 1; i < 4; ++i) {
-        const int r = tid >> 4, cc = tid & 15;
-        for (int j = 0; j < i; ++j) {
+        for (int e = tid; e < 256 * i; e += CT) {
+            const int j = e >> 8, r = (e & 255) >> 4, cc = e & 15;
             float x = 0.0f;
             for (int kb = j; kb < i; ++kb)
                 for (int u = 0; u < 16; ++u)
                     x = fmaf(lds_ld<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * kb + u)),
                              lds_ld<float>(sm, L::RGA + 4 * ((16 * kb + u) * RA + 16 * j + cc)), x);
-            lds_st<float>(sm, L::XS + 4 * (256 * j + tid), x);
+            lds_st<float>(sm, L::XS + 4 * e, x);
         }
         __syncthreads();
-        for (int j = 0; j < i; ++j) {
+        for (int e = tid; e < 256 * i; e += CT) {
+            const int j = e >> 8, r = (e & 255) >> 4, cc = e & 15;
             float x = 0.0f;
             for (int u = 0; u < 16; ++u)
                 x = fmaf(lds_ld<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * i + u)),
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         __syncthreads();
     }
     // T as bf16 (lower blocks; the upper ones are zero)
-    for (int e = tid; e < 10 * 256; e += BT) {
+    for (int e = tid; e < 10 * 256; e += CT) {
         int i, j;
         lower_tile(e >> 8, i, j);
         const int r = 16 * i + ((e & 255) >> 4), s = 16 * j + (e & 15);
@@ -354,10 +363,10 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
     __syncthreads();
 
     // ---- wy_w = T KB (bf16 [token][D] in RGC)
-    for (int t = wv; t < 4 * NTD; t += 4) {
-        const int mi = t & 3, ni = t >> 2;
-        const f32x4 x = tile_mm<false, true>(sm, L::TB, RC, L::KB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
-        st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * ni, x, l16, q4);
+    for (int t = wv; t < 4 * NTD; t += NW) {
+        const int mi = t & 3, nt = t >> 2;
+        const f32x4 x = tile_mm<false, true>(sm, L::TB, RC, L::KB, RK, 16 * mi, 16 * nt, 64, f32x4{0, 0, 0, 0}, l16, q4);
+        st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * nt, x, l16, q4);
     }
     __syncthreads();
 
@@ -366,12 +375,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
         const int srcs[3] = {L::QH, L::RR, L::RGC};
         for (int m = 0; m < 3; ++m)
-            for (int e = tid; e < 64 * D / 8; e += BT) {
+            for (int e = tid; e < 64 * D / 8; e += CT) {
                 const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 *reinterpret_cast<bf16x8 *>(rec + m * 128 * D + 2 * (r * D + c0)) =
                     lds_ld<bf16x8>(sm, srcs[m] + 2 * (r * RK + c0));
             }
-        for (int e = tid; e < 64 * 8; e += BT) {
+        for (int e = tid; e < 64 * 8; e += CT) {
             const int r = e >> 3, c0 = 8 * (e & 7);
             *reinterpret_cast<bf16x8 *>(rec + 3 * 128 * D + 2 * (r * 64 + c0)) = lds_ld<bf16x8>(sm, L::PB + 2 * (r * RC + c0));
         }
@@ -385,22 +394,24 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         const float *gam = reinterpret_cast<const float *>(sm + L::GAM);
 
         // ---- U = T WV - wy_w S_in (bf16 [token][D] in RGA); wave wv takes
-        // the column tiles wv, wv + 4, ... and all four row tiles
-        for (int nn = 0; nn < NTW; ++nn) {
-            const int ni = wv + 4 * nn;
-            f32x4 wu[4], ws[4];
-            for (int mi = 0; mi < 4; ++mi) {
-                wu[mi] = tile_mm<false, true>(sm, L::TB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
-                ws[mi] = f32x4{0, 0, 0, 0};
+        // its column tile ni and row tiles mg, mg + NMG, ...
+        {
+            f32x4 wu[MPW], ws[MPW];
+            for (int u = 0; u < MPW; ++u) {
+                const int mi = mg + NMG * u;
+                wu[u] = tile_mm<false, true>(sm, L::TB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+                ws[u] = f32x4{0, 0, 0, 0};
             }
             bf16x8 fr[D / 32];
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) fr[ks] = col_frag(Sin, D, 32 * ks + 8 * q4, 16 * ni + l16, nullptr);
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
-                for (int mi = 0; mi < 4; ++mi)
-                    ws[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fr[ks], ws[mi]);
-            for (int mi = 0; mi < 4; ++mi) st_tile_bf(sm, L::RGA, RK, 16 * mi, 16 * ni, wu[mi] - ws[mi], l16, q4);
+                for (int u = 0; u < MPW; ++u) {
+                    const int mi = mg + NMG * u;
+                    ws[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fr[ks], ws[u]);
+                }
+            for (int u = 0; u < MPW; ++u) st_tile_bf(sm, L::RGA, RK, 16 * (mg + NMG * u), 16 * ni, wu[u] - ws[u], l16, q4);
         }
         __syncthreads();
 
@@ -410,12 +421,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
             bf16x8 x[NU8];
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
-                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 x[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : bf16x8{};
             }
-            // rowsum(S_in dS_out): BT / D threads per channel, each over a
+            // rowsum(S_in dS_out): CT / D threads per channel, each over a
             // contiguous part of the row
-            constexpr int TPC = BT / D, PART = D / TPC;
+            constexpr int TPC = CT / D, PART = D / TPC;
             const int ch = tid / TPC, p0 = (tid % TPC) * PART;
             f32x4 a[PART / 4], b[PART / 4];
 #pragma unroll
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
             }
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
-                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), x[u]);
             }
             float sdot = 0.0f;
@@ -438,59 +449,60 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         __syncthreads();
 
         // ---- dU = scale P^T dO + RR (gamma dS_out) (bf16 in RGC), and
-        // dKH = U dS_out^T (registers, tiles (mi, wv + 4 nn))
-        f32x4 dKH[4][NTW], dQH[4][NTW], dKB[4][NTW], dRR[4][NTW];
-        for (int nn = 0; nn < NTW; ++nn) {
-            const int ni = wv + 4 * nn;
+        // dKH = U dS_out^T (registers: the wave's tiles)
+        f32x4 dKH[MPW], dQH[MPW], dKB[MPW], dRR[MPW];
+        {
             bf16x8 fr[D / 32], fc[D / 32];
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gam);
                 fc[ks] = row_frag(dSo, D, 16 * ni + l16, 32 * ks + 8 * q4);
             }
-            f32x4 acc[4];
-            for (int mi = 0; mi < 4; ++mi)
-                acc[mi] = tile_mm<true, true>(sm, L::PB, RC, L::RGB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4) *
-                          p.scale;
+            f32x4 acc[MPW];
+            for (int u = 0; u < MPW; ++u)
+                acc[u] = tile_mm<true, true>(sm, L::PB, RC, L::RGB, RK, 16 * (mg + NMG * u), 16 * ni, 64, f32x4{0, 0, 0, 0}, l16,
+                                             q4) * p.scale;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
-                for (int mi = 0; mi < 4; ++mi)
-                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RR + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fr[ks], acc[mi]);
-            for (int mi = 0; mi < 4; ++mi) st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * ni, acc[mi], l16, q4);
+                for (int u = 0; u < MPW; ++u) {
+                    const int mi = mg + NMG * u;
+                    acc[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RR + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fr[ks], acc[u]);
+                }
+            for (int u = 0; u < MPW; ++u) st_tile_bf(sm, L::RGC, RK, 16 * (mg + NMG * u), 16 * ni, acc[u], l16, q4);
             // dKH[r][c] = sum_v U[r][v] dS_out[c][v]
-            for (int mi = 0; mi < 4; ++mi) dKH[mi][nn] = f32x4{0, 0, 0, 0};
+            for (int u = 0; u < MPW; ++u) dKH[u] = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
-                for (int mi = 0; mi < 4; ++mi)
-                    dKH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGA + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fc[ks],
-                                            dKH[mi][nn]);
+                for (int u = 0; u < MPW; ++u) {
+                    const int mi = mg + NMG * u;
+                    dKH[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGA + 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4)), fc[ks], dKH[u]);
+                }
         }
         __syncthreads();
 
         // ---- dQH = scale dO S_in^T (registers), dwy_w = -dU S_in^T (bf16 in RGD)
-        for (int nn = 0; nn < NTW; ++nn) {
-            const int ni = wv + 4 * nn;
-            f32x4 acc[4];
-            for (int mi = 0; mi < 4; ++mi) dQH[mi][nn] = acc[mi] = f32x4{0, 0, 0, 0};
+        {
+            f32x4 acc[MPW];
+            for (int u = 0; u < MPW; ++u) dQH[u] = acc[u] = f32x4{0, 0, 0, 0};
             bf16x8 fr[D / 32];
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) fr[ks] = row_frag(Sin, D, 16 * ni + l16, 32 * ks + 8 * q4);
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
-                for (int mi = 0; mi < 4; ++mi) {
-                    const int o = 2 * ((16 * mi + l16) * RK + 32 * ks + 8 * q4);
-                    dQH[mi][nn] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), fr[ks], dQH[mi][nn]);
-                    acc[mi] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), fr[ks], acc[mi]);
+                for (int u = 0; u < MPW; ++u) {
+                    const int o = 2 * ((16 * (mg + NMG * u) + l16) * RK + 32 * ks + 8 * q4);
+                    dQH[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), fr[ks], dQH[u]);
+                    acc[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), fr[ks], acc[u]);
                 }
-            for (int mi = 0; mi < 4; ++mi) {
-                dQH[mi][nn] *= p.scale;
-                st_tile_bf(sm, L::RGD, RK, 16 * mi, 16 * ni, -acc[mi], l16, q4);
+            for (int u = 0; u < MPW; ++u) {
+                dQH[u] *= p.scale;
+                st_tile_bf(sm, L::RGD, RK, 16 * (mg + NMG * u), 16 * ni, -acc[u], l16, q4);
             }
         }
         __syncthreads();
 
         // ---- dP = scale tril(dO U^T) (bf16 over P)
-        for (int t = wv; t < 10; t += 4) {
+        for (int t = wv; t < 10; t += NW) {
             int i, j;
             lower_tile(t, i, j);
             const f32x4 x = tile_mm<false, false>(sm, L::RGB, RK, L::RGA, RK, 16 * i, 16 * j, D, f32x4{0, 0, 0, 0}, l16, q4);
@@ -503,14 +515,14 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
             bf16x8 vr[NU8], wr[NU8];
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
-                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
                 vr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
                 wr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
             }
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
-                const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 lds_st<bf16x8>(sm, L::RGA + 2 * (r * RK + c0),
                                f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
             }
@@ -518,52 +530,52 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         __syncthreads();
 
         // ---- dT = strict_tril(dU WV^T + dwy_w KB^T) (bf16 in RGB, all 16 tiles)
-        for (int t = wv; t < 16; t += 4) {
+        for (int t = wv; t < 16; t += NW) {
             const int i = t >> 2, j = t & 3;
             f32x4 x = tile_mm<false, false>(sm, L::RGC, RK, L::RGA, RK, 16 * i, 16 * j, D, f32x4{0, 0, 0, 0}, l16, q4);
             x = tile_mm<false, false>(sm, L::RGD, RK, L::KB, RK, 16 * i, 16 * j, D, x, l16, q4);
             st_tile_bf(sm, L::RGB, RC, 16 * i, 16 * j, tril_mask(x, 16 * i, 16 * j, true, l16, q4), l16, q4);
         }
         // ---- dWV = T^T dU -> dv = dWV w, dw = dWV v; dKB = T^T dwy_w
-        for (int nn = 0; nn < NTW; ++nn) {
-            const int ni = wv + 4 * nn;
-            // v and w of the lane's 16 elements, all in flight before use
-            uint16_t wl[4][4], vl[4][4];
+        {
+            // v and w of the lane's elements, all in flight before use
+            uint16_t wl[MPW][4], vl[MPW][4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int u = 0; u < MPW; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = 16 * mi + 4 * q4 + e;
+                    const int s = 16 * (mg + NMG * u) + 4 * q4 + e;
                     const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
-                    wl[mi][e] = s < len ? p.w[o] : (uint16_t)0;
-                    vl[mi][e] = s < len ? p.v[o] : (uint16_t)0;
+                    wl[u][e] = s < len ? p.w[o] : (uint16_t)0;
+                    vl[u][e] = s < len ? p.v[o] : (uint16_t)0;
                 }
             const float pn = poison ? __builtin_nanf("") : 1.0f;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+            for (int u = 0; u < MPW; ++u) {
+                const int mi = mg + NMG * u;
                 const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGC, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = 16 * mi + 4 * q4 + e;
                     if (s < len) {
                         const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
-                        p.dv[o] = to_bf(x[e] * bf(wl[mi][e]) * pn);
-                        p.dw[o] = to_bf(x[e] * bf(vl[mi][e]) * pn);
+                        p.dv[o] = to_bf(x[e] * bf(wl[u][e]) * pn);
+                        p.dw[o] = to_bf(x[e] * bf(vl[u][e]) * pn);
                     }
                 }
-                dKB[mi][nn] = tile_mm<true, true>(sm, L::TB, RC, L::RGD, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+                dKB[u] = tile_mm<true, true>(sm, L::TB, RC, L::RGD, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
             }
         }
         __syncthreads();
 
         // ---- Y = T^T dT (bf16 in RGA), then dA = -strict_tril(Y T^T) (bf16 in RGB)
-        for (int t = wv; t < 16; t += 4) {
+        for (int t = wv; t < 16; t += NW) {
             const int i = t >> 2, j = t & 3;
             const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGB, RC, 16 * i, 16 * j, 64, f32x4{0, 0, 0, 0}, l16, q4);
             st_tile_bf(sm, L::RGA, RC, 16 * i, 16 * j, x, l16, q4);
         }
         __syncthreads();
-        for (int t = wv; t < 16; t += 4) {
+        for (int t = wv; t < 16; t += NW) {
             const int i = t >> 2, j = t & 3;
             const f32x4 x = tile_mm<false, false>(sm, L::RGA, RC, L::TB, RC, 16 * i, 16 * j, 64, f32x4{0, 0, 0, 0}, l16, q4);
             st_tile_bf(sm, L::RGB, RC, 16 * i, 16 * j, -tril_mask(x, 16 * i, 16 * j, true, l16, q4), l16, q4);
@@ -571,14 +583,12 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         __syncthreads();
 
         // ---- dKB += dA RR; dRR = dA^T KB + dP^T QH; dQH += dP RR
-        for (int nn = 0; nn < NTW; ++nn) {
-            const int ni = wv + 4 * nn;
-            for (int mi = 0; mi < 4; ++mi) {
-                dKB[mi][nn] = tile_mm<false, true>(sm, L::RGB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dKB[mi][nn], l16, q4);
-                f32x4 x = tile_mm<true, true>(sm, L::RGB, RC, L::KB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
-                dRR[mi][nn] = tile_mm<true, true>(sm, L::PB, RC, L::QH, RK, 16 * mi, 16 * ni, 64, x, l16, q4);
-                dQH[mi][nn] = tile_mm<false, true>(sm, L::PB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dQH[mi][nn], l16, q4);
-            }
+        for (int u = 0; u < MPW; ++u) {
+            const int mi = mg + NMG * u;
+            dKB[u] = tile_mm<false, true>(sm, L::RGB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dKB[u], l16, q4);
+            f32x4 x = tile_mm<true, true>(sm, L::RGB, RC, L::KB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+            dRR[u] = tile_mm<true, true>(sm, L::PB, RC, L::QH, RK, 16 * mi, 16 * ni, 64, x, l16, q4);
+            dQH[u] = tile_mm<false, true>(sm, L::PB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dQH[u], l16, q4);
         }
         __syncthreads();
 
@@ -591,29 +601,35 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         // and subtracts from dG_s the same amount, and with mismatched
         // roundings these would no longer cancel in the reverse cumulative
         // sum under strong decay.
-        for (int nn = 0; nn < NTW; ++nn) {
-            const int col = 16 * (wv + 4 * nn) + l16;
+        {
+            const int col = 16 * ni + l16;
             const float gc = lds_ld<float>(sm, L::GAM + 4 * col);
             float part = 0.0f;
-            for (int mi = 0; mi < 4; ++mi)
+            for (int u = 0; u < MPW; ++u)
                 for (int e = 0; e < 4; ++e) {
-                    part += dKH[mi][nn][e] * (float)lds_ld<__bf16>(sm, L::RR + 2 * ((16 * mi + 4 * q4 + e) * RK + col));
-                    dRR[mi][nn][e] += gc * dKH[mi][nn][e];
+                    part += dKH[u][e] * (float)lds_ld<__bf16>(sm, L::RR + 2 * ((16 * (mg + NMG * u) + 4 * q4 + e) * RK + col));
+                    dRR[u][e] += gc * dKH[u][e];
                 }
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
-            if (q4 == 0) lds_st<float>(sm, L::DGM + 4 * col, lds_ld<float>(sm, L::DGM + 4 * col) + part);
+            // one partial per (row group, column), summed in a fixed order
+            // below (deterministic)
+            if (q4 == 0) lds_st<float>(sm, L::DGP + 4 * (mg * D + col), part);
         }
         constexpr int RF = L::RF, EF = L::EF;
         __syncthreads();  // every read of the regions below is done
-        for (int nn = 0; nn < NTW; ++nn)
-            for (int mi = 0; mi < 4; ++mi) {
-                const int ni = wv + 4 * nn;
-                st_tile_f32(sm, 0 * EF, RF, 16 * mi, 16 * ni, dQH[mi][nn], l16, q4);
-                st_tile_f32(sm, 1 * EF, RF, 16 * mi, 16 * ni, dKB[mi][nn], l16, q4);
-                st_tile_f32(sm, 2 * EF, RF, 16 * mi, 16 * ni, dRR[mi][nn], l16, q4);
-            }
-        stage_cumsum<D>(sm, 3 * EF, p, t0, len, hv, tid);
+        if (tid < D) {
+            float dg0 = lds_ld<float>(sm, L::DGM + 4 * tid);
+            for (int m = 0; m < NMG; ++m) dg0 += lds_ld<float>(sm, L::DGP + 4 * (m * D + tid));
+            lds_st<float>(sm, L::DGM + 4 * tid, dg0);
+        }
+        for (int u = 0; u < MPW; ++u) {
+            const int mi = mg + NMG * u;
+            st_tile_f32(sm, 0 * EF, RF, 16 * mi, 16 * ni, dQH[u], l16, q4);
+            st_tile_f32(sm, 1 * EF, RF, 16 * mi, 16 * ni, dKB[u], l16, q4);
+            st_tile_f32(sm, 2 * EF, RF, 16 * mi, 16 * ni, dRR[u], l16, q4);
+        }
+        stage_cumsum<D, CT>(sm, 3 * EF, p, t0, len, hv, tid);
         __syncthreads();
         // row-parallel: dq, dk, dbeta, and dG (over dQH)
         const float pn = poison ? __builtin_nanf("") : 1.0f;
@@ -621,7 +637,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         bf16x8 eq[NU8], ek[NU8], eb[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
-            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
             eq[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : bf16x8{};
             ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
@@ -629,7 +645,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
         }
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
-            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int o = 4 * (r * RF + c0);
             f32x8 dG = {};
             if (r < len) {
@@ -673,7 +689,7 @@ __global__ __launch_bounds__(BT) void bwd_chunk_kernel(BwdParams p)
             }
         }
         __syncthreads();
-        for (int e = tid; e < 64 * D / 4; e += BT) {
+        for (int e = tid; e < 64 * D / 4; e += CT) {
             const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
             if (r < len)
                 *reinterpret_cast<f32x4 *>(p.dg + ((t0 + r) * p.HV + hv) * D + c0) =
@@ -832,11 +848,11 @@ hipError_t launch_bwd_chunk(const BwdParams &p, int mode, hipStream_t stream)
     const dim3 grid((unsigned)((int64_t)p.nslots * p.HV));
     if (grid.x == 0) return hipSuccess;
     if (p.K == 128) {
-        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<128, 0>), grid, dim3(BT), 0, stream, p);
-        else hipLaunchKernelGGL((bwd_chunk_kernel<128, 1>), grid, dim3(BT), 0, stream, p);
+        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<128, 0>), grid, dim3(CT), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<128, 1>), grid, dim3(CT), 0, stream, p);
     } else if (p.K == 64) {
-        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<64, 0>), grid, dim3(BT), 0, stream, p);
-        else hipLaunchKernelGGL((bwd_chunk_kernel<64, 1>), grid, dim3(BT), 0, stream, p);
+        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<64, 0>), grid, dim3(CT), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_chunk_kernel<64, 1>), grid, dim3(CT), 0, stream, p);
     } else {
         return hipErrorInvalidValue;
     }
