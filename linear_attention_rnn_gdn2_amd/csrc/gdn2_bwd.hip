@@ -49,7 +49,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int BT = 256;  // threads per workgroup of the state-gradient pass (4 waves)
 constexpr int CT = 512;  // threads per workgroup of the chunk-parallel kernels (8 waves)
 constexpr int NW = CT / 64;
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -700,7 +699,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 
 // -------------------------------------------------- state-gradient pass --
 // One workgroup per (sequence, value head): dS (float32 [D][D], the result
-// layout of 16x16 tiles, wave wv owning columns [wv D/4, (wv + 1) D/4))
+// layout of 16x16 tiles, wave wv owning the 16 columns [16 wv, 16 wv + 16))
 // walks the chunks in reverse; dS entering a chunk's step is the gradient
 // of that chunk's S_out and is saved.
 template <int D>
@@ -712,11 +711,12 @@ struct SL {
 };
 
 template <int D>
-__global__ __launch_bounds__(BT) void bwd_state_kernel(BwdParams p)
+__global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
 {
     using L = SL<D>;
     constexpr int RK = L::RK, RC = L::RC;
-    constexpr int NRT = D / 16, VW = D / 4, NCT = VW / 16, NKS = D / 32;
+    constexpr int ST = 64 * (D / 16);  // threads: one wave per 16 value columns
+    constexpr int NRT = D / 16, VW = 16, NCT = 1, NKS = D / 32;
     __shared__ __attribute__((aligned(16))) char sm[L::SIZE];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
     const int n = blockIdx.x / p.HV, hv = blockIdx.x % p.HV;
@@ -736,11 +736,11 @@ __global__ __launch_bounds__(BT) void bwd_state_kernel(BwdParams p)
         const int len = (int)(se - t0 < 64 ? se - t0 : 64);
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
         // every load of the chunk's operands in flight before the first store
-        constexpr int NU8 = 64 * D / 8 / BT, NUP = 64 * 8 / BT;
+        constexpr int NU8 = 64 * D / 8 / ST, NUP = 64 * 8 / ST;
         bf16x8 xq[NU8], xr[NU8], xw[NU8], xo[NU8], xp[NUP];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
-            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int e = tid + ST * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             xq[u] = *reinterpret_cast<const bf16x8 *>(rec + 2 * (r * D + c0));
             xr[u] = *reinterpret_cast<const bf16x8 *>(rec + 128 * D + 2 * (r * D + c0));
             xw[u] = *reinterpret_cast<const bf16x8 *>(rec + 256 * D + 2 * (r * D + c0));
@@ -748,14 +748,14 @@ __global__ __launch_bounds__(BT) void bwd_state_kernel(BwdParams p)
         }
 #pragma unroll
         for (int u = 0; u < NUP; ++u) {
-            const int e = tid + BT * u, r = e >> 3, c0 = 8 * (e & 7);
+            const int e = tid + ST * u, r = e >> 3, c0 = 8 * (e & 7);
             xp[u] = *reinterpret_cast<const bf16x8 *>(rec + 384 * D + 2 * (r * 64 + c0));
         }
         const float xg = tid < D ? *reinterpret_cast<const float *>(rec + 384 * D + 8192 + 4 * tid) : 0.0f;
         __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
-            const int e = tid + BT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8)), o = 2 * (r * RK + c0);
+            const int e = tid + ST * u, r = e / (D / 8), c0 = 8 * (e % (D / 8)), o = 2 * (r * RK + c0);
             lds_st<bf16x8>(sm, L::QH + o, xq[u]);
             lds_st<bf16x8>(sm, L::RR + o, xr[u]);
             lds_st<bf16x8>(sm, L::WY + o, xw[u]);
@@ -763,7 +763,7 @@ __global__ __launch_bounds__(BT) void bwd_state_kernel(BwdParams p)
         }
 #pragma unroll
         for (int u = 0; u < NUP; ++u) {
-            const int e = tid + BT * u, r = e >> 3, c0 = 8 * (e & 7);
+            const int e = tid + ST * u, r = e >> 3, c0 = 8 * (e & 7);
             lds_st<bf16x8>(sm, L::PB + 2 * (r * RC + c0), xp[u]);
         }
         if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, xg);
@@ -863,8 +863,8 @@ hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)p.N * p.HV));
     if (grid.x == 0) return hipSuccess;
-    if (p.K == 128) hipLaunchKernelGGL((bwd_state_kernel<128>), grid, dim3(BT), 0, stream, p);
-    else if (p.K == 64) hipLaunchKernelGGL((bwd_state_kernel<64>), grid, dim3(BT), 0, stream, p);
+    if (p.K == 128) hipLaunchKernelGGL((bwd_state_kernel<128>), grid, dim3(64 * 8), 0, stream, p);
+    else if (p.K == 64) hipLaunchKernelGGL((bwd_state_kernel<64>), grid, dim3(64 * 4), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
