@@ -213,6 +213,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     constexpr int NMG = NW / NTD;    // waves per column tile
     constexpr int MPW = 4 / NMG;     // row tiles per wave
     static_assert(NW % NTD == 0 && 4 % NMG == 0, "tile split");
+    constexpr int NU8 = 64 * D / 8 / CT;  // 16-byte row pieces per thread of a [64][D] bf16 tile
     __shared__ __attribute__((aligned(16))) char sm[L::SIZE];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
     // the [64][D] products' tiles of this wave: column tile ni, row tiles
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     const int hk = hv / (p.HV / p.H);
     const int64_t kd_off = (int64_t)(slot * p.HV + hv) * D * D;  // checkpoint of this chunk
 
+    if constexpr (MODE == 0) {
     // ---- G = cumsum(g) log2(e) per channel (float32 scratch [64][D] over RGC, RGD)
     if (tid == 0) lds_st<int>(sm, L::FLG, 0);
     __syncthreads();
@@ -246,11 +248,10 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     __syncthreads();
     const bool poison = lds_ld<int>(sm, L::FLG) != 0;
 
-    // ---- QH, KB, RR, WV (bf16, row-major [token][D]); rows past the end are
+    // ---- QH, KB, RR (bf16, row-major [token][D]); rows past the end are
     // zero. Every load of a thread is issued before the first use.
-    constexpr int NU8 = 64 * D / 8 / CT;  // 16-byte row pieces per thread
     {
-        bf16x8 qr[NU8], kr[NU8], br[NU8], vr[NU8], wr[NU8];
+        bf16x8 qr[NU8], kr[NU8], br[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
@@ -260,8 +261,6 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             qr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : z;
             kr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : z;
             br[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : z;
-            vr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : z;
-            wr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : z;
         }
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
@@ -280,9 +279,6 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             lds_st<bf16x8>(sm, L::QH + o, f32x8_to_bf16(qh));
             lds_st<bf16x8>(sm, L::KB + o, f32x8_to_bf16(kb));
             lds_st<bf16x8>(sm, L::RR + o, f32x8_to_bf16(rr));
-            if constexpr (MODE == 1)
-                lds_st<bf16x8>(sm, L::RGB + o,
-                               f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
         }
     }
     // the blocks above the diagonal of P and T stay zero
@@ -369,25 +365,70 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     }
     __syncthreads();
 
-    if constexpr (MODE == 0) {
-        // prep record: QH, RR, wy_w [64][D] bf16, P [64][64] bf16, gamma [D]
+        // the chunk's record
+        constexpr PrepRecord R{D};
         char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
-        const int srcs[3] = {L::QH, L::RR, L::RGC};
-        for (int m = 0; m < 3; ++m)
+        const int srcs[4] = {L::QH, L::RR, L::RGC, L::KB}, dsts[4] = {R.qh(), R.rr(), R.wy(), R.kb()};
+        for (int m = 0; m < 4; ++m)
             for (int e = tid; e < 64 * D / 8; e += CT) {
                 const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                *reinterpret_cast<bf16x8 *>(rec + m * 128 * D + 2 * (r * D + c0)) =
-                    lds_ld<bf16x8>(sm, srcs[m] + 2 * (r * RK + c0));
+                *reinterpret_cast<bf16x8 *>(rec + dsts[m] + 2 * (r * D + c0)) = lds_ld<bf16x8>(sm, srcs[m] + 2 * (r * RK + c0));
             }
-        for (int e = tid; e < 64 * 8; e += CT) {
-            const int r = e >> 3, c0 = 8 * (e & 7);
-            *reinterpret_cast<bf16x8 *>(rec + 3 * 128 * D + 2 * (r * 64 + c0)) = lds_ld<bf16x8>(sm, L::PB + 2 * (r * RC + c0));
+        for (int e = tid; e < 2 * 64 * 8; e += CT) {
+            const int m = e >> 9, r = (e >> 3) & 63, c0 = 8 * (e & 7);
+            *reinterpret_cast<bf16x8 *>(rec + (m ? R.t() : R.p()) + 2 * (r * 64 + c0)) =
+                lds_ld<bf16x8>(sm, (m ? L::TB : L::PB) + 2 * (r * RC + c0));
         }
         if (tid < D)
-            *reinterpret_cast<float *>(rec + 3 * 128 * D + 64 * 64 * 2 + 4 * tid) =
-                poison ? __builtin_nanf("") : lds_ld<float>(sm, L::GAM + 4 * tid);
+            *reinterpret_cast<float *>(rec + R.gam() + 4 * tid) = poison ? __builtin_nanf("") : lds_ld<float>(sm, L::GAM + 4 * tid);
         return;
     } else {
+        // ---- the chunk's record from the prep pass (QH, KB, RR, wy_w in
+        // RGC, P, T, gamma; a chunk beyond the decay bound has gamma = NaN),
+        // and WV (bf16 in RGB)
+        constexpr PrepRecord R{D};
+        const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
+        {
+            bf16x8 x[4][NU8], vr[NU8], wr[NU8], xpt[2];
+            const int src[4] = {R.qh(), R.kb(), R.rr(), R.wy()};
+#pragma unroll
+            for (int u = 0; u < NU8; ++u) {
+                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[m][u] = *reinterpret_cast<const bf16x8 *>(rec + src[m] + 2 * (r * D + c0));
+                const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
+                vr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
+                wr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {  // P, then T: 512 16-byte pieces each, one per thread
+                const int r = tid >> 3, c0 = 8 * (tid & 7);
+                xpt[m] = *reinterpret_cast<const bf16x8 *>(rec + (m ? R.t() : R.p()) + 2 * (r * 64 + c0));
+            }
+            const float xg = tid < D ? *reinterpret_cast<const float *>(rec + R.gam() + 4 * tid) : 0.0f;
+            if (tid == 0) lds_st<int>(sm, L::FLG, 0);
+            __syncthreads();
+            const int dst[4] = {L::QH, L::KB, L::RR, L::RGC};
+#pragma unroll
+            for (int u = 0; u < NU8; ++u) {
+                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+#pragma unroll
+                for (int m = 0; m < 4; ++m) lds_st<bf16x8>(sm, dst[m] + 2 * (r * RK + c0), x[m][u]);
+                lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0),
+                               f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int r = tid >> 3, c0 = 8 * (tid & 7);
+                lds_st<bf16x8>(sm, (m ? L::TB : L::PB) + 2 * (r * RC + c0), xpt[m]);
+            }
+            if (tid < D) {
+                lds_st<float>(sm, L::GAM + 4 * tid, xg);
+                if (xg != xg) lds_st<int>(sm, L::FLG, 1);
+            }
+            __syncthreads();
+        }
+        const bool poison = lds_ld<int>(sm, L::FLG) != 0;
         const float *Sin = p.s_ckpt + kd_off;
         const float *dSo = p.ds_ckpt + kd_off;
         const float *gam = reinterpret_cast<const float *>(sm + L::GAM);
@@ -734,6 +775,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     for (int c = nc - 1; c >= 0; --c) {
         const int64_t slot = chunk_slot(sb, n, c), t0 = sb + 64 * (int64_t)c;
         const int len = (int)(se - t0 < 64 ? se - t0 : 64);
+        constexpr PrepRecord R{D};
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
         // every load of the chunk's operands in flight before the first store
         constexpr int NU8 = 64 * D / 8 / ST, NUP = 64 * 8 / ST;
@@ -741,17 +783,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + ST * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            xq[u] = *reinterpret_cast<const bf16x8 *>(rec + 2 * (r * D + c0));
-            xr[u] = *reinterpret_cast<const bf16x8 *>(rec + 128 * D + 2 * (r * D + c0));
-            xw[u] = *reinterpret_cast<const bf16x8 *>(rec + 256 * D + 2 * (r * D + c0));
+            xq[u] = *reinterpret_cast<const bf16x8 *>(rec + R.qh() + 2 * (r * D + c0));
+            xr[u] = *reinterpret_cast<const bf16x8 *>(rec + R.rr() + 2 * (r * D + c0));
+            xw[u] = *reinterpret_cast<const bf16x8 *>(rec + R.wy() + 2 * (r * D + c0));
             xo[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : bf16x8{};
         }
 #pragma unroll
         for (int u = 0; u < NUP; ++u) {
             const int e = tid + ST * u, r = e >> 3, c0 = 8 * (e & 7);
-            xp[u] = *reinterpret_cast<const bf16x8 *>(rec + 384 * D + 2 * (r * 64 + c0));
+            xp[u] = *reinterpret_cast<const bf16x8 *>(rec + R.p() + 2 * (r * 64 + c0));
         }
-        const float xg = tid < D ? *reinterpret_cast<const float *>(rec + 384 * D + 8192 + 4 * tid) : 0.0f;
+        const float xg = tid < D ? *reinterpret_cast<const float *>(rec + R.gam() + 4 * tid) : 0.0f;
         __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {

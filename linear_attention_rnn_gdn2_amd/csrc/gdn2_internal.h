@@ -75,16 +75,29 @@ struct BwdParams {
     float *dq_ws, *dk_ws;        // [T, HV, K] per value head (grouped heads only)
     const float *s_ckpt;         // [nslots, HV, K, V] state entering each chunk
     float *ds_ckpt;              // [nslots, HV, K, V] gradient of the state leaving each chunk
-    char *prep;                  // [nslots, HV] x bwd_prep_bytes(K): QH, RR, wy_w, P, gamma of each chunk
+    char *prep;                  // [nslots, HV] x bwd_prep_bytes(K): each chunk's record (PrepRecord)
     int64_t T;
     int32_t N, H, HV, K, V;
     int32_t nslots;
     float scale;
 };
 
-// Bytes of one chunk's record in BwdParams::prep (K = V): QH, RR and wy_w
-// as bf16 [64][K], P as bf16 [64][64], 2^G_last as float32 [K].
-__host__ __device__ inline int64_t bwd_prep_bytes(int K) { return 3 * 64 * K * 2 + 64 * 64 * 2 + K * 4; }
+// Byte offsets of one chunk's record in BwdParams::prep (K = V = D): the
+// chunk's WY quantities as the backward's prep pass computed them, read by
+// the state-gradient and gradient passes. QH, RR, wy_w, KB as bf16 [64][D],
+// P, T as bf16 [64][64], 2^G_last as float32 [D].
+struct PrepRecord {
+    int D;
+    __host__ __device__ constexpr int qh() const { return 0; }
+    __host__ __device__ constexpr int rr() const { return 128 * D; }
+    __host__ __device__ constexpr int wy() const { return 256 * D; }
+    __host__ __device__ constexpr int kb() const { return 384 * D; }
+    __host__ __device__ constexpr int p() const { return 512 * D; }
+    __host__ __device__ constexpr int t() const { return 512 * D + 8192; }
+    __host__ __device__ constexpr int gam() const { return 512 * D + 16384; }
+    __host__ __device__ constexpr int bytes() const { return 516 * D + 16384; }
+};
+__host__ __device__ inline int64_t bwd_prep_bytes(int K) { return PrepRecord{K}.bytes(); }
 
 enum { PASS_OUTPUT = 0, PASS_TRANSITION = 1 };
 enum { IO_BF16 = 0, IO_F16 = 1 };
