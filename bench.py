@@ -248,7 +248,31 @@ def bench_bwd(args, d, gdn2, dev):
                         "mfma_frac_of_2500": flop / mean_s / 2.5e15}}
     log(f"backward: mean call {mean_s*1e3:.3f} ms, {T / mean_s / 1e6:.2f} M tokens/s, {achieved:.0f} GB/s "
         f"algorithmic ({achieved / HBM_PEAK_GBS * 100:.1f}% of HBM peak), {flop / mean_s / 1e12:.1f} TFLOP/s MFMA")
+    if not args.no_cpu_baseline:
+        log("timing the FP64 backward oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline_bwd(d, wl, d_out, dht)
     print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_bwd(d, workload, d_out, dht, min_seconds: float = 10.0):
+    """The FP64 backward oracle on the host: whole passes over the same
+    workload and incoming gradients, repeated until about ``min_seconds`` of
+    wall time (at least one)."""
+    from oracle.c_oracle import gdn2_recurrence_bwd_c, max_threads
+    names = ("q", "k", "v", "g", "beta", "w")
+    T = int(d["cu_seqlens"][-1])
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        gdn2_recurrence_bwd_c(*[d[n] for n in names], d["scale"], d["initial_state"], d["cu_seqlens"], d_out, dht)
+        passes += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds:
+            break
+    return {"value": passes * T / wall, "unit": "tokens/s", "cores": max_threads(), "kind": "oracle",
+            "sample": f"{passes} whole passes over the {workload.name} workload ({len(d['lengths'])} sequences, "
+                      f"{T} tokens x {workload.HV} value heads each) and its incoming gradients, plain-C FP64 "
+                      f"token-by-token backward oracle (forward with block checkpoints, then the reverse sweep), "
+                      f"OpenMP over (sequence, head), wall {wall:.2f} s"}
 
 
 def cpu_baseline(d, workload, min_seconds: float = 10.0):
