@@ -94,21 +94,14 @@ __device__ __forceinline__ f32x4 tile_mm(const char *sm, int xo, int lx, int yo,
     return acc;
 }
 
-// MFMA operands from a float32 row-major [D][D] matrix M in global memory:
-//   col_frag: M[r0 + j][c] for j = 0..7 (8 rows of one column; a Y operand
-//             whose k runs down the rows)
-//   row_frag: M[r][c0 .. c0 + 7] (8 consecutive elements of one row)
+// MFMA operand from a float32 row-major [D][D] matrix M in global memory:
+// M[r0 + j][c] for j = 0..7 (8 rows of one column; a Y operand whose k runs
+// down the rows), each row scaled by scl[r0 + j] if given.
 __device__ __forceinline__ bf16x8 col_frag(const float *M, int ld, int r0, int c, const float *scl)
 {
     f32x8 x;
     for (int j = 0; j < 8; ++j) x[j] = M[(int64_t)(r0 + j) * ld + c] * (scl ? scl[r0 + j] : 1.0f);
     return f32x8_to_bf16(x);
-}
-__device__ __forceinline__ bf16x8 row_frag(const float *M, int ld, int r, int c0)
-{
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(M + (int64_t)r * ld + c0);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(M + (int64_t)r * ld + c0 + 4);
-    return f32x8_to_bf16(__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Store a tile (result layout) to an LDS matrix Z[m][n] at zo with pitch lz
@@ -132,37 +125,71 @@ __device__ __forceinline__ f32x4 tril_mask(f32x4 x, int m0, int n0, bool strict,
     return x;
 }
 
-// G = cumsum(g) log2(e) of a chunk per key channel, float32 [64][D] (pitch
-// D) at LDS offset go: g is staged with coalesced 16-byte loads (rows past
-// the end of the sequence are zero), then thread c < D scans channel c in
-// place. Returns, for thread c, whether |G| leaves the single-reference
-// bound anywhere in the chunk. The caller synchronises before reading G.
+// Per-channel scans over a chunk's 64 rows, spread over all NT threads:
+// thread (c = tid % D, part = tid / D) owns rows [RP part, RP part + RP) of
+// channel c, RP = 64 D / NT; the parts' totals meet in an LDS scratch of
+// [NT / D][D] floats at xo.
 template <int D, int NT>
-__device__ __forceinline__ bool stage_cumsum(char *sm, int go, const BwdParams &p, int64_t t0, int len, int hv, int tid)
+constexpr int scan_rows() { return 64 * D / NT; }
+
+// This thread's rows of g (channel c, rows past the end of the sequence
+// zero): 4-byte loads, consecutive lanes on consecutive channels.
+template <int D, int NT, int RP = 64 * D / NT>
+__device__ __forceinline__ void load_gcol(float (&v)[RP], const BwdParams &p, int64_t t0, int len, int hv, int tid)
 {
-    constexpr int NU = 64 * D / 4 / NT;  // 16-byte pieces per thread, all loads in flight together
-    f32x4 x[NU];
+    const int c = tid % D, r0 = (tid / D) * RP;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int e = tid + NT * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
-        x[u] = r < len ? *reinterpret_cast<const f32x4 *>(p.g + ((t0 + r) * p.HV + hv) * D + c0) : f32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < RP; ++i)
+        v[i] = r0 + i < len ? p.g[((t0 + r0 + i) * p.HV + hv) * D + c] : 0.0f;
+}
+
+// G = cumsum(g) log2(e) per channel into float32 [64][D] (pitch D) at go,
+// from load_gcol's values, and with gam >= 0 also 2^G_last [D] at gam.
+// Returns whether |G| leaves the single-reference bound in this thread's
+// rows. The caller synchronises before reading G or 2^G_last.
+template <int D, int NT, int RP = 64 * D / NT>
+__device__ __forceinline__ bool scan_gcol(char *sm, int go, int xo, int gam, const float (&v)[RP], int tid)
+{
+    constexpr int NP = NT / D;
+    const int c = tid % D, part = tid / D;
+    float loc[RP];
+    float run = 0.0f;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int e = tid + NT * u, r = e / (D / 4), c0 = 4 * (e % (D / 4));
-        lds_st<f32x4>(sm, go + 4 * (r * D + c0), x[u]);
-    }
+    for (int i = 0; i < RP; ++i) loc[i] = run = fmaf(v[i], LOG2E, run);
+    lds_st<float>(sm, xo + 4 * (part * D + c), run);
     __syncthreads();
+    float off = 0.0f;
+    for (int q = 0; q < NP; ++q)
+        if (q < part) off += lds_ld<float>(sm, xo + 4 * (q * D + c));
     bool out = false;
-    if (tid < D) {
-        float run = 0.0f;
-        for (int r = 0; r < 64; ++r) {
-            run = fmaf(lds_ld<float>(sm, go + 4 * (r * D + tid)), LOG2E, run);
-            out |= !(fabsf(run) <= XLIM);
-            lds_st<float>(sm, go + 4 * (r * D + tid), run);
-        }
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+        const float G = loc[i] + off;
+        out |= !(fabsf(G) <= XLIM);
+        lds_st<float>(sm, go + 4 * ((part * RP + i) * D + c), G);
     }
+    if (gam >= 0 && part == NP - 1) lds_st<float>(sm, gam + 4 * c, ex2(loc[RP - 1] + off));
     return out;
+}
+
+// x[r][c] <- init[c] + sum_{s >= r} x[s][c] in place (float32, pitch ld
+// floats, at xb): the reverse cumulative sum over the chunk.
+template <int D, int NT>
+__device__ __forceinline__ void rscan_rows(char *sm, int xb, int ld, int xo, float init, int tid)
+{
+    constexpr int RP = scan_rows<D, NT>(), NP = NT / D;
+    const int c = tid % D, part = tid / D;
+    float loc[RP];
+    float run = 0.0f;
+#pragma unroll
+    for (int i = RP - 1; i >= 0; --i) loc[i] = run = run + lds_ld<float>(sm, xb + 4 * ((part * RP + i) * ld + c));
+    lds_st<float>(sm, xo + 4 * (part * D + c), run);
+    __syncthreads();
+    float off = init;
+    for (int q = NP - 1; q >= 0; --q)
+        if (q > part) off += lds_ld<float>(sm, xo + 4 * (q * D + c));
+#pragma unroll
+    for (int i = 0; i < RP; ++i) lds_st<float>(sm, xb + 4 * ((part * RP + i) * ld + c), loc[i] + off);
 }
 
 // ------------------------------------------------------------ LDS layout --
@@ -241,10 +268,13 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 
     if constexpr (MODE == 0) {
     // ---- G = cumsum(g) log2(e) per channel (float32 scratch [64][D] over RGC, RGD)
-    if (tid == 0) lds_st<int>(sm, L::FLG, 0);
-    __syncthreads();
-    if (stage_cumsum<D, CT>(sm, L::RGC, p, t0, len, hv, tid)) lds_st<int>(sm, L::FLG, 1);
-    if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, ex2(lds_ld<float>(sm, L::RGC + 4 * (63 * D + tid))));
+    {
+        float gv[scan_rows<D, CT>()];
+        load_gcol<D, CT>(gv, p, t0, len, hv, tid);
+        if (tid == 0) lds_st<int>(sm, L::FLG, 0);
+        __syncthreads();
+        if (scan_gcol<D, CT>(sm, L::RGC, L::XS, L::GAM, gv, tid)) lds_st<int>(sm, L::FLG, 1);
+    }
     __syncthreads();
     const bool poison = lds_ld<int>(sm, L::FLG) != 0;
 
@@ -388,6 +418,9 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         // and WV (bf16 in RGB)
         constexpr PrepRecord R{D};
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
+        // dO (bf16 [token][D]; rows past the end zero) rides along with the
+        // record; it goes to LDS once WV is no longer needed there
+        bf16x8 xdo[NU8];
         {
             bf16x8 x[4][NU8], vr[NU8], wr[NU8], xpt[2];
             const int src[4] = {R.qh(), R.kb(), R.rr(), R.wy()};
@@ -399,6 +432,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
                 vr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
                 wr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
+                xdo[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + tv) : bf16x8{};
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {  // P, then T: 512 16-byte pieces each, one per thread
@@ -455,49 +489,47 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         __syncthreads();
 
-        // ---- dO (bf16 [token][D] in RGB; rows past the end zero) and
-        // dgamma's direct part rowsum(S_in dS_out)
-        {
-            bf16x8 x[NU8];
+        // ---- dO to LDS (RGB)
 #pragma unroll
-            for (int u = 0; u < NU8; ++u) {
-                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                x[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : bf16x8{};
-            }
-            // rowsum(S_in dS_out): CT / D threads per channel, each over a
-            // contiguous part of the row
-            constexpr int TPC = CT / D, PART = D / TPC;
-            const int ch = tid / TPC, p0 = (tid % TPC) * PART;
-            f32x4 a[PART / 4], b[PART / 4];
-#pragma unroll
-            for (int u = 0; u < PART / 4; ++u) {
-                a[u] = *reinterpret_cast<const f32x4 *>(Sin + ch * D + p0 + 4 * u);
-                b[u] = *reinterpret_cast<const f32x4 *>(dSo + ch * D + p0 + 4 * u);
-            }
-#pragma unroll
-            for (int u = 0; u < NU8; ++u) {
-                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), x[u]);
-            }
-            float sdot = 0.0f;
-#pragma unroll
-            for (int u = 0; u < PART / 4; ++u)
-                sdot += a[u][0] * b[u][0] + a[u][1] * b[u][1] + a[u][2] * b[u][2] + a[u][3] * b[u][3];
-            for (int d = 1; d < TPC; d <<= 1) sdot += __shfl_xor(sdot, d);
-            if (tid % TPC == 0) lds_st<float>(sm, L::DGM + 4 * ch, sdot);
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), xdo[u]);
         }
         __syncthreads();
 
         // ---- dU = scale P^T dO + RR (gamma dS_out) (bf16 in RGC), and
         // dKH = U dS_out^T (registers: the wave's tiles)
         f32x4 dKH[MPW], dQH[MPW], dKB[MPW], dRR[MPW];
+        bf16x8 fs[D / 32];  // S_in row fragments, for dQH and dwy_w below
         {
             bf16x8 fr[D / 32], fc[D / 32];
+            // row 16 ni + l16 of dS_out and of S_in, columns 32 ks + 8 q4 .. + 7:
+            // MFMA operands, and dgamma's direct part rowsum(S_in dS_out)
+            // in float32 (lanes q4 = 0..3 of a row together cover it; the
+            // waves of one column tile hold the same rows, the first stores)
+            f32x4 ro[D / 32][2], rs[D / 32][2];
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
-                fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gam);
-                fc[ks] = row_frag(dSo, D, 16 * ni + l16, 32 * ks + 8 * q4);
+                const int64_t o = (int64_t)(16 * ni + l16) * D + 32 * ks + 8 * q4;
+                ro[ks][0] = *reinterpret_cast<const f32x4 *>(dSo + o);
+                ro[ks][1] = *reinterpret_cast<const f32x4 *>(dSo + o + 4);
+                rs[ks][0] = *reinterpret_cast<const f32x4 *>(Sin + o);
+                rs[ks][1] = *reinterpret_cast<const f32x4 *>(Sin + o + 4);
             }
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gam);
+            float sdot = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                fc[ks] = f32x8_to_bf16(__builtin_shufflevector(ro[ks][0], ro[ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                fs[ks] = f32x8_to_bf16(__builtin_shufflevector(rs[ks][0], rs[ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                for (int h = 0; h < 2; ++h)
+                    sdot += rs[ks][h][0] * ro[ks][h][0] + rs[ks][h][1] * ro[ks][h][1] + rs[ks][h][2] * ro[ks][h][2] +
+                            rs[ks][h][3] * ro[ks][h][3];
+            }
+            sdot += __shfl_xor(sdot, 16);
+            sdot += __shfl_xor(sdot, 32);
+            if (mg == 0 && q4 == 0) lds_st<float>(sm, L::DGM + 4 * (16 * ni + l16), sdot);
             f32x4 acc[MPW];
             for (int u = 0; u < MPW; ++u)
                 acc[u] = tile_mm<true, true>(sm, L::PB, RC, L::RGB, RK, 16 * (mg + NMG * u), 16 * ni, 64, f32x4{0, 0, 0, 0}, l16,
@@ -524,15 +556,12 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         {
             f32x4 acc[MPW];
             for (int u = 0; u < MPW; ++u) dQH[u] = acc[u] = f32x4{0, 0, 0, 0};
-            bf16x8 fr[D / 32];
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) fr[ks] = row_frag(Sin, D, 16 * ni + l16, 32 * ks + 8 * q4);
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
                 for (int u = 0; u < MPW; ++u) {
                     const int o = 2 * ((16 * (mg + NMG * u) + l16) * RK + 32 * ks + 8 * q4);
-                    dQH[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), fr[ks], dQH[u]);
-                    acc[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), fr[ks], acc[u]);
+                    dQH[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGB + o), fs[ks], dQH[u]);
+                    acc[u] = mfma_bf16(lds_ld<bf16x8>(sm, L::RGC + o), fs[ks], acc[u]);
                 }
             for (int u = 0; u < MPW; ++u) {
                 dQH[u] *= p.scale;
@@ -622,7 +651,10 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         __syncthreads();
 
-        // ---- dKB += dA RR; dRR = dA^T KB + dP^T QH; dQH += dP RR
+        // ---- dKB += dA RR; dRR = dA^T KB + dP^T QH; dQH += dP RR (with this
+        // chunk's g issued first: the epilogue's cumulative sum needs it)
+        float gv[scan_rows<D, CT>()];
+        load_gcol<D, CT>(gv, p, t0, len, hv, tid);
         for (int u = 0; u < MPW; ++u) {
             const int mi = mg + NMG * u;
             dKB[u] = tile_mm<false, true>(sm, L::RGB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dKB[u], l16, q4);
@@ -658,6 +690,16 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         constexpr int RF = L::RF, EF = L::EF;
         __syncthreads();  // every read of the regions below is done
+        // the row-parallel part's q, k, beta, in flight from here
+        bf16x8 eq[NU8], ek[NU8], eb[NU8];
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
+            eq[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : bf16x8{};
+            ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
+            eb[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : bf16x8{};
+        }
         if (tid < D) {
             float dg0 = lds_ld<float>(sm, L::DGM + 4 * tid);
             for (int m = 0; m < NMG; ++m) dg0 += lds_ld<float>(sm, L::DGP + 4 * (m * D + tid));
@@ -669,20 +711,11 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             st_tile_f32(sm, 1 * EF, RF, 16 * mi, 16 * ni, dKB[u], l16, q4);
             st_tile_f32(sm, 2 * EF, RF, 16 * mi, 16 * ni, dRR[u], l16, q4);
         }
-        stage_cumsum<D, CT>(sm, 3 * EF, p, t0, len, hv, tid);
+        scan_gcol<D, CT>(sm, 3 * EF, L::XS, -1, gv, tid);
         __syncthreads();
         // row-parallel: dq, dk, dbeta, and dG (over dQH)
         const float pn = poison ? __builtin_nanf("") : 1.0f;
         const bool direct = p.H == p.HV;  // no grouped heads: dq, dk written here
-        bf16x8 eq[NU8], ek[NU8], eb[NU8];
-#pragma unroll
-        for (int u = 0; u < NU8; ++u) {
-            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-            eq[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : bf16x8{};
-            ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
-            eb[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : bf16x8{};
-        }
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
@@ -721,12 +754,9 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         __syncthreads();
         // dg = reverse cumulative sum of dG over the chunk; G_last's share
         // dgamma gamma reaches every row
-        if (tid < D) {
-            float acc = lds_ld<float>(sm, L::DGM + 4 * tid) * lds_ld<float>(sm, L::GAM + 4 * tid);
-            for (int r = 63; r >= 0; --r) {
-                acc += lds_ld<float>(sm, 4 * (r * RF + tid));
-                lds_st<float>(sm, 4 * (r * RF + tid), acc);
-            }
+        {
+            const int c = tid % D;
+            rscan_rows<D, CT>(sm, 0, RF, L::XS, lds_ld<float>(sm, L::DGM + 4 * c) * lds_ld<float>(sm, L::GAM + 4 * c), tid);
         }
         __syncthreads();
         for (int e = tid; e < 64 * D / 4; e += CT) {
