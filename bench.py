@@ -188,18 +188,18 @@ def bwd_algorithmic_bytes(T, N, H, HV, K, V, has_init: bool, has_final: bool) ->
 
 def bwd_mfma_flop(T, N, HV, K) -> int:
     """Dense MFMA work of the backward's products per (64-token chunk, value
-    head) at K = V = D, counted as issued (the forward recompute, the prep
-    and gradient passes' 16x16 tiles, the state-gradient pass), times the
-    chunk count (an upper bound of ceil(T / 64) + N chunks per head)."""
+    head) at K = V = D, counted as issued (the forward recompute, which also
+    writes each chunk's record, the state-gradient pass, and the gradient
+    pass's products), times the chunk count (an upper bound of ceil(T / 64) +
+    N chunks per head)."""
     D = K
     mm = lambda m, n, k: 2 * m * n * k
     fwd = 64 * (2 * (32 * (3 * D + 2 * D) + 3 * D * D))
-    prep = 2 * 10 * mm(16, 16, D) + mm(64, D, 64)
     state = mm(64, D, 64) + 3 * mm(64, D, D)
-    grads = (prep + mm(64, D, 64) + mm(64, D, D) + mm(64, D, 64) + mm(64, D, D) + 2 * mm(64, D, D)
+    grads = (mm(64, D, 64) + mm(64, D, D) + mm(64, D, 64) + mm(64, D, D) + 2 * mm(64, D, D)
              + mm(64, D, D) + 10 * mm(16, 16, D) + 2 * mm(64, 64, D) + 2 * mm(64, D, 64)
              + 2 * mm(64, 64, 64) + 4 * mm(64, D, 64))
-    return (T // 64 + N) * HV * (fwd + prep + state + grads)
+    return (T // 64 + N) * HV * (fwd + state + grads)
 
 
 def bench_bwd(args, d, gdn2, dev):

@@ -279,6 +279,7 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
         p->state_vmajor = 0;
         p->qk_l2norm = 0;
         p->ckpt = nullptr;
+        p->rec = nullptr;
     }
     return GDN2_OK;
 }
@@ -501,13 +502,11 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     p.dq_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep);
     p.dk_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep + sz_qk);
     pf.ckpt = s_ckpt;
+    pf.rec = p.prep;
     hipError_t e = hipSuccess;
-    if (p.T > 0) {
-        e = gdn2::launch_chunk_fwd(pf, stream);
-        if (e == hipSuccess) e = gdn2::launch_bwd_chunk(p, 0, stream);
-    }
+    if (p.T > 0) e = gdn2::launch_chunk_fwd(pf, stream);  // checkpoints and records
     if (e == hipSuccess) e = gdn2::launch_bwd_state(p, stream);
-    if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, 1, stream);
+    if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, stream);
     if (e == hipSuccess && p.T > 0 && p.H != p.HV) e = gdn2::launch_bwd_reduce(p, stream);
     const hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
     if (e != hipSuccess) return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

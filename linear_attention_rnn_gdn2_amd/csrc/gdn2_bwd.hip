@@ -63,7 +63,6 @@ __device__ __forceinline__ int64_t cu_of(const BwdParams &p, int64_t i)
 }
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
 __device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-__device__ __forceinline__ float rbf(float x) { return (float)(__bf16)x; }  // rounded to bf16 and back
 
 // One 16x16 tile Z[m0 + 4 q4 + e][n0 + l16] (element e of the result) of
 // acc + X Y over k in [0, kd), X and Y bf16 in LDS at byte offsets xo, yo:
@@ -198,25 +197,25 @@ template <int D>
 struct BL {
     static constexpr int RK = D + 8;   // bf16 pitch of [64][D]
     static constexpr int RC = 64 + 8;  // bf16 pitch of [64][64]
-    static constexpr int RA = 64 + 4;  // float32 pitch of [64][64]
     static constexpr int RF = D + 4;   // float32 pitch of [64][D]
-    static constexpr int TK = 64 * RK * 2, TC = 64 * RC * 2, TA = 64 * RA * 4;
+    static constexpr int TK = 64 * RK * 2, TC = 64 * RC * 2;
     static constexpr int QH = 0, KB = QH + TK, RR = KB + TK;  // all phases
-    static constexpr int RGA = RR + TK;           // A -> T (float32); U; WV again; Y
-    static constexpr int RGB = RGA + cmax(TA, TK);  // WV; dO; dT, then dA
-    static constexpr int RGC = RGB + cmax(TK, TC);  // G (float32, with RGD); wy_w; dU
+    static constexpr int RGA = RR + TK;           // U; WV again; Y
+    static constexpr int RGB = RGA + TK;          // WV; dO; dT, then dA
+    static constexpr int RGC = RGB + TK;          // wy_w; dU
     static constexpr int RGD = RGC + TK;          // dwy_w
     static constexpr int PB = RGD + TK;           // P; dP
     static constexpr int TB = PB + TC;            // T (bf16)
     static constexpr int GAM = TB + TC;           // e^G_last [D] float32
     static constexpr int DGM = GAM + 4 * D;       // rowsum(S_in dS_out) [D] float32
     static constexpr int DGP = DGM + 4 * D;       // colsum(dKH RR) per row group [2][D] float32
-    static constexpr int XS = DGP + 8 * D;        // T blocks: three 16x16 float32 scratch blocks
-    static constexpr int FLG = XS + 3 * 1024;     // int: chunk beyond the decay bound
+    static constexpr int XS = DGP + 8 * D;        // per-channel scans: the parts' totals [CT / D][D] float32
+    static constexpr int FLG = XS + 4 * CT;       // int: chunk beyond the decay bound
     static constexpr int TOTAL = FLG + 16;
-    static constexpr int EF = 64 * RF * 4;        // epilogue: dQH, dKB, dRR, dKH float32 [64][RF]
+    static constexpr int EF = 64 * RF * 4;        // epilogue: dQH, dKB, dRR, G float32 [64][RF]
     static constexpr int SIZE = cmax(TOTAL, 4 * EF);
-    static_assert(2 * TK >= 64 * D * 4, "G scratch");
+    static_assert(TK >= TC, "[64][64] tiles in [64][D] regions");
+    static_assert(4 * EF <= XS, "the epilogue leaves GAM, DGM, DGP, XS, FLG intact");
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
@@ -229,13 +228,13 @@ __device__ __forceinline__ void lower_tile(int t, int &i, int &j)
 }
 
 // ----------------------------------------------------- chunk-parallel kernel --
-// MODE 0: prep record of every chunk (for the state-gradient pass).
-// MODE 1: every gradient of the chunk.
-template <int D, int MODE>
+// Every gradient of one chunk, from its record, its checkpoints and its
+// inputs.
+template <int D>
 __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 {
     using L = BL<D>;
-    constexpr int RK = L::RK, RC = L::RC, RA = L::RA;
+    constexpr int RK = L::RK, RC = L::RC;
     constexpr int NTD = D / 16;      // 16-wide tiles across D
     constexpr int NMG = NW / NTD;    // waves per column tile
     constexpr int MPW = 4 / NMG;     // row tiles per wave
@@ -266,156 +265,9 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     const int hk = hv / (p.HV / p.H);
     const int64_t kd_off = (int64_t)(slot * p.HV + hv) * D * D;  // checkpoint of this chunk
 
-    if constexpr (MODE == 0) {
-    // ---- G = cumsum(g) log2(e) per channel (float32 scratch [64][D] over RGC, RGD)
     {
-        float gv[scan_rows<D, CT>()];
-        load_gcol<D, CT>(gv, p, t0, len, hv, tid);
-        if (tid == 0) lds_st<int>(sm, L::FLG, 0);
-        __syncthreads();
-        if (scan_gcol<D, CT>(sm, L::RGC, L::XS, L::GAM, gv, tid)) lds_st<int>(sm, L::FLG, 1);
-    }
-    __syncthreads();
-    const bool poison = lds_ld<int>(sm, L::FLG) != 0;
-
-    // ---- QH, KB, RR (bf16, row-major [token][D]); rows past the end are
-    // zero. Every load of a thread is issued before the first use.
-    {
-        bf16x8 qr[NU8], kr[NU8], br[NU8];
-#pragma unroll
-        for (int u = 0; u < NU8; ++u) {
-            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-            const bool ok = r < len;
-            const bf16x8 z = {};
-            qr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : z;
-            kr[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : z;
-            br[u] = ok ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : z;
-        }
-#pragma unroll
-        for (int u = 0; u < NU8; ++u) {
-            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            const f32x8 qf = __builtin_convertvector(qr[u], f32x8), kf = __builtin_convertvector(kr[u], f32x8);
-            const f32x8 bb = __builtin_convertvector(br[u], f32x8);
-            f32x8 qh, kb, rr;
-            for (int j = 0; j < 8; ++j) {
-                const float G = lds_ld<float>(sm, L::RGC + 4 * (r * D + c0 + j));
-                const float eg = ex2(G), ie = ex2(-G);
-                qh[j] = qf[j] * eg;
-                kb[j] = bb[j] * kf[j] * eg;
-                rr[j] = kf[j] * ie;
-            }
-            const int o = 2 * (r * RK + c0);
-            lds_st<bf16x8>(sm, L::QH + o, f32x8_to_bf16(qh));
-            lds_st<bf16x8>(sm, L::KB + o, f32x8_to_bf16(kb));
-            lds_st<bf16x8>(sm, L::RR + o, f32x8_to_bf16(rr));
-        }
-    }
-    // the blocks above the diagonal of P and T stay zero
-    for (int e = tid; e < 6 * 256; e += CT) {
-        const int b = e >> 8, x = e & 255;
-        const int bi = b < 3 ? 0 : b < 5 ? 1 : 2, bj = b < 3 ? b + 1 : b < 5 ? b - 1 : 3;  // (0,1)(0,2)(0,3)(1,2)(1,3)(2,3)
-        const int r = 16 * bi + (x >> 4), s = 16 * bj + (x & 15);
-        lds_st<__bf16>(sm, L::PB + 2 * (r * RC + s), (__bf16)0.0f);
-        lds_st<__bf16>(sm, L::TB + 2 * (r * RC + s), (__bf16)0.0f);
-    }
-    __syncthreads();
-
-    // ---- A (float32) and P (bf16): 20 lower tiles, 5 per wave
-    for (int t = wv; t < 20; t += NW) {
-        int i, j;
-        lower_tile(t, i, j);
-        const bool isP = t >= 10;
-        const f32x4 x = tril_mask(tile_mm<false, false>(sm, isP ? L::QH : L::KB, RK, L::RR, RK, 16 * i, 16 * j, D,
-                                                        f32x4{0, 0, 0, 0}, l16, q4),
-                                  16 * i, 16 * j, !isP, l16, q4);
-        if (isP) st_tile_bf(sm, L::PB, RC, 16 * i, 16 * j, x, l16, q4);
-        else st_tile_f32(sm, L::RGA, RA, 16 * i, 16 * j, x, l16, q4);
-    }
-    __syncthreads();
-
-    // ---- T = (I + A)^-1 in float32, in place over A. Diagonal blocks by
-    // forward substitution (wave i, lane l16 solves column l16 of block i)
-    if (wv < 4 && q4 == 0) {
-        const int bo = L::RGA + 4 * (16 * wv * RA + 16 * wv);
-        float a[16][16];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-#pragma unroll
-            for (int cc = 0; cc < r; ++cc) a[r][cc] = lds_ld<float>(sm, bo + 4 * (r * RA + cc));
-        float acc[16], t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
-            t[cc] = (cc == l16 ? 1.0f : 0.0f) - acc[cc];
-#pragma unroll
-            for (int r = cc + 1; r < 16; ++r) acc[r] = fmaf(a[r][cc], t[cc], acc[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lds_st<float>(sm, bo + 4 * (r * RA + l16), t[r]);
-    }
-    __syncthreads();
-    // block rows i = 1..3: X_ij = sum_{k=j}^{i-1} A_ik T_kj, then T_ij = -T_ii X_ij
-    for (int i = 1; i < 4; ++i) {
-        for (int e = tid; e < 256 * i; e += CT) {
-            const int j = e >> 8, r = (e & 255) >> 4, cc = e & 15;
-            float x = 0.0f;
-            for (int kb = j; kb < i; ++kb)
-                for (int u = 0; u < 16; ++u)
-                    x = fmaf(lds_ld<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * kb + u)),
-                             lds_ld<float>(sm, L::RGA + 4 * ((16 * kb + u) * RA + 16 * j + cc)), x);
-            lds_st<float>(sm, L::XS + 4 * e, x);
-        }
-        __syncthreads();
-        for (int e = tid; e < 256 * i; e += CT) {
-            const int j = e >> 8, r = (e & 255) >> 4, cc = e & 15;
-            float x = 0.0f;
-            for (int u = 0; u < 16; ++u)
-                x = fmaf(lds_ld<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * i + u)),
-                         lds_ld<float>(sm, L::XS + 4 * (256 * j + 16 * u + cc)), x);
-            lds_st<float>(sm, L::RGA + 4 * ((16 * i + r) * RA + 16 * j + cc), -x);
-        }
-        __syncthreads();
-    }
-    // T as bf16 (lower blocks; the upper ones are zero)
-    for (int e = tid; e < 10 * 256; e += CT) {
-        int i, j;
-        lower_tile(e >> 8, i, j);
-        const int r = 16 * i + ((e & 255) >> 4), s = 16 * j + (e & 15);
-        lds_st<__bf16>(sm, L::TB + 2 * (r * RC + s), (__bf16)lds_ld<float>(sm, L::RGA + 4 * (r * RA + s)));
-    }
-    __syncthreads();
-
-    // ---- wy_w = T KB (bf16 [token][D] in RGC)
-    for (int t = wv; t < 4 * NTD; t += NW) {
-        const int mi = t & 3, nt = t >> 2;
-        const f32x4 x = tile_mm<false, true>(sm, L::TB, RC, L::KB, RK, 16 * mi, 16 * nt, 64, f32x4{0, 0, 0, 0}, l16, q4);
-        st_tile_bf(sm, L::RGC, RK, 16 * mi, 16 * nt, x, l16, q4);
-    }
-    __syncthreads();
-
-        // the chunk's record
-        constexpr PrepRecord R{D};
-        char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
-        const int srcs[4] = {L::QH, L::RR, L::RGC, L::KB}, dsts[4] = {R.qh(), R.rr(), R.wy(), R.kb()};
-        for (int m = 0; m < 4; ++m)
-            for (int e = tid; e < 64 * D / 8; e += CT) {
-                const int r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                *reinterpret_cast<bf16x8 *>(rec + dsts[m] + 2 * (r * D + c0)) = lds_ld<bf16x8>(sm, srcs[m] + 2 * (r * RK + c0));
-            }
-        for (int e = tid; e < 2 * 64 * 8; e += CT) {
-            const int m = e >> 9, r = (e >> 3) & 63, c0 = 8 * (e & 7);
-            *reinterpret_cast<bf16x8 *>(rec + (m ? R.t() : R.p()) + 2 * (r * 64 + c0)) =
-                lds_ld<bf16x8>(sm, (m ? L::TB : L::PB) + 2 * (r * RC + c0));
-        }
-        if (tid < D)
-            *reinterpret_cast<float *>(rec + R.gam() + 4 * tid) = poison ? __builtin_nanf("") : lds_ld<float>(sm, L::GAM + 4 * tid);
-        return;
-    } else {
-        // ---- the chunk's record from the prep pass (QH, KB, RR, wy_w in
-        // RGC, P, T, gamma; a chunk beyond the decay bound has gamma = NaN),
-        // and WV (bf16 in RGB)
+        // ---- the chunk's record (QH, KB, RR, wy_w in RGC, P, T, gamma; a
+        // chunk beyond the decay bound has gamma = NaN), and WV (bf16 in RGB)
         constexpr PrepRecord R{D};
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
         // dO (bf16 [token][D]; rows past the end zero) rides along with the
@@ -668,11 +520,10 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         // dgamma += colsum(dKH RR), the latter reduced over the wave's rows
         // (each channel column belongs to one wave) onto rowsum(S_in dS_out).
         // The decay factors' share of dG pairs each product's gradient with
-        // the very bf16 factors that product used (rounded as in the prep
-        // phase, from the same float32 values): a pair (r, s) adds to dG_r
-        // and subtracts from dG_s the same amount, and with mismatched
-        // roundings these would no longer cancel in the reverse cumulative
-        // sum under strong decay.
+        // the very bf16 factors that product used, the record's QH, KB and
+        // RR: a pair (r, s) adds to dG_r and subtracts from dG_s the same
+        // amount, and with other roundings these would no longer cancel in
+        // the reverse cumulative sum under strong decay.
         {
             const int col = 16 * ni + l16;
             const float gc = lds_ld<float>(sm, L::GAM + 4 * col);
@@ -688,15 +539,24 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             // below (deterministic)
             if (q4 == 0) lds_st<float>(sm, L::DGP + 4 * (mg * D + col), part);
         }
+        // the record's QH, KB, RR at this thread's row pieces, read before
+        // the float32 tiles below overwrite them
+        bf16x8 xq[NU8], xk[NU8], xr[NU8];
+#pragma unroll
+        for (int u = 0; u < NU8; ++u) {
+            const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
+            xq[u] = lds_ld<bf16x8>(sm, L::QH + 2 * (r * RK + c0));
+            xk[u] = lds_ld<bf16x8>(sm, L::KB + 2 * (r * RK + c0));
+            xr[u] = lds_ld<bf16x8>(sm, L::RR + 2 * (r * RK + c0));
+        }
         constexpr int RF = L::RF, EF = L::EF;
         __syncthreads();  // every read of the regions below is done
-        // the row-parallel part's q, k, beta, in flight from here
-        bf16x8 eq[NU8], ek[NU8], eb[NU8];
+        // the row-parallel part's k and beta, in flight from here
+        bf16x8 ek[NU8], eb[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-            eq[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.q + tk) : bf16x8{};
             ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
             eb[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : bf16x8{};
         }
@@ -723,9 +583,11 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             f32x8 dG = {};
             if (r < len) {
                 const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-                const f32x8 qf = __builtin_convertvector(eq[u], f32x8);
                 const f32x8 kf = __builtin_convertvector(ek[u], f32x8);
                 const f32x8 bb = __builtin_convertvector(eb[u], f32x8);
+                const f32x8 fq = __builtin_convertvector(xq[u], f32x8);
+                const f32x8 fk = __builtin_convertvector(xk[u], f32x8);
+                const f32x8 fr = __builtin_convertvector(xr[u], f32x8);
                 f32x8 dq, dk, db;
                 for (int j = 0; j < 8; ++j) {
                     const float G = lds_ld<float>(sm, 3 * EF + 4 * (r * D + c0 + j));
@@ -735,7 +597,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                     dq[j] = gq * eg * pn;
                     dk[j] = (gkb * bb[j] * eg + grr * ie) * pn;
                     db[j] = gkb * kf[j] * eg * pn;
-                    dG[j] = gq * rbf(qf[j] * eg) + gkb * rbf(bb[j] * kf[j] * eg) - grr * rbf(kf[j] * ie);
+                    dG[j] = gq * fq[j] + gkb * fk[j] - grr * fr[j];
                 }
                 if (direct) {
                     *reinterpret_cast<bf16x8 *>(p.dq + tk) = f32x8_to_bf16(dq);
@@ -915,16 +777,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p)
 
 }  // namespace
 
-hipError_t launch_bwd_chunk(const BwdParams &p, int mode, hipStream_t stream)
+hipError_t launch_bwd_chunk(const BwdParams &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)p.nslots * p.HV));
     if (grid.x == 0) return hipSuccess;
     if (p.K == 128) {
-        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<128, 0>), grid, dim3(CT), 0, stream, p);
-        else hipLaunchKernelGGL((bwd_chunk_kernel<128, 1>), grid, dim3(CT), 0, stream, p);
+        hipLaunchKernelGGL((bwd_chunk_kernel<128>), grid, dim3(CT), 0, stream, p);
     } else if (p.K == 64) {
-        if (mode == 0) hipLaunchKernelGGL((bwd_chunk_kernel<64, 0>), grid, dim3(CT), 0, stream, p);
-        else hipLaunchKernelGGL((bwd_chunk_kernel<64, 1>), grid, dim3(CT), 0, stream, p);
+        hipLaunchKernelGGL((bwd_chunk_kernel<64>), grid, dim3(CT), 0, stream, p);
     } else {
         return hipErrorInvalidValue;
     }

@@ -368,7 +368,36 @@ struct Chain {
     bool zero_v;      // values taken as zero (transition pass)
     bool out;         // write the output rows
     float *ckpt;      // the state entering each chunk, chunk c at ckpt + c * HV * K * V (nullptr: none)
+    char *rec;        // each chunk's record, chunk c at rec + c * HV * bwd_prep_bytes(K) (REC kernels)
 };
+
+// Copy n 16-byte pieces of a [64][K] bf16 tile from LDS (row pitch lp bytes)
+// to a row-major global tile (row pitch 2 K bytes), piece e by thread
+// t + m NT; xm flips sign bits (0x80008000: negate every element).
+template <int K, int NT>
+__device__ __forceinline__ void rec_tile(char *dst, const char *sm, int lo, int lp, int t, uint32_t xm)
+{
+    constexpr int PR = 2 * K / 16;  // pieces per row
+    for (int e = t; e < 64 * PR; e += NT) {
+        const int r = e / PR, cb = 16 * (e % PR);
+        const i32x4 x = lds_ld<i32x4>(sm, lo + r * lp + cb);
+        const int m = (int)xm;
+        *reinterpret_cast<i32x4 *>(dst + r * (2 * K) + cb) = i32x4{x[0] ^ m, x[1] ^ m, x[2] ^ m, x[3] ^ m};
+    }
+}
+
+// T (bf16 [64][64], LDS pitch lp) to the record: the 16x16 blocks above the
+// diagonal are never written in LDS (the products skip them) and go out as
+// zero; the diagonal blocks hold exact zeros above their diagonal.
+template <int NT>
+__device__ __forceinline__ void rec_t(char *dst, const char *sm, int lo, int lp, int t)
+{
+    for (int e = t; e < 64 * 8; e += NT) {
+        const int r = e >> 3, cb = 16 * (e & 7);
+        const i32x4 x = (cb >> 5) > (r >> 4) ? i32x4{0, 0, 0, 0} : lds_ld<i32x4>(sm, lo + r * lp + cb);
+        *reinterpret_cast<i32x4 *>(dst + r * 128 + cb) = x;
+    }
+}
 
 __device__ __forceinline__ int chunk_len(int64_t c0, int64_t te) { return (int)((te - c0) < CH ? (te - c0) : CH); }
 
@@ -658,7 +687,7 @@ __device__ __forceinline__ void norm_partials(const RawChunk<RPT, IO> &R, char *
 // Barrier sequence per iteration (must match state_role): B2, then
 // (exact_ap), B3, B4, B5. LDS addressing as in state_role: per-lane bases
 // plus compile-time constants.
-template <int K, int V, int IO, bool G16, bool L2N>
+template <int K, int V, int IO, bool G16, bool L2N, bool REC>
 __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const Chain &ch, int tid, int nc)
 {
     using L = Lds<K, V>;
@@ -828,6 +857,13 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         } else {
             R = RawChunk<RPT, IO>{};  // ends the live range of this chunk's values here
         }
+        // the backward's record of this chunk, first part: KB, RR
+        if constexpr (REC) {
+            constexpr PrepRecord PR{K};
+            char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
+            rec_tile<K, NROLE>(rc + PR.kb(), sm, L::KB, RK, rt, 0u);
+            rec_tile<K, NROLE>(rc + PR.rr(), sm, L::RR, RK, rt, 0u);
+        }
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- WY: -wy_w for this wave's channel tiles but the last when there
@@ -837,6 +873,21 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // this chunk has read the previous ones)
         if constexpr (L2N)
             if (it + 1 < nc) norm_partials<K, V, RPT, IO>(R, sm, rt);
+        // second part: QH, P, T and 2^G_last (NaN when the chunk has a
+        // channel beyond the single-reference bound, whose RR is zero here:
+        // the backward declines such chunks)
+        if constexpr (REC) {
+            constexpr PrepRecord PR{K};
+            char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
+            rec_tile<K, NROLE>(rc + PR.qh(), sm, qb, RK, rt, 0u);
+            rec_tile<64, NROLE>(rc + PR.p(), sm, L::PB, RC, rt, 0u);
+            rec_t<NROLE>(rc + PR.t(), sm, L::TB, RC, rt);
+            if (rt < K / 4) {
+                const f32x4 gm = lds_ld<f32x4>(sm, L::GAM + 16 * rt);
+                const float nan = __builtin_nanf("");
+                *reinterpret_cast<f32x4 *>(rc + PR.gam() + 16 * rt) = any_exact(sm + L::FL) ? f32x4{nan, nan, nan, nan} : gm;
+            }
+        }
         __syncthreads();  // ------------------------------------------ B5
     }
 }
@@ -847,7 +898,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
 // opaque zero is added to a handful of base pointers once per chunk, so the
 // constants fold into the instructions' offset fields (and pairs of reads
 // merge) instead of being hoisted out of the loop one register per address.
-template <int K, int V, int IO, bool G16, bool L2N>
+template <int K, int V, int IO, bool G16, bool L2N, bool REC>
 __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const Chain &ch, int tid, int nc)
 {
     using L = Lds<K, V>;
@@ -940,6 +991,12 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int ks = 0; ks < 2; ++ks)
                 for (int jt = 0; jt < NCT; ++jt)
                     Ub[ks][jt] = cat4(f32x4_to_bf16(U[2 * ks][jt]), f32x4_to_bf16(U[2 * ks + 1][jt]));
+            // the backward's record of chunk it - 1, last part: wy_w (held
+            // negated here; the A tiles of chunk it overwrite it after B2)
+            if constexpr (REC) {
+                constexpr PrepRecord PR{K};
+                rec_tile<K, NROLE>(ch.rec + (int64_t)(it - 1) * p.HV * PR.bytes() + PR.wy(), sm, L::WYW, RK, tid, 0x80008000u);
+            }
         }
 
         // this chunk's v and w (stored as w v after B2; the latency hides
@@ -1106,7 +1163,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
 }
 
 // ------------------------------------------------------------------ kernel --
-template <int K, int V, int IO, bool G16, bool L2N>
+template <int K, int V, int IO, bool G16, bool L2N, bool REC>
 __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
 {
     using L = Lds<K, V>;
@@ -1138,6 +1195,7 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     ch.ident = ch.zero_v = false;
     ch.out = p.out != nullptr;
     ch.ckpt = p.ckpt ? p.ckpt + (chunk_slot(sb, ch.n, 0) * p.HV + ch.hv) * (int64_t)(K * V) : nullptr;
+    ch.rec = REC ? p.rec + (chunk_slot(sb, ch.n, 0) * p.HV + ch.hv) * bwd_prep_bytes(K) : nullptr;
     if (p.seg_chunks) {
         const int64_t nch = (se - sb + CH - 1) / CH;
         const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;
@@ -1181,8 +1239,8 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     // a wave-uniform test, so that the two roles are separate branches and
     // not one exec-masked instruction stream (whose wait-counter analysis
     // would mix the roles' outstanding loads)
-    if (__builtin_amdgcn_readfirstlane(tid) >= NROLE) key_role<K, V, IO, G16, L2N>(smem, p, ch, tid, nc);
-    else state_role<K, V, IO, G16, L2N>(smem, p, ch, tid, nc);
+    if (__builtin_amdgcn_readfirstlane(tid) >= NROLE) key_role<K, V, IO, G16, L2N, REC>(smem, p, ch, tid, nc);
+    else state_role<K, V, IO, G16, L2N, REC>(smem, p, ch, tid, nc);
 }
 
 // ------------------------------------------------------ segment combine --
@@ -1258,8 +1316,8 @@ namespace {
 template <int K, int V, int IO, bool G16>
 void launch_chunk_l2(const FwdParams &p, dim3 grid, hipStream_t stream)
 {
-    if (p.qk_l2norm) hipLaunchKernelGGL((chunk_fwd_kernel<K, V, IO, G16, true>), grid, dim3(NTHR), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_fwd_kernel<K, V, IO, G16, false>), grid, dim3(NTHR), 0, stream, p);
+    if (p.qk_l2norm) hipLaunchKernelGGL((chunk_fwd_kernel<K, V, IO, G16, true, false>), grid, dim3(NTHR), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_fwd_kernel<K, V, IO, G16, false, false>), grid, dim3(NTHR), 0, stream, p);
 }
 template <int K, int V>
 void launch_chunk_typed(const FwdParams &p, dim3 grid, hipStream_t stream)
@@ -1279,6 +1337,18 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
 {
     const int64_t items = (int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1) * (p.pass == PASS_TRANSITION ? 2 : 1);
     const dim3 grid((unsigned)items);
+    if (p.rec) {
+        // the backward's recompute: bf16 io, float32 g, no L2 normalisation
+        if (p.io != IO_BF16 || p.gtype != G_F32 || p.qk_l2norm || !p.ckpt || p.seg_chunks || p.K != p.V)
+            return hipErrorInvalidValue;
+        if (p.K == 128)
+            hipLaunchKernelGGL((chunk_fwd_kernel<128, 128, IO_BF16, false, false, true>), grid, dim3(NTHR), 0, stream, p);
+        else if (p.K == 64)
+            hipLaunchKernelGGL((chunk_fwd_kernel<64, 64, IO_BF16, false, false, true>), grid, dim3(NTHR), 0, stream, p);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (p.K == 128 && p.V == 128)
         launch_chunk_typed<128, 128>(p, grid, stream);
     else if (p.K == 64 && p.V == 64)

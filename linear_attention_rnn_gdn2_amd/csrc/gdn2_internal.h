@@ -50,6 +50,9 @@ struct FwdParams {
     // ckpt[slot][hv] with slot = cu[n] / 64 + n + c for chunk c of sequence
     // n (whole-sequence path only; out may then be nullptr: no output)
     float *ckpt;
+    // Optional, with ckpt (bf16 io, float32 g, no L2 normalisation): every
+    // chunk's record (PrepRecord) at rec + (slot * HV + hv) * bwd_prep_bytes(K)
+    char *rec;
 };
 
 // Checkpoint slot of chunk c of sequence n that starts at token cu_n: unique
@@ -83,8 +86,8 @@ struct BwdParams {
 };
 
 // Byte offsets of one chunk's record in BwdParams::prep (K = V = D): the
-// chunk's WY quantities as the backward's prep pass computed them, read by
-// the state-gradient and gradient passes. QH, RR, wy_w, KB as bf16 [64][D],
+// chunk's WY quantities as the forward with checkpoints computed them, read
+// by the state-gradient and gradient passes. QH, RR, wy_w, KB as bf16 [64][D],
 // P, T as bf16 [64][64], 2^G_last as float32 [D].
 struct PrepRecord {
     int D;
@@ -136,10 +139,11 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);
 // workgroup per (sequence, value head, 32 value columns).
 hipError_t launch_recurrent_fwd(const FwdParams &p, hipStream_t stream);
 
-// The backward: chunk-parallel prep (mode 0) and gradients (mode 1), the
-// sequential pass of the state gradient over chunks in reverse, and the sum
-// of dq, dk over the value heads of each q/k head.
-hipError_t launch_bwd_chunk(const BwdParams &p, int mode, hipStream_t stream);
+// The backward (after the forward with checkpoints and records): the
+// sequential pass of the state gradient over chunks in reverse, the
+// chunk-parallel gradients, and the sum of dq, dk over the value heads of
+// each q/k head.
+hipError_t launch_bwd_chunk(const BwdParams &p, hipStream_t stream);
 hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream);
 hipError_t launch_bwd_reduce(const BwdParams &p, hipStream_t stream);
 
