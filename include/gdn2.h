@@ -308,17 +308,18 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  * [-1.3, 0] per token always satisfy it.
  *
  * Evaluation: the forward runs again and keeps the float32 state entering
- * every chunk; a chunk-parallel pass builds each chunk's WY quantities; one
- * workgroup per (sequence, value head) carries the state gradient over the
- * chunks in reverse; a chunk-parallel pass forms every gradient; a last pass
- * sums dq and dk over grouped value heads (HV > H). Arithmetic is float32 with bf16
+ * every chunk and each chunk's WY quantities (its record); one workgroup
+ * per (sequence, value head) carries the state gradient over the chunks in
+ * reverse; a chunk-parallel pass forms every gradient; a last pass sums dq
+ * and dk over grouped value heads (HV > H). Arithmetic is float32 with bf16
  * MFMA operands, as in the forward.
  *
  * Ownership and memory: the caller owns every buffer; inputs are only read.
  * A stream-ordered workspace (hipMallocAsync / hipFreeAsync on `stream`) of
  *   (T / 64 + N) * HV * (2 * K * V * 4 + 516 * K + 16384) bytes,
  *   plus 2 * T * HV * K * 4 bytes when HV > H (per-value-head dq and dk)
- * (rounded up per part) holds the checkpoints and partial gradients; if it
+ * (rounded up per part) holds the checkpoints, the records and partial
+ * gradients; if it
  * cannot be allocated the call fails with GDN2_ERR_HIP and enqueues nothing.
  *
  * Errors as gdn2_chunk_fwd: NULL_ARG for a missing required tensor, DTYPE,

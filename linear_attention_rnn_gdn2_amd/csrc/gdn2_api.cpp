@@ -482,7 +482,7 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
                           dg, dbeta, dw, d_initial_state, &p, &pf);
     if (rc != GDN2_OK) return rc;
     // stream-ordered workspace: forward checkpoints, state-gradient
-    // checkpoints, prep records, per-value-head dq and dk
+    // checkpoints, chunk records, per-value-head dq and dk
     const size_t state = (size_t)p.K * p.V * sizeof(float);
     const size_t chunks = (size_t)p.nslots * (size_t)p.HV;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };

@@ -24,19 +24,20 @@
 //   dRR   = dA^T KB + dP^T QH + gamma dKH
 //
 // then through the decay factors to dq, dk, dbeta, dg (a reverse cumulative
-// sum over the chunk) and through WV to dv, dw. Four launches follow the
-// forward with per-chunk state checkpoints:
+// sum over the chunk) and through WV to dv, dw. Three launches follow the
+// forward, which saves the state entering every chunk and every chunk's
+// record (QH, RR, wy_w, KB, P, T, gamma):
 //
-//   prep   (chunk-parallel)  QH, RR, wy_w, P, gamma of every chunk
 //   state  (one workgroup per (sequence, value head), chunks in reverse)
 //          the dS_in recurrence on MFMA, saving dS_out of every chunk
-//   grads  (chunk-parallel)  every gradient of the chunk from the forward
-//          checkpoint S_in, the saved dS_out and dO
+//   grads  (chunk-parallel)  every gradient of the chunk from its record,
+//          the forward checkpoint S_in, the saved dS_out and dO
 //   reduce dq, dk summed over the value heads of each q/k head
 //
 // Bounded decay: as in the forward's single-reference factorisation, every
-// |G| (log2 units) of a chunk must stay within 2^120; a chunk beyond it has
-// its gradients (and, through gamma, the state gradient) set to NaN.
+// |G| (log2 units) of a chunk must stay within 2^120; a chunk beyond it
+// (decided by the forward that writes the record, whose gamma is then NaN)
+// has its gradients and, through gamma, the state gradient set to NaN.
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
