@@ -319,8 +319,8 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  *   (T / 64 + N) * HV * (2 * K * V * 4 + 516 * K + 16384) bytes,
  *   plus 2 * T * HV * K * 4 bytes when HV > H (per-value-head dq and dk)
  * (rounded up per part) holds the checkpoints, the records and partial
- * gradients; if it
- * cannot be allocated the call fails with GDN2_ERR_HIP and enqueues nothing.
+ * gradients; if it cannot be allocated the call fails with GDN2_ERR_HIP and
+ * enqueues nothing.
  *
  * Errors as gdn2_chunk_fwd: NULL_ARG for a missing required tensor, DTYPE,
  * SHAPE, HEADS, UNSUPPORTED, LAYOUT for a non-dense tensor, ALIAS when an
