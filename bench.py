@@ -104,13 +104,15 @@ def _find(dirpath, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirpath}")
 
 
-def summarize_profiles(outdir: str, tag: str):
+def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
     """Turn the rocprofv3 CSVs of the PROFILE_STEPS runs under ``outdir`` into
     the committed text summaries: the kernel-trace statistics, and the HBM
     bytes per launch of the forward kernel from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by the same counter's reading for a plain
     device copy of 1 GiB (so that bytes per KiB-unit are calibrated, not
-    assumed)."""
+    assumed). The summaries go to ``dest`` (default: profiles/)."""
+    dest = dest or os.path.join(ROOT, "profiles")
+    traffic_file = os.path.join(dest, os.path.basename(TRAFFIC_FILE))
     src_hash = kernel_source_hash()
     stats = _csv_rows(_find(os.path.join(outdir, "kt"), "_kernel_stats.csv"))
     lines = [f"# rocprofv3 kernel-trace statistics: GDN-2 forward, {tag}", "",
@@ -148,10 +150,10 @@ def summarize_profiles(outdir: str, tag: str):
               f"forward kernel: FETCH_SIZE {sum(kf)/len(kf):.1f} KiB/dispatch ({len(kf)} dispatches), "
               f"WRITE_SIZE {sum(kw)/len(kw):.1f} KiB/dispatch ({len(kw)} dispatches)",
               f"  -> HBM read {fetch/1e6:.2f} MB, write {write/1e6:.2f} MB, total {(fetch+write)/1e6:.2f} MB per launch"]
-    txt = os.path.join(ROOT, "profiles", f"{KERNEL_TAG}_{tag}.txt")
+    txt = os.path.join(dest, f"{KERNEL_TAG}_{tag}.txt")
     with open(txt, "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file, "w") as f:
         json.dump({"kernel_source_hash": src_hash, "hbm_bytes_per_launch": fetch + write,
                    "hbm_read_bytes": fetch, "hbm_write_bytes": write,
                    "fetch_scale": fetch_scale, "write_scale": write_scale,
@@ -168,7 +170,7 @@ def summarize_profiles(outdir: str, tag: str):
         for r in rows:
             bl.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
                       f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {r['Name']}")
-        with open(os.path.join(ROOT, "profiles", f"bwd_kernels_{tag}.txt"), "w") as f:
+        with open(os.path.join(dest, f"bwd_kernels_{tag}.txt"), "w") as f:
             f.write("\n".join(bl) + "\n")
         log("\n".join(bl))
 
