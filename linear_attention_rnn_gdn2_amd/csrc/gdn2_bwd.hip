@@ -62,7 +62,6 @@ __device__ __forceinline__ int64_t cu_of(const BwdParams &p, int64_t i)
     if (!p.cu) return i == 0 ? 0 : p.T;
     return p.cu64 ? static_cast<const int64_t *>(p.cu)[i] : (int64_t) static_cast<const int32_t *>(p.cu)[i];
 }
-__device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
 __device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // One 16x16 tile Z[m0 + 4 q4 + e][n0 + l16] (element e of the result) of
@@ -212,7 +211,8 @@ struct BL {
     static constexpr int DGP = DGM + 4 * D;       // colsum(dKH RR) per row group [2][D] float32
     static constexpr int XS = DGP + 8 * D;        // per-channel scans: the parts' totals [CT / D][D] float32
     static constexpr int FLG = XS + 4 * CT;       // int: chunk beyond the decay bound
-    static constexpr int TOTAL = FLG + 16;
+    static constexpr int DWV = FLG + 16;          // dWV bf16 [64][D] (pitch D), for the epilogue's dv, dw
+    static constexpr int TOTAL = DWV + 64 * D * 2;
     static constexpr int EF = 64 * RF * 4;        // epilogue: dQH, dKB, dRR, G float32 [64][RF]
     static constexpr int SIZE = cmax(TOTAL, 4 * EF);
     static_assert(TK >= TC, "[64][64] tiles in [64][D] regions");
@@ -458,35 +458,14 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             x = tile_mm<false, false>(sm, L::RGD, RK, L::KB, RK, 16 * i, 16 * j, D, x, l16, q4);
             st_tile_bf(sm, L::RGB, RC, 16 * i, 16 * j, tril_mask(x, 16 * i, 16 * j, true, l16, q4), l16, q4);
         }
-        // ---- dWV = T^T dU -> dv = dWV w, dw = dWV v; dKB = T^T dwy_w
-        {
-            // v and w of the lane's elements, all in flight before use
-            uint16_t wl[MPW][4], vl[MPW][4];
+        // ---- dWV = T^T dU (bf16 in DWV: dv = dWV w and dw = dWV v are formed
+        // row-parallel in the epilogue); dKB = T^T dwy_w
 #pragma unroll
-            for (int u = 0; u < MPW; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = 16 * (mg + NMG * u) + 4 * q4 + e;
-                    const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
-                    wl[u][e] = s < len ? p.w[o] : (uint16_t)0;
-                    vl[u][e] = s < len ? p.v[o] : (uint16_t)0;
-                }
-            const float pn = poison ? __builtin_nanf("") : 1.0f;
-#pragma unroll
-            for (int u = 0; u < MPW; ++u) {
-                const int mi = mg + NMG * u;
-                const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGC, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = 16 * mi + 4 * q4 + e;
-                    if (s < len) {
-                        const int64_t o = ((t0 + s) * p.HV + hv) * D + 16 * ni + l16;
-                        p.dv[o] = to_bf(x[e] * bf(wl[u][e]) * pn);
-                        p.dw[o] = to_bf(x[e] * bf(vl[u][e]) * pn);
-                    }
-                }
-                dKB[u] = tile_mm<true, true>(sm, L::TB, RC, L::RGD, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
-            }
+        for (int u = 0; u < MPW; ++u) {
+            const int mi = mg + NMG * u;
+            const f32x4 x = tile_mm<true, true>(sm, L::TB, RC, L::RGC, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
+            st_tile_bf(sm, L::DWV, D, 16 * mi, 16 * ni, x, l16, q4);
+            dKB[u] = tile_mm<true, true>(sm, L::TB, RC, L::RGD, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
         }
         __syncthreads();
 
@@ -552,14 +531,16 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         constexpr int RF = L::RF, EF = L::EF;
         __syncthreads();  // every read of the regions below is done
-        // the row-parallel part's k and beta, in flight from here
-        bf16x8 ek[NU8], eb[NU8];
+        // the row-parallel part's k, beta, v and w, in flight from here
+        bf16x8 ek[NU8], eb[NU8], ev[NU8], ew[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
             ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
             eb[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : bf16x8{};
+            ev[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
+            ew[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
         }
         if (tid < D) {
             float dg0 = lds_ld<float>(sm, L::DGM + 4 * tid);
@@ -610,6 +591,10 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                     *reinterpret_cast<f32x4 *>(p.dk_ws + tv + 4) = __builtin_shufflevector(dk, dk, 4, 5, 6, 7);
                 }
                 *reinterpret_cast<bf16x8 *>(p.dbeta + tv) = f32x8_to_bf16(db);
+                // dv = dWV w, dw = dWV v
+                const f32x8 dwv = __builtin_convertvector(lds_ld<bf16x8>(sm, L::DWV + 2 * (r * D + c0)), f32x8) * pn;
+                *reinterpret_cast<bf16x8 *>(p.dv + tv) = f32x8_to_bf16(dwv * __builtin_convertvector(ew[u], f32x8));
+                *reinterpret_cast<bf16x8 *>(p.dw + tv) = f32x8_to_bf16(dwv * __builtin_convertvector(ev[u], f32x8));
             }
             lds_st<f32x4>(sm, o, __builtin_shufflevector(dG, dG, 0, 1, 2, 3));
             lds_st<f32x4>(sm, o + 16, __builtin_shufflevector(dG, dG, 4, 5, 6, 7));
