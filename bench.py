@@ -204,6 +204,37 @@ def bwd_mfma_flop(T, N, HV, K) -> int:
     return (T // 64 + N) * HV * (fwd + state + grads)
 
 
+def measured_peaks(dev):
+    """Context for the spec peaks, measured on this device after the timed
+    region: a 1 GiB device-to-device copy (read + write bytes per second)
+    and a 8192^3 bf16 GEMM through torch (the vendor library)."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src), 5)
+    t_mm = timed(lambda: torch.mm(a, b), 5)
+    out = {"copy_GBps": 2 * n * 4 / t_copy / 1e9, "bf16_gemm_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
+           "note": "measured on this device: 1 GiB copy (read + write), 8192^3 bf16 torch.mm"}
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_bwd(args, d, gdn2, dev):
     """Time gdn2.chunk_bwd (all of its launches, workspace included) over the
     workload and print one JSON line."""
@@ -408,6 +439,9 @@ def main():
     }
     log(f"mean launch {mean_launch_s*1e3:.3f} ms, wall/step {ms_per_step:.3f} ms, "
         f"{value/1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
+    rec["measured_peaks"] = measured_peaks(dev)
+    log(f"measured on this device: copy {rec['measured_peaks']['copy_GBps']:.0f} GB/s, "
+        f"bf16 GEMM {rec['measured_peaks']['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on the host")
         rec["cpu_baseline"] = cpu_baseline(d, wl)
