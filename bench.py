@@ -84,9 +84,12 @@ PROFILE_STEPS = {
 KERNEL_TAG = "chunk_fwd_kernel"
 
 
+PROFILE_DIR = "profile_out"  # where the profile runs write their CSVs (git-ignored)
+
+
 def profile_command(name: str) -> str:
     opts, bench_opts = PROFILE_STEPS[name]
-    return (f"rocprofv3 {opts} -f csv -d gpurun_out/{name} -o {name} -- "
+    return (f"rocprofv3 {opts} -f csv -d {PROFILE_DIR}/{name} -o {name} -- "
             f"python -u bench.py {bench_opts}")
 
 
