@@ -74,9 +74,9 @@ def measured_traffic(src_hash: str, launches_per_profile: int = 1):
 
 PROFILE_STEPS = {
     # name: (rocprofv3 options, bench.py options)
-    "kt": ("--kernel-trace --stats", "--steps 10 --warmup 2 --no-cpu-baseline"),
-    "pmc_fetch": ("--pmc FETCH_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline"),
-    "pmc_write": ("--pmc WRITE_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline"),
+    "kt": ("--kernel-trace --stats", "--steps 10 --warmup 2 --no-cpu-baseline --no-peaks"),
+    "pmc_fetch": ("--pmc FETCH_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
+    "pmc_write": ("--pmc WRITE_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
     "cal_fetch": ("--pmc FETCH_SIZE", "--copy-probe-mib 1024"),
     "cal_write": ("--pmc WRITE_SIZE", "--copy-probe-mib 1024"),
     "bkt": ("--kernel-trace --stats", "--mode bwd --steps 5 --warmup 1"),
@@ -91,6 +91,10 @@ def profile_command(name: str) -> str:
     opts, bench_opts = PROFILE_STEPS[name]
     return (f"rocprofv3 {opts} -f csv -d {PROFILE_DIR}/{name} -o {name} -- "
             f"python -u bench.py {bench_opts}")
+
+
+def _short(name: str, n: int = 110) -> str:
+    return name if len(name) <= n else name[:n] + "..."
 
 
 def _csv_rows(path):
@@ -124,7 +128,7 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
              f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
     for r in stats:
         lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
-                     f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {r['Name']}")
+                     f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {_short(r['Name'])}")
 
     def counter(name, want_kernel, value_min=0.0):
         rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
@@ -172,7 +176,7 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
               f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
         for r in rows:
             bl.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
-                      f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {r['Name']}")
+                      f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {_short(r['Name'])}")
         with open(os.path.join(dest, f"bwd_kernels_{tag}.txt"), "w") as f:
             f.write("\n".join(bl) + "\n")
         log("\n".join(bl))
@@ -337,6 +341,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / GEMM context")
     ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
                     help="fwd: the chunked prefill forward (the headline); bwd: its backward "
                          "(gradients of every input and of the initial state)")
@@ -442,9 +447,10 @@ def main():
     }
     log(f"mean launch {mean_launch_s*1e3:.3f} ms, wall/step {ms_per_step:.3f} ms, "
         f"{value/1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
-    rec["measured_peaks"] = measured_peaks(dev)
-    log(f"measured on this device: copy {rec['measured_peaks']['copy_GBps']:.0f} GB/s, "
-        f"bf16 GEMM {rec['measured_peaks']['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
+    if not args.no_peaks:
+        rec["measured_peaks"] = measured_peaks(dev)
+        log(f"measured on this device: copy {rec['measured_peaks']['copy_GBps']:.0f} GB/s, "
+            f"bf16 GEMM {rec['measured_peaks']['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on the host")
         rec["cpu_baseline"] = cpu_baseline(d, wl)
