@@ -456,6 +456,52 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
 
 }  // namespace
 
+namespace {
+// Enqueue the chunked forward of p on `stream`: whole sequences, or, with
+// split > 0 giving more than one segment, the split run (transition pass,
+// combine, output pass; stream-ordered workspace). The transition pass
+// writes no checkpoints or records; the output pass writes them per
+// segment. Without workspace the sequences run whole. Returns a gdn2
+// status (and sets the error message).
+int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream)
+{
+    const int64_t chunks = (p.T + 63) / 64;
+    const int64_t nseg = split > 0 ? (chunks + split - 1) / split : 1;
+    if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
+        const size_t state = (size_t)p.K * p.V * sizeof(float);
+        const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
+        void *ws = nullptr;
+        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && hipMallocAsync(&ws, 3 * one, stream) == hipSuccess) {
+            p.seg_chunks = split;
+            p.nseg = (int32_t)nseg;
+            p.wb = static_cast<float *>(ws);
+            p.wm = reinterpret_cast<float *>(static_cast<char *>(ws) + one);
+            p.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * one);
+            gdn2::FwdParams pt = p;
+            pt.pass = gdn2::PASS_TRANSITION;
+            pt.ckpt = nullptr;
+            pt.rec = nullptr;
+            hipError_t e = gdn2::launch_chunk_fwd(pt, stream);
+            if (e == hipSuccess) e = gdn2::launch_seg_combine(p, stream);
+            if (e == hipSuccess) e = gdn2::launch_chunk_fwd(p, stream);
+            const hipError_t ef = hipFreeAsync(ws, stream);
+            if (e != hipSuccess)
+                return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+            if (ef != hipSuccess)
+                return fail(GDN2_ERR_HIP, "workspace release failed: %s", hipGetErrorString(ef));
+            return GDN2_OK;
+        }
+        (void)hipGetLastError();  // no workspace: run the sequences whole instead
+    }
+    p.seg_chunks = 0;
+    p.nseg = 1;
+    const hipError_t e = gdn2::launch_chunk_fwd(p, stream);
+    if (e != hipSuccess)
+        return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN2_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int gdn2_chunk_bwd_check(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v, const gdn2_tensor *g,
@@ -503,12 +549,22 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     p.dk_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep + sz_qk);
     pf.ckpt = s_ckpt;
     pf.rec = p.prep;
+    // the forward again, writing checkpoints and records (split into
+    // segments as the forward itself would split this shape)
+    int frc = GDN2_OK;
+    if (p.T > 0) {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) == hipSuccess) ncu = cu_count(dev);
+        frc = run_forward(pf, gdn2_split_plan(p.T, p.N, p.HV, ncu), stream);
+    }
     hipError_t e = hipSuccess;
-    if (p.T > 0) e = gdn2::launch_chunk_fwd(pf, stream);  // checkpoints and records
-    if (e == hipSuccess) e = gdn2::launch_bwd_state(p, stream);
-    if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, stream);
-    if (e == hipSuccess && p.T > 0 && p.H != p.HV) e = gdn2::launch_bwd_reduce(p, stream);
+    if (frc == GDN2_OK) {
+        e = gdn2::launch_bwd_state(p, stream);
+        if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, stream);
+        if (e == hipSuccess && p.T > 0 && p.H != p.HV) e = gdn2::launch_bwd_reduce(p, stream);
+    }
     const hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+    if (frc != GDN2_OK) return frc;
     if (e != hipSuccess) return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     if (ef != hipSuccess) return fail(GDN2_ERR_HIP, "workspace release failed: %s", hipGetErrorString(ef));
     return GDN2_OK;
@@ -556,38 +612,7 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_t
         if (hipGetDevice(&dev) == hipSuccess) ncu = cu_count(dev);
         split = gdn2_split_plan(p.T, p.N, p.HV, ncu);
     }
-    const int64_t chunks = (p.T + 63) / 64;
-    const int64_t nseg = split > 0 ? (chunks + split - 1) / split : 1;
-    if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
-        // sequence split: transition pass, combine, output pass, all on
-        // `stream`, with a stream-ordered workspace
-        const size_t state = (size_t)p.K * p.V * sizeof(float);
-        const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
-        void *ws = nullptr;
-        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && hipMallocAsync(&ws, 3 * one, stream) == hipSuccess) {
-            p.seg_chunks = split;
-            p.nseg = (int32_t)nseg;
-            p.wb = static_cast<float *>(ws);
-            p.wm = reinterpret_cast<float *>(static_cast<char *>(ws) + one);
-            p.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * one);
-            gdn2::FwdParams pt = p;
-            pt.pass = gdn2::PASS_TRANSITION;
-            hipError_t e = gdn2::launch_chunk_fwd(pt, stream);
-            if (e == hipSuccess) e = gdn2::launch_seg_combine(p, stream);
-            if (e == hipSuccess) e = gdn2::launch_chunk_fwd(p, stream);
-            const hipError_t ef = hipFreeAsync(ws, stream);
-            if (e != hipSuccess)
-                return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-            if (ef != hipSuccess)
-                return fail(GDN2_ERR_HIP, "workspace release failed: %s", hipGetErrorString(ef));
-            return GDN2_OK;
-        }
-        (void)hipGetLastError();  // no workspace: run the sequences whole instead
-    }
-    hipError_t e = gdn2::launch_chunk_fwd(p, stream);
-    if (e != hipSuccess)
-        return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return GDN2_OK;
+    return run_forward(p, split, stream);
 }
 
 int gdn2_recurrent_fwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,

@@ -1203,6 +1203,10 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
         const int64_t span = (int64_t)p.seg_chunks * CH;
         ch.tb = sb + seg * span;
         ch.te = se < ch.tb + span ? se : ch.tb + span;
+        // checkpoints and records of the segment's chunks (output pass)
+        const int64_t skip = (int64_t)seg * p.seg_chunks * p.HV;
+        if (ch.ckpt) ch.ckpt += skip * (K * V);
+        if (ch.rec) ch.rec += skip * bwd_prep_bytes(K);
         const int64_t sseg = (((int64_t)ch.n * p.HV + ch.hv) * p.nseg + seg) * K * V;  // [N, HV, nseg, K, V]
         if (p.pass == PASS_TRANSITION) {
             // nothing follows the last segment; the first one's map is not needed
@@ -1339,7 +1343,7 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
     const dim3 grid((unsigned)items);
     if (p.rec) {
         // the backward's recompute: bf16 io, float32 g, no L2 normalisation
-        if (p.io != IO_BF16 || p.gtype != G_F32 || p.qk_l2norm || !p.ckpt || p.seg_chunks || p.K != p.V)
+        if (p.io != IO_BF16 || p.gtype != G_F32 || p.qk_l2norm || !p.ckpt || p.pass != PASS_OUTPUT || p.K != p.V)
             return hipErrorInvalidValue;
         if (p.K == 128)
             hipLaunchKernelGGL((chunk_fwd_kernel<128, 128, IO_BF16, false, false, true>), grid, dim3(NTHR), 0, stream, p);

@@ -48,7 +48,8 @@ struct FwdParams {
     float *ws;             // [N, HV, nseg, K, V] entering state of segment j >= 1
     // Optional: the float32 K-major state entering every chunk, written to
     // ckpt[slot][hv] with slot = cu[n] / 64 + n + c for chunk c of sequence
-    // n (whole-sequence path only; out may then be nullptr: no output)
+    // n (whole sequences, or the output pass of a split run; out may then
+    // be nullptr: no output)
     float *ckpt;
     // Optional, with ckpt (bf16 io, float32 g, no L2 normalisation): every
     // chunk's record (PrepRecord) at rec + (slot * HV + hv) * bwd_prep_bytes(K)

@@ -96,6 +96,8 @@ def assert_parity(got, ref, tag):
     ((65, 0, 1, 130, 64, 63), 2, 4, 128),        # ragged varlen, empty and 1-token sequences, grouped heads
     ((200, 77), 1, 3, 64),                       # three value heads per q/k head
     ((1000,), 4, 4, 128),                        # 16 chunks with a ragged tail
+    ((4096,), 2, 2, 64),                         # few long chains: the recompute runs split
+    ((3000, 2100), 1, 2, 128),                   # split recompute, ragged segments
 ])
 def test_bwd_matches_oracle(lib, c_oracle, lengths, H, HV, D):
     d = case(lengths, H, HV, D, seed=sum(lengths) + D)
