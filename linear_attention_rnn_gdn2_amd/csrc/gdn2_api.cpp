@@ -500,6 +500,54 @@ int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream)
         return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN2_OK;
 }
+
+// Enqueue the backward's state-gradient pass: whole sequences, or, with
+// split > 0 giving more than one segment, split like the forward
+// (transition pass, the forward's combine in processing order, output pass).
+hipError_t run_bwd_state(gdn2::BwdParams p, int32_t split, hipStream_t stream)
+{
+    const int64_t chunks = (p.T + 63) / 64;
+    const int64_t nseg = split > 0 ? (chunks + split - 1) / split : 1;
+    if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
+        const size_t state = (size_t)p.K * p.V * sizeof(float);
+        const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
+        void *ws = nullptr;
+        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && hipMallocAsync(&ws, 3 * one, stream) == hipSuccess) {
+            p.seg_chunks = split;
+            p.nseg = (int32_t)nseg;
+            p.wb = static_cast<float *>(ws);
+            p.wm = reinterpret_cast<float *>(static_cast<char *>(ws) + one);
+            p.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * one);
+            gdn2::BwdParams pt = p;
+            pt.pass = gdn2::PASS_TRANSITION;
+            gdn2::FwdParams pc{};
+            pc.cu = p.cu;
+            pc.cu64 = p.cu64;
+            pc.T = p.T;
+            pc.N = p.N;
+            pc.H = p.H;
+            pc.HV = p.HV;
+            pc.K = p.K;
+            pc.V = p.V;
+            pc.seg_chunks = p.seg_chunks;
+            pc.nseg = p.nseg;
+            pc.wb = p.wb;
+            pc.wm = p.wm;
+            pc.ws = p.ws;
+            p.pass = gdn2::PASS_OUTPUT;
+            hipError_t e = gdn2::launch_bwd_state(pt, stream);
+            if (e == hipSuccess) e = gdn2::launch_seg_combine(pc, stream);
+            if (e == hipSuccess) e = gdn2::launch_bwd_state(p, stream);
+            const hipError_t ef = hipFreeAsync(ws, stream);
+            return e != hipSuccess ? e : ef;
+        }
+        (void)hipGetLastError();  // no workspace: whole sequences
+    }
+    p.seg_chunks = 0;
+    p.nseg = 1;
+    p.pass = gdn2::PASS_OUTPUT;
+    return gdn2::launch_bwd_state(p, stream);
+}
 }  // namespace
 
 extern "C" {
@@ -551,15 +599,14 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     pf.rec = p.prep;
     // the forward again, writing checkpoints and records (split into
     // segments as the forward itself would split this shape)
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess) ncu = cu_count(dev);
+    const int32_t split = gdn2_split_plan(p.T, p.N, p.HV, ncu);
     int frc = GDN2_OK;
-    if (p.T > 0) {
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) == hipSuccess) ncu = cu_count(dev);
-        frc = run_forward(pf, gdn2_split_plan(p.T, p.N, p.HV, ncu), stream);
-    }
+    if (p.T > 0) frc = run_forward(pf, split, stream);
     hipError_t e = hipSuccess;
     if (frc == GDN2_OK) {
-        e = gdn2::launch_bwd_state(p, stream);
+        e = run_bwd_state(p, split, stream);
         if (e == hipSuccess && p.T > 0) e = gdn2::launch_bwd_chunk(p, stream);
         if (e == hipSuccess && p.T > 0 && p.H != p.HV) e = gdn2::launch_bwd_reduce(p, stream);
     }

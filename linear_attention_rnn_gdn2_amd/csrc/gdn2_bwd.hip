@@ -638,19 +638,59 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     constexpr int NRT = D / 16, VW = 16, NCT = 1, NKS = D / 32;
     __shared__ __attribute__((aligned(16))) char sm[L::SIZE];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
-    const int n = blockIdx.x / p.HV, hv = blockIdx.x % p.HV;
+    // work item: (sequence, value head), times the segment and, in the
+    // transition pass, the kind (0: end gradient, 1: map from the identity
+    // with dO taken as zero)
+    int item = blockIdx.x;
+    const int kind = p.pass == PASS_TRANSITION ? item & 1 : 0;
+    if (p.pass == PASS_TRANSITION) item >>= 1;
+    const int seg = p.seg_chunks ? item % p.nseg : 0;
+    if (p.seg_chunks) item /= p.nseg;
+    const int n = item / p.HV, hv = item % p.HV;
     const int64_t sb = cu_of(p, n), se = cu_of(p, n + 1);
     const int nc = (int)((se - sb + 63) / 64);
     const int vbase = wv * VW;
     const int64_t head = ((int64_t)n * p.HV + hv) * D * D;
 
+    // the chunks [c_lo, c_hi) walked, the entering gradient (src; nullptr:
+    // zero), and where the leaving one goes
+    int c_lo = 0, c_hi = nc;
+    const float *src = p.dht ? p.dht + head : nullptr;
+    float *dst = p.dh0 ? p.dh0 + head : nullptr;
+    bool ident = false, zero_do = false, save = true;
+    if (p.seg_chunks) {
+        const int last = nc > 0 ? (nc - 1) / p.seg_chunks : 0;
+        if (seg > last) return;  // past the start of this sequence
+        c_lo = (last - seg) * p.seg_chunks;
+        c_hi = c_lo + p.seg_chunks < nc ? c_lo + p.seg_chunks : nc;
+        const int64_t sseg = (((int64_t)n * p.HV + hv) * p.nseg + seg) * D * D;
+        if (p.pass == PASS_TRANSITION) {
+            // nothing follows the last segment; the first one's map is not needed
+            if (seg >= last || (kind == 1 && seg == 0)) return;
+            save = false;
+            if (kind == 0) {
+                if (seg > 0) src = nullptr;
+                dst = p.wb + sseg;
+            } else {
+                src = nullptr;
+                ident = zero_do = true;
+                dst = p.wm + sseg;
+            }
+        } else {
+            if (seg > 0) src = p.ws + sseg;
+            if (seg < last) dst = nullptr;
+        }
+    }
+
     f32x4 dS[NRT][NCT];
     for (int rt = 0; rt < NRT; ++rt)
         for (int jt = 0; jt < NCT; ++jt)
-            for (int e = 0; e < 4; ++e)
-                dS[rt][jt][e] = p.dht ? p.dht[head + (16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rt + 4 * q4 + e, col = vbase + 16 * jt + l16;
+                dS[rt][jt][e] = ident ? (row == col ? 1.0f : 0.0f) : src ? src[row * D + col] : 0.0f;
+            }
 
-    for (int c = nc - 1; c >= 0; --c) {
+    for (int c = c_hi - 1; c >= c_lo; --c) {
         const int64_t slot = chunk_slot(sb, n, c), t0 = sb + 64 * (int64_t)c;
         const int len = (int)(se - t0 < 64 ? se - t0 : 64);
         constexpr PrepRecord R{D};
@@ -664,7 +704,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
             xq[u] = *reinterpret_cast<const bf16x8 *>(rec + R.qh() + 2 * (r * D + c0));
             xr[u] = *reinterpret_cast<const bf16x8 *>(rec + R.rr() + 2 * (r * D + c0));
             xw[u] = *reinterpret_cast<const bf16x8 *>(rec + R.wy() + 2 * (r * D + c0));
-            xo[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : bf16x8{};
+            xo[u] = r < len && !zero_do ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0)
+                                        : bf16x8{};
         }
 #pragma unroll
         for (int u = 0; u < NUP; ++u) {
@@ -688,10 +729,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
         }
         if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, xg);
         // the gradient of this chunk's S_out
-        float *dso = p.ds_ckpt + (slot * p.HV + hv) * D * D;
-        for (int rt = 0; rt < NRT; ++rt)
-            for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e) dso[(16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
+        if (save) {
+            float *dso = p.ds_ckpt + (slot * p.HV + hv) * D * D;
+            for (int rt = 0; rt < NRT; ++rt)
+                for (int jt = 0; jt < NCT; ++jt)
+                    for (int e = 0; e < 4; ++e) dso[(16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
+        }
         __syncthreads();
 
         // dU = scale P^T dO + RR (gamma dS): tokens x this wave's columns.
@@ -736,10 +779,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
             }
         }
     }
-    if (p.dh0)
+    if (dst)
         for (int rt = 0; rt < NRT; ++rt)
             for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e) p.dh0[head + (16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
+                for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
 }
 
 // ------------------------------------------------------------- reduce --
@@ -779,7 +822,7 @@ hipError_t launch_bwd_chunk(const BwdParams &p, hipStream_t stream)
 
 hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((int64_t)p.N * p.HV));
+    const dim3 grid((unsigned)((int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1) * (p.pass == PASS_TRANSITION ? 2 : 1)));
     if (grid.x == 0) return hipSuccess;
     if (p.K == 128) hipLaunchKernelGGL((bwd_state_kernel<128>), grid, dim3(64 * 8), 0, stream, p);
     else if (p.K == 64) hipLaunchKernelGGL((bwd_state_kernel<64>), grid, dim3(64 * 4), 0, stream, p);

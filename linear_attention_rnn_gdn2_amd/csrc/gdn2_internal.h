@@ -84,6 +84,14 @@ struct BwdParams {
     int32_t N, H, HV, K, V;
     int32_t nslots;
     float scale;
+    // Split state-gradient pass (seg_chunks > 0), as the forward's: segments
+    // of seg_chunks chunks numbered in processing order (segment 0 holds the
+    // sequence's last chunks); pass PASS_TRANSITION gives each segment's end
+    // gradient from dht or zero (wb) and its K x K map (wm), the forward's
+    // combine chains them (ws), PASS_OUTPUT walks every segment from its
+    // entering gradient. wb, wm, ws: [N, HV, nseg, K, V] float32.
+    int32_t seg_chunks, nseg, pass;
+    float *wb, *wm, *ws;
 };
 
 // Byte offsets of one chunk's record in BwdParams::prep (K = V = D): the
