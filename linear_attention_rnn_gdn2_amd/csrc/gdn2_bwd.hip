@@ -629,7 +629,7 @@ struct SL {
     static constexpr int SIZE = GAM + 4 * D;
 };
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
 {
     using L = SL<D>;
@@ -641,11 +641,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     // work item: (sequence, value head), times the segment and, in the
     // transition pass, the kind (0: end gradient, 1: map from the identity
     // with dO taken as zero)
+    // (the whole-sequence instantiation folds all of this away)
     int item = blockIdx.x;
-    const int kind = p.pass == PASS_TRANSITION ? item & 1 : 0;
-    if (p.pass == PASS_TRANSITION) item >>= 1;
-    const int seg = p.seg_chunks ? item % p.nseg : 0;
-    if (p.seg_chunks) item /= p.nseg;
+    const bool trans = SPLIT && p.pass == PASS_TRANSITION;
+    const int kind = trans ? item & 1 : 0;
+    if (trans) item >>= 1;
+    const int seg = SPLIT ? item % p.nseg : 0;
+    if (SPLIT) item /= p.nseg;
     const int n = item / p.HV, hv = item % p.HV;
     const int64_t sb = cu_of(p, n), se = cu_of(p, n + 1);
     const int nc = (int)((se - sb + 63) / 64);
@@ -658,13 +660,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     const float *src = p.dht ? p.dht + head : nullptr;
     float *dst = p.dh0 ? p.dh0 + head : nullptr;
     bool ident = false, zero_do = false, save = true;
-    if (p.seg_chunks) {
+    if constexpr (SPLIT) {
         const int last = nc > 0 ? (nc - 1) / p.seg_chunks : 0;
         if (seg > last) return;  // past the start of this sequence
         c_lo = (last - seg) * p.seg_chunks;
         c_hi = c_lo + p.seg_chunks < nc ? c_lo + p.seg_chunks : nc;
         const int64_t sseg = (((int64_t)n * p.HV + hv) * p.nseg + seg) * D * D;
-        if (p.pass == PASS_TRANSITION) {
+        if (trans) {
             // nothing follows the last segment; the first one's map is not needed
             if (seg >= last || (kind == 1 && seg == 0)) return;
             save = false;
@@ -824,9 +826,16 @@ hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)((int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1) * (p.pass == PASS_TRANSITION ? 2 : 1)));
     if (grid.x == 0) return hipSuccess;
-    if (p.K == 128) hipLaunchKernelGGL((bwd_state_kernel<128>), grid, dim3(64 * 8), 0, stream, p);
-    else if (p.K == 64) hipLaunchKernelGGL((bwd_state_kernel<64>), grid, dim3(64 * 4), 0, stream, p);
-    else return hipErrorInvalidValue;
+    const bool split = p.seg_chunks > 0;
+    if (p.K == 128) {
+        if (split) hipLaunchKernelGGL((bwd_state_kernel<128, true>), grid, dim3(64 * 8), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_state_kernel<128, false>), grid, dim3(64 * 8), 0, stream, p);
+    } else if (p.K == 64) {
+        if (split) hipLaunchKernelGGL((bwd_state_kernel<64, true>), grid, dim3(64 * 4), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_state_kernel<64, false>), grid, dim3(64 * 4), 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
