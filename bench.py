@@ -80,6 +80,8 @@ PROFILE_STEPS = {
     "cal_fetch": ("--pmc FETCH_SIZE", "--copy-probe-mib 1024"),
     "cal_write": ("--pmc WRITE_SIZE", "--copy-probe-mib 1024"),
     "bkt": ("--kernel-trace --stats", "--mode bwd --steps 5 --warmup 1"),
+    "bpmc_fetch": ("--pmc FETCH_SIZE", "--mode bwd --steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
+    "bpmc_write": ("--pmc WRITE_SIZE", "--mode bwd --steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
 }
 KERNEL_TAG = "chunk_fwd_kernel"
 
@@ -177,6 +179,27 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
         for r in rows:
             bl.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
                       f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {_short(r['Name'])}")
+        if os.path.isdir(os.path.join(outdir, "bpmc_fetch")) and os.path.isdir(os.path.join(outdir, "bpmc_write")):
+            bl += ["", "## HBM traffic per launch of each backward kernel (rocprofv3 --pmc, one counter per run)", "",
+                   f"scaled by the 1 GiB copy calibration of the forward's runs: fetch x{fetch_scale:.3f}, "
+                   f"write x{write_scale:.3f}", "",
+                   "commands:", "  " + profile_command("bpmc_fetch"), "  " + profile_command("bpmc_write"), "",
+                   f"{'read MB':>10} {'write MB':>10}  kernel"]
+            ours = lambda n: "gdn2::" in n
+            per = {}
+            for name, key, scale in (("bpmc_fetch", 0, fetch_scale), ("bpmc_write", 1, write_scale)):
+                rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
+                for r in rows:
+                    if ours(r["Kernel_Name"]):
+                        per.setdefault(r["Kernel_Name"], ([], []))[key].append(
+                            float(r["Counter_Value"]) * 1024 * scale)
+            total = 0.0
+            for kname, (fv, wv) in sorted(per.items()):
+                rd = sum(fv) / len(fv) if fv else 0.0
+                wr = sum(wv) / len(wv) if wv else 0.0
+                total += rd + wr
+                bl.append(f"{rd/1e6:>10.1f} {wr/1e6:>10.1f}  {_short(kname)}")
+            bl.append(f"sum over the kernels of one call: {total/1e6:.1f} MB")
         with open(os.path.join(dest, f"bwd_kernels_{tag}.txt"), "w") as f:
             f.write("\n".join(bl) + "\n")
         log("\n".join(bl))

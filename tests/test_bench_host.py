@@ -84,6 +84,14 @@ def test_counter_summary_on_synthetic_profiles(tmp_path):
                [[1, copy, "FETCH_SIZE", 9.0], [2, fwd, "FETCH_SIZE", 1000.0], [3, fwd, "FETCH_SIZE", 1000.0]])
     _write_csv(str(out / "pmc_write" / "pmc_write_counter_collection.csv"), ctr_hdr,
                [[2, fwd, "WRITE_SIZE", 400.0], [3, fwd, "WRITE_SIZE", 600.0]])
+    bwd_a = "void gdn2::(anonymous namespace)::bwd_chunk_kernel<128>(gdn2::BwdParams)"
+    bwd_b = "void gdn2::(anonymous namespace)::bwd_state_kernel<128, false>(gdn2::BwdParams)"
+    other = "void at::native::elementwise_kernel<128, 4>()"
+    _write_csv(str(out / "bpmc_fetch" / "bpmc_fetch_counter_collection.csv"), ctr_hdr,
+               [[1, other, "FETCH_SIZE", 5e6], [2, bwd_a, "FETCH_SIZE", 1000.0], [3, bwd_a, "FETCH_SIZE", 3000.0],
+                [4, bwd_b, "FETCH_SIZE", 500.0]])
+    _write_csv(str(out / "bpmc_write" / "bpmc_write_counter_collection.csv"), ctr_hdr,
+               [[2, bwd_a, "WRITE_SIZE", 250.0], [4, bwd_b, "WRITE_SIZE", 750.0]])
     dest = tmp_path / "profiles"
     dest.mkdir()
     bench.summarize_profiles(str(out), "synthetic", dest=str(dest))
@@ -95,7 +103,13 @@ def test_counter_summary_on_synthetic_profiles(tmp_path):
     assert rec["kernel_source_hash"] == bench.kernel_source_hash()
     txt = open(dest / "chunk_fwd_kernel_synthetic.txt").read()
     assert "900.0" in txt and "total 2.56 MB per launch" in txt
-    assert os.path.exists(dest / "bwd_kernels_synthetic.txt")
+    # backward: bwd_chunk reads 2,000 KiB x 2 and writes 250 KiB, bwd_state
+    # reads 500 KiB x 2 and writes 750 KiB; torch's own kernels are left out
+    btxt = open(dest / "bwd_kernels_synthetic.txt").read()
+    assert "     4.1        0.3  " + bwd_a in btxt
+    assert "     1.0        0.8  " + bwd_b in btxt
+    assert "sum over the kernels of one call: 6.1 MB" in btxt
+    assert "elementwise" not in btxt
 
 
 def test_traffic_is_null_for_another_source(tmp_path, monkeypatch):
