@@ -374,7 +374,7 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
         if (N < 1) return fail(GDN2_ERR_SHAPE, "cu_seqlens needs at least 2 entries (N >= 1)");
         if (!cu->data) return fail(GDN2_ERR_NULL_ARG, "cu_seqlens: data is NULL");
     }
-    const int64_t nslots = T / 64 + N;
+    const int64_t nslots = gdn2::slot_count(T, N);
     if (N * HV > INT32_MAX || nslots * HV > INT32_MAX)
         return fail(GDN2_ERR_SHAPE, "N * HV or the chunk count times HV exceeds the grid limit");
     const int64_t ss[4] = {N, HV, K, V};
@@ -465,8 +465,7 @@ namespace {
 // status (and sets the error message).
 int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream)
 {
-    const int64_t chunks = (p.T + 63) / 64;
-    const int64_t nseg = split > 0 ? (chunks + split - 1) / split : 1;
+    const int64_t nseg = split > 0 ? gdn2::seg_count(p.T, split) : 1;
     if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
         const size_t state = (size_t)p.K * p.V * sizeof(float);
         const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
@@ -506,8 +505,7 @@ int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream)
 // (transition pass, the forward's combine in processing order, output pass).
 hipError_t run_bwd_state(gdn2::BwdParams p, int32_t split, hipStream_t stream)
 {
-    const int64_t chunks = (p.T + 63) / 64;
-    const int64_t nseg = split > 0 ? (chunks + split - 1) / split : 1;
+    const int64_t nseg = split > 0 ? gdn2::seg_count(p.T, split) : 1;
     if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
         const size_t state = (size_t)p.K * p.V * sizeof(float);
         const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;

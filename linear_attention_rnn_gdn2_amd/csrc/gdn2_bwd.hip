@@ -57,11 +57,8 @@ constexpr float XLIM = 120.0f;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-__device__ __forceinline__ int64_t cu_of(const BwdParams &p, int64_t i)
-{
-    if (!p.cu) return i == 0 ? 0 : p.T;
-    return p.cu64 ? static_cast<const int64_t *>(p.cu)[i] : (int64_t) static_cast<const int32_t *>(p.cu)[i];
-}
+// Token range of sequence n (clamped into [0, T]).
+__device__ __forceinline__ SeqRange seq_of(const BwdParams &p, int64_t n) { return seq_range(p.cu, p.cu64, p.T, n); }
 __device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // One 16x16 tile Z[m0 + 4 q4 + e][n0 + l16] (element e of the result) of
@@ -251,16 +248,11 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     // last one whose first slot is not past it
     const int hv = blockIdx.x % p.HV;
     const int64_t slot = blockIdx.x / p.HV;
-    int lo = 0, hi = p.N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (chunk_slot(cu_of(p, mid), mid, 0) <= slot) lo = mid;
-        else hi = mid - 1;
-    }
-    const int n = lo;
-    const int64_t sb = cu_of(p, n), se = cu_of(p, n + 1);
-    const int64_t c = slot - chunk_slot(sb, n, 0);
-    if (c * 64 >= se - sb) return;  // no chunk in this slot
+    int n;
+    int64_t c;
+    if (!slot_owner(p.cu, p.cu64, p.T, p.N, slot, &n, &c)) return;  // no chunk in this slot
+    const SeqRange sr = seq_of(p, n);
+    const int64_t sb = sr.b, se = sr.e;
     const int64_t t0 = sb + c * 64;
     const int len = (int)(se - t0 < 64 ? se - t0 : 64);
     const int hk = hv / (p.HV / p.H);
@@ -649,8 +641,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     const int seg = SPLIT ? item % p.nseg : 0;
     if (SPLIT) item /= p.nseg;
     const int n = item / p.HV, hv = item % p.HV;
-    const int64_t sb = cu_of(p, n), se = cu_of(p, n + 1);
-    const int nc = (int)((se - sb + 63) / 64);
+    const SeqRange sr = seq_of(p, n);
+    const int64_t sb = sr.b, se = sr.e;
+    const int nc = (int)chunks_of(sr);
     const int vbase = wv * VW;
     const int64_t head = ((int64_t)n * p.HV + hv) * D * D;
 
@@ -661,7 +654,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     float *dst = p.dh0 ? p.dh0 + head : nullptr;
     bool ident = false, zero_do = false, save = true;
     if constexpr (SPLIT) {
-        const int last = nc > 0 ? (nc - 1) / p.seg_chunks : 0;
+        const int last = seg_last(sr, p.seg_chunks);
         if (seg > last) return;  // past the start of this sequence
         c_lo = (last - seg) * p.seg_chunks;
         c_hi = c_lo + p.seg_chunks < nc ? c_lo + p.seg_chunks : nc;

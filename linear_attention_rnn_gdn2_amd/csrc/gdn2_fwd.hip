@@ -1182,8 +1182,8 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     ch.n = item / p.HV;
     ch.hv = item - ch.n * p.HV;
     ch.hk = ch.hv / (p.HV / p.H);
-    const int64_t sb = p.cu ? cu_at(p, ch.n) : 0;
-    const int64_t se = p.cu ? cu_at(p, ch.n + 1) : p.T;
+    const SeqRange sr = seq_of(p, ch.n);
+    const int64_t sb = sr.b, se = sr.e;
     const int64_t shead = ((int64_t)ch.n * p.HV + ch.hv) * K * V;  // [N, HV, K, V] states
     ch.tb = sb;
     ch.te = se;
@@ -1197,8 +1197,7 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     ch.ckpt = p.ckpt ? p.ckpt + (chunk_slot(sb, ch.n, 0) * p.HV + ch.hv) * (int64_t)(K * V) : nullptr;
     ch.rec = REC ? p.rec + (chunk_slot(sb, ch.n, 0) * p.HV + ch.hv) * bwd_prep_bytes(K) : nullptr;
     if (p.seg_chunks) {
-        const int64_t nch = (se - sb + CH - 1) / CH;
-        const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;
+        const int last = seg_last(sr, p.seg_chunks);
         if (seg > last) return;  // past the end of this sequence
         const int64_t span = (int64_t)p.seg_chunks * CH;
         ch.tb = sb + seg * span;
@@ -1266,10 +1265,7 @@ __global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams
     const int ncb = V / CMB_COLS;
     const int chain = blockIdx.x / ncb, cb = blockIdx.x - chain * ncb;
     const int n = chain / p.HV;
-    const int64_t sb = p.cu ? cu_at(p, n) : 0;
-    const int64_t se = p.cu ? cu_at(p, n + 1) : p.T;
-    const int64_t nch = (se - sb + CH - 1) / CH;
-    const int last = nch > 0 ? (int)((nch - 1) / p.seg_chunks) : 0;
+    const int last = seg_last(seq_of(p, n), p.seg_chunks);
     if (last == 0) return;
     const int t = threadIdx.x, r = t >> 1, c = CMB_COLS / 2 * (t & 1);
     const int64_t seg0 = (int64_t)chain * p.nseg * K * V;  // chain = n * HV + hv

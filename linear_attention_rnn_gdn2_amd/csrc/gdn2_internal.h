@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gdn2_index.h"
+
 namespace gdn2 {
 
 // Validated, resolved arguments of one forward call. Pointers are device
@@ -55,10 +57,6 @@ struct FwdParams {
     // chunk's record (PrepRecord) at rec + (slot * HV + hv) * bwd_prep_bytes(K)
     char *rec;
 };
-
-// Checkpoint slot of chunk c of sequence n that starts at token cu_n: unique
-// over all chunks of a packed batch and below T / 64 + N.
-__host__ __device__ inline int64_t chunk_slot(int64_t cu_n, int64_t n, int64_t c) { return cu_n / 64 + n + c; }
 
 // Arguments of the backward kernels (all tensors dense, row-major).
 struct BwdParams {
@@ -135,11 +133,8 @@ __device__ inline void state_st(float *s, bool b16, int64_t e, float x)
     else s[e] = x;
 }
 
-// cu_seqlens[i] as int64 (either stored type)
-__host__ __device__ inline int64_t cu_at(const FwdParams &p, int64_t i)
-{
-    return p.cu64 ? static_cast<const int64_t *>(p.cu)[i] : (int64_t) static_cast<const int32_t *>(p.cu)[i];
-}
+// Token range of sequence n of a call (clamped into [0, T]).
+__host__ __device__ inline SeqRange seq_of(const FwdParams &p, int64_t n) { return seq_range(p.cu, p.cu64, p.T, n); }
 
 // Enqueue the fused chunked forward on `stream` (one pass, as p describes).
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);

@@ -78,8 +78,8 @@ __global__ __launch_bounds__(RB_THR) void recurrent_fwd_kernel(FwdParams p)
     item /= NVB;
     const int hv = item % p.HV, n = item / p.HV;
     const int hk = hv / (p.HV / p.H);
-    const int64_t tb = p.cu ? cu_at(p, n) : 0;
-    const int64_t te = p.cu ? cu_at(p, n + 1) : p.T;
+    const SeqRange rng = seq_of(p, n);
+    const int64_t tb = rng.b, te = rng.e;
 
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int v = lane & 31, rg = 2 * wave + (lane >> 5);

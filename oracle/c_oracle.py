@@ -12,7 +12,7 @@ import os
 
 import numpy as np
 
-from .build import LIB
+from .build import LIB, build_c_oracle
 from .recurrence import l2_normalize_rows, resolve_scale
 
 _F64, _F32, _BF16 = 0, 1, 2
@@ -23,7 +23,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB):
-            raise RuntimeError(f"C oracle not built ({LIB}); run oracle.build.build_c_oracle()")
+            build_c_oracle()  # a clean checkout: compile it (gcc, seconds)
         lib = ctypes.CDLL(LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         lib.gdn2_oracle_fwd.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int,
