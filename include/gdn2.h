@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 4
+#define GDN2_ABI_VERSION 5
 
 /* Element types a tensor descriptor may carry. */
 typedef enum gdn2_dtype {
@@ -207,6 +207,39 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
                         const gdn2_tensor *cu_seqlens, const gdn2_tensor *out,
                         const gdn2_tensor *final_state,
                         const gdn2_fwd_options *opts, hipStream_t stream);
+
+/* Bytes of the fixed device array that gdn2_chunk_fwd_noalloc uses (64 MiB). */
+#define GDN2_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * gdn2_chunk_fwd_noalloc -- gdn2_chunk_fwd_opts for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, results and errors as
+ * gdn2_chunk_fwd_opts; it calls no hipMalloc, hipMallocAsync, hipFree or
+ * other allocating routine.
+ *
+ * Where the split run needs a workspace (3 * N * HV * nseg * K * V * 4
+ * bytes, see gdn2_chunk_fwd_opts), it is taken from a static device array of
+ * GDN2_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends. Nothing in it needs clearing: every byte a call reads
+ * was written earlier in the same call. With seq_split_chunks = 0 the
+ * automatic plan lengthens its segments until the workspace fits (whole
+ * sequences if none does); an explicit seq_split_chunks whose workspace
+ * exceeds the array is rejected with GDN2_ERR_UNSUPPORTED and a message
+ * naming both sizes. Device ordinals 0..63.
+ *
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (e.g. on two streams without ordering between them) race on it
+ * and give undefined results. Calls ordered on one stream are safe.
+ */
+int gdn2_chunk_fwd_noalloc(const gdn2_tensor *q, const gdn2_tensor *k,
+                           const gdn2_tensor *v, const gdn2_tensor *g,
+                           const gdn2_tensor *beta, const gdn2_tensor *w,
+                           float scale, const gdn2_tensor *initial_state,
+                           const gdn2_tensor *cu_seqlens,
+                           const gdn2_tensor *out,
+                           const gdn2_tensor *final_state,
+                           const gdn2_fwd_options *opts, hipStream_t stream);
 
 /*
  * gdn2_recurrent_fwd -- the same operation evaluated token by token: for

@@ -14,6 +14,7 @@
 #include <stddef.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 #include <utility>
 
@@ -457,20 +458,38 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
 }  // namespace
 
 namespace {
-// Enqueue the chunked forward of p on `stream`: whole sequences, or, with
-// split > 0 giving more than one segment, the split run (transition pass,
-// combine, output pass; stream-ordered workspace). The transition pass
-// writes no checkpoints or records; the output pass writes them per
-// segment. Without workspace the sequences run whole. Returns a gdn2
-// status (and sets the error message).
-int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream)
+// Bytes of the split run's workspace (segment end states, transitions and
+// entering states) for segments of `split` chunks; 0 when the run would not
+// split, SIZE_MAX when the count overflows.
+size_t split_workspace_bytes(const gdn2::FwdParams &p, int32_t split)
 {
     const int64_t nseg = split > 0 ? gdn2::seg_count(p.T, split) : 1;
-    if (split > 0 && nseg > 1 && nseg <= INT32_MAX) {
-        const size_t state = (size_t)p.K * p.V * sizeof(float);
-        const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
-        void *ws = nullptr;
-        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && hipMallocAsync(&ws, 3 * one, stream) == hipSuccess) {
+    if (split <= 0 || nseg <= 1) return 0;
+    if (nseg > INT32_MAX) return SIZE_MAX;
+    const size_t state = (size_t)p.K * p.V * sizeof(float);
+    const size_t items = (size_t)p.N * p.HV * (size_t)nseg;
+    if (items / nseg != (size_t)p.N * p.HV || items > SIZE_MAX / (3 * state)) return SIZE_MAX;
+    return 3 * items * state;
+}
+
+// Enqueue the chunked forward of p on `stream`: whole sequences, or, with
+// split > 0 giving more than one segment, the split run (transition pass,
+// combine, output pass). Its workspace is `fixed` when given (the caller
+// has checked that it is large enough), else stream-ordered
+// (hipMallocAsync / hipFreeAsync on `stream`; if that allocation fails the
+// sequences run whole). The transition pass writes no checkpoints or
+// records; the output pass writes them per segment. Returns a gdn2 status
+// (and sets the error message).
+int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream, void *fixed = nullptr)
+{
+    const size_t bytes = split_workspace_bytes(p, split);
+    if (bytes > 0 && bytes != SIZE_MAX) {
+        const int64_t nseg = gdn2::seg_count(p.T, split);
+        const size_t one = bytes / 3;
+        void *ws = fixed;
+        const bool own = !fixed;
+        if (own && hipMallocAsync(&ws, bytes, stream) != hipSuccess) ws = nullptr;
+        if (ws) {
             p.seg_chunks = split;
             p.nseg = (int32_t)nseg;
             p.wb = static_cast<float *>(ws);
@@ -483,7 +502,7 @@ int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream)
             hipError_t e = gdn2::launch_chunk_fwd(pt, stream);
             if (e == hipSuccess) e = gdn2::launch_seg_combine(p, stream);
             if (e == hipSuccess) e = gdn2::launch_chunk_fwd(p, stream);
-            const hipError_t ef = hipFreeAsync(ws, stream);
+            const hipError_t ef = own ? hipFreeAsync(ws, stream) : hipSuccess;
             if (e != hipSuccess)
                 return fail(GDN2_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
             if (ef != hipSuccess)
@@ -548,7 +567,92 @@ hipError_t run_bwd_state(gdn2::BwdParams p, int32_t split, hipStream_t stream)
 }
 }  // namespace
 
+// ------------------------------------------------- allocation-free entry --
+// gdn2_chunk_fwd_noalloc takes the split run's workspace from this array
+// instead of allocating one. Every GPU the library runs on holds its own
+// copy until the process ends, at its own address. Host code uses that
+// address as hipGetSymbolAddress returns it for the current device
+// (scratch_on), never the array's name, which on the host is only a
+// stand-in for the symbol.
+static __device__ __align__(256) char scratch[GDN2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_addr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// The device address of `scratch` on device dev, which must be current:
+// looked up once per device, the first time the entry point runs there.
+void *scratch_on(int dev, hipError_t *err)
+{
+    std::call_once(scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        scratch_addr[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    *err = scratch_err[dev];
+    return scratch_addr[dev];
+}
+
+// The shortest segment length, at least `split`, whose workspace fits in
+// `cap` bytes (-1: none does, so sequences run whole).
+int32_t fit_split(const gdn2::FwdParams &p, int32_t split, size_t cap)
+{
+    if (split <= 0 || split_workspace_bytes(p, split) <= cap) return split;
+    const size_t per_seg = 3 * (size_t)p.N * p.HV * (size_t)p.K * p.V * sizeof(float);
+    const int64_t max_seg = (int64_t)(cap / per_seg);
+    if (max_seg < 2) return -1;
+    const int64_t chunks = (p.T + gdn2::CHUNK - 1) / gdn2::CHUNK;
+    const int64_t L = (chunks + max_seg - 1) / max_seg;
+    return L > INT32_MAX ? -1 : (int32_t)(L > split ? L : split);
+}
+}  // namespace
+
 extern "C" {
+
+int gdn2_chunk_fwd_noalloc(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
+                           const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
+                           const gdn2_tensor *initial_state, const gdn2_tensor *cu_seqlens,
+                           const gdn2_tensor *out, const gdn2_tensor *final_state,
+                           const gdn2_fwd_options *opts, hipStream_t stream)
+{
+    gdn2::FwdParams p;
+    int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p);
+    if (rc != GDN2_OK) return rc;
+    Options o;
+    if ((rc = read_options(opts, &o)) != GDN2_OK) return rc;
+    p.state_vmajor = o.vmajor;
+    p.qk_l2norm = o.l2norm;
+    p.seg_chunks = 0;
+    p.nseg = 1;
+    p.pass = gdn2::PASS_OUTPUT;
+    p.wb = p.wm = p.ws = nullptr;
+    const size_t cap = GDN2_NOALLOC_SCRATCH_BYTES;
+    int32_t split = o.split;
+    if (split > 0) {
+        const size_t need = split_workspace_bytes(p, split);
+        if (need > cap)
+            return fail(GDN2_ERR_UNSUPPORTED,
+                        "seq_split_chunks %d needs %zu bytes of scratch; gdn2_chunk_fwd_noalloc holds %zu "
+                        "(use longer segments, -1, or gdn2_chunk_fwd_opts)",
+                        split, need, cap);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN2_ERR_HIP, "no current device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GDN2_ERR_UNSUPPORTED, "device %d: gdn2_chunk_fwd_noalloc serves devices 0..%d", dev,
+                    kMaxDevices - 1);
+    if (split == 0) split = fit_split(p, gdn2_split_plan(p.T, p.N, p.HV, cu_count(dev)), cap);
+    void *ws = nullptr;
+    if (split_workspace_bytes(p, split) > 0) {
+        ws = scratch_on(dev, &e);
+        if (!ws) return fail(GDN2_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+    }
+    // ws is set whenever the run splits, so run_forward allocates nothing
+    return run_forward(p, split, stream, ws);
+}
 
 int gdn2_chunk_bwd_check(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v, const gdn2_tensor *g,
                          const gdn2_tensor *beta, const gdn2_tensor *w, float scale,

@@ -25,7 +25,8 @@ _LAYOUTS = {"kv": GDN2_STATE_KV, "vk": GDN2_STATE_VK}
 STATUS = {0: "OK", -1: "NULL_ARG", -2: "DTYPE", -3: "SHAPE", -4: "HEADS",
           -5: "UNSUPPORTED", -6: "LAYOUT", -7: "ALIAS", -8: "HIP"}
 
-EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_opts", "gdn2_chunk_fwd_check", "gdn2_split_plan",
+EXPORTED = ["gdn2_chunk_fwd", "gdn2_chunk_fwd_opts", "gdn2_chunk_fwd_noalloc", "gdn2_chunk_fwd_check",
+            "gdn2_split_plan",
             "gdn2_recurrent_fwd", "gdn2_recurrent_fwd_opts", "gdn2_recurrent_fwd_check",
             "gdn2_chunk_bwd", "gdn2_chunk_bwd_check", "gdn2_last_error", "gdn2_abi_version"]
 
@@ -75,6 +76,9 @@ def load_library():
         lib.gdn2_chunk_fwd_opts.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P,
                                             ctypes.POINTER(Gdn2FwdOptions), ctypes.c_void_p]
         lib.gdn2_chunk_fwd_opts.restype = ctypes.c_int
+        lib.gdn2_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P,
+                                               ctypes.POINTER(Gdn2FwdOptions), ctypes.c_void_p]
+        lib.gdn2_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.gdn2_recurrent_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P, ctypes.c_void_p]
         lib.gdn2_recurrent_fwd.restype = ctypes.c_int
         lib.gdn2_recurrent_fwd_opts.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P, P,
@@ -188,6 +192,26 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
         opts = make_options(seq_split, state_layout, qk_l2norm)
         rc = lib.gdn2_chunk_fwd_opts(*[_ptr(d) for d in descs], _scale_arg(scale),
                                      *[_ptr(d) for d in rest], ctypes.byref(opts), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise Gdn2Error(rc, last_error())
+    return out, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
+                      cu_seqlens=None, out=None, final_state=None, seq_split=None, state_layout="kv",
+                      qk_l2norm=False):
+    """:func:`chunk_fwd` through ``gdn2_chunk_fwd_noalloc``: the library
+    allocates no device memory (a split run's workspace is its fixed device
+    array). ``out`` and ``final_state`` must be preallocated by the caller
+    (``final_state`` None: not produced)."""
+    lib = load_library()
+    if out is None:
+        raise ValueError("chunk_fwd_noalloc needs a preallocated out")
+    _, _, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, False, out, final_state, g, beta, w)
+    stream = torch.cuda.current_stream(v.device).cuda_stream
+    opts = make_options(seq_split, state_layout, qk_l2norm)
+    rc = lib.gdn2_chunk_fwd_noalloc(*[_ptr(d) for d in descs], _scale_arg(scale), *[_ptr(d) for d in rest],
+                                    ctypes.byref(opts), ctypes.c_void_p(stream))
     if rc != 0:
         raise Gdn2Error(rc, last_error())
     return out, final_state

@@ -333,3 +333,31 @@ def test_bwd_no_cpu_path(gdn2):
     c, _ = bwd_case()
     with pytest.raises(ValueError):
         gdn2.chunk_bwd(c["q"], c["k"], c["v"], c["g"], c["beta"], c["w"], c["d_out"])
+
+
+def test_noalloc_rejects_oversized_split_before_device_work(gdn2):
+    """gdn2_chunk_fwd_noalloc: an explicit segment length whose workspace
+    exceeds the fixed scratch array is UNSUPPORTED, with both sizes in the
+    message, before any device query (host tensors here)."""
+    import ctypes
+    lib = gdn2.load_library()
+    cap = int(re.search(r"#define GDN2_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+              .group(1)) << 20
+    P = lambda x: None if x is None else ctypes.byref(x)
+    # 100 one-chunk segments x 16 heads x 3 x 16 KiB = 75 MiB > 64 MiB
+    T, H, K = 6400, 16, 64
+    t = dict(q=torch.zeros(T, H, K, dtype=torch.bfloat16), k=torch.zeros(T, H, K, dtype=torch.bfloat16),
+             v=torch.zeros(T, H, K, dtype=torch.bfloat16), out=torch.zeros(T, H, K, dtype=torch.bfloat16))
+    descs = [gdn2.describe(t.get(n)) for n in ("q", "k", "v", "g", "beta", "w")]
+    rest = [gdn2.describe(t.get(n)) for n in ("initial_state", "cu_seqlens", "out", "final_state")]
+    need = 3 * 1 * H * 100 * K * K * 4
+    assert need > cap
+    opts = gdn2.make_options(seq_split=1)
+    rc = lib.gdn2_chunk_fwd_noalloc(*[P(x) for x in descs], 0.0, *[P(x) for x in rest], ctypes.byref(opts), None)
+    assert gdn2.STATUS[rc] == "UNSUPPORTED"
+    msg = gdn2.last_error()
+    assert str(need) in msg and str(cap) in msg, msg
+    # argument errors come first, as for gdn2_chunk_fwd_opts
+    bad = gdn2.Gdn2FwdOptions(4, 0)
+    rc = lib.gdn2_chunk_fwd_noalloc(*[P(x) for x in descs], 0.0, *[P(x) for x in rest], ctypes.byref(bad), None)
+    assert rc == -3 and "options" in gdn2.last_error()

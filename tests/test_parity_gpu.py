@@ -90,15 +90,42 @@ def assert_parity(tag, out, fin, ro, rs):
         assert rs_rel <= REL_L2 and rs_max <= MAX_ABS, msg
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_workload_parity(lib, c_oracle, cfg):
-    say(f"[workload {cfg}] {WORKLOADS[cfg].name}: drawing inputs")
-    d = make_inputs(cfg)
-    say(f"[workload {cfg}] T={int(d['cu_seqlens'][-1])} running GPU")
+def assert_slices(tag, out, fin, ro, rs, cu):
+    """The bar on every (sequence, value head) slice of the output and the
+    final state on its own: a wrong chunk or head cannot hide in the
+    whole-tensor norm."""
+    o = out.float().cpu().double().numpy()
+    s = fin.cpu().double().numpy()
+    worst_o = worst_s = (0.0, None)
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        for hv in range(o.shape[1]):
+            if b > a:
+                rel, mx = metrics(o[a:b, hv], ro[a:b, hv])
+                assert rel <= REL_L2 and mx <= MAX_ABS, f"{tag}: output of sequence {n} head {hv}: {rel:.3e} {mx:.3e}"
+                worst_o = max(worst_o, (rel, (n, hv)))
+            rel, mx = metrics(s[n, hv], rs[n, hv])
+            assert rel <= REL_L2 and mx <= MAX_ABS, f"{tag}: state of sequence {n} head {hv}: {rel:.3e} {mx:.3e}"
+            worst_s = max(worst_s, (rel, (n, hv)))
+    say(f"{tag}: worst (sequence, head) rel-L2: out {worst_o[0]:.3e} at {worst_o[1]}, "
+        f"state {worst_s[0]:.3e} at {worst_s[1]}")
+
+
+@pytest.mark.parametrize("cfg,seed", [(0, None), (1, None), (2, None), (3, None), (4, None),
+                                      (2, 100), (2, 101), (2, 102), (4, 100), (4, 101), (4, 102)])
+def test_workload_parity(lib, c_oracle, cfg, seed):
+    """Every workload at full size (seed = its id), and the headline and
+    long-decay workloads at three more seeds, against the C oracle: whole
+    tensors, then every (sequence, value head) slice."""
+    say(f"[workload {cfg} seed {seed}] {WORKLOADS[cfg].name}: drawing inputs")
+    d = make_inputs(cfg, seed)
+    say(f"[workload {cfg} seed {seed}] T={int(d['cu_seqlens'][-1])} running GPU")
     out, fin = run_gpu(lib, d)
-    say(f"[workload {cfg}] running oracle")
+    say(f"[workload {cfg} seed {seed}] running oracle")
     ro, rs = ref(c_oracle, d)
-    assert_parity(f"workload {cfg}", out, fin, ro, rs)
+    tag = f"workload {cfg} seed {seed}"
+    assert_parity(tag, out, fin, ro, rs)
+    assert_slices(tag, out, fin, ro, rs, d["cu_seqlens"].tolist())
 
 
 EDGE_LENGTHS = [1, 63, 64, 65, 0, 127, 129, 200, 17]

@@ -78,12 +78,14 @@ def test_defaults_extreme_decay_and_inplace(lib, c_oracle):
     assert torch.equal(o1, o2) and torch.equal(f1, f2), "in-place state update differs"
 
 
-@pytest.mark.parametrize("K", [64, 128])
-def test_prefill_then_decode_equals_one_pass(lib, c_oracle, K):
+@pytest.mark.parametrize("K,steps", [(64, 5), (128, 5), (64, 128), (128, 128)])
+def test_prefill_then_decode_equals_one_pass(lib, c_oracle, K, steps):
     """Chunked prefill of the first tokens, then token steps from its final
-    state (in place), against one pass of the oracle over all tokens."""
+    state (in place), against one pass of the oracle over all tokens. With
+    128 steps the state is carried through 128 changing decode tokens (the
+    Flash-GDN-2 README's decode audit length); the decoded tokens' outputs
+    are also held to the bar on their own."""
     lens = [300, 129, 70]
-    steps = 5
     d = synth([L + steps for L in lens], 2, 2, K, K, seed=330 + K, init_std=0.02, beta_max=2.0)
     dev = torch.device("cuda:0")
     cu = d["cu_seqlens"].tolist()
@@ -108,3 +110,5 @@ def test_prefill_then_decode_equals_one_pass(lib, c_oracle, K):
             got[cu[i] + lens[i] + s] = outs[1 + s][i]
     ro, rs = ref(c_oracle, d)
     assert_parity(f"prefill {lens} + {steps} decode steps K={K}", got, state, ro, rs)
+    dec = [t for i in range(len(lens)) for t in range(cu[i] + lens[i], cu[i + 1])]
+    assert_parity(f"the {steps} decoded tokens alone K={K}", got[dec], None, ro[dec], None)
