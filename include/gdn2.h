@@ -334,11 +334,12 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  *   d_initial_state [N, HV, K, V]                          float32, or NULL (not written)
  * scale == 0 means 1/sqrt(K). Supported sizes as gdn2_chunk_fwd.
  *
- * Decay bound: in every 64-token chunk the running in-chunk sum of g of
- * every key channel must stay within 120 ln 2 (about 83) in magnitude;
- * the gradients of a chunk beyond it, and every state gradient reaching
- * back through it, are NaN (not silently wrong). Inputs whose g stays in
- * [-1.3, 0] per token always satisfy it.
+ * Strong decay: any g <= 0 is supported. A key channel whose running
+ * in-chunk sum of g leaves about -83 (120 ln 2) within a chunk cannot use
+ * the chunk-start factors e^G and e^-G (the second overflows); such a
+ * channel's share of the intra-chunk products is differentiated exactly,
+ * per pair of rows with e^(G_r - G_s) <= 1 (burn-gdn2 README, numerical
+ * stability), at some extra cost for the chunks that have one.
  *
  * Evaluation: the forward runs again and keeps the float32 state entering
  * every chunk and each chunk's WY quantities (its record); one workgroup

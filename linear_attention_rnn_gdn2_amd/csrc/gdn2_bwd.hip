@@ -57,6 +57,16 @@ constexpr float XLIM = 120.0f;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// The record's gamma carries a flagged channel in its sign bit: the factor
+// by which RR's column enters K-hat (gamma, or 1 where the column holds
+// K-hat itself).
+__device__ __forceinline__ f32x4 khat_factor(f32x4 g)
+{
+    f32x4 r;
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_signbit(g[e]) ? 1.0f : g[e];
+    return r;
+}
+
 // Token range of sequence n (clamped into [0, T]).
 __device__ __forceinline__ SeqRange seq_of(const BwdParams &p, int64_t n) { return seq_range(p.cu, p.cu64, p.T, n); }
 __device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -67,9 +77,10 @@ __device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(u
 //             xo + 2 (k lx + m)   (XT true: read with transpose reads)
 //   Y[k][n] at yo + 2 (n ly + k)   (YT false: k contiguous)
 //             yo + 2 (k ly + n)   (YT true: transpose reads)
+// With yz, this lane's Y column (n0 + l16) is taken as zero.
 template <bool XT, bool YT>
 __device__ __forceinline__ f32x4 tile_mm(const char *sm, int xo, int lx, int yo, int ly, int m0, int n0, int kd,
-                                         f32x4 acc, int l16, int q4)
+                                         f32x4 acc, int l16, int q4, bool yz = false)
 {
     for (int k0 = 0; k0 < kd; k0 += 32) {
         bf16x8 a, b;
@@ -85,6 +96,7 @@ __device__ __forceinline__ f32x4 tile_mm(const char *sm, int xo, int lx, int yo,
             const int o = yo + 2 * ((k0 + 8 * q4 + (l16 >> 2)) * ly + n0 + 4 * (l16 & 3));
             b = cat4(lds_tr(sm, o), lds_tr(sm, o + 8 * ly));
         }
+        if (yz) b = bf16x8{};
         acc = mfma_bf16(a, b, acc);
     }
     return acc;
@@ -143,8 +155,11 @@ __device__ __forceinline__ void load_gcol(float (&v)[RP], const BwdParams &p, in
 // from load_gcol's values, and with gam >= 0 also 2^G_last [D] at gam.
 // Returns whether |G| leaves the single-reference bound in this thread's
 // rows. The caller synchronises before reading G or 2^G_last.
+// With skip >= 0, channels whose int at skip + 4 c is nonzero are not
+// stored (their slots are written by the caller).
 template <int D, int NT, int RP = 64 * D / NT>
-__device__ __forceinline__ bool scan_gcol(char *sm, int go, int xo, int gam, const float (&v)[RP], int tid)
+__device__ __forceinline__ bool scan_gcol(char *sm, int go, int xo, int gam, const float (&v)[RP], int tid,
+                                          int skip = -1)
 {
     constexpr int NP = NT / D;
     const int c = tid % D, part = tid / D;
@@ -158,11 +173,12 @@ __device__ __forceinline__ bool scan_gcol(char *sm, int go, int xo, int gam, con
     for (int q = 0; q < NP; ++q)
         if (q < part) off += lds_ld<float>(sm, xo + 4 * (q * D + c));
     bool out = false;
+    const bool keep = skip < 0 || lds_ld<int>(sm, skip + 4 * c) == 0;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
         const float G = loc[i] + off;
         out |= !(fabsf(G) <= XLIM);
-        lds_st<float>(sm, go + 4 * ((part * RP + i) * D + c), G);
+        if (keep) lds_st<float>(sm, go + 4 * ((part * RP + i) * D + c), G);
     }
     if (gam >= 0 && part == NP - 1) lds_st<float>(sm, gam + 4 * c, ex2(loc[RP - 1] + off));
     return out;
@@ -204,16 +220,25 @@ struct BL {
     static constexpr int PB = RGD + TK;           // P; dP
     static constexpr int TB = PB + TC;            // T (bf16)
     static constexpr int GAM = TB + TC;           // e^G_last [D] float32
-    static constexpr int DGM = GAM + 4 * D;       // rowsum(S_in dS_out) [D] float32
+    static constexpr int GMU = GAM + 4 * D;       // [D]: K-hat = RR GMU per channel (gamma, 1 if flagged)
+    static constexpr int FLC = GMU + 4 * D;       // int [D]: 1 for a flagged channel (strong decay)
+    static constexpr int XLS = FLC + 4 * D;       // int [D]: the flagged channels in order
+    static constexpr int CSL = XLS + 4 * D;       // int [D]: a flagged channel's place in XLS
+    static constexpr int DGM = CSL + 4 * D;       // rowsum(S_in dS_out) [D] float32
     static constexpr int DGP = DGM + 4 * D;       // colsum(dKH RR) per row group [2][D] float32
     static constexpr int XS = DGP + 8 * D;        // per-channel scans: the parts' totals [CT / D][D] float32
-    static constexpr int FLG = XS + 4 * CT;       // int: chunk beyond the decay bound
+    static constexpr int FLG = XS + 4 * CT;       // int: any flagged channel; then (int) their number
     static constexpr int DWV = FLG + 16;          // dWV bf16 [64][D] (pitch D), for the epilogue's dv, dw
+    // flagged channels' exact pass, NXB channels at a time: G, q, k, beta
+    // float32 [4][NXB][64] in RGA; alpha, pi, kappa float32 [3][NXB][64] in RGC
+    static constexpr int NXB = D / 8;
     static constexpr int TOTAL = DWV + 64 * D * 2;
     static constexpr int EF = 64 * RF * 4;        // epilogue: dQH, dKB, dRR, G float32 [64][RF]
     static constexpr int SIZE = cmax(TOTAL, 4 * EF);
     static_assert(TK >= TC, "[64][64] tiles in [64][D] regions");
-    static_assert(4 * EF <= XS, "the epilogue leaves GAM, DGM, DGP, XS, FLG intact");
+    static_assert(4 * EF <= GAM, "the epilogue leaves GAM .. FLG intact");
+    static_assert(4 * NXB * 64 * 4 <= TK && 3 * NXB * 64 * 4 <= TK, "exact pass in RGA, RGC");
+    static_assert(RGC + 3 * NXB * 64 * 4 <= 3 * EF, "exact results below the epilogue's G tile");
     static_assert(SIZE <= 160 * 1024, "LDS budget");
 };
 
@@ -223,6 +248,84 @@ __device__ __forceinline__ void lower_tile(int t, int &i, int &j)
     const int u = t % 10;  // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
     i = u >= 6 ? 3 : u >= 3 ? 2 : u >= 1 ? 1 : 0;
     j = u - i * (i + 1) / 2;
+}
+
+// ------------------------------------------------------ flagged channels --
+// A flagged channel (strong decay: |G| beyond the single-reference range in
+// this chunk; the forward's record marks it with a negated gamma) took no part in
+// the RR products: its share of A and P is exact per pair of rows. With
+// E_rs = 2^(G_r - G_s) (G in log2 units, so E_rs = e^(G_r - G_s) in natural
+// units), the share of the gradients is
+//   alpha_r = sum_{s <= r} dA_rs k_s E_rs      -> d(beta k)_r
+//   pi_r    = sum_{s <= r} dP_rs k_s E_rs      -> dq_r
+//   kappa_r = sum_{r' >= r} (dA_r'r (beta k)_r' + dP_r'r q_r') E_r'r -> dk_r
+//   dG_r   += (beta k)_r alpha_r + q_r pi_r - k_r kappa_r
+// (dA is strictly and dP inclusively lower triangular, so the diagonal terms
+// are the right ones). This pass takes channels b0 .. b0 + nb - 1 of the
+// list XLS: it stages their G, q, k, beta in RGA (float32 [4][NXB][64]) and
+// leaves alpha, pi, kappa in RGC (float32 [3][NXB][64]). Every thread takes
+// part; it ends synchronised.
+template <int D>
+__device__ __forceinline__ void exact_pass(char *sm, const BwdParams &p, int64_t t0, int len, int hk, int hv, int b0,
+                                           int nb, int tid)
+{
+    using L = BL<D>;
+    constexpr int NXB = L::NXB, TPX = CT / NXB, RPX = 64 / TPX;  // threads per channel, rows per thread
+    constexpr int A = 4 * 64 * NXB;                              // bytes per staged array
+    const int x = tid / TPX, part = tid % TPX;
+    const bool on = x < nb;
+    const int c = on ? lds_ld<int>(sm, L::XLS + 4 * (b0 + x)) : 0;
+    const int sx = L::RGA + 4 * 64 * x;  // this channel's staged rows
+    float gl[RPX], run = 0.0f;
+#pragma unroll
+    for (int h = 0; h < RPX; ++h) {
+        const int r = RPX * part + h;
+        const bool ok = on && r < len;
+        const int64_t tr = t0 + r;
+        run += ok ? p.g[(tr * p.HV + hv) * D + c] * LOG2E : 0.0f;
+        gl[h] = run;
+        const float qv = ok ? bf16_bits_to_f32(p.q[(tr * p.H + hk) * D + c]) : 0.0f;
+        const float kv = ok ? bf16_bits_to_f32(p.k[(tr * p.H + hk) * D + c]) : 0.0f;
+        const float bv = ok ? bf16_bits_to_f32(p.beta[(tr * p.HV + hv) * D + c]) : 0.0f;
+        lds_st<float>(sm, sx + 1 * A + 4 * r, qv);
+        lds_st<float>(sm, sx + 2 * A + 4 * r, kv);
+        lds_st<float>(sm, sx + 3 * A + 4 * r, bv);
+    }
+    // inclusive cumulative sum over the channel's TPX threads
+    float inc = run;
+    for (int d = 1; d < TPX; d <<= 1) {
+        const float o = __shfl_up(inc, d, TPX);
+        if (part >= d) inc += o;
+    }
+#pragma unroll
+    for (int h = 0; h < RPX; ++h) lds_st<float>(sm, sx + 4 * (RPX * part + h), gl[h] + inc - run);
+    __syncthreads();
+    // rows part and 63 - part (RPX = 2) or part (RPX = 1): alpha and pi
+    // run over s <= r, kappa over r' >= r, so every thread has 65 terms
+    // per row of each kind
+#pragma unroll
+    for (int h = 0; h < RPX; ++h) {
+        const int r = h ? 63 - part : part;
+        const float Gr = lds_ld<float>(sm, sx + 4 * r);
+        float al = 0.0f, pi = 0.0f, ka = 0.0f;
+        for (int s2 = 0; s2 <= r; ++s2) {
+            const float ke = lds_ld<float>(sm, sx + 2 * A + 4 * s2) * ex2(Gr - lds_ld<float>(sm, sx + 4 * s2));
+            al = fmaf((float)lds_ld<__bf16>(sm, L::RGB + 2 * (r * L::RC + s2)), ke, al);
+            pi = fmaf((float)lds_ld<__bf16>(sm, L::PB + 2 * (r * L::RC + s2)), ke, pi);
+        }
+        for (int r2 = r; r2 < 64; ++r2) {
+            const float e = ex2(lds_ld<float>(sm, sx + 4 * r2) - Gr);
+            const float bk = lds_ld<float>(sm, sx + 3 * A + 4 * r2) * lds_ld<float>(sm, sx + 2 * A + 4 * r2);
+            const float w = (float)lds_ld<__bf16>(sm, L::RGB + 2 * (r2 * L::RC + r)) * bk +
+                            (float)lds_ld<__bf16>(sm, L::PB + 2 * (r2 * L::RC + r)) * lds_ld<float>(sm, sx + 1 * A + 4 * r2);
+            ka = fmaf(w, e, ka);
+        }
+        const int ro = L::RGC + 4 * (64 * x + r);
+        lds_st<float>(sm, ro, al);
+        lds_st<float>(sm, ro + A, pi);
+        lds_st<float>(sm, ro + 2 * A, ka);
+    }
+    __syncthreads();
 }
 
 // ----------------------------------------------------- chunk-parallel kernel --
@@ -302,15 +405,18 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 lds_st<bf16x8>(sm, (m ? L::TB : L::PB) + 2 * (r * RC + c0), xpt[m]);
             }
             if (tid < D) {
-                lds_st<float>(sm, L::GAM + 4 * tid, xg);
-                if (xg != xg) lds_st<int>(sm, L::FLG, 1);
+                const bool fl = __builtin_signbit(xg);
+                lds_st<float>(sm, L::GAM + 4 * tid, fabsf(xg));
+                lds_st<float>(sm, L::GMU + 4 * tid, fl ? 1.0f : xg);
+                lds_st<int>(sm, L::FLC + 4 * tid, fl ? 1 : 0);
+                if (fl) lds_st<int>(sm, L::FLG, 1);
             }
             __syncthreads();
         }
-        const bool poison = lds_ld<int>(sm, L::FLG) != 0;
+        const bool flagged = lds_ld<int>(sm, L::FLG) != 0;  // workgroup-uniform
         const float *Sin = p.s_ckpt + kd_off;
         const float *dSo = p.ds_ckpt + kd_off;
-        const float *gam = reinterpret_cast<const float *>(sm + L::GAM);
+        const float *gmu = reinterpret_cast<const float *>(sm + L::GMU);
 
         // ---- U = T WV - wy_w S_in (bf16 [token][D] in RGA); wave wv takes
         // its column tile ni and row tiles mg, mg + NMG, ...
@@ -342,7 +448,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         __syncthreads();
 
-        // ---- dU = scale P^T dO + RR (gamma dS_out) (bf16 in RGC), and
+        // ---- dU = scale P^T dO + RR (GMU dS_out) (bf16 in RGC), and
         // dKH = U dS_out^T (registers: the wave's tiles)
         f32x4 dKH[MPW], dQH[MPW], dKB[MPW], dRR[MPW];
         bf16x8 fs[D / 32];  // S_in row fragments, for dQH and dwy_w below
@@ -362,7 +468,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 rs[ks][1] = *reinterpret_cast<const f32x4 *>(Sin + o + 4);
             }
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gam);
+            for (int ks = 0; ks < D / 32; ++ks) fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gmu);
             float sdot = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
@@ -479,18 +585,76 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         // chunk's g issued first: the epilogue's cumulative sum needs it)
         float gv[scan_rows<D, CT>()];
         load_gcol<D, CT>(gv, p, t0, len, hv, tid);
+        // a flagged channel's RR column holds K-hat: not an operand here
+        const int colc = 16 * ni + l16;
+        const bool fcol = flagged && lds_ld<int>(sm, L::FLC + 4 * colc) != 0;
         for (int u = 0; u < MPW; ++u) {
             const int mi = mg + NMG * u;
-            dKB[u] = tile_mm<false, true>(sm, L::RGB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dKB[u], l16, q4);
+            dKB[u] = tile_mm<false, true>(sm, L::RGB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dKB[u], l16, q4, fcol);
             f32x4 x = tile_mm<true, true>(sm, L::RGB, RC, L::KB, RK, 16 * mi, 16 * ni, 64, f32x4{0, 0, 0, 0}, l16, q4);
             dRR[u] = tile_mm<true, true>(sm, L::PB, RC, L::QH, RK, 16 * mi, 16 * ni, 64, x, l16, q4);
-            dQH[u] = tile_mm<false, true>(sm, L::PB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dQH[u], l16, q4);
+            dQH[u] = tile_mm<false, true>(sm, L::PB, RC, L::RR, RK, 16 * mi, 16 * ni, 64, dQH[u], l16, q4, fcol);
         }
         __syncthreads();
+
+        // ---- flagged channels: the exact pass, NXB at a time, folded into
+        // this wave's tiles of a flagged column as the final dq (dQH), dbeta
+        // (dKB), dk (dRR) and dG (dGf): the products above and dKH (K-hat
+        // is the record's RR column there) give the rest
+        f32x4 dGf[MPW];
+        if (flagged) {
+            if (wv == 0) {  // the flagged channels in order
+                int cnt = 0;
+                for (int cb = 0; cb < D; cb += 64) {
+                    const int c = cb + lane;
+                    const bool f = lds_ld<int>(sm, L::FLC + 4 * c) != 0;
+                    const uint64_t m = __ballot(f);
+                    if (f) {
+                        const int pos = cnt + __popcll(m & ((1ull << lane) - 1));
+                        lds_st<int>(sm, L::XLS + 4 * pos, c);
+                        lds_st<int>(sm, L::CSL + 4 * c, pos);
+                    }
+                    cnt += __popcll(m);
+                }
+                if (lane == 0) lds_st<int>(sm, L::FLG, cnt);
+            }
+            __syncthreads();
+            const int nx = lds_ld<int>(sm, L::FLG);
+            const int mypos = fcol ? lds_ld<int>(sm, L::CSL + 4 * colc) : -1;
+            constexpr int A = 4 * 64 * L::NXB;
+            for (int b0 = 0; b0 < nx; b0 += L::NXB) {
+                const int nb = nx - b0 < L::NXB ? nx - b0 : L::NXB;
+                exact_pass<D>(sm, p, t0, len, hk, hv, b0, nb, tid);
+                if (mypos >= b0 && mypos < b0 + nb) {
+                    const int sx = L::RGA + 4 * 64 * (mypos - b0), rx = L::RGC + 4 * 64 * (mypos - b0);
+                    const float Gl = lds_ld<float>(sm, sx + 4 * 63);
+                    for (int u = 0; u < MPW; ++u)
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 16 * (mg + NMG * u) + 4 * q4 + e;
+                            const float Gr = lds_ld<float>(sm, sx + 4 * r);
+                            const float qq = lds_ld<float>(sm, sx + A + 4 * r), kk = lds_ld<float>(sm, sx + 2 * A + 4 * r);
+                            const float bb = lds_ld<float>(sm, sx + 3 * A + 4 * r);
+                            const float al = lds_ld<float>(sm, rx + 4 * r), pi = lds_ld<float>(sm, rx + A + 4 * r);
+                            const float ka = lds_ld<float>(sm, rx + 2 * A + 4 * r);
+                            const int ro = 2 * (r * RK + colc);
+                            const float qh = (float)lds_ld<__bf16>(sm, L::QH + ro), kb = (float)lds_ld<__bf16>(sm, L::KB + ro);
+                            const float kh = (float)lds_ld<__bf16>(sm, L::RR + ro);
+                            const float eg = ex2(Gr), gq = dQH[u][e], gkb = dKB[u][e], dkh = dKH[u][e];
+                            dQH[u][e] = gq * eg + pi;
+                            dKB[u][e] = (gkb * eg + al) * kk;
+                            dRR[u][e] = (gkb * eg + al) * bb + ka + dkh * ex2(Gl - Gr);
+                            dGf[u][e] = gq * qh + gkb * kb + bb * kk * al + qq * pi - kk * ka - dkh * kh;
+                        }
+                }
+                __syncthreads();  // the batch's staging and results are consumed
+            }
+        }
 
         // ---- epilogue. dKH enters as K-hat = RR gamma: dRR += gamma dKH and
         // dgamma += colsum(dKH RR), the latter reduced over the wave's rows
         // (each channel column belongs to one wave) onto rowsum(S_in dS_out).
+        // (A flagged channel: K-hat is the RR column itself, so G_last gets
+        // colsum(dKH RR) with factor 1 and dk its share from the fold.)
         // The decay factors' share of dG pairs each product's gradient with
         // the very bf16 factors that product used, the record's QH, KB and
         // RR: a pair (r, s) adds to dG_r and subtracts from dG_s the same
@@ -503,7 +667,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             for (int u = 0; u < MPW; ++u)
                 for (int e = 0; e < 4; ++e) {
                     part += dKH[u][e] * (float)lds_ld<__bf16>(sm, L::RR + 2 * ((16 * (mg + NMG * u) + 4 * q4 + e) * RK + col));
-                    dRR[u][e] += gc * dKH[u][e];
+                    if (!fcol) dRR[u][e] += gc * dKH[u][e];
                 }
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
@@ -535,8 +699,11 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             ew[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
         }
         if (tid < D) {
-            float dg0 = lds_ld<float>(sm, L::DGM + 4 * tid);
-            for (int m = 0; m < NMG; ++m) dg0 += lds_ld<float>(sm, L::DGP + 4 * (m * D + tid));
+            // G_last's gradient: gamma rowsum(S_in dS_out) + GMU colsum(dKH RR)
+            float cs = 0.0f;
+            for (int m = 0; m < NMG; ++m) cs += lds_ld<float>(sm, L::DGP + 4 * (m * D + tid));
+            const float dg0 = lds_ld<float>(sm, L::DGM + 4 * tid) * lds_ld<float>(sm, L::GAM + 4 * tid) +
+                              cs * lds_ld<float>(sm, L::GMU + 4 * tid);
             lds_st<float>(sm, L::DGM + 4 * tid, dg0);
         }
         for (int u = 0; u < MPW; ++u) {
@@ -545,10 +712,14 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             st_tile_f32(sm, 1 * EF, RF, 16 * mi, 16 * ni, dKB[u], l16, q4);
             st_tile_f32(sm, 2 * EF, RF, 16 * mi, 16 * ni, dRR[u], l16, q4);
         }
-        scan_gcol<D, CT>(sm, 3 * EF, L::XS, -1, gv, tid);
+        scan_gcol<D, CT>(sm, 3 * EF, L::XS, -1, gv, tid, flagged ? L::FLC : -1);
+        // a flagged column's G slot (pitch D, as scan_gcol's) carries its
+        // final dG instead
+        if (fcol)
+            for (int u = 0; u < MPW; ++u) st_tile_f32(sm, 3 * EF, D, 16 * (mg + NMG * u), 16 * ni, dGf[u], l16, q4);
         __syncthreads();
-        // row-parallel: dq, dk, dbeta, and dG (over dQH)
-        const float pn = poison ? __builtin_nanf("") : 1.0f;
+        // row-parallel: dq, dk, dbeta, and dG (over dQH); a flagged channel's
+        // tiles hold its final values
         const bool direct = p.H == p.HV;  // no grouped heads: dq, dk written here
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
@@ -565,13 +736,20 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 f32x8 dq, dk, db;
                 for (int j = 0; j < 8; ++j) {
                     const float G = lds_ld<float>(sm, 3 * EF + 4 * (r * D + c0 + j));
-                    const float eg = ex2(G), ie = ex2(-G);
                     const float gq = lds_ld<float>(sm, 0 * EF + o + 4 * j), gkb = lds_ld<float>(sm, 1 * EF + o + 4 * j);
                     const float grr = lds_ld<float>(sm, 2 * EF + o + 4 * j);
-                    dq[j] = gq * eg * pn;
-                    dk[j] = (gkb * bb[j] * eg + grr * ie) * pn;
-                    db[j] = gkb * kf[j] * eg * pn;
-                    dG[j] = gq * fq[j] + gkb * fk[j] - grr * fr[j];
+                    if (flagged && lds_ld<int>(sm, L::FLC + 4 * (c0 + j)) != 0) {
+                        dq[j] = gq;
+                        db[j] = gkb;
+                        dk[j] = grr;
+                        dG[j] = G;
+                    } else {
+                        const float eg = ex2(G), ie = ex2(-G);
+                        dq[j] = gq * eg;
+                        dk[j] = gkb * bb[j] * eg + grr * ie;
+                        db[j] = gkb * kf[j] * eg;
+                        dG[j] = gq * fq[j] + gkb * fk[j] - grr * fr[j];
+                    }
                 }
                 if (direct) {
                     *reinterpret_cast<bf16x8 *>(p.dq + tk) = f32x8_to_bf16(dq);
@@ -584,7 +762,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 }
                 *reinterpret_cast<bf16x8 *>(p.dbeta + tv) = f32x8_to_bf16(db);
                 // dv = dWV w, dw = dWV v
-                const f32x8 dwv = __builtin_convertvector(lds_ld<bf16x8>(sm, L::DWV + 2 * (r * D + c0)), f32x8) * pn;
+                const f32x8 dwv = __builtin_convertvector(lds_ld<bf16x8>(sm, L::DWV + 2 * (r * D + c0)), f32x8);
                 *reinterpret_cast<bf16x8 *>(p.dv + tv) = f32x8_to_bf16(dwv * __builtin_convertvector(ew[u], f32x8));
                 *reinterpret_cast<bf16x8 *>(p.dw + tv) = f32x8_to_bf16(dwv * __builtin_convertvector(ev[u], f32x8));
             }
@@ -596,14 +774,13 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         // dgamma gamma reaches every row
         {
             const int c = tid % D;
-            rscan_rows<D, CT>(sm, 0, RF, L::XS, lds_ld<float>(sm, L::DGM + 4 * c) * lds_ld<float>(sm, L::GAM + 4 * c), tid);
+            rscan_rows<D, CT>(sm, 0, RF, L::XS, lds_ld<float>(sm, L::DGM + 4 * c), tid);
         }
         __syncthreads();
         for (int e = tid; e < 64 * D / 4; e += CT) {
             const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
             if (r < len)
-                *reinterpret_cast<f32x4 *>(p.dg + ((t0 + r) * p.HV + hv) * D + c0) =
-                    lds_ld<f32x4>(sm, 4 * (r * RF + c0)) * pn;
+                *reinterpret_cast<f32x4 *>(p.dg + ((t0 + r) * p.HV + hv) * D + c0) = lds_ld<f32x4>(sm, 4 * (r * RF + c0));
         }
     }
 }
@@ -618,7 +795,7 @@ struct SL {
     static constexpr int RK = D + 8, RC = 64 + 8;
     static constexpr int TK = 64 * RK * 2, TC = 64 * RC * 2;
     static constexpr int QH = 0, RR = TK, WY = 2 * TK, DO = 3 * TK, PB = 4 * TK, GAM = 4 * TK + TC;
-    static constexpr int SIZE = GAM + 4 * D;
+    static constexpr int SIZE = GAM + 4 * D;  // GAM: the record's gamma, negated in flagged channels
 };
 
 template <int D, bool SPLIT>
@@ -732,14 +909,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
         }
         __syncthreads();
 
-        // dU = scale P^T dO + RR (gamma dS): tokens x this wave's columns.
-        // gamma dS as bf16 operands: k slab ks holds channels
-        // {32 ks + 4 q4 + e} then {32 ks + 16 + 4 q4 + e}; RR is read in
-        // the same channel order.
+        // dU = scale P^T dO + K-hat dS, K-hat = RR gamma (a flagged
+        // channel's RR column holds K-hat itself, with factor 1): tokens x
+        // this wave's columns. K-hat's factor times dS as bf16 operands: k
+        // slab ks holds channels {32 ks + 4 q4 + e} then
+        // {32 ks + 16 + 4 q4 + e}; RR is read in the same channel order.
         bf16x8 gS[NKS][NCT];
         for (int ks = 0; ks < NKS; ++ks) {
-            const f32x4 g0 = lds_ld<f32x4>(sm, L::GAM + 4 * (32 * ks + 4 * q4));
-            const f32x4 g1 = lds_ld<f32x4>(sm, L::GAM + 4 * (32 * ks + 16 + 4 * q4));
+            const f32x4 g0 = khat_factor(lds_ld<f32x4>(sm, L::GAM + 4 * (32 * ks + 4 * q4)));
+            const f32x4 g1 = khat_factor(lds_ld<f32x4>(sm, L::GAM + 4 * (32 * ks + 16 + 4 * q4)));
             for (int jt = 0; jt < NCT; ++jt)
                 gS[ks][jt] = cat4(f32x4_to_bf16(dS[2 * ks][jt] * g0), f32x4_to_bf16(dS[2 * ks + 1][jt] * g1));
         }
@@ -761,7 +939,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
             for (int jt = 0; jt < NCT; ++jt)
                 dUb[ks][jt] = cat4(f32x4_to_bf16(dU[2 * ks][jt]), f32x4_to_bf16(dU[2 * ks + 1][jt]));
         for (int rt = 0; rt < NRT; ++rt) {
-            const f32x4 gr = lds_ld<f32x4>(sm, L::GAM + 4 * (16 * rt + 4 * q4));
+            const f32x4 gr = __builtin_elementwise_abs(lds_ld<f32x4>(sm, L::GAM + 4 * (16 * rt + 4 * q4)));
             for (int jt = 0; jt < NCT; ++jt) {
                 f32x4 acc = tile_mm<true, true>(sm, L::QH, RK, L::DO, RK, 16 * rt, vbase + 16 * jt, 64, f32x4{0, 0, 0, 0},
                                                 l16, q4) * p.scale;

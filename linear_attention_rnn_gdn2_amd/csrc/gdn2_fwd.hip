@@ -93,6 +93,15 @@ __device__ __forceinline__ float io_bits_to_f32(uint16_t b)
 }
 template <typename T8>
 __device__ __forceinline__ f32x8 to_f32x8(T8 x) { return __builtin_convertvector(x, f32x8); }
+// The 16 bits of element j of a vector of eight 16-bit values, taken from
+// its 32-bit words (extracting a 16-bit float element and bit-casting it,
+// inside an unrolled loop, was compiled to the same element for every j).
+template <typename T8>
+__device__ __forceinline__ uint16_t bits16(T8 x, int j)
+{
+    const i32x4 w = __builtin_bit_cast(i32x4, x);
+    return (uint16_t)((uint32_t)w[j >> 1] >> (16 * (j & 1)));
+}
 
 // A float32 4-vector as the sum of two bf16 4-vectors (high part rounded to
 // nearest even, low part the rounded remainder).
@@ -147,7 +156,12 @@ struct Lds {
     static constexpr int VP = V + 8;   // bf16 elements per [token][V] row
     static constexpr int CP = CH + 8;  // bf16 elements per [token][token] row
     static constexpr int AP = CH + 4;  // fp32 elements per [token][token] row
-    static constexpr int NXB = K == 128 ? 16 : 8;  // exact channels per batch
+    static constexpr int NXB = K == 128 ? 16 : 8;  // exact channels per batch (scalar path)
+    // flagged channels on MFMA: slots per key wave, slots, bf16 pitch of an
+    // operand row of XNS slots (bank-spread)
+    static constexpr int XSW = K == 128 ? 8 : 4;
+    static constexpr int XNS = 4 * XSW;
+    static constexpr int XP = XNS + 4;
 
     static constexpr int KB = 0;                                   // beta k 2^G          [64][KP]  E -> WY
     static constexpr int RR = KB + CH * KP * 2;                    // k 2^-G              [64][KP]  E -> AP
@@ -169,10 +183,18 @@ struct Lds {
     static constexpr int XL = XF + K * 4;                          // exact-channel list  [K] int
     static constexpr int FL = XL + K * 4;                          // per key wave: any exact channel [4] int
     static constexpr int XN = FL + 16;                             // exact-channel count int
-    static constexpr int NP = XN + 16;                             // q/k L2 norms: per key wave partial sums of squares [4][64] (q, k) fp32
+    static constexpr int XC = XN + 16;                             // per key wave: flagged-channel count [4] int
+    static constexpr int NP = XC + 16;                             // q/k L2 norms: per key wave partial sums of squares [4][64] (q, k) fp32
     static constexpr int NRM = NP + 4 * CH * 8;                    // q/k L2 norms: reciprocal norms [64] (q, k) fp32  E -> exact AP
-    static constexpr int TOTAL = NRM + CH * 8;
+    static constexpr int XQ = NRM + CH * 8;                        // flagged channels: raw q, k, beta [3][XNS][64] io  E -> B2x
+    static constexpr int TOTAL = XQ + 3 * XNS * CH * 2;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    // flagged channels on MFMA: staged G [XNS][64] fp32 in TB, row-side
+    // operands (224 rows) in the QH buffer of the other parity, column-side
+    // operands (160 rows) in WV
+    static_assert(XNS * CH * 4 <= CH * CP * 2, "staged G in TB");
+    static_assert(224 * XP * 2 <= QH_SZ, "row-side operands in a QH buffer");
+    static_assert(160 * XP * 2 <= WV_SZ, "column-side operands in WV");
 };
 
 // Value-side thread map of the state waves (4 waves over a 64-row x
@@ -639,11 +661,84 @@ __device__ __forceinline__ void wyw_tile(char *sm, int ct, int l16, int q4)
     }
 }
 
-// Whether any key wave flagged an exact channel in this chunk.
-__device__ __forceinline__ bool any_exact(const char *fl)
+// ------------------------------------------------ flagged channels, MFMA --
+// A channel is flagged when its |G| leaves the single-reference range
+// somewhere in the chunk (strong decay). Its share of A and P then uses
+// tile-relative factors. For rows r in row tile i and s in column tile
+// j < i, 2^(G_r - G_s) = 2^(G_r - R_i) 2^(R_i - G_s) with R_i = G at row
+// 16 i - 1 (the end of tile i - 1): since g <= 0 both exponents are <= 0
+// and both factors lie in [0, 1]. For the diagonal tile (i, i) the
+// reference is row 16 i + 7, M_i: each exponent then spans at most 8
+// tokens, within float32 range while every per-token |g| log2 e stays
+// within XSUP. (The burn-gdn2 README's numerical-stability section: the
+// factors stay tile-local, so strong decay cannot overflow them.)
+// Key wave w gives its flagged channels slots XSW w .. XSW w + XSW - 1. In
+// phase E it stages their G (float32, [slot][row] in TB); after B2 it builds
+// the bf16 operands (row side X = beta k or q times 2^(G_r - ref), column
+// side Y = k 2^(ref - G_s)), and after one more barrier every A / P tile
+// adds sum over slots of Y_s X_r on v_mfma_f32_16x16x16_bf16, 16 slots per
+// product. A chunk with more flagged channels in one key wave than it has
+// slots, or with a flagged channel beyond XSUP, takes the scalar per-pair
+// path (exact_ap) instead.
+constexpr float XSUP = 15.0f;
+
+// Operand rows (XP bf16 each). X, in the QH buffer of the other parity:
+// X_off[isP][i - 1][16] for row tiles i = 1..3, X_mid[isP][i][16]. Y, in WV:
+// Y_off for reference i, rows 0 .. 16 i - 1, at 8 (i - 1) i; Y_mid[i][16]
+// at 96.
+__device__ __forceinline__ int xrow_off(int isP, int i) { return 16 * (3 * isP + i - 1); }
+__device__ __forceinline__ int xrow_mid(int isP, int i) { return 96 + 16 * (4 * isP + i); }
+__device__ __forceinline__ int yrow_off(int i) { return 8 * (i - 1) * i; }
+__device__ __forceinline__ int yrow_mid(int i) { return 96 + 16 * i; }
+
+// How the chunk's A and P are formed: 0 single reference only, 1 flagged
+// channels on MFMA, 2 the scalar per-pair path (the key waves' worst). The
+// same for every thread (a scalar, so that the paths are uniform branches).
+__device__ __forceinline__ int chunk_path(const char *fl)
 {
     const i32x4 f = *reinterpret_cast<const i32x4 *>(fl);
-    return (f[0] | f[1] | f[2] | f[3]) != 0;
+    const int a = f[0] > f[1] ? f[0] : f[1], b = f[2] > f[3] ? f[2] : f[3];
+    return __builtin_amdgcn_readfirstlane(a > b ? a : b);
+}
+
+// Bit b: some key wave owning a slot of product batch b (slots 16 b ..
+// 16 b + 15) has a flagged channel.
+template <int K, int V>
+__device__ __forceinline__ int xbatches(const char *sm)
+{
+    using L = Lds<K, V>;
+    const i32x4 c = lds_ld<i32x4>(sm, L::XC);
+    int m = 0;
+    for (int w = 0; w < 4; ++w)
+        if (c[w] > 0) m |= 1 << (w * L::XSW / 16);
+    return __builtin_amdgcn_readfirstlane(m);
+}
+
+// The flagged channels' share of tile (i, j) of A (isP 0) or P (isP 1) in
+// ap_tile's transposed layout, added to acc; xb: byte offset of the X rows.
+template <int K, int V>
+__device__ __forceinline__ f32x4 xtile(const char *sm, int xb, int i, int j, int isP, int nbm, int l16, int q4,
+                                       f32x4 acc)
+{
+    using L = Lds<K, V>;
+    constexpr int XB2 = 2 * L::XP;  // bytes per operand row
+    const int ya = L::WV + XB2 * ((i > j ? yrow_off(i) + 16 * j : yrow_mid(i)) + l16) + 8 * q4;
+    const int xa = xb + XB2 * ((i > j ? xrow_off(isP, i) : xrow_mid(isP, i)) + l16) + 8 * q4;
+    for (int b = 0; b < L::XNS / 16; ++b)
+        if (nbm & (1 << b))
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_ld<bf16x4>(sm, ya + 32 * b), lds_ld<bf16x4>(sm, xa + 32 * b),
+                                                             acc, 0, 0, 0);
+    return acc;
+}
+
+// T's blocks (0, 1) and (2, 3) read as zero by the WY products; thread t of
+// 128 clears 8 bytes (again after TB held staged G).
+template <int K, int V>
+__device__ __forceinline__ void zero_t_upper(char *sm, int t)
+{
+    using L = Lds<K, V>;
+    const int b = t >> 6, rr = (t >> 2) & 15, cc = (t & 3) * 4;
+    lds_st<uint64_t>(sm, L::TB + 2 * ((32 * b + rr) * L::CP + 32 * b + 16 + cc), 0ull);
 }
 
 // Wait for a chunk's raw inputs (the asm consumes the registers).
@@ -680,6 +775,62 @@ __device__ __forceinline__ void norm_partials(const RawChunk<RPT, IO> &R, char *
             sk += __shfl_xor(sk, d);
         }
         if (em.cgl == 0) lds_st<f32x2>(sm, L::NP + 8 * (w * CH + em.row0 + i), f32x2{sq, sk});
+    }
+}
+
+// Flagged channels on MFMA, operand build (key waves, after B2): key wave
+// rw fills its XSW slots, lane = row r: for slot k < cnt (the wave's
+// flagged count) the row-side X (KB and QH forms) and column-side Y factors
+// of every tile row r takes part in, from the G and raw q, k, beta that
+// phase E staged; slots k >= cnt are zero. xb: byte offset of the X rows.
+template <int K, int V, int IO, bool L2N>
+__device__ __forceinline__ void xbuild(char *sm, int cnt, int rw, int r, int xb)
+{
+    using L = Lds<K, V>;
+    constexpr int XSW = L::XSW, XB2 = 2 * L::XP;
+    const int i0 = r >> 4, rl = r & 15;  // row tile, row within it
+    float nq = 1.0f, nk = 1.0f;
+    if constexpr (L2N) {
+        const f32x2 nr = lds_ld<f32x2>(sm, L::NRM + 8 * r);
+        nq = nr[0];
+        nk = nr[1];
+    }
+    const int xo = xb + XB2 * (xrow_off(0, i0 > 0 ? i0 : 1) + rl), xoq = xo + XB2 * 48;  // X_off KB / QH (i0 >= 1)
+    const int xm = xb + XB2 * (xrow_mid(0, i0) + rl), xmq = xm + XB2 * 64;              // X_mid KB / QH
+    const int y1 = L::WV + XB2 * (yrow_off(1) + r), y2 = L::WV + XB2 * (yrow_off(2) + r),
+              y3 = L::WV + XB2 * (yrow_off(3) + r);                                       // Y_off, reference tiles 1..3
+    const int ym = L::WV + XB2 * (yrow_mid(i0) + rl);                                      // Y_mid
+    for (int k = 0; k < XSW; ++k) {
+        const int slot = XSW * rw + k, o = 2 * slot;
+        __bf16 xkb = 0, xqh = 0, mkb = 0, mqh = 0, v1 = 0, v2 = 0, v3 = 0, vm = 0;
+        if (k < cnt) {  // wave-uniform
+            const int gs = L::TB + 4 * CH * slot, qs = L::XQ + 2 * CH * slot;
+            const float Gr = lds_ld<float>(sm, gs + 4 * r), Mi = lds_ld<float>(sm, gs + 4 * (16 * i0 + 7));
+            const float R1 = lds_ld<float>(sm, gs + 4 * 15), R2 = lds_ld<float>(sm, gs + 4 * 31),
+                        R3 = lds_ld<float>(sm, gs + 4 * 47);
+            const float qv = io_bits_to_f32<IO>(lds_ld<uint16_t>(sm, qs + 2 * r)) * nq;
+            const float kv = io_bits_to_f32<IO>(lds_ld<uint16_t>(sm, qs + 2 * L::XNS * CH + 2 * r)) * nk;
+            const float bk = io_bits_to_f32<IO>(lds_ld<uint16_t>(sm, qs + 4 * L::XNS * CH + 2 * r)) * kv;
+            const float e = ex2(Gr - (i0 == 1 ? R1 : i0 == 2 ? R2 : R3)), em = ex2(Gr - Mi);
+            xkb = (__bf16)(bk * e);
+            xqh = (__bf16)(qv * e);
+            mkb = (__bf16)(bk * em);
+            mqh = (__bf16)(qv * em);
+            v1 = (__bf16)(kv * ex2(R1 - Gr));
+            v2 = (__bf16)(kv * ex2(R2 - Gr));
+            v3 = (__bf16)(kv * ex2(R3 - Gr));
+            vm = (__bf16)(kv * ex2(Mi - Gr));
+        }
+        if (i0 >= 1) {
+            lds_st<__bf16>(sm, xo + o, xkb);
+            lds_st<__bf16>(sm, xoq + o, xqh);
+        }
+        lds_st<__bf16>(sm, xm + o, mkb);
+        lds_st<__bf16>(sm, xmq + o, mqh);
+        if (i0 < 1) lds_st<__bf16>(sm, y1 + o, v1);
+        if (i0 < 2) lds_st<__bf16>(sm, y2 + o, v2);
+        if (i0 < 3) lds_st<__bf16>(sm, y3 + o, v3);
+        lds_st<__bf16>(sm, ym + o, vm);
     }
 }
 
@@ -736,6 +887,8 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // KT = k 2^(G_last - G)
         bf16x8 ktr[RPT];
         f32x8 egl;
+        uint32_t wmask = 0;  // flagged channels of this wave (bit 8 cgl + j; wave-uniform)
+        int wcnt = 0;
         if (act) {
             // all of this chunk's raw inputs are complete here: the next
             // chunk's g is issued below, and a later wait for q, k, beta
@@ -746,9 +899,6 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                 const f32x8 gi = decay_row<RPT, IO, G16>(R, i, g_f16);
                 for (int j = 0; j < 8; ++j) G[i][j] = (i ? G[i - 1][j] : 0.0f) + gi[j] * LOG2E;
             }
-            // the next chunk's g (this chunk's is consumed): a whole chunk
-            // period ahead of its use
-            if (it + 1 < nc) load_decay<K, RPT, IO, G16>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
             for (int j = 0; j < 8; ++j) {
                 float incl, tot;
                 wave_scan<M::NCG>(G[RPT - 1][j], lane, incl, tot);
@@ -769,7 +919,43 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                 anyb |= b;
             }
             const bool wx = anyb != 0;  // wave-uniform: any exact channel of this wave
-            if (lane == 0) lds_st<int>(sm, L::FL + 4 * rw, wx ? 1 : 0);
+            // this wave's path: 0 none flagged, 1 flagged channels on MFMA
+            // (G staged in TB), 2 scalar per-pair path (too many flagged
+            // channels for the wave's slots, or one whose per-token decay
+            // exceeds XSUP: G's steps, the first one across lanes)
+            int wst = 0;
+            if (wx) {
+                bool sup = false;
+                for (int j = 0; j < 8; ++j) {
+                    const uint64_t b = __ballot(xf[j]);
+                    for (int g = 0; g < M::NCG; ++g)
+                        if (b & group_lanes<M::NCG>(g)) wmask |= 1u << (8 * g + j);
+                    const float prev = __shfl(G[RPT - 1][j], lane - M::NCG);
+                    float st = fabsf(G[0][j] - (em.rg ? prev : 0.0f));
+                    for (int i = 1; i < RPT; ++i) st = fmaxf(st, fabsf(G[i][j] - G[i - 1][j]));
+                    sup |= xf[j] && !(st <= XSUP);
+                }
+                wcnt = __popc(wmask);
+                wst = (__ballot(sup) != 0 || wcnt > L::XSW) ? 2 : 1;
+            }
+            if (wst == 1)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (xf[j]) {
+                        const int cw = 8 * em.cgl + j;
+                        const int slot = L::XSW * rw + __popc(wmask & ((1u << cw) - 1u));
+                        for (int i = 0; i < RPT; ++i) {
+                            const int r = row0 + i, qs = L::XQ + 2 * (CH * slot + r);
+                            lds_st<float>(sm, L::TB + 4 * (CH * slot + r), G[i][j]);
+                            lds_st<uint16_t>(sm, qs, bits16(R.q[i], j));
+                            lds_st<uint16_t>(sm, qs + 2 * L::XNS * CH, bits16(R.k[i], j));
+                            lds_st<uint16_t>(sm, qs + 4 * L::XNS * CH, bits16(R.b[i], j));
+                        }
+                    }
+            if (lane == 0) {
+                lds_st<int>(sm, L::FL + 4 * rw, wst);
+                lds_st<int>(sm, L::XC + 4 * rw, wcnt);
+            }
             if (em.rg == 0) {
                 lds_st<i32x4>(b_c, L::XF, i32x4{xf[0], xf[1], xf[2], xf[3]});
                 lds_st<i32x4>(b_c, L::XF + 16, i32x4{xf[4], xf[5], xf[6], xf[7]});
@@ -819,7 +1005,19 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
                 lds_st<bf16x8>(b_e, L::RR + i * RK, f32x8_to_bf16(rr));
                 lds_st<bf16x8>(b_e, qb + i * RK, f32x8_to_bf16(qh));
                 ktr[i] = f32x8_to_bf16(kt);
+                // the backward's record: RR, with K-hat in flagged channels
+                if constexpr (REC) {
+                    constexpr PrepRecord PR{K};
+                    f32x8 rk;
+                    for (int j = 0; j < 8; ++j) rk[j] = xf[j] ? kt[j] : rr[j];
+                    *reinterpret_cast<bf16x8 *>(ch.rec + (int64_t)it * p.HV * PR.bytes() + PR.rr() +
+                                                2 * ((row0 + i) * K + c0k)) = f32x8_to_bf16(rk);
+                }
             }
+            // the next chunk's g (this chunk's is consumed): a chunk period
+            // ahead of its use, and issued last, so that no register copy
+            // in this phase targets a load in flight
+            if (it + 1 < nc) load_decay<K, RPT, IO, G16>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
         }
         __syncthreads();  // ------------------------------------------ B2
         if (!act) break;
@@ -836,12 +1034,26 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         }
 
         // ---- AP + T1: A's diagonal tile rw, then its block of T
-        if (!any_exact(sm + L::FL)) {
+        const int path = chunk_path(sm + L::FL);
+        if (path == 0) {
             const char *const b_k8 = sm + l16 * RK + 16 * q4 + rw * 16 * RK;  // rows 16 rw + l16, columns 8q4
             const f32x4 x = ap_mask(ap_tile_at<K>(b_k8 + L::RR, b_k8 + L::KB), true, false, l16, q4);
             lds_st<f32x4>(sm, L::AB + l16 * RA + 16 * q4 + rw * (16 * RA + 64), x);
+        } else if (path == 1) {
+            // flagged channels on MFMA: build their operands, then (after
+            // one more barrier, which the state waves match) add them to the
+            // diagonal tile
+            const int xb = L::QH + ((it + 1) & 1) * L::QH_SZ;
+            xbuild<K, V, IO, L2N>(sm, wcnt, rw, lane, xb);
+            const char *const b_k8 = sm + l16 * RK + 16 * q4 + rw * 16 * RK;
+            const f32x4 x0 = ap_tile_at<K>(b_k8 + L::RR, b_k8 + L::KB);
+            __syncthreads();  // ----------------------------------------- B2x
+            const f32x4 x = ap_mask(xtile<K, V>(sm, xb, rw, rw, 0, xbatches<K, V>(sm), l16, q4, x0), true, false, l16, q4);
+            lds_st<f32x4>(sm, L::AB + l16 * RA + 16 * q4 + rw * (16 * RA + 64), x);
+            if (rt < 128) zero_t_upper<K, V>(sm, rt);  // TB held the staged G
         } else {
             exact_ap<K, V, IO, G16, L2N>(sm, p, ch, c0, len, qb, tid);
+            if (rt < 128) zero_t_upper<K, V>(sm, rt);  // TB may hold staged G
         }
         if (q4 == 0)
             t1_block<K, V>(sm + L::AB + rw * (16 * RA + 64), sm + L::AB + 4 * l16 + rw * (16 * RA + 64),
@@ -862,7 +1074,6 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             constexpr PrepRecord PR{K};
             char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
             rec_tile<K, NROLE>(rc + PR.kb(), sm, L::KB, RK, rt, 0u);
-            rec_tile<K, NROLE>(rc + PR.rr(), sm, L::RR, RK, rt, 0u);
         }
         __syncthreads();  // ------------------------------------------ B4
 
@@ -873,9 +1084,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // this chunk has read the previous ones)
         if constexpr (L2N)
             if (it + 1 < nc) norm_partials<K, V, RPT, IO>(R, sm, rt);
-        // second part: QH, P, T and 2^G_last (NaN when the chunk has a
-        // channel beyond the single-reference bound, whose RR is zero here:
-        // the backward declines such chunks)
+        // second part: QH, P, T and 2^G_last (negated in flagged channels)
         if constexpr (REC) {
             constexpr PrepRecord PR{K};
             char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
@@ -884,11 +1093,55 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             rec_t<NROLE>(rc + PR.t(), sm, L::TB, RC, rt);
             if (rt < K / 4) {
                 const f32x4 gm = lds_ld<f32x4>(sm, L::GAM + 16 * rt);
-                const float nan = __builtin_nanf("");
-                *reinterpret_cast<f32x4 *>(rc + PR.gam() + 16 * rt) = any_exact(sm + L::FL) ? f32x4{nan, nan, nan, nan} : gm;
+                const i32x4 xf = lds_ld<i32x4>(sm, L::XF + 16 * rt);
+                f32x4 gs;
+                for (int e = 0; e < 4; ++e) gs[e] = xf[e] ? -gm[e] : gm[e];
+                *reinterpret_cast<f32x4 *>(rc + PR.gam() + 16 * rt) = gs;
             }
         }
         __syncthreads();  // ------------------------------------------ B5
+    }
+}
+
+// Phase AP of a state wave: its four tiles (t = 4 + rw + 4 m) of A and P
+// from the single-reference operands. Every operand read of the four tiles
+// is issued before the first product, so that their LDS round trips overlap
+// and the four accumulation chains interleave.
+template <int K, int V>
+__device__ __forceinline__ void state_ap_tiles(const char *sm, int o_k8, int it, int rw, f32x4 (&acc)[4])
+{
+    using L = Lds<K, V>;
+    constexpr int RK = 2 * L::KP;
+    const char *const b_k8 = sm + o_k8;
+    const int xq = L::QH + (it & 1) * L::QH_SZ;  // QH of this chunk for P tiles
+    bf16x8 ra[4][K / 32], xa[4][K / 32];
+    for (int m = 0; m < 4; ++m) {
+        const int t = 4 + rw + 4 * m;
+        const int i = tile_i(t), j = tile_j(t);
+        const int xo = (t >= 10 ? xq : L::KB) + 16 * i * RK;
+        for (int ks = 0; ks < K / 32; ++ks) {
+            ra[m][ks] = lds_ld<bf16x8>(b_k8, L::RR + 16 * j * RK + 64 * ks);
+            xa[m][ks] = lds_ld<bf16x8>(b_k8, xo + 64 * ks);
+        }
+    }
+    for (int m = 0; m < 4; ++m) acc[m] = f32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < K / 32; ++ks)
+        for (int m = 0; m < 4; ++m) acc[m] = mfma_bf16(ra[m][ks], xa[m][ks], acc[m]);
+}
+
+// The causal part of the four tiles: A as float32 into AB, P as bf16 into PB.
+template <int K, int V>
+__device__ __forceinline__ void state_ap_store(char *sm, const f32x4 (&acc)[4], int rw, int o_c4, int o_a4, int l16, int q4)
+{
+    using L = Lds<K, V>;
+    constexpr int RC = 2 * L::CP, RA = 4 * L::AP;
+    for (int m = 0; m < 4; ++m) {
+        const int t = 4 + rw + 4 * m;
+        const int i = tile_i(t), j = tile_j(t);
+        const bool isP = t >= 10;
+        const f32x4 x = ap_mask(acc[m], i == j, isP, l16, q4);
+        if (isP) lds_st<bf16x4>(sm, L::PB + o_c4 + 16 * i * RC + 32 * j, f32x4_to_bf16(x));
+        else lds_st<f32x4>(sm, L::AB + o_a4 + 16 * i * RA + 64 * j, x);
     }
 }
 
@@ -1056,39 +1309,31 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         if (!act) break;
 
         // ---- AP: the 16 tiles that are not A's diagonal, four per state
-        // wave. Every operand read of the four tiles is issued before the
-        // first product, so that their LDS round trips overlap and the four
-        // accumulation chains interleave.
-        if (!any_exact(sm + L::FL)) {
-            const char *const b_k8 = sm + o_k8;
-            const int xq = L::QH + (it & 1) * L::QH_SZ;  // QH of this chunk for P tiles
-            bf16x8 ra[4][K / 32], xa[4][K / 32];
-            for (int m = 0; m < 4; ++m) {
-                const int t = 4 + rw + 4 * m;
-                const int i = tile_i(t), j = tile_j(t);
-                const int xo = (t >= 10 ? xq : L::KB) + 16 * i * RK;
-                for (int ks = 0; ks < K / 32; ++ks) {
-                    ra[m][ks] = lds_ld<bf16x8>(b_k8, L::RR + 16 * j * RK + 64 * ks);
-                    xa[m][ks] = lds_ld<bf16x8>(b_k8, xo + 64 * ks);
-                }
-            }
+        // wave
+        const int path = chunk_path(sm + L::FL);
+        if (path == 0) {
             f32x4 acc[4];
-            for (int m = 0; m < 4; ++m) acc[m] = f32x4{0, 0, 0, 0};
-            for (int ks = 0; ks < K / 32; ++ks)
-                for (int m = 0; m < 4; ++m) acc[m] = mfma_bf16(ra[m][ks], xa[m][ks], acc[m]);
+            state_ap_tiles<K, V>(sm, o_k8, it, rw, acc);
+            state_ap_store<K, V>(sm, acc, rw, o_c4, o_a4, l16, q4);
+        } else if (path == 1) {
+            // the flagged channels' share, once the key waves have built
+            // their operands (a block of its own, so that the single-
+            // reference block above compiles as if it were alone)
+            f32x4 acc[4];
+            state_ap_tiles<K, V>(sm, o_k8, it, rw, acc);
+            __syncthreads();  // ----------------------------------------- B2x
+            const int xb = L::QH + ((it + 1) & 1) * L::QH_SZ, nbm = xbatches<K, V>(sm);
             for (int m = 0; m < 4; ++m) {
                 const int t = 4 + rw + 4 * m;
-                const int i = tile_i(t), j = tile_j(t);
-                const bool isP = t >= 10;
-                const f32x4 x = ap_mask(acc[m], i == j, isP, l16, q4);
-                if (isP) lds_st<bf16x4>(sm, L::PB + o_c4 + 16 * i * RC + 32 * j, f32x4_to_bf16(x));
-                else lds_st<f32x4>(sm, L::AB + o_a4 + 16 * i * RA + 64 * j, x);
+                acc[m] = xtile<K, V>(sm, xb, tile_i(t), tile_j(t), t >= 10 ? 1 : 0, nbm, l16, q4, acc[m]);
             }
+            state_ap_store<K, V>(sm, acc, rw, o_c4, o_a4, l16, q4);
         } else {
             exact_ap<K, V, IO, G16, L2N>(sm, p, ch, c0, len, L::QH + (it & 1) * L::QH_SZ, tid);
         }
-        // w v of this chunk, row-major
-        {
+        // w v of this chunk, row-major (with flagged channels on MFMA, WV
+        // holds their column-side operands until B3: stored after it)
+        if (path != 1) {
             char *const b_wv = sm + emv.row0 * RV + 2 * emv.c0;
             for (int i = 0; i < RPTV; ++i) {
                 const f32x8 wv = to_f32x8(vr[i]) * to_f32x8(wr[i]);
@@ -1096,6 +1341,13 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             }
         }
         __syncthreads();  // ------------------------------------------ B3
+        if (path == 1) {
+            char *const b_wv = sm + emv.row0 * RV + 2 * emv.c0;
+            for (int i = 0; i < RPTV; ++i) {
+                const f32x8 wv = to_f32x8(vr[i]) * to_f32x8(wr[i]);
+                lds_st<bf16x8>(b_wv, L::WV + i * RV, f32x8_to_bf16(wv));
+            }
+        }
 
         // ---- T2: block column j = rw of T,
         // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, i = j+1..3, on bf16 MFMA

@@ -95,7 +95,11 @@ struct BwdParams {
 // Byte offsets of one chunk's record in BwdParams::prep (K = V = D): the
 // chunk's WY quantities as the forward with checkpoints computed them, read
 // by the state-gradient and gradient passes. QH, RR, wy_w, KB as bf16 [64][D],
-// P, T as bf16 [64][64], 2^G_last as float32 [D].
+// P, T as bf16 [64][64], and gamma = 2^G_last as float32 [D] with the sign
+// bit set (-gamma, -0.0 when it underflows) for a flagged channel: strong
+// decay, where k 2^-G would overflow, so that the channel's RR column holds
+// the exact K-hat = k 2^(G_last - G) instead of RR (K-hat = RR gamma
+// elsewhere).
 struct PrepRecord {
     int D;
     __host__ __device__ constexpr int qh() const { return 0; }

@@ -127,10 +127,11 @@ def test_fp16_io(lib, c_oracle, path, K, H, HV):
 
 @pytest.mark.parametrize("path", ["chunk", "split", "rec"])
 @pytest.mark.parametrize("gt", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("g_ext", [0.0, 300.0])
+@pytest.mark.parametrize("g_ext", [0.0, 8.0, 300.0])
 def test_16bit_decay(lib, c_oracle, path, gt, g_ext):
-    """g in bf16 or fp16, with and without extreme-decay channels (the exact
-    per-pair path reads g too); the oracle reads the rounded g."""
+    """g in bf16 or fp16, with and without extreme-decay channels (8: their
+    share of A and P on MFMA from the staged decay sums; 300: the scalar
+    per-pair path, which reads g again); the oracle reads the rounded g."""
     d = synth(LENS if path != "rec" else [1, 5, 0, 33], 2, 2, 128, 128, seed=204, init_std=0.02,
               g_extreme_max=g_ext, extreme_frac=0.1 if g_ext else 0.0, beta_max=2.0)
     d["g"] = d["g"].to(gt)
@@ -162,9 +163,11 @@ def test_qk_l2norm(lib, c_oracle, path, K, H, HV):
     assert_parity(f"l2norm {path}", out, fin, ro, rs)
 
 
-def test_qk_l2norm_extreme_decay(lib, c_oracle):
-    """L2 normalisation together with the exact per-pair path."""
-    d = unnormalised(synth([500, 64, 130], 2, 2, 128, 128, seed=206, init_std=0.02, g_extreme_max=300.0,
+@pytest.mark.parametrize("g_ext", [8.0, 300.0])
+def test_qk_l2norm_extreme_decay(lib, c_oracle, g_ext):
+    """L2 normalisation together with both extreme-decay paths (the flagged
+    channels' operands take the normalised q and k)."""
+    d = unnormalised(synth([500, 64, 130], 2, 2, 128, 128, seed=206, init_std=0.02, g_extreme_max=g_ext,
                            extreme_frac=0.1, beta_max=2.0), 8)
     for path in ("chunk", "split"):
         out, fin = call(lib, path, dev(d), d, qk_l2norm=True)

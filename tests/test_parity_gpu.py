@@ -177,17 +177,36 @@ def test_all_sequences_empty(lib):
     assert torch.equal(fin[0].cpu(), torch.zeros_like(fin[0].cpu()))
 
 
-@pytest.mark.parametrize("g_ext", [8.0, 40.0, 300.0])
-def test_extreme_decay(lib, c_oracle, g_ext):
-    """Per-channel extreme decay with beta up to 2. g_ext = 8 stays on the
-    factored fast path; 40 and 300 push 8-token half-tiles past 64 in log
-    decay and take the exact per-pair path."""
-    say(f"[extreme decay] g_ext={g_ext}")
-    d = synth([500, 64, 130], 2, 2, 128, 128, seed=105, init_std=0.02, g_max=0.1,
-              g_extreme_max=g_ext, extreme_frac=0.1, beta_max=2.0)
+@pytest.mark.parametrize("g_ext,frac,K", [(8.0, 0.1, 128), (8.0, 0.1, 64), (8.0, 0.5, 128), (40.0, 0.1, 128),
+                                          (300.0, 0.1, 128)])
+def test_extreme_decay(lib, c_oracle, g_ext, frac, K):
+    """Per-channel extreme decay with beta up to 2. With g_ext = 8 on 10% of
+    the channels the flagged channels' share of A and P runs on MFMA with
+    tile-relative factors; half the channels flagged overflows the key
+    waves' slots and g_ext = 40 or 300 exceeds the per-token bound of the
+    diagonal tiles' midpoint factors: both take the scalar per-pair path."""
+    say(f"[extreme decay] g_ext={g_ext} frac={frac} K={K}")
+    d = synth([500, 64, 130], 2, 2, K, K, seed=105, init_std=0.02, g_max=0.1,
+              g_extreme_max=g_ext, extreme_frac=frac, beta_max=2.0)
     out, fin = run_gpu(lib, d)
     ro, rs = ref(c_oracle, d)
-    assert_parity(f"extreme decay {g_ext}", out, fin, ro, rs)
+    assert_parity(f"extreme decay {g_ext} {frac} K={K}", out, fin, ro, rs)
+
+
+def test_extreme_decay_one_key_wave(lib, c_oracle):
+    """Flagged channels all among the first 32 key channels (one key wave's
+    share): the other waves' slots are zero and one MFMA batch is empty.
+    Also every channel at g = -3 per token in one sequence (all flagged)."""
+    d = synth([300, 200], 2, 4, 128, 128, seed=111, init_std=0.02, beta_max=2.0)
+    gen = torch.Generator().manual_seed(5)
+    d["g"][:, :, 3:9] = -8.0 * torch.rand(d["g"][:, :, 3:9].shape, generator=gen)
+    out, fin = run_gpu(lib, d)
+    ro, rs = ref(c_oracle, d)
+    assert_parity("flagged channels 3..8", out, fin, ro, rs)
+    d["g"][300:] = -3.0
+    out, fin = run_gpu(lib, d)
+    ro, rs = ref(c_oracle, d)
+    assert_parity("every channel at g = -3 in sequence 1", out, fin, ro, rs)
 
 
 def test_packed_equals_separate_bitwise(lib):
