@@ -421,7 +421,11 @@ __device__ __forceinline__ void rec_t(char *dst, const char *sm, int lo, int lp,
     }
 }
 
-__device__ __forceinline__ int chunk_len(int64_t c0, int64_t te) { return (int)((te - c0) < CH ? (te - c0) : CH); }
+// Valid rows of the chunk starting at token c0 (0 past the end).
+__device__ __forceinline__ int chunk_len(int64_t c0, int64_t te)
+{
+    return (int)(te - c0 <= 0 ? 0 : te - c0 < CH ? te - c0 : CH);
+}
 
 // --------------------------------------------------------------- phase AP --
 // One 16x16 tile of A (X = KB) or P (X = QH), computed transposed:
@@ -1016,8 +1020,11 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
             }
             // the next chunk's g (this chunk's is consumed): a chunk period
             // ahead of its use, and issued last, so that no register copy
-            // in this phase targets a load in flight
-            if (it + 1 < nc) load_decay<K, RPT, IO, G16>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
+            // in this phase targets a load in flight. Issued past the last
+            // chunk too, with an empty range (no memory access): an
+            // unconditional load leaves the register allocator no value to
+            // merge at the loop head
+            load_decay<K, RPT, IO, G16>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hv, row0, c0k);
         }
         __syncthreads();  // ------------------------------------------ B2
         if (!act) break;
@@ -1064,11 +1071,7 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // while the state waves build T's off-diagonal blocks (the issue
         // stalls until the CU's memory pipeline has room); WY and the next
         // phase E hide the latency
-        if (it + 1 < nc) {
-            load_keys<K, RPT, IO>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);
-        } else {
-            R = RawChunk<RPT, IO>{};  // ends the live range of this chunk's values here
-        }
+        load_keys<K, RPT, IO>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);  // empty range past the end
         // the backward's record of this chunk, first part: KB, RR
         if constexpr (REC) {
             constexpr PrepRecord PR{K};
@@ -1253,9 +1256,11 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         }
 
         // this chunk's v and w (stored as w v after B2; the latency hides
-        // behind the rest of phase S, AP and T1)
+        // behind the rest of phase S, AP and T1); past the last chunk an
+        // empty range (no memory access), so that the loads are
+        // unconditional
         typename IoT<IO>::v8 vr[RPTV], wr[RPTV];
-        if (act) load_values<V, RPTV, IO>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0, ch.zero_v);
+        load_values<V, RPTV, IO>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0, ch.zero_v);
 
         // ---- S, second half: the output, computed transposed,
         // O^T = scale (S^T QH^T + U^T P^T), stored as 4 consecutive values
