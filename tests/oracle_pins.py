@@ -287,6 +287,22 @@ def pin_defaults(fn):
         _close(got[1], base[1], 1e-14, "defaults state")
 
 
+def pin_default_scale_key_dim(fn):
+    """The default scale is 1/sqrt(K), K the q/k head dimension, also when
+    the value dimension differs (FlashInfer docs, ``scale``: one over the
+    square root of the head size of the q.k product). Pinned through the
+    retrieval identity, not the formula: with beta = 1, unit k and q = k
+    the delta rule returns exactly scale * w * v, so the output's magnitude
+    shows the scale used: 1/4 at (K, V) = (16, 4), 1/2 at (4, 16)."""
+    for K, V, want in ((16, 4, 0.25), (4, 16, 0.5)):
+        q, k, v, g, beta, w, S0 = _rand_case(28, T=11, H=1, HV=1, K=K, V=V, g_max=1.0)
+        ones = np.ones_like(beta)
+        for sc in (None, 0.0):
+            o, S = fn(k, k, v, g, ones, w, sc, S0)
+            assert S.shape == (1, 1, K, V), f"state shape {S.shape} at (K, V) = ({K}, {V})"
+            _close(o, want * w * v, TOL, f"default scale at (K, V) = ({K}, {V})")
+
+
 def pin_varlen(fn):
     """Packed sequences == separate calls, each from its own initial state; an
     empty sequence returns its initial state."""
@@ -337,7 +353,7 @@ def pin_qk_l2norm(fn):
     assert np.all(np.isfinite(o4)) and np.all(o4[5] == 0.0), "l2norm zero row"
 
 
-ALL_PINS = [pin_hand_worked, pin_matrix_form, pin_retrieval, pin_linear_attention,
+ALL_PINS = [pin_hand_worked, pin_matrix_form, pin_retrieval, pin_default_scale_key_dim, pin_linear_attention,
             pin_gated_linear_attention, pin_scalar_gdn, pin_wy_solve, pin_split_carry,
             pin_linearity, pin_key_permutation, pin_value_permutation, pin_heads_and_gva,
             pin_single_token, pin_defaults, pin_varlen, pin_qk_l2norm]

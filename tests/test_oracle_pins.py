@@ -130,6 +130,19 @@ def test_wrong_gva_mapping_is_caught():
         pins.pin_heads_and_gva(wrong)
 
 
+def test_default_scale_from_value_dim_is_caught(monkeypatch):
+    """A default scale taken from the value dimension (1/sqrt(V)) fails the
+    default-scale pin."""
+    real = rec.resolve_scale
+
+    def wrong(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None,
+              cu_seqlens=None, heads=None):
+        sc = real(scale, v.shape[2])
+        return gdn2_recurrence(q, k, v, g, beta, w, sc, initial_state, cu_seqlens, heads)
+    with pytest.raises(AssertionError):
+        pins.pin_default_scale_key_dim(wrong)
+
+
 def _wrong_norm(kind):
     def norm(x, eps=1e-12):
         x = rec._f64(x)
