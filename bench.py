@@ -72,18 +72,34 @@ def measured_traffic(src_hash: str, launches_per_profile: int = 1):
     return rec.get("hbm_bytes_per_launch")
 
 
+# SQ counter passes (each within one run's hardware limits: at most 8 SQ,
+# 2 TA and 2 GRBM counters; the derived ones are rocprofv3's own formulas:
+# MfmaUtil = MFMA busy cycles / (GPU cycles x SIMDs), VALUBusy = VALU active
+# cycles / (CUs x GPU cycles), LDSBankConflict = bank-conflict stall cycles /
+# (GPU cycles x CUs), LdsUtil = indexed-LDS active cycles / (GPU cycles x CUs))
+SQ_PASSES = {
+    "sq1": "MfmaUtil VALUBusy SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32",
+    "sq2": "LDSBankConflict LdsUtil SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES",
+    "sq3": "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_WAVES SQ_INSTS_VMEM_RD TA_BUSY_avr TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+}
+_Q = "--no-cpu-baseline --no-peaks --no-extra"
 PROFILE_STEPS = {
     # name: (rocprofv3 options, bench.py options)
-    "kt": ("--kernel-trace --stats", "--steps 10 --warmup 2 --no-cpu-baseline --no-peaks"),
-    "pmc_fetch": ("--pmc FETCH_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
-    "pmc_write": ("--pmc WRITE_SIZE", "--steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
+    "kt": ("--kernel-trace --stats", f"--steps 10 --warmup 2 {_Q}"),
+    "pmc_fetch": ("--pmc FETCH_SIZE", f"--steps 2 --warmup 1 {_Q}"),
+    "pmc_write": ("--pmc WRITE_SIZE", f"--steps 2 --warmup 1 {_Q}"),
     "cal_fetch": ("--pmc FETCH_SIZE", "--copy-probe-mib 1024"),
     "cal_write": ("--pmc WRITE_SIZE", "--copy-probe-mib 1024"),
+    **{n: (f"--pmc {c}", f"--steps 2 --warmup 1 {_Q}") for n, c in SQ_PASSES.items()},
+    "kt4": ("--kernel-trace --stats", f"--workload 4 --steps 5 --warmup 1 {_Q}"),
+    **{n + "_4": (f"--pmc {c}", f"--workload 4 --steps 1 --warmup 1 {_Q}") for n, c in SQ_PASSES.items()},
     "bkt": ("--kernel-trace --stats", "--mode bwd --steps 5 --warmup 1"),
-    "bpmc_fetch": ("--pmc FETCH_SIZE", "--mode bwd --steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
-    "bpmc_write": ("--pmc WRITE_SIZE", "--mode bwd --steps 2 --warmup 1 --no-cpu-baseline --no-peaks"),
+    "bpmc_fetch": ("--pmc FETCH_SIZE", f"--mode bwd --steps 2 --warmup 1 {_Q}"),
+    "bpmc_write": ("--pmc WRITE_SIZE", f"--mode bwd --steps 2 --warmup 1 {_Q}"),
+    **{"b" + n: (f"--pmc {c}", f"--mode bwd --steps 2 --warmup 1 {_Q}") for n, c in SQ_PASSES.items()},
 }
 KERNEL_TAG = "chunk_fwd_kernel"
+CU_NUM, SIMD_NUM = 256, 1024  # MI355X
 
 
 PROFILE_DIR = "profile_out"  # where the profile runs write their CSVs (git-ignored)
@@ -113,24 +129,116 @@ def _find(dirpath, suffix):
     raise FileNotFoundError(f"no *{suffix} under {dirpath}")
 
 
-def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
+def _stats_lines(outdir, name):
+    rows = _csv_rows(_find(os.path.join(outdir, name), "_kernel_stats.csv"))
+    out = [f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
+    for r in rows:
+        out.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
+                   f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {_short(r['Name'])}")
+    return out
+
+
+def _resource_lines(outdir, name, want):
+    """Per-kernel resources from the kernel trace: VGPRs (arch + accumulation),
+    SGPRs, LDS bytes per workgroup, scratch, workgroup and grid size."""
+    try:
+        rows = _csv_rows(_find(os.path.join(outdir, name), "_kernel_trace.csv"))
+    except FileNotFoundError:
+        return ["(no kernel trace CSV)"]
+    cols = [("VGPR_Count", "VGPR"), ("Arch_VGPR_Count", "VGPR"), ("Accum_VGPR_Count", "AGPR"),
+            ("SGPR_Count", "SGPR"), ("LDS_Block_Size", "LDS B"), ("Scratch_Size", "scratch"),
+            ("Workgroup_Size_X", "WG"), ("Workgroup_Size", "WG"), ("Grid_Size_X", "grid"), ("Grid_Size", "grid")]
+    have = [(c, h) for c, h in cols if rows and c in rows[0]]
+    seen, out = set(), ["VGPR as rocprofv3 prints it: its granule count times 4; gfx950 allocates 8 VGPRs per "
+                        "granule, so the allocation is twice this figure (the compiler's resource remark for the "
+                        "forward kernel: 246 VGPRs, allocated 248)", "",
+                        "  ".join(f"{h:>9}" for _, h in have) + "  kernel"]
+    for r in rows:
+        if not want(r["Kernel_Name"]) or r["Kernel_Name"] in seen:
+            continue
+        seen.add(r["Kernel_Name"])
+        out.append("  ".join(f"{r[c]:>9}" for c, _ in have) + "  " + _short(r["Kernel_Name"]))
+    return out
+
+
+def _counter_means(outdir, names, want):
+    """{(kernel, grid size): {counter: mean over its dispatches}} from the
+    counter CSVs of the runs ``names``, and each one's mean duration (ns) in
+    those runs."""
+    vals, dur = {}, {}
+    for name in names:
+        d = os.path.join(outdir, name)
+        if not os.path.isdir(d):
+            continue
+        for r in _csv_rows(_find(d, "_counter_collection.csv")):
+            if not want(r["Kernel_Name"]):
+                continue
+            # one launch shape per key: a split run's transition pass (two
+            # walks per segment) and output pass share the kernel
+            k = (r["Kernel_Name"], int(r.get("Grid_Size") or 0))
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if "End_Timestamp" in r and "Start_Timestamp" in r:
+                dur.setdefault(k, {})[(name, r.get("Dispatch_Id"))] = \
+                    float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    means = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    durs = {k: sum(v.values()) / len(v) for k, v in dur.items()}
+    return means, durs
+
+
+def _sq_lines(outdir, prefix, suffix, want, chunk_heads, title):
+    """The SQ counter passes of one workload, per kernel: rocprofv3's derived
+    utilisations, and instruction counts per (64-token chunk, value head)
+    summed over the workgroup's waves."""
+    names = [prefix + n + suffix for n in SQ_PASSES]
+    if not all(os.path.isdir(os.path.join(outdir, n)) for n in names):
+        return []
+    means, durs = _counter_means(outdir, names, want)
+    cmds = [profile_command(n) for n in names]
+    out = ["", f"## SQ counters per launch ({title}; rocprofv3 --pmc, three passes)", "", "commands:"]
+    out += ["  " + c for c in cmds]
+    out += ["", f"per chunk-head: divided by the {chunk_heads} (64-token chunk, value head) pairs of one call", ""]
+    for k, c in sorted(means.items()):
+        g = lambda n: c.get(n, float("nan"))
+        ch = chunk_heads
+        out.append(_short(k[0]) + (f"  [grid {k[1]} threads]" if k[1] else ""))
+        dur = durs.get(k)
+        if dur:
+            out.append(f"  mean dispatch {dur/1e3:.1f} us in the counter runs")
+        out.append(f"  MFMA busy (MfmaUtil) {g('MfmaUtil'):.1f} %   VALU busy (VALUBusy) {g('VALUBusy'):.1f} %   "
+                   f"MFMA/VALU co-issue cycles {g('SQ_VALU_MFMA_COEXEC_CYCLES')/ch:.0f} per chunk-head")
+        out.append(f"  LDS: bank-conflict stall (LDSBankConflict) {g('LDSBankConflict'):.2f} %, "
+                   f"busy (LdsUtil) {g('LdsUtil'):.1f} %, wait for LDS issue {g('SQ_WAIT_INST_LDS')*4/ch:.0f} "
+                   f"wave-cycles per chunk-head")
+        out.append(f"  TA busy {g('TA_BUSY_avr'):.0f} cycles (mean over TA instances), address path stalled by "
+                   f"TC {g('TA_ADDR_STALLED_BY_TC_CYCLES_sum'):.0f} cycles (sum)")
+        out.append(f"  instructions per chunk-head: VALU {g('SQ_INSTS_VALU')/ch:.0f} (transcendental f32 "
+                   f"{g('SQ_INSTS_VALU_TRANS_F32')/ch:.0f}), MFMA {g('SQ_INSTS_MFMA')/ch:.0f}, LDS "
+                   f"{g('SQ_INSTS_LDS')/ch:.0f}, vector-memory reads {g('SQ_INSTS_VMEM_RD')/ch:.0f}")
+        out.append(f"  waves {g('SQ_WAVES'):.0f}; wave-cycles waiting for issue {g('SQ_WAIT_INST_ANY')*4/ch:.0f}, "
+                   f"active on any instruction {g('SQ_ACTIVE_INST_ANY')/ch:.0f} per chunk-head")
+    return out
+
+
+def _chunk_heads(config_id: int) -> int:
+    from linear_attention_rnn_gdn2_amd.workloads import WORKLOADS, lengths_of
+    return sum((n + 63) // 64 for n in lengths_of(config_id)) * WORKLOADS[config_id].HV
+
+
+def summarize_profiles(outdir: str, dest: str | None = None):
     """Turn the rocprofv3 CSVs of the PROFILE_STEPS runs under ``outdir`` into
-    the committed text summaries: the kernel-trace statistics, and the HBM
-    bytes per launch of the forward kernel from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by the same counter's reading for a plain
-    device copy of 1 GiB (so that bytes per KiB-unit are calibrated, not
-    assumed). The summaries go to ``dest`` (default: profiles/)."""
+    the committed text summaries, each headed by the hash of the sources it
+    was taken on: per forward workload the kernel-trace statistics, the
+    kernel's resources and its SQ counters, plus (varlen) the HBM bytes per
+    launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the
+    same counter's reading for a plain device copy of 1 GiB (so that bytes
+    per KiB-unit are calibrated, not assumed); the same for every backward
+    kernel. The summaries go to ``dest`` (default: profiles/)."""
     dest = dest or os.path.join(ROOT, "profiles")
     traffic_file = os.path.join(dest, os.path.basename(TRAFFIC_FILE))
     src_hash = kernel_source_hash()
-    stats = _csv_rows(_find(os.path.join(outdir, "kt"), "_kernel_stats.csv"))
-    lines = [f"# rocprofv3 kernel-trace statistics: GDN-2 forward, {tag}", "",
-             f"kernel source hash (sha256 over csrc/{', '.join(FWD_KERNEL_SOURCES)}, first 16 hex): {src_hash}",
-             "command (from the repository root):", "  " + profile_command("kt"), "",
-             f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
-    for r in stats:
-        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
-                     f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {_short(r['Name'])}")
+    head = f"kernel source hash (sha256 over csrc/{', '.join(FWD_KERNEL_SOURCES)}, first 16 hex): {src_hash}"
+    fwd = lambda n: KERNEL_TAG in n
+    ours = lambda n: "gdn2::" in n
 
     def counter(name, want_kernel, value_min=0.0):
         rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
@@ -140,13 +248,18 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
             raise ValueError(f"{name}: no matching dispatch")
         return vals
 
-    fwd = lambda n: KERNEL_TAG in n
     copy = lambda n: "copyBuffer" in n
     copy_bytes = 1024 * (1 << 20)
     cal_f = max(counter("cal_fetch", copy))
     cal_w = max(counter("cal_write", copy))
     fetch_scale = copy_bytes / (cal_f * 1024)  # bytes per counted byte
     write_scale = copy_bytes / (cal_w * 1024)
+
+    # forward, varlen H32 D128 (the headline workload)
+    lines = [f"# rocprofv3 summary: GDN-2 forward (chunk_fwd_kernel), varlen H32 D128", "", head, "",
+             "## kernel-trace statistics", "", "command (from the repository root):",
+             "  " + profile_command("kt"), ""] + _stats_lines(outdir, "kt")
+    lines += ["", "## resources (kernel trace)", ""] + _resource_lines(outdir, "kt", ours)
     kf = counter("pmc_fetch", fwd)
     kw = counter("pmc_write", fwd)
     fetch = sum(kf) / len(kf) * 1024 * fetch_scale
@@ -159,8 +272,8 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
               f"forward kernel: FETCH_SIZE {sum(kf)/len(kf):.1f} KiB/dispatch ({len(kf)} dispatches), "
               f"WRITE_SIZE {sum(kw)/len(kw):.1f} KiB/dispatch ({len(kw)} dispatches)",
               f"  -> HBM read {fetch/1e6:.2f} MB, write {write/1e6:.2f} MB, total {(fetch+write)/1e6:.2f} MB per launch"]
-    txt = os.path.join(dest, f"{KERNEL_TAG}_{tag}.txt")
-    with open(txt, "w") as f:
+    lines += _sq_lines(outdir, "", "", fwd, _chunk_heads(2), "varlen")
+    with open(os.path.join(dest, f"{KERNEL_TAG}_varlen_h32_d128.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(traffic_file, "w") as f:
         json.dump({"kernel_source_hash": src_hash, "hbm_bytes_per_launch": fetch + write,
@@ -170,22 +283,30 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
                   f, indent=1)
         f.write("\n")
     log("\n".join(lines))
-    bdir = os.path.join(outdir, "bkt")
-    if os.path.isdir(bdir):
-        rows = _csv_rows(_find(bdir, "_kernel_stats.csv"))
-        bl = [f"# rocprofv3 kernel-trace statistics: GDN-2 backward (gdn2_chunk_bwd), {tag}", "",
-              "command (from the repository root):", "  " + profile_command("bkt"), "",
-              f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'share %':>8}  kernel"]
-        for r in rows:
-            bl.append(f"{int(r['Calls']):>6} {float(r['AverageNs'])/1e3:>10.1f} {float(r['MinNs'])/1e3:>10.1f} "
-                      f"{float(r['MaxNs'])/1e3:>10.1f} {float(r['Percentage']):>8.2f}  {_short(r['Name'])}")
+
+    # forward, long_decay H16 D128 (strong decay: flagged channels in every chunk)
+    if os.path.isdir(os.path.join(outdir, "kt4")):
+        l4 = [f"# rocprofv3 summary: GDN-2 forward, long_decay H16 D128 (split walk)", "", head, "",
+              "## kernel-trace statistics", "", "command (from the repository root):",
+              "  " + profile_command("kt4"), ""] + _stats_lines(outdir, "kt4")
+        l4 += ["", "## resources (kernel trace)", ""] + _resource_lines(outdir, "kt4", ours)
+        l4 += _sq_lines(outdir, "", "_4", ours, _chunk_heads(4), "long_decay")
+        with open(os.path.join(dest, f"{KERNEL_TAG}_long_decay_h16_d128.txt"), "w") as f:
+            f.write("\n".join(l4) + "\n")
+        log("\n".join(l4))
+
+    # backward, varlen
+    if os.path.isdir(os.path.join(outdir, "bkt")):
+        bl = [f"# rocprofv3 summary: GDN-2 backward (gdn2_chunk_bwd), varlen H32 D128", "", head, "",
+              "## kernel-trace statistics", "", "command (from the repository root):",
+              "  " + profile_command("bkt"), ""] + _stats_lines(outdir, "bkt")
+        bl += ["", "## resources (kernel trace)", ""] + _resource_lines(outdir, "bkt", ours)
         if os.path.isdir(os.path.join(outdir, "bpmc_fetch")) and os.path.isdir(os.path.join(outdir, "bpmc_write")):
             bl += ["", "## HBM traffic per launch of each backward kernel (rocprofv3 --pmc, one counter per run)", "",
                    f"scaled by the 1 GiB copy calibration of the forward's runs: fetch x{fetch_scale:.3f}, "
                    f"write x{write_scale:.3f}", "",
                    "commands:", "  " + profile_command("bpmc_fetch"), "  " + profile_command("bpmc_write"), "",
                    f"{'read MB':>10} {'write MB':>10}  kernel"]
-            ours = lambda n: "gdn2::" in n
             per = {}
             for name, key, scale in (("bpmc_fetch", 0, fetch_scale), ("bpmc_write", 1, write_scale)):
                 rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
@@ -200,7 +321,8 @@ def summarize_profiles(outdir: str, tag: str, dest: str | None = None):
                 total += rd + wr
                 bl.append(f"{rd/1e6:>10.1f} {wr/1e6:>10.1f}  {_short(kname)}")
             bl.append(f"sum over the kernels of one call: {total/1e6:.1f} MB")
-        with open(os.path.join(dest, f"bwd_kernels_{tag}.txt"), "w") as f:
+        bl += _sq_lines(outdir, "b", "", ours, _chunk_heads(2), "backward, varlen")
+        with open(os.path.join(dest, f"bwd_kernels_varlen_h32_d128.txt"), "w") as f:
             f.write("\n".join(bl) + "\n")
         log("\n".join(bl))
 
@@ -357,12 +479,104 @@ def cpu_baseline(d, workload, min_seconds: float = 10.0):
                       f"OpenMP over (sequence, head), wall {wall:.2f} s"}
 
 
+def _device_set(d, dev):
+    import torch
+    wl = d["workload"]
+    T, N = int(d["cu_seqlens"][-1]), len(d["lengths"])
+    x = {n: d[n].to(dev) for n in ("q", "k", "v", "g", "beta", "w")}
+    x["initial_state"] = None if d["initial_state"] is None else d["initial_state"].to(dev)
+    x["cu_seqlens"] = d["cu_seqlens"].to(dev)
+    x["out"] = torch.empty((T, wl.HV, wl.V), dtype=torch.bfloat16, device=dev)
+    x["final_state"] = torch.empty((N, wl.HV, wl.K, wl.V), dtype=torch.float32, device=dev)
+    return x
+
+
+def _set_bytes(x) -> int:
+    return sum(t.numel() * t.element_size() for t in x.values() if t is not None)
+
+
+def input_sets(config_id, seed, dev, cold: bool, cache_bytes: int = 512 << 20):
+    """The device input sets a timed run rotates through: one, or with
+    ``cold`` at least three whose total exceeds ``cache_bytes`` (more than the
+    MI355X's 256 MB last-level cache, so that no launch finds its inputs
+    there from the previous one). Set i is drawn with seed + 1000 i."""
+    from linear_attention_rnn_gdn2_amd.workloads import make_inputs
+    d = make_inputs(config_id, seed)
+    sets = [_device_set(d, dev)]
+    if cold:
+        per = _set_bytes(sets[0])
+        n = max(3, -(-(cache_bytes + 1) // per))
+        for i in range(1, n):
+            sets.append(_device_set(make_inputs(config_id, seed + 1000 * i), dev))
+    return d, sets
+
+
+def time_forward(gdn2, sets, scale, steps, warmup, dev):
+    """Warm up, then time ``steps`` calls, call i on input set i mod len(sets):
+    returns (per-call times in ms from HIP events on the launch stream, wall
+    seconds of the whole timed region)."""
+    import torch
+
+    def call(x):
+        gdn2.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["w"], scale=scale,
+                       initial_state=x["initial_state"], cu_seqlens=x["cu_seqlens"],
+                       out=x["out"], final_state=x["final_state"])
+
+    for i in range(warmup):
+        call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        call(sets[i % len(sets)])
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def other_workloads(gdn2, dev, ids, steps, seed_base):
+    """Tokens/s and roofline fraction of further workloads (each its own
+    seeded draw). single rotates cold input sets (each set is smaller than
+    the last-level cache); gva and long_decay move several GB per call."""
+    import torch
+    from linear_attention_rnn_gdn2_amd.workloads import WORKLOADS
+    res = []
+    for c in ids:
+        wl = WORKLOADS[c]
+        cold = c == 1
+        d, sets = input_sets(c, c if seed_base is None else seed_base, dev, cold)
+        T, N = int(d["cu_seqlens"][-1]), len(d["lengths"])
+        ms, wall = time_forward(gdn2, sets, d["scale"], steps, 2, dev)
+        mean_s = sum(ms) / len(ms) / 1e3
+        algo = algorithmic_bytes(T, N, wl.H, wl.HV, wl.K, wl.V, d["initial_state"] is not None, True)
+        r = {"workload": f"{wl.name}: {N} x {T // N} tokens, H={wl.H} HV={wl.HV} K={wl.K} V={wl.V}",
+             "tokens_per_s": T / mean_s, "mean_call_ms": mean_s * 1e3, "wall_ms_per_step": wall / steps * 1e3,
+             "algorithmic_bytes_per_call": algo, "roofline_frac": algo / mean_s / 1e9 / HBM_PEAK_GBS,
+             "input_sets": len(sets), "input_bytes_total": sum(_set_bytes(x) for x in sets)}
+        log(f"{wl.name}: mean call {mean_s*1e3:.3f} ms, {T / mean_s / 1e6:.2f} M tokens/s, "
+            f"{algo / mean_s / 1e9 / HBM_PEAK_GBS * 100:.1f}% of HBM peak ({len(sets)} input set(s))")
+        res.append(r)
+        del d, sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic inputs (default: the workload id)")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="rotate at least three input sets totalling more than 512 MB through the timed calls")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the single / gva / long_decay timings that follow the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / GEMM context")
     ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd",
@@ -381,7 +595,7 @@ def main():
             print(profile_command(n))
         return
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, "varlen_h32_d128")
+        summarize_profiles(args.summarize_profiles)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -405,48 +619,25 @@ def main():
         log(f"copied {args.copy_probe_mib} MiB twice")
         return
     gdn2.load_library()
-    log(f"drawing workload {args.workload}")
-    d = make_inputs(args.workload)
+    seed = args.workload if args.seed is None else args.seed
+    log(f"drawing workload {args.workload} (seed {seed})")
     if args.mode == "bwd":
-        bench_bwd(args, d, gdn2, dev)
+        bench_bwd(args, make_inputs(args.workload, seed), gdn2, dev)
         return
+    d, sets = input_sets(args.workload, seed, dev, args.cold_cache)
     wl = d["workload"]
     T = int(d["cu_seqlens"][-1])
     N = len(d["lengths"])
-    names = ("q", "k", "v", "g", "beta", "w")
-    gpu = {n: d[n].to(dev) for n in names}
-    s0 = None if d["initial_state"] is None else d["initial_state"].to(dev)
-    cu = d["cu_seqlens"].to(dev)
-    out = torch.empty((T, wl.HV, wl.V), dtype=torch.bfloat16, device=dev)
-    fin = torch.empty((N, wl.HV, wl.K, wl.V), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    def step():
-        gdn2.chunk_fwd(**gpu, scale=d["scale"], initial_state=s0, cu_seqlens=cu, out=out, final_state=fin)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    has_init = d["initial_state"] is not None
+    launch_ms, wall = time_forward(gdn2, sets, d["scale"], args.steps, args.warmup, dev)
     mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     ms_per_step = wall / args.steps * 1e3
     value = T / (ms_per_step / 1e3)
 
-    algo = algorithmic_bytes(T, N, wl.H, wl.HV, wl.K, wl.V, s0 is not None, True)
+    algo = algorithmic_bytes(T, N, wl.H, wl.HV, wl.K, wl.V, has_init, True)
     achieved = algo / mean_launch_s / 1e9
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(src_hash)
+    traffic = measured_traffic(src_hash) if args.workload == 2 else None
     rec = {
         "metric": METRIC,
         "value": value,
@@ -461,7 +652,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {N} sequences, {T} tokens (lengths {d['lengths']}), "
-                               f"H={wl.H} HV={wl.HV} K={wl.K} V={wl.V}, chunk 64, seed {args.workload}",
+                               f"H={wl.H} HV={wl.HV} K={wl.K} V={wl.V}, chunk 64, seed {seed}"
+                               + (f", {len(sets)} input sets rotated" if len(sets) > 1 else ""),
                    "global_batch": N, "seq_len": T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -470,13 +662,19 @@ def main():
     }
     log(f"mean launch {mean_launch_s*1e3:.3f} ms, wall/step {ms_per_step:.3f} ms, "
         f"{value/1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic ({achieved/HBM_PEAK_GBS*100:.1f}% of HBM peak)")
+    cpu_d = d
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        rec["other_workloads"] = other_workloads(gdn2, dev, [c for c in (1, 3, 4) if c != args.workload],
+                                                 args.steps, args.seed)
     if not args.no_peaks:
         rec["measured_peaks"] = measured_peaks(dev)
         log(f"measured on this device: copy {rec['measured_peaks']['copy_GBps']:.0f} GB/s, "
             f"bf16 GEMM {rec['measured_peaks']['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("timing the FP64 oracle on the host")
-        rec["cpu_baseline"] = cpu_baseline(d, wl)
+        rec["cpu_baseline"] = cpu_baseline(cpu_d, wl)
     print(json.dumps(rec), flush=True)
 
 

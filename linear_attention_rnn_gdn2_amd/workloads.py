@@ -133,15 +133,20 @@ def make_inputs(config_id: int, seed: int | None = None):
     return d
 
 
-def total_tokens(config_id: int, seed: int | None = None) -> int:
-    """Total packed length of a workload without drawing the tensors."""
+def lengths_of(config_id: int, seed: int | None = None) -> list:
+    """Sequence lengths of a workload without drawing the tensors (the
+    lengths are the generator's first draw)."""
     wl = WORKLOADS[config_id]
     if wl.lengths is not None:
-        return int(sum(wl.lengths))
+        return [int(x) for x in wl.lengths]
     gen = torch.Generator(device="cpu")
     gen.manual_seed(int(config_id if seed is None else seed))
-    lens = torch.randint(wl.len_range[0], wl.len_range[1] + 1, (wl.n_seqs,), generator=gen)
-    return int(lens.sum())
+    return torch.randint(wl.len_range[0], wl.len_range[1] + 1, (wl.n_seqs,), generator=gen).tolist()
+
+
+def total_tokens(config_id: int, seed: int | None = None) -> int:
+    """Total packed length of a workload without drawing the tensors."""
+    return int(sum(lengths_of(config_id, seed)))
 
 
 

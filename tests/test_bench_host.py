@@ -92,20 +92,39 @@ def test_counter_summary_on_synthetic_profiles(tmp_path):
                 [4, bwd_b, "FETCH_SIZE", 500.0]])
     _write_csv(str(out / "bpmc_write" / "bpmc_write_counter_collection.csv"), ctr_hdr,
                [[2, bwd_a, "WRITE_SIZE", 250.0], [4, bwd_b, "WRITE_SIZE", 750.0]])
+    # SQ passes: 1,000 VALU instructions per (chunk, value head) of the
+    # varlen call and rocprofv3's derived utilisations passed through
+    ch = bench._chunk_heads(2)
+    _write_csv(str(out / "sq1" / "sq1_counter_collection.csv"), ctr_hdr,
+               [[2, fwd, "MfmaUtil", 12.5], [2, fwd, "VALUBusy", 40.0], [2, fwd, "SQ_INSTS_VALU", 1000.0 * ch],
+                [2, fwd, "SQ_INSTS_MFMA", 300.0 * ch], [2, fwd, "SQ_INSTS_VALU_TRANS_F32", 80.0 * ch],
+                [3, copy, "SQ_INSTS_VALU", 1.0]])
+    _write_csv(str(out / "sq2" / "sq2_counter_collection.csv"), ctr_hdr,
+               [[2, fwd, "LDSBankConflict", 1.25], [2, fwd, "LdsUtil", 30.0], [2, fwd, "SQ_INSTS_LDS", 500.0 * ch],
+                [2, fwd, "SQ_WAIT_INST_LDS", 10.0 * ch], [2, fwd, "SQ_VALU_MFMA_COEXEC_CYCLES", 7.0 * ch]])
+    _write_csv(str(out / "sq3" / "sq3_counter_collection.csv"), ctr_hdr,
+               [[2, fwd, "SQ_WAIT_INST_ANY", 5.0 * ch], [2, fwd, "SQ_ACTIVE_INST_ANY", 9.0 * ch],
+                [2, fwd, "SQ_WAVES", 2048.0], [2, fwd, "SQ_INSTS_VMEM_RD", 20.0 * ch],
+                [2, fwd, "TA_BUSY_avr", 123.0], [2, fwd, "TA_ADDR_STALLED_BY_TC_CYCLES_sum", 45.0]])
     dest = tmp_path / "profiles"
     dest.mkdir()
-    bench.summarize_profiles(str(out), "synthetic", dest=str(dest))
+    bench.summarize_profiles(str(out), dest=str(dest))
     rec = json.load(open(dest / "hbm_traffic_varlen_h32_d128.json"))
     assert rec["fetch_scale"] == pytest.approx(2.0)
     assert rec["write_scale"] == pytest.approx(1.0)
     assert rec["hbm_read_bytes"] == pytest.approx(2_048_000)
     assert rec["hbm_write_bytes"] == pytest.approx(512_000)
     assert rec["kernel_source_hash"] == bench.kernel_source_hash()
-    txt = open(dest / "chunk_fwd_kernel_synthetic.txt").read()
+    txt = open(dest / "chunk_fwd_kernel_varlen_h32_d128.txt").read()
     assert "900.0" in txt and "total 2.56 MB per launch" in txt
+    assert bench.kernel_source_hash() in txt
+    assert "MFMA busy (MfmaUtil) 12.5 %   VALU busy (VALUBusy) 40.0 %" in txt
+    assert "VALU 1000 (transcendental f32 80), MFMA 300, LDS 500, vector-memory reads 20" in txt
+    assert "bank-conflict stall (LDSBankConflict) 1.25 %" in txt and "wait for LDS issue 40 " in txt
+    assert "copyBuffer" not in txt.split("## SQ counters")[1]
     # backward: bwd_chunk reads 2,000 KiB x 2 and writes 250 KiB, bwd_state
     # reads 500 KiB x 2 and writes 750 KiB; torch's own kernels are left out
-    btxt = open(dest / "bwd_kernels_synthetic.txt").read()
+    btxt = open(dest / "bwd_kernels_varlen_h32_d128.txt").read()
     assert "     4.1        0.3  " + bwd_a in btxt
     assert "     1.0        0.8  " + bwd_b in btxt
     assert "sum over the kernels of one call: 6.1 MB" in btxt
