@@ -61,7 +61,7 @@ enum {
     GDN2_ERR_DTYPE = -2,       /* a tensor has the wrong element type */
     GDN2_ERR_SHAPE = -3,       /* ranks or extents disagree */
     GDN2_ERR_HEADS = -4,       /* HV is not a positive multiple of H */
-    GDN2_ERR_UNSUPPORTED = -5, /* (K, V) not in {(64,64), (128,128)} */
+    GDN2_ERR_UNSUPPORTED = -5, /* K or V not 64 or 128 (the backward: K != V), or an option out of range */
     GDN2_ERR_LAYOUT = -6,      /* a tensor's strides or alignment are not accepted */
     GDN2_ERR_ALIAS = -7,       /* an output overlaps an input */
     GDN2_ERR_HIP = -8          /* the HIP runtime reported an error */
@@ -107,15 +107,16 @@ enum {
  * error (NULL_ARG) for every tensor; an optional tensor is omitted by passing
  * a NULL descriptor pointer.
  *
- * Supported: (K, V) = (64, 64) or (128, 128); any T >= 0, N >= 1, H >= 1,
- * HV a multiple of H. Empty sequences are allowed (their final state equals
- * their initial state).
+ * Supported: K and V each 64 or 128, equal or not (the Flash-GDN-2 README,
+ * training paragraph: both head dimensions in {64, 128}); any T >= 0,
+ * N >= 1, H >= 1, HV a multiple of H. Empty sequences are allowed (their
+ * final state equals their initial state).
  *
  * Ownership: the caller owns every buffer. Inputs and initial_state are only
  * read; out and final_state must be preallocated and are fully written. The
  * library keeps no pointer after the call returns. When it splits sequences
  * (see gdn2_chunk_fwd_opts) it takes a stream-ordered workspace of
- * 3 * N * HV * nseg * K * V * 4 bytes with hipMallocAsync on `stream` and
+ * N * HV * nseg * (2 K V + K K) * 4 bytes with hipMallocAsync on `stream` and
  * returns it with hipFreeAsync on the same stream (nseg = segments per
  * sequence, at most ceil(ceil(T / 64) / segment chunks)); if that
  * allocation fails it runs the sequences whole instead. Otherwise it
@@ -218,7 +219,7 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k,
  * gdn2_chunk_fwd_opts; it calls no hipMalloc, hipMallocAsync, hipFree or
  * other allocating routine.
  *
- * Where the split run needs a workspace (3 * N * HV * nseg * K * V * 4
+ * Where the split run needs a workspace (N * HV * nseg * (2 K V + K K) * 4
  * bytes, see gdn2_chunk_fwd_opts), it is taken from a static device array of
  * GDN2_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
  * the process ends. Nothing in it needs clearing: every byte a call reads
@@ -332,7 +333,8 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  *   dv, dw [T, HV, V], dbeta [T, HV, K]                    bf16
  *   dg [T, HV, K]                                          float32 (gradient of the natural-log g)
  *   d_initial_state [N, HV, K, V]                          float32, or NULL (not written)
- * scale == 0 means 1/sqrt(K). Supported sizes as gdn2_chunk_fwd.
+ * scale == 0 means 1/sqrt(K). Supported sizes: (K, V) = (64, 64) or
+ * (128, 128) (GDN2_ERR_UNSUPPORTED otherwise; the forward also takes K != V).
  *
  * Strong decay: any g <= 0 is supported. A key channel whose running
  * in-chunk sum of g leaves about -83 (120 ln 2) within a chunk cannot use

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgdn2.so")
 SOURCES = [os.path.join(HERE, "csrc", "gdn2_api.cpp"), os.path.join(HERE, "csrc", "gdn2_fwd.hip"),
-           os.path.join(HERE, "csrc", "gdn2_recurrent.hip"), os.path.join(HERE, "csrc", "gdn2_bwd.hip")]
+           os.path.join(HERE, "csrc", "gdn2_fwd_mixed.hip"), os.path.join(HERE, "csrc", "gdn2_recurrent.hip"),
+           os.path.join(HERE, "csrc", "gdn2_bwd.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -22,8 +23,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile every source and link libgdn2.so; returns its path."""
-    objs = []
+    """Compile every source (in parallel, one hipcc per source) and link
+    libgdn2.so; returns its path."""
+    objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(HERE, "csrc", os.path.basename(src) + ".o")
         cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
@@ -31,8 +33,16 @@ def build_library(verbose: bool = False) -> str:
             cmd = [HIPCC, "-x", "hip"] + FLAGS + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=subprocess.PIPE if not verbose else None)
+        procs.append((cmd, subprocess.Popen(cmd, stderr=None if verbose else subprocess.PIPE)))
         objs.append(obj)
+    failed = []
+    for cmd, pr in procs:
+        _, err = pr.communicate()
+        if pr.returncode != 0:
+            failed.append((cmd, err))
+    if failed:
+        cmd, err = failed[0]
+        raise subprocess.CalledProcessError(1, cmd, stderr=err)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

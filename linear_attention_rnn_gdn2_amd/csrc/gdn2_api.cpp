@@ -172,7 +172,8 @@ bool overlaps(const gdn2_tensor *a, const gdn2_tensor *b)
 int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
              const gdn2_tensor *g, const gdn2_tensor *beta, const gdn2_tensor *w, float scale,
              const gdn2_tensor *h0, const gdn2_tensor *cu, const gdn2_tensor *out,
-             const gdn2_tensor *ht, gdn2::FwdParams *p, bool allow_inplace_state = false)
+             const gdn2_tensor *ht, gdn2::FwdParams *p, bool allow_inplace_state = false,
+             bool state_vmajor = false)
 {
     g_last_error.clear();
     if (!q) return fail(GDN2_ERR_NULL_ARG, "q is NULL");
@@ -191,8 +192,8 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     if (H < 1 || HV < H || HV % H != 0)
         return fail(GDN2_ERR_HEADS, "value heads (%lld) must be a positive multiple of q/k heads (%lld)",
                     (long long)HV, (long long)H);
-    if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
-        return fail(GDN2_ERR_UNSUPPORTED, "(K, V) = (%lld, %lld) not supported; use (64, 64) or (128, 128)",
+    if ((K != 64 && K != 128) || (V != 64 && V != 128))
+        return fail(GDN2_ERR_UNSUPPORTED, "(K, V) = (%lld, %lld) not supported; K and V must each be 64 or 128",
                     (long long)K, (long long)V);
     if (T > INT32_MAX)
         return fail(GDN2_ERR_SHAPE, "T = %lld exceeds the int32 range of cu_seqlens", (long long)T);
@@ -215,7 +216,8 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
     }
     if (N * HV > INT32_MAX)
         return fail(GDN2_ERR_SHAPE, "N * HV = %lld exceeds the grid limit", (long long)(N * HV));
-    const int64_t ss[4] = {N, HV, K, V};
+    // states: [N, HV, K, V], or [N, HV, V, K] with the V-major layout option
+    const int64_t ss[4] = {N, HV, state_vmajor ? V : K, state_vmajor ? K : V};
     if (h0 && (rc = check_tensor(h0, "initial_state", GDN2_DTYPE_F32, GDN2_DTYPE_BF16, 4, ss))) return rc;
     if (ht && (rc = check_tensor(ht, "final_state", GDN2_DTYPE_F32, GDN2_DTYPE_BF16, 4, ss))) return rc;
 
@@ -281,6 +283,7 @@ int validate(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *v,
         p->qk_l2norm = 0;
         p->ckpt = nullptr;
         p->rec = nullptr;
+        p->tonly = 0;
     }
     return GDN2_OK;
 }
@@ -353,7 +356,8 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
         return fail(GDN2_ERR_HEADS, "value heads (%lld) must be a positive multiple of q/k heads (%lld)",
                     (long long)HV, (long long)H);
     if (!((K == 64 && V == 64) || (K == 128 && V == 128)))
-        return fail(GDN2_ERR_UNSUPPORTED, "(K, V) = (%lld, %lld) not supported; use (64, 64) or (128, 128)",
+        return fail(GDN2_ERR_UNSUPPORTED,
+                    "(K, V) = (%lld, %lld) not supported by the backward; it takes (64, 64) or (128, 128)",
                     (long long)K, (long long)V);
     if (T > INT32_MAX) return fail(GDN2_ERR_SHAPE, "T = %lld exceeds the int32 range", (long long)T);
     const int64_t qs[3] = {T, H, K}, vs[3] = {T, HV, V}, gs[3] = {T, HV, K};
@@ -458,6 +462,14 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
 }  // namespace
 
 namespace {
+// Workspace bytes per (sequence, value head, segment) of a split run: its
+// end state from a zero start and its entering state (K x V each), and its
+// transition map (K x K), all float32.
+size_t split_item_bytes(const gdn2::FwdParams &p)
+{
+    return (2 * (size_t)p.K * p.V + (size_t)p.K * p.K) * sizeof(float);
+}
+
 // Bytes of the split run's workspace (segment end states, transitions and
 // entering states) for segments of `split` chunks; 0 when the run would not
 // split, SIZE_MAX when the count overflows.
@@ -466,10 +478,10 @@ size_t split_workspace_bytes(const gdn2::FwdParams &p, int32_t split)
     const int64_t nseg = split > 0 ? gdn2::seg_count(p.T, split) : 1;
     if (split <= 0 || nseg <= 1) return 0;
     if (nseg > INT32_MAX) return SIZE_MAX;
-    const size_t state = (size_t)p.K * p.V * sizeof(float);
     const size_t items = (size_t)p.N * p.HV * (size_t)nseg;
-    if (items / nseg != (size_t)p.N * p.HV || items > SIZE_MAX / (3 * state)) return SIZE_MAX;
-    return 3 * items * state;
+    const size_t per = split_item_bytes(p);
+    if (items / nseg != (size_t)p.N * p.HV || items > SIZE_MAX / per) return SIZE_MAX;
+    return items * per;
 }
 
 // Enqueue the chunked forward of p on `stream`: whole sequences, or, with
@@ -485,7 +497,8 @@ int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream, void *fixe
     const size_t bytes = split_workspace_bytes(p, split);
     if (bytes > 0 && bytes != SIZE_MAX) {
         const int64_t nseg = gdn2::seg_count(p.T, split);
-        const size_t one = bytes / 3;
+        const size_t items = (size_t)p.N * p.HV * (size_t)nseg;
+        const size_t sz_b = items * p.K * p.V * sizeof(float), sz_m = items * p.K * p.K * sizeof(float);
         void *ws = fixed;
         const bool own = !fixed;
         if (own && hipMallocAsync(&ws, bytes, stream) != hipSuccess) ws = nullptr;
@@ -493,8 +506,8 @@ int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream, void *fixe
             p.seg_chunks = split;
             p.nseg = (int32_t)nseg;
             p.wb = static_cast<float *>(ws);
-            p.wm = reinterpret_cast<float *>(static_cast<char *>(ws) + one);
-            p.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * one);
+            p.wm = reinterpret_cast<float *>(static_cast<char *>(ws) + sz_b);
+            p.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + sz_b + sz_m);
             gdn2::FwdParams pt = p;
             pt.pass = gdn2::PASS_TRANSITION;
             pt.ckpt = nullptr;
@@ -600,7 +613,7 @@ void *scratch_on(int dev, hipError_t *err)
 int32_t fit_split(const gdn2::FwdParams &p, int32_t split, size_t cap)
 {
     if (split <= 0 || split_workspace_bytes(p, split) <= cap) return split;
-    const size_t per_seg = 3 * (size_t)p.N * p.HV * (size_t)p.K * p.V * sizeof(float);
+    const size_t per_seg = (size_t)p.N * p.HV * split_item_bytes(p);
     const int64_t max_seg = (int64_t)(cap / per_seg);
     if (max_seg < 2) return -1;
     const int64_t chunks = (p.T + gdn2::CHUNK - 1) / gdn2::CHUNK;
@@ -618,10 +631,12 @@ int gdn2_chunk_fwd_noalloc(const gdn2_tensor *q, const gdn2_tensor *k, const gdn
                            const gdn2_fwd_options *opts, hipStream_t stream)
 {
     gdn2::FwdParams p;
-    int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p);
-    if (rc != GDN2_OK) return rc;
     Options o;
-    if ((rc = read_options(opts, &o)) != GDN2_OK) return rc;
+    int rc = read_options(opts, &o);
+    if (rc != GDN2_OK) return rc;
+    rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p,
+                  false, o.vmajor != 0);
+    if (rc != GDN2_OK) return rc;
     p.state_vmajor = o.vmajor;
     p.qk_l2norm = o.l2norm;
     p.seg_chunks = 0;
@@ -745,10 +760,12 @@ int gdn2_chunk_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_t
                         const gdn2_fwd_options *opts, hipStream_t stream)
 {
     gdn2::FwdParams p;
-    int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p);
-    if (rc != GDN2_OK) return rc;
     Options o;
-    if ((rc = read_options(opts, &o)) != GDN2_OK) return rc;
+    int rc = read_options(opts, &o);
+    if (rc != GDN2_OK) return rc;
+    rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p,
+                  false, o.vmajor != 0);
+    if (rc != GDN2_OK) return rc;
     int32_t split = o.split;
     p.state_vmajor = o.vmajor;
     p.qk_l2norm = o.l2norm;
@@ -780,10 +797,12 @@ int gdn2_recurrent_fwd_opts(const gdn2_tensor *q, const gdn2_tensor *k, const gd
                             const gdn2_fwd_options *opts, hipStream_t stream)
 {
     gdn2::FwdParams p;
-    int rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p, true);
-    if (rc != GDN2_OK) return rc;
     Options o;
-    if ((rc = read_options(opts, &o)) != GDN2_OK) return rc;
+    int rc = read_options(opts, &o);
+    if (rc != GDN2_OK) return rc;
+    rc = validate(q, k, v, g, beta, w, scale, initial_state, cu_seqlens, out, final_state, &p,
+                  true, o.vmajor != 0);
+    if (rc != GDN2_OK) return rc;
     p.state_vmajor = o.vmajor;
     p.qk_l2norm = o.l2norm;
     p.seg_chunks = 0;

@@ -295,7 +295,7 @@ __device__ __forceinline__ void load_values(typename IoT<IO>::v8 *v, typename Io
     const int rs = (int)p.sv * 2, rsw = (int)p.sw * 2;  // token strides (bytes)
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(p.v + c0 * p.sv + hv * p.hsv, zero_v ? 0 : len * rs);
     const __amdgpu_buffer_rsrc_t rw =
-        p.w ? buf_rsrc(p.w + c0 * p.sw + hv * p.hsw, len * rsw) : buf_rsrc(kOnes16[IO], 16);
+        p.w ? buf_rsrc(p.w + c0 * p.sw + hv * p.hsw, zero_v ? 0 : len * rsw) : buf_rsrc(kOnes16[IO], 16);
     const int sw = p.w ? rsw : 0, cw = p.w ? 2 * c0v : 0;
     for (int i = 0; i < RPTV; ++i) {
         const int r = row0 + i;
@@ -1431,8 +1431,9 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     // transition pass, the kind (0: end state from the segment's entering
     // state or zero, 1: transition map from the identity with zero values)
     int item = blockIdx.x;
-    const int kind = p.pass == PASS_TRANSITION ? item & 1 : 0;
-    if (p.pass == PASS_TRANSITION) item >>= 1;
+    const bool both = p.pass == PASS_TRANSITION && p.tonly == 0;
+    const int kind = both ? item & 1 : p.pass == PASS_TRANSITION ? p.tonly - 1 : 0;
+    if (both) item >>= 1;
     const int seg = p.seg_chunks ? item % p.nseg : 0;
     if (p.seg_chunks) item /= p.nseg;
     Chain ch;
@@ -1473,6 +1474,9 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
                 if (seg > 0) ch.s0 = nullptr;
                 ch.s1 = p.wb + sseg;
             } else {
+                // the K x K map: this walk runs in the square kernel
+                // (template V == K; a K != V run launches it for these
+                // walks alone), so sseg strides K x K
                 ch.s0 = nullptr;
                 ch.ident = ch.zero_v = true;
                 ch.s1 = p.wm + sseg;
@@ -1526,6 +1530,7 @@ __global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams
     if (last == 0) return;
     const int t = threadIdx.x, r = t >> 1, c = CMB_COLS / 2 * (t & 1);
     const int64_t seg0 = (int64_t)chain * p.nseg * K * V;  // chain = n * HV + hv
+    const int64_t map0 = (int64_t)chain * p.nseg * K * K;  // the maps: K x K each
     const int col = cb * CMB_COLS + c;
     float s0 = p.wb[seg0 + r * V + col], s1 = p.wb[seg0 + r * V + col + 1];
     p.ws[seg0 + (int64_t)K * V + r * V + col] = s0;
@@ -1534,7 +1539,7 @@ __global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams
         // row r of M_j and this thread's entries of B_j, all loads in flight
         // together (one memory round trip per step)
         const int64_t sj = seg0 + (int64_t)j * K * V;
-        const float *m = p.wm + sj + (int64_t)r * K;
+        const float *m = p.wm + map0 + (int64_t)j * K * K + (int64_t)r * K;
         f32x4 mr[K / 4];
         for (int k4 = 0; k4 < K / 4; ++k4) mr[k4] = *reinterpret_cast<const f32x4 *>(m + 4 * k4);
         float a0 = p.wb[sj + r * V + col], a1 = p.wb[sj + r * V + col + 1];
@@ -1555,18 +1560,6 @@ __global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams
 }
 
 }  // namespace
-
-hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream)
-{
-    const dim3 grid((unsigned)(p.N * p.HV * (p.V / CMB_COLS)));
-    if (p.K == 128 && p.V == 128)
-        hipLaunchKernelGGL((seg_combine_kernel<128, 128>), grid, dim3(cmb_threads<128>()), 0, stream, p);
-    else if (p.K == 64 && p.V == 64)
-        hipLaunchKernelGGL((seg_combine_kernel<64, 64>), grid, dim3(cmb_threads<64>()), 0, stream, p);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
-}
 
 namespace {
 // one instantiation per (K, V, io type, 16-bit g, L2 normalisation)
@@ -1590,14 +1583,44 @@ void launch_chunk_typed(const FwdParams &p, dim3 grid, hipStream_t stream)
 }
 }  // namespace
 
+#ifdef GDN2_FWD_MIXED
+// ----------------------------------------------- K != V translation unit --
+hipError_t launch_chunk_fwd_mixed(const FwdParams &p, unsigned grid, hipStream_t stream)
+{
+    if (p.rec || (p.pass == PASS_TRANSITION && p.tonly != 1)) return hipErrorInvalidValue;
+    if (p.K == 128 && p.V == 64)
+        launch_chunk_typed<128, 64>(p, dim3(grid), stream);
+    else if (p.K == 64 && p.V == 128)
+        launch_chunk_typed<64, 128>(p, dim3(grid), stream);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+#else
+hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.N * p.HV * (p.V / CMB_COLS)));
+    if (p.K == 128 && p.V == 128)
+        hipLaunchKernelGGL((seg_combine_kernel<128, 128>), grid, dim3(cmb_threads<128>()), 0, stream, p);
+    else if (p.K == 64 && p.V == 64)
+        hipLaunchKernelGGL((seg_combine_kernel<64, 64>), grid, dim3(cmb_threads<64>()), 0, stream, p);
+    else if (p.K == 128 && p.V == 64)
+        hipLaunchKernelGGL((seg_combine_kernel<128, 64>), grid, dim3(cmb_threads<128>()), 0, stream, p);
+    else if (p.K == 64 && p.V == 128)
+        hipLaunchKernelGGL((seg_combine_kernel<64, 128>), grid, dim3(cmb_threads<64>()), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
 {
-    const int64_t items = (int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1) * (p.pass == PASS_TRANSITION ? 2 : 1);
-    const dim3 grid((unsigned)items);
+    const int64_t items = (int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1);
     if (p.rec) {
         // the backward's recompute: bf16 io, float32 g, no L2 normalisation
         if (p.io != IO_BF16 || p.gtype != G_F32 || p.qk_l2norm || !p.ckpt || p.pass != PASS_OUTPUT || p.K != p.V)
             return hipErrorInvalidValue;
+        const dim3 grid((unsigned)items);
         if (p.K == 128)
             hipLaunchKernelGGL((chunk_fwd_kernel<128, 128, IO_BF16, false, false, true>), grid, dim3(NTHR), 0, stream, p);
         else if (p.K == 64)
@@ -1606,6 +1629,20 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
+    if (p.K != p.V) {
+        if (p.pass != PASS_TRANSITION) return launch_chunk_fwd_mixed(p, (unsigned)items, stream);
+        // a split run's transition pass: the end-state walks in the K x V
+        // kernel, the K x K transition maps in the square one
+        FwdParams p0 = p, p1 = p;
+        p0.tonly = 1;
+        p1.tonly = 2;
+        const hipError_t e = launch_chunk_fwd_mixed(p0, (unsigned)items, stream);
+        if (e != hipSuccess) return e;
+        if (p.K == 128) launch_chunk_typed<128, 128>(p1, dim3((unsigned)items), stream);
+        else launch_chunk_typed<64, 64>(p1, dim3((unsigned)items), stream);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)(items * (p.pass == PASS_TRANSITION && p.tonly == 0 ? 2 : 1)));
     if (p.K == 128 && p.V == 128)
         launch_chunk_typed<128, 128>(p, grid, stream);
     else if (p.K == 64 && p.V == 64)
@@ -1614,5 +1651,6 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
+#endif
 
 }  // namespace gdn2

@@ -45,6 +45,10 @@ struct FwdParams {
     int32_t seg_chunks;
     int32_t nseg;
     int32_t pass;          // PASS_OUTPUT or PASS_TRANSITION
+    // transition pass: 0 both walks of every segment (grid item parity), 1
+    // only the end-state walks, 2 only the transition-map walks (K != V: the
+    // map is K x K, walked by the square kernel)
+    int32_t tonly;
     float *wb;             // [N, HV, nseg, K, V] segment end state from a zero start (segment 0: from h0)
     float *wm;             // [N, HV, nseg, K, K] segment transition (state map S_in -> S_out minus wb)
     float *ws;             // [N, HV, nseg, K, V] entering state of segment j >= 1
@@ -142,6 +146,10 @@ __host__ __device__ inline SeqRange seq_of(const FwdParams &p, int64_t n) { retu
 
 // Enqueue the fused chunked forward on `stream` (one pass, as p describes).
 hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);
+// The forward kernel at K != V ((128, 64) or (64, 128)), compiled in a
+// translation unit of its own: whole sequences, a split run's output pass,
+// or its end-state walks (tonly == 1) on `grid` workgroups.
+hipError_t launch_chunk_fwd_mixed(const FwdParams &p, unsigned grid, hipStream_t stream);
 
 // Enqueue the token-by-token forward (decode and short spans): one
 // workgroup per (sequence, value head, 32 value columns).

@@ -193,6 +193,10 @@ hipError_t launch_recurrent_fwd(const FwdParams &p, hipStream_t stream)
         launch_rec_typed<128, 128>(p, grid, stream);
     else if (p.K == 64 && p.V == 64)
         launch_rec_typed<64, 64>(p, grid, stream);
+    else if (p.K == 128 && p.V == 64)
+        launch_rec_typed<128, 64>(p, grid, stream);
+    else if (p.K == 64 && p.V == 128)
+        launch_rec_typed<64, 128>(p, grid, stream);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

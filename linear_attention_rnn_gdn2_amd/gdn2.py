@@ -148,7 +148,8 @@ def split_plan(T, N, HV, num_cu):
     return load_library().gdn2_split_plan(int(T), int(N), int(HV), int(num_cu))
 
 
-def _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out, final_state, g, beta, w):
+def _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out, final_state, g, beta, w,
+             state_layout="kv"):
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("w", w),
                     ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
         if t is not None and not t.is_cuda:
@@ -159,7 +160,8 @@ def _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out, final_
     if out is None:
         out = torch.empty((T, HV, V), dtype=q.dtype, device=v.device)
     if final_state is None and output_final_state:
-        final_state = torch.empty((N, HV, K, V), dtype=torch.float32, device=v.device)
+        shape = (N, HV, V, K) if state_layout == "vk" else (N, HV, K, V)
+        final_state = torch.empty(shape, dtype=torch.float32, device=v.device)
     descs = [describe(x) for x in (q, k, v, g, beta, w)]
     rest = [describe(x) for x in (initial_state, cu_seqlens, out, final_state)]
     return out, final_state, descs, rest
@@ -172,8 +174,8 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
 
     q, k [T, H, K] and v, w [T, HV, V], beta [T, HV, K], out: bf16 or
     float16 (q's type); g [T, HV, K] float32, bf16 or float16;
-    initial_state [N, HV, K, V] float32 ([N, HV, V, K] with
-    ``state_layout="vk"``); cu_seqlens [N + 1] int32 or int64 (None: one
+    initial_state and final_state [N, HV, K, V] float32 or bf16
+    ([N, HV, V, K] with ``state_layout="vk"``); cu_seqlens [N + 1] int32 or int64 (None: one
     sequence). Strided views are accepted where the rows are contiguous.
     ``scale`` None or 0 means 1/sqrt(K). Returns (out [T, HV, V],
     final_state or None); preallocated ``out`` / ``final_state`` are written
@@ -183,7 +185,7 @@ def chunk_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=None
     """
     lib = load_library()
     out, final_state, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out,
-                                             final_state, g, beta, w)
+                                             final_state, g, beta, w, state_layout)
     stream = torch.cuda.current_stream(v.device).cuda_stream
     if seq_split is None and state_layout == "kv" and not qk_l2norm:
         rc = lib.gdn2_chunk_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),
@@ -207,7 +209,8 @@ def chunk_fwd_noalloc(q, k, v, g=None, beta=None, w=None, scale=None, initial_st
     lib = load_library()
     if out is None:
         raise ValueError("chunk_fwd_noalloc needs a preallocated out")
-    _, _, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, False, out, final_state, g, beta, w)
+    _, _, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, False, out, final_state, g, beta, w,
+                                 state_layout)
     stream = torch.cuda.current_stream(v.device).cuda_stream
     opts = make_options(seq_split, state_layout, qk_l2norm)
     rc = lib.gdn2_chunk_fwd_noalloc(*[_ptr(d) for d in descs], _scale_arg(scale), *[_ptr(d) for d in rest],
@@ -227,7 +230,7 @@ def recurrent_fwd(q, k, v, g=None, beta=None, w=None, scale=None, initial_state=
     """
     lib = load_library()
     out, final_state, descs, rest = _prepare(q, k, v, initial_state, cu_seqlens, output_final_state, out,
-                                             final_state, g, beta, w)
+                                             final_state, g, beta, w, state_layout)
     stream = torch.cuda.current_stream(v.device).cuda_stream
     if state_layout == "kv" and not qk_l2norm:
         rc = lib.gdn2_recurrent_fwd(*[_ptr(d) for d in descs], _scale_arg(scale),

