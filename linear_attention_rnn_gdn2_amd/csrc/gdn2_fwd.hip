@@ -1106,6 +1106,38 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
     }
 }
 
+// ---------------------------------------------------------------- phase T2 --
+// Block column J of T below the diagonal, state wave J:
+// T_iJ = -T_ii sum_{k=J}^{i-1} A_ik T_kJ, i = J+1..3, on bf16 MFMA with
+// float32 operands split into high and low bf16 parts (three products; the
+// dropped low x low term is 2^-16 relative). T_kJ (k > J) stay in registers
+// in the MFMA result layout, which is the B operand layout of the 16x16x16
+// product. Every A tile and diagonal block of the column is read before the
+// first product, so that the dependent chain (two products per block row)
+// waits for LDS once, not once per product.
+template <int K, int V, int J>
+__device__ __forceinline__ void t2_column(char *sm, int l16, int q4)
+{
+    using L = Lds<K, V>;
+    constexpr int RA = 4 * L::AP, RC = 2 * L::CP;
+    const char *const b_a4 = sm + l16 * RA + 16 * q4;                                // rows 16i + l16, columns 4q4
+    const char *const b_tc = sm + 4 * q4 * RA + 4 * l16 + J * (16 * RA + 64);        // rows 4q4 + e, column l16
+    f32x4 tjj, a[4][4];  // a[i][k]: A_ik for J <= k < i, T_ii for k = i
+    for (int e = 0; e < 4; ++e) tjj[e] = lds_ld<float>(b_tc, L::AB + e * RA);
+    for (int i = J + 1; i < 4; ++i)
+        for (int k = J; k <= i; ++k) a[i][k] = lds_ld<f32x4>(b_a4, L::AB + 16 * i * RA + 64 * k);
+    Split4 Tc[4];
+    Tc[J] = split4(tjj);
+    char *const b_tb = sm + 4 * q4 * RC + 2 * l16 + 32 * J;
+    for (int i = J + 1; i < 4; ++i) {
+        f32x4 X = {0, 0, 0, 0};
+        for (int k = J; k < i; ++k) X = mfma3(split4(a[i][k]), Tc[k], X);
+        const f32x4 Y = mfma3(split4(-a[i][i]), split4(X), f32x4{0, 0, 0, 0});
+        Tc[i] = split4(Y);
+        for (int e = 0; e < 4; ++e) lds_st<__bf16>(b_tb, L::TB + (16 * i + e) * RC, (__bf16)Y[e]);
+    }
+}
+
 // Phase AP of a state wave: its four tiles (t = 4 + rw + 4 m) of A and P
 // from the single-reference operands. Every operand read of the four tiles
 // is issued before the first product, so that their LDS round trips overlap
@@ -1354,33 +1386,10 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             }
         }
 
-        // ---- T2: block column j = rw of T,
-        // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, i = j+1..3, on bf16 MFMA
-        // with float32 operands split into high and low bf16 parts (three
-        // products; the dropped low x low term is 2^-16 relative). T_kj
-        // (k > j) stay in registers in the MFMA result layout, which is the
-        // B operand layout of the 16x16x16 product.
-        if (rw < 3) {
-            const int j = rw;
-            const char *const b_a4 = sm + o_a4;
-            const char *const b_tc = sm + 4 * q4 * RA + 4 * l16 + j * (16 * RA + 64);  // rows 4q4 + e, column l16
-            f32x4 tjj;
-            for (int e = 0; e < 4; ++e) tjj[e] = lds_ld<float>(b_tc, L::AB + e * RA);
-            const Split4 bjj = split4(tjj);
-            Split4 Tc[4];
-            char *const b_tb = sm + 4 * q4 * RC + 2 * l16 + 32 * j;
-            for (int i = 1; i < 4; ++i) {
-                if (i <= j) continue;
-                f32x4 X = {0, 0, 0, 0};
-                for (int kb = 0; kb < 3; ++kb) {
-                    if (kb < j || kb >= i) continue;
-                    X = mfma3(split4(lds_ld<f32x4>(b_a4, L::AB + 16 * i * RA + 64 * kb)), kb == j ? bjj : Tc[kb], X);
-                }
-                const f32x4 Y = mfma3(split4(-lds_ld<f32x4>(b_a4, L::AB + 16 * i * RA + 64 * i)), split4(X), f32x4{0, 0, 0, 0});
-                Tc[i] = split4(Y);
-                for (int e = 0; e < 4; ++e) lds_st<__bf16>(b_tb, L::TB + (16 * i + e) * RC, (__bf16)Y[e]);
-            }
-        }
+        // ---- T2: block column j = rw of T (t2_column)
+        if (rw == 0) t2_column<K, V, 0>(sm, l16, q4);
+        else if (rw == 1) t2_column<K, V, 1>(sm, l16, q4);
+        else if (rw == 2) t2_column<K, V, 2>(sm, l16, q4);
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- WY: the last -wy_w channel tile of key wave rw (K = 128), then
