@@ -1181,6 +1181,17 @@ __device__ __forceinline__ void state_ap_store(char *sm, const f32x4 (&acc)[4], 
 }
 
 // ----------------------------------------------------------- state waves --
+// Register row order of the state. S is held in the MFMA result layout:
+// lane (l16, q4) holds rows 4 q4 + e (e = 0..3) of each 16-row tile rt,
+// column l16. Those rows stand for key channels in a permuted order: tile
+// rt = 2 ks + h, lane quarter q4, element e is channel
+// 32 ks + 8 q4 + 4 h + e. Then the bf16 operand built from the tile pair
+// (2 ks, 2 ks + 1) holds channels 32 ks + 8 q4 .. + 7 in order, so the LDS
+// operands it meets (wy_w and QH, stored in natural channel order) are one
+// 16-byte read per lane instead of two 8-byte reads (which share banks at
+// the padded row pitch).
+__device__ __forceinline__ int state_chan(int rt, int q4, int e) { return 32 * (rt >> 1) + 8 * q4 + 4 * (rt & 1) + e; }
+
 // LDS addressing in the chunk loops: every access is (per-lane base) +
 // (compile-time constant). The lane parts are loop invariant; the per-chunk
 // opaque zero is added to a handful of base pointers once per chunk, so the
@@ -1206,7 +1217,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int vbase = rw * VW;
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
-                for (int e = 0; e < 4; ++e) S[it][jt][e] = 16 * it + 4 * q4 + e == vbase + 16 * jt + l16 ? 1.0f : 0.0f;
+                for (int e = 0; e < 4; ++e) S[it][jt][e] = state_chan(it, q4, e) == vbase + 16 * jt + l16 ? 1.0f : 0.0f;
     } else if (ch.s0) {
         const int lane = tid & 63, rw = tid >> 6;
         const int l16 = lane & 15, q4 = lane >> 4;
@@ -1216,7 +1227,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         for (int it = 0; it < NRT; ++it)
             for (int jt = 0; jt < NCT; ++jt)
                 for (int e = 0; e < 4; ++e)
-                    S[it][jt][e] = state_ld(h0, ch.s0_b16, (16 * it + 4 * q4 + e) * sr + (vbase + 16 * jt + l16) * sc);
+                    S[it][jt][e] = state_ld(h0, ch.s0_b16, state_chan(it, q4, e) * sr + (vbase + 16 * jt + l16) * sc);
         // complete these loads here: left outstanding into the chunk
         // loop, they make every later write of S wait on the vector
         // memory counter, which then also waits for the v, w prefetch
@@ -1242,29 +1253,29 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         const int vbase = rw * VW;
         const EMap<V> emv(tid);
         // per-lane byte offsets of the access patterns
-        const int o_k4 = l16 * RK + 8 * q4;                           // K-pitched rows 16i + l16, columns 32ks + 4q4 (+16)
-        const int o_c4 = l16 * RC + 8 * q4;                           // the same in a 64-column tile
+        const int o_c4 = l16 * RC + 8 * q4;                           // 64-column rows 16i + l16, columns 32ks + 4q4 (+16)
         const int o_k8 = l16 * RK + 16 * q4;                          // K-pitched rows, columns 32ks + 8q4
         const int o_c8 = l16 * RC + 16 * q4;                          // 64-column rows, columns 32ks + 8q4
         const int o_a4 = l16 * RA + 16 * q4;                          // fp32 tile rows 16i + l16, columns 4q4
         const int64_t c0 = ch.tb + (int64_t)it * CH;
         const bool act = it < nc;
         const int len = act ? chunk_len(c0, ch.te) : 0;
-        const char *const b_k4 = sm + o_k4;
+        const char *const b_k8 = sm + o_k8;
         const char *const b_c4 = sm + o_c4;
 
         // ---- S, first half (chunk it - 1): U = wy_u - wy_w S. S as bf16
-        // operands: k slab ks holds state rows {32ks + 4q4 + e} then
-        // {32ks + 16 + 4q4 + e}, e = 0..3; LDS operands are read with the
-        // same k order, and U as bf16 operands (Ub) in the same way over
-        // tokens.
+        // operands: k slab ks holds channels 32ks + 8q4 + 0..7 (state_chan),
+        // so wy_w and QH are read 8 consecutive channels per lane; U as
+        // bf16 operands (Ub): token slab ks holds tokens {32ks + 4q4 + e}
+        // then {32ks + 16 + 4q4 + e}, e = 0..3, and P is read in the same
+        // token order.
         bf16x8 Ub[2][NCT], Sb[NKS][NCT];
         if (it > 0 && ch.ckpt) {
             // the float32 state entering chunk it - 1 (for the backward)
             float *const dst = ch.ckpt + (int64_t)(it - 1) * p.HV * (K * V) + vbase + l16;
             for (int rt = 0; rt < NRT; ++rt)
                 for (int jt = 0; jt < NCT; ++jt)
-                    for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * q4 + e) * V + 16 * jt] = S[rt][jt][e];
+                    for (int e = 0; e < 4; ++e) dst[state_chan(rt, q4, e) * V + 16 * jt] = S[rt][jt][e];
         }
         if (it > 0) {
             for (int ks = 0; ks < NKS; ++ks)
@@ -1273,7 +1284,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int i = 0; i < 4; ++i)
                 for (int ks = 0; ks < NKS; ++ks) {
                     const int o = L::WYW + 16 * i * RK + 64 * ks;
-                    const bf16x8 aw = cat4(lds_ld<bf16x4>(b_k4, o), lds_ld<bf16x4>(b_k4, o + 32));
+                    const bf16x8 aw = lds_ld<bf16x8>(b_k8, o);
                     for (int jt = 0; jt < NCT; ++jt) U[i][jt] = mfma_bf16(aw, Sb[ks][jt], U[i][jt]);
                 }
             for (int ks = 0; ks < 2; ++ks)
@@ -1302,7 +1313,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         if (it > 0) {
             const int64_t cp = c0 - CH;
             const int lenp = chunk_len(cp, ch.te);
-            const char *const b_q = b_k4 + ((it - 1) & 1) * L::QH_SZ;
+            const char *const b_q = b_k8 + ((it - 1) & 1) * L::QH_SZ;
             if (ch.out) {
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * i + l16;
@@ -1310,7 +1321,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                     for (int jt = 0; jt < NCT; ++jt) Y[jt] = f32x4{0, 0, 0, 0};
                     for (int ks = 0; ks < NKS; ++ks) {
                         const int o = L::QH + 16 * i * RK + 64 * ks;
-                        const bf16x8 bq = cat4(lds_ld<bf16x4>(b_q, o), lds_ld<bf16x4>(b_q, o + 32));
+                        const bf16x8 bq = lds_ld<bf16x8>(b_q, o);
                         for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Sb[ks][jt], bq, Y[jt]);
                     }
                     for (int ks = 0; ks <= (i >> 1); ++ks) {
@@ -1325,13 +1336,16 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                                 __builtin_convertvector(Y[jt] * p.scale, typename IoT<IO>::v4);
                 }
             }
-            const char *const b_kt = sm + (4 * q4 + (l16 >> 2)) * RK + 8 * (l16 & 3);  // KT transpose reads
-            const char *const b_g = sm + 16 * q4;
+            // KT transpose reads: lane group l16 & 3 reads 4 channels, which
+            // become rows 4 (l16 & 3) + e of the A operand, in state_chan order
+            const char *const b_kt = sm + (4 * q4 + (l16 >> 2)) * RK + 16 * (l16 & 3);
+            const char *const b_g = sm + 32 * q4;
             for (int rtile = 0; rtile < NRT; ++rtile) {
-                const f32x4 gam = lds_ld<f32x4>(b_g, L::GAM + 64 * rtile);
+                const int cb = 32 * (rtile >> 1) + 4 * (rtile & 1);  // state_chan(rtile, q4, e) - 8 q4 - e
+                const f32x4 gam = lds_ld<f32x4>(b_g, L::GAM + 4 * cb);
                 bf16x8 ak[2];
                 for (int ks = 0; ks < 2; ++ks) {
-                    const int o = L::KT + 32 * ks * RK + 32 * rtile;
+                    const int o = L::KT + 32 * ks * RK + 2 * cb;
                     ak[ks] = cat4(lds_tr(b_kt, o), lds_tr(b_kt, o + 16 * RK));
                 }
                 for (int jt = 0; jt < NCT; ++jt) {
@@ -1423,7 +1437,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             for (int jt = 0; jt < NCT; ++jt)
                 for (int e = 0; e < 4; ++e)
                     state_st(ch.s1, ch.s1_b16,
-                             (16 * it + 4 * q4 + e) * (ch.s1_vm ? 1 : V) + (vbase + 16 * jt + l16) * (ch.s1_vm ? K : 1),
+                             state_chan(it, q4, e) * (ch.s1_vm ? 1 : V) + (vbase + 16 * jt + l16) * (ch.s1_vm ? K : 1),
                              S[it][jt][e]);
     }
 }
