@@ -321,17 +321,17 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  *
  * Tensors (every one dense, row-major; shapes and roles as in
  * gdn2_chunk_fwd):
- *   q, k [T, H, K], v, w [T, HV, V], beta [T, HV, K]      bf16 (required)
- *   g [T, HV, K]                                           float32 (required)
+ *   q, k [T, H, K], v, w [T, HV, V], beta [T, HV, K]      bf16 or float16, one type (required)
+ *   g [T, HV, K]                                           float32, bf16 or float16 (required)
  *   initial_state [N, HV, K, V]                            float32, K-major, or NULL (zero)
  *   cu_seqlens [N + 1]                                     int32 or int64, or NULL (one sequence)
- *   d_out [T, HV, V]                                       bf16 (required)
+ *   d_out [T, HV, V]                                       q's type (required)
  *   d_final_state [N, HV, K, V]                            float32, or NULL (zero)
  * Outputs (caller-allocated, fully written):
- *   dq, dk [T, H, K]                                       bf16: sums over the value heads that
+ *   dq, dk [T, H, K]                                       q's type: sums over the value heads that
  *                                                          read each q/k head
- *   dv, dw [T, HV, V], dbeta [T, HV, K]                    bf16
- *   dg [T, HV, K]                                          float32 (gradient of the natural-log g)
+ *   dv, dw [T, HV, V], dbeta [T, HV, K]                    q's type
+ *   dg [T, HV, K]                                          g's type (gradient of the natural-log g)
  *   d_initial_state [N, HV, K, V]                          float32, or NULL (not written)
  * scale == 0 means 1/sqrt(K). Supported sizes: (K, V) = (64, 64) or
  * (128, 128) (GDN2_ERR_UNSUPPORTED otherwise; the forward also takes K != V).

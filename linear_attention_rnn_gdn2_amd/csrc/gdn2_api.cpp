@@ -347,9 +347,10 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
     for (int i = 0; i < 13; ++i)
         if (!req[i]) return fail(GDN2_ERR_NULL_ARG, "%s is NULL (required by the backward)", req_names[i]);
     int rc;
-    if ((rc = check_tensor(q, "q", GDN2_DTYPE_BF16, -1, 3, nullptr))) return rc;
+    if ((rc = check_tensor(q, "q", GDN2_DTYPE_BF16, GDN2_DTYPE_F16, 3, nullptr))) return rc;
+    const int32_t io = q->dtype;  // q, k, v, beta, w, d_out and the gradients share one 16-bit type
     const int64_t T = q->shape[0], H = q->shape[1], K = q->shape[2];
-    if ((rc = check_tensor(v, "v", GDN2_DTYPE_BF16, -1, 3, nullptr))) return rc;
+    if ((rc = check_tensor(v, "v", io, -1, 3, nullptr))) return rc;
     if (v->shape[0] != T) return fail(GDN2_ERR_SHAPE, "v: dimension 0 is %lld, expected %lld", (long long)v->shape[0], (long long)T);
     const int64_t HV = v->shape[1], V = v->shape[2];
     if (H < 1 || HV < H || HV % H != 0)
@@ -361,17 +362,20 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
                     (long long)K, (long long)V);
     if (T > INT32_MAX) return fail(GDN2_ERR_SHAPE, "T = %lld exceeds the int32 range", (long long)T);
     const int64_t qs[3] = {T, H, K}, vs[3] = {T, HV, V}, gs[3] = {T, HV, K};
-    if ((rc = check_tensor(k, "k", GDN2_DTYPE_BF16, -1, 3, qs))) return rc;
-    if ((rc = check_tensor(w, "w", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
-    if ((rc = check_tensor(g, "g", GDN2_DTYPE_F32, -1, 3, gs))) return rc;
-    if ((rc = check_tensor(beta, "beta", GDN2_DTYPE_BF16, -1, 3, gs))) return rc;
-    if ((rc = check_tensor(dout, "d_out", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
-    if ((rc = check_tensor(dq, "dq", GDN2_DTYPE_BF16, -1, 3, qs))) return rc;
-    if ((rc = check_tensor(dk, "dk", GDN2_DTYPE_BF16, -1, 3, qs))) return rc;
-    if ((rc = check_tensor(dv, "dv", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
-    if ((rc = check_tensor(dw, "dw", GDN2_DTYPE_BF16, -1, 3, vs))) return rc;
-    if ((rc = check_tensor(dg, "dg", GDN2_DTYPE_F32, -1, 3, gs))) return rc;
-    if ((rc = check_tensor(dbeta, "dbeta", GDN2_DTYPE_BF16, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(k, "k", io, -1, 3, qs))) return rc;
+    if ((rc = check_tensor(w, "w", io, -1, 3, vs))) return rc;
+    if (g->dtype != GDN2_DTYPE_F32 && g->dtype != GDN2_DTYPE_BF16 && g->dtype != GDN2_DTYPE_F16)
+        return fail(GDN2_ERR_DTYPE, "g: expected float32, bf16 or float16, got %s", dtype_name(g->dtype));
+    const int32_t gt = g->dtype;  // g and dg share one type
+    if ((rc = check_tensor(g, "g", gt, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(beta, "beta", io, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(dout, "d_out", io, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(dq, "dq", io, -1, 3, qs))) return rc;
+    if ((rc = check_tensor(dk, "dk", io, -1, 3, qs))) return rc;
+    if ((rc = check_tensor(dv, "dv", io, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(dw, "dw", io, -1, 3, vs))) return rc;
+    if ((rc = check_tensor(dg, "dg", gt, -1, 3, gs))) return rc;
+    if ((rc = check_tensor(dbeta, "dbeta", io, -1, 3, gs))) return rc;
     int64_t N = 1;
     if (cu) {
         if ((rc = check_tensor(cu, "cu_seqlens", GDN2_DTYPE_I32, GDN2_DTYPE_I64, 1, nullptr))) return rc;
@@ -404,7 +408,9 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
         p->k = static_cast<const uint16_t *>(k->data);
         p->v = static_cast<const uint16_t *>(v->data);
         p->w = static_cast<const uint16_t *>(w->data);
-        p->g = static_cast<const float *>(g->data);
+        p->g = g->data;
+        p->io = io == GDN2_DTYPE_F16 ? gdn2::IO_F16 : gdn2::IO_BF16;
+        p->gtype = gt == GDN2_DTYPE_F32 ? gdn2::G_F32 : gt == GDN2_DTYPE_BF16 ? gdn2::G_BF16 : gdn2::G_F16;
         p->beta = static_cast<const uint16_t *>(beta->data);
         p->dout = static_cast<const uint16_t *>(dout->data);
         p->cu = cu ? cu->data : nullptr;
@@ -416,7 +422,7 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
         p->dv = static_cast<uint16_t *>(dv->data);
         p->dw = static_cast<uint16_t *>(dw->data);
         p->dbeta = static_cast<uint16_t *>(dbeta->data);
-        p->dg = static_cast<float *>(dg->data);
+        p->dg = dg->data;
         p->T = T;
         p->N = (int32_t)N;
         p->H = (int32_t)H;
@@ -444,8 +450,8 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
         pf->K = (int32_t)K;
         pf->V = (int32_t)V;
         pf->scale = scale == 0.0f ? (float)(1.0 / sqrt((double)K)) : scale;
-        pf->io = gdn2::IO_BF16;
-        pf->gtype = gdn2::G_F32;
+        pf->io = io == GDN2_DTYPE_F16 ? gdn2::IO_F16 : gdn2::IO_BF16;
+        pf->gtype = gt == GDN2_DTYPE_F32 ? gdn2::G_F32 : gt == GDN2_DTYPE_BF16 ? gdn2::G_BF16 : gdn2::G_F16;
         // dense row-major strides (elements)
         pf->sq = pf->sk = H * K;
         pf->hsq = pf->hsk = K;

@@ -69,7 +69,45 @@ __device__ __forceinline__ f32x4 khat_factor(f32x4 g)
 
 // Token range of sequence n (clamped into [0, T]).
 __device__ __forceinline__ SeqRange seq_of(const BwdParams &p, int64_t n) { return seq_range(p.cu, p.cu64, p.T, n); }
-__device__ __forceinline__ uint16_t to_bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+// Element access in the caller's types: q, k, v, w, beta, d_out and their
+// gradients in the io type (bf16 or fp16, p.io), g and dg in p.gtype
+// (float32, bf16 or fp16). Wave-uniform branches on the kernel arguments.
+__device__ __forceinline__ float io1_f32(uint16_t b, int io)
+{
+    return io == IO_F16 ? (float)__builtin_bit_cast(_Float16, b) : bf16_bits_to_f32(b);
+}
+__device__ __forceinline__ uint16_t f32_io1(float x, int io)
+{
+    return io == IO_F16 ? __builtin_bit_cast(uint16_t, (_Float16)x) : __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+// 8 consecutive values (16 bytes, raw), widened to float32
+__device__ __forceinline__ i32x4 ld_raw8(const uint16_t *p) { return *reinterpret_cast<const i32x4 *>(p); }
+__device__ __forceinline__ f32x8 io8_f32(i32x4 raw, int io)
+{
+    return io == IO_F16 ? __builtin_convertvector(__builtin_bit_cast(f16x8, raw), f32x8)
+                        : __builtin_convertvector(__builtin_bit_cast(bf16x8, raw), f32x8);
+}
+// the same values as a bf16 MFMA operand (exact for bf16 io, rounded for fp16)
+__device__ __forceinline__ bf16x8 io8_bf16(i32x4 raw, int io)
+{
+    return io == IO_F16 ? f32x8_to_bf16(io8_f32(raw, io)) : __builtin_bit_cast(bf16x8, raw);
+}
+__device__ __forceinline__ void st_io8(uint16_t *p, f32x8 x, int io)
+{
+    if (io == IO_F16) *reinterpret_cast<f16x8 *>(p) = __builtin_convertvector(x, f16x8);
+    else *reinterpret_cast<bf16x8 *>(p) = f32x8_to_bf16(x);
+}
+__device__ __forceinline__ float g_at(const BwdParams &p, int64_t i)
+{
+    if (p.gtype == G_F32) return static_cast<const float *>(p.g)[i];
+    return io1_f32(static_cast<const uint16_t *>(p.g)[i], p.gtype == G_F16 ? IO_F16 : IO_BF16);
+}
+__device__ __forceinline__ void st_g4(const BwdParams &p, int64_t i, f32x4 x)
+{
+    if (p.gtype == G_F32) *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dg) + i) = x;
+    else if (p.gtype == G_F16) *reinterpret_cast<f16x4 *>(static_cast<uint16_t *>(p.dg) + i) = __builtin_convertvector(x, f16x4);
+    else *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.dg) + i) = __builtin_convertvector(x, bf16x4);
+}
 
 // One 16x16 tile Z[m0 + 4 q4 + e][n0 + l16] (element e of the result) of
 // acc + X Y over k in [0, kd), X and Y bf16 in LDS at byte offsets xo, yo:
@@ -148,7 +186,7 @@ __device__ __forceinline__ void load_gcol(float (&v)[RP], const BwdParams &p, in
     const int c = tid % D, r0 = (tid / D) * RP;
 #pragma unroll
     for (int i = 0; i < RP; ++i)
-        v[i] = r0 + i < len ? p.g[((t0 + r0 + i) * p.HV + hv) * D + c] : 0.0f;
+        v[i] = r0 + i < len ? g_at(p, ((t0 + r0 + i) * p.HV + hv) * D + c) : 0.0f;
 }
 
 // G = cumsum(g) log2(e) per channel into float32 [64][D] (pitch D) at go,
@@ -282,11 +320,11 @@ __device__ __forceinline__ void exact_pass(char *sm, const BwdParams &p, int64_t
         const int r = RPX * part + h;
         const bool ok = on && r < len;
         const int64_t tr = t0 + r;
-        run += ok ? p.g[(tr * p.HV + hv) * D + c] * LOG2E : 0.0f;
+        run += ok ? g_at(p, (tr * p.HV + hv) * D + c) * LOG2E : 0.0f;
         gl[h] = run;
-        const float qv = ok ? bf16_bits_to_f32(p.q[(tr * p.H + hk) * D + c]) : 0.0f;
-        const float kv = ok ? bf16_bits_to_f32(p.k[(tr * p.H + hk) * D + c]) : 0.0f;
-        const float bv = ok ? bf16_bits_to_f32(p.beta[(tr * p.HV + hv) * D + c]) : 0.0f;
+        const float qv = ok ? io1_f32(p.q[(tr * p.H + hk) * D + c], p.io) : 0.0f;
+        const float kv = ok ? io1_f32(p.k[(tr * p.H + hk) * D + c], p.io) : 0.0f;
+        const float bv = ok ? io1_f32(p.beta[(tr * p.HV + hv) * D + c], p.io) : 0.0f;
         lds_st<float>(sm, sx + 1 * A + 4 * r, qv);
         lds_st<float>(sm, sx + 2 * A + 4 * r, kv);
         lds_st<float>(sm, sx + 3 * A + 4 * r, bv);
@@ -368,9 +406,10 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
         // dO (bf16 [token][D]; rows past the end zero) rides along with the
         // record; it goes to LDS once WV is no longer needed there
-        bf16x8 xdo[NU8];
+        i32x4 xdo[NU8];
         {
-            bf16x8 x[4][NU8], vr[NU8], wr[NU8], xpt[2];
+            bf16x8 x[4][NU8], xpt[2];
+            i32x4 vr[NU8], wr[NU8];
             const int src[4] = {R.qh(), R.kb(), R.rr(), R.wy()};
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
@@ -378,9 +417,9 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) x[m][u] = *reinterpret_cast<const bf16x8 *>(rec + src[m] + 2 * (r * D + c0));
                 const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
-                vr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
-                wr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
-                xdo[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.dout + tv) : bf16x8{};
+                vr[u] = r < len ? ld_raw8(p.v + tv) : i32x4{};
+                wr[u] = r < len ? ld_raw8(p.w + tv) : i32x4{};
+                xdo[u] = r < len ? ld_raw8(p.dout + tv) : i32x4{};
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {  // P, then T: 512 16-byte pieces each, one per thread
@@ -396,8 +435,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
 #pragma unroll
                 for (int m = 0; m < 4; ++m) lds_st<bf16x8>(sm, dst[m] + 2 * (r * RK + c0), x[m][u]);
-                lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0),
-                               f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
+                lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), f32x8_to_bf16(io8_f32(vr[u], p.io) * io8_f32(wr[u], p.io)));
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -444,7 +482,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-            lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), xdo[u]);
+            lds_st<bf16x8>(sm, L::RGB + 2 * (r * RK + c0), io8_bf16(xdo[u], p.io));
         }
         __syncthreads();
 
@@ -532,19 +570,18 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
 
         // ---- WV again (bf16 in RGA)
         {
-            bf16x8 vr[NU8], wr[NU8];
+            i32x4 vr[NU8], wr[NU8];
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
                 const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
                 const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
-                vr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
-                wr[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
+                vr[u] = r < len ? ld_raw8(p.v + tv) : i32x4{};
+                wr[u] = r < len ? ld_raw8(p.w + tv) : i32x4{};
             }
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
                 const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                lds_st<bf16x8>(sm, L::RGA + 2 * (r * RK + c0),
-                               f32x8_to_bf16(__builtin_convertvector(vr[u], f32x8) * __builtin_convertvector(wr[u], f32x8)));
+                lds_st<bf16x8>(sm, L::RGA + 2 * (r * RK + c0), f32x8_to_bf16(io8_f32(vr[u], p.io) * io8_f32(wr[u], p.io)));
             }
         }
         __syncthreads();
@@ -688,15 +725,15 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         constexpr int RF = L::RF, EF = L::EF;
         __syncthreads();  // every read of the regions below is done
         // the row-parallel part's k, beta, v and w, in flight from here
-        bf16x8 ek[NU8], eb[NU8], ev[NU8], ew[NU8];
+        i32x4 ek[NU8], eb[NU8], ev[NU8], ew[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-            ek[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.k + tk) : bf16x8{};
-            eb[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.beta + tv) : bf16x8{};
-            ev[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.v + tv) : bf16x8{};
-            ew[u] = r < len ? *reinterpret_cast<const bf16x8 *>(p.w + tv) : bf16x8{};
+            ek[u] = r < len ? ld_raw8(p.k + tk) : i32x4{};
+            eb[u] = r < len ? ld_raw8(p.beta + tv) : i32x4{};
+            ev[u] = r < len ? ld_raw8(p.v + tv) : i32x4{};
+            ew[u] = r < len ? ld_raw8(p.w + tv) : i32x4{};
         }
         if (tid < D) {
             // G_last's gradient: gamma rowsum(S_in dS_out) + GMU colsum(dKH RR)
@@ -728,8 +765,8 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             f32x8 dG = {};
             if (r < len) {
                 const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
-                const f32x8 kf = __builtin_convertvector(ek[u], f32x8);
-                const f32x8 bb = __builtin_convertvector(eb[u], f32x8);
+                const f32x8 kf = io8_f32(ek[u], p.io);
+                const f32x8 bb = io8_f32(eb[u], p.io);
                 const f32x8 fq = __builtin_convertvector(xq[u], f32x8);
                 const f32x8 fk = __builtin_convertvector(xk[u], f32x8);
                 const f32x8 fr = __builtin_convertvector(xr[u], f32x8);
@@ -752,19 +789,19 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                     }
                 }
                 if (direct) {
-                    *reinterpret_cast<bf16x8 *>(p.dq + tk) = f32x8_to_bf16(dq);
-                    *reinterpret_cast<bf16x8 *>(p.dk + tk) = f32x8_to_bf16(dk);
+                    st_io8(p.dq + tk, dq, p.io);
+                    st_io8(p.dk + tk, dk, p.io);
                 } else {
                     *reinterpret_cast<f32x4 *>(p.dq_ws + tv) = __builtin_shufflevector(dq, dq, 0, 1, 2, 3);
                     *reinterpret_cast<f32x4 *>(p.dq_ws + tv + 4) = __builtin_shufflevector(dq, dq, 4, 5, 6, 7);
                     *reinterpret_cast<f32x4 *>(p.dk_ws + tv) = __builtin_shufflevector(dk, dk, 0, 1, 2, 3);
                     *reinterpret_cast<f32x4 *>(p.dk_ws + tv + 4) = __builtin_shufflevector(dk, dk, 4, 5, 6, 7);
                 }
-                *reinterpret_cast<bf16x8 *>(p.dbeta + tv) = f32x8_to_bf16(db);
+                st_io8(p.dbeta + tv, db, p.io);
                 // dv = dWV w, dw = dWV v
                 const f32x8 dwv = __builtin_convertvector(lds_ld<bf16x8>(sm, L::DWV + 2 * (r * D + c0)), f32x8);
-                *reinterpret_cast<bf16x8 *>(p.dv + tv) = f32x8_to_bf16(dwv * __builtin_convertvector(ew[u], f32x8));
-                *reinterpret_cast<bf16x8 *>(p.dw + tv) = f32x8_to_bf16(dwv * __builtin_convertvector(ev[u], f32x8));
+                st_io8(p.dv + tv, dwv * io8_f32(ew[u], p.io), p.io);
+                st_io8(p.dw + tv, dwv * io8_f32(ev[u], p.io), p.io);
             }
             lds_st<f32x4>(sm, o, __builtin_shufflevector(dG, dG, 0, 1, 2, 3));
             lds_st<f32x4>(sm, o + 16, __builtin_shufflevector(dG, dG, 4, 5, 6, 7));
@@ -780,7 +817,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         for (int e = tid; e < 64 * D / 4; e += CT) {
             const int r = e / (D / 4), c0 = 4 * (e % (D / 4));
             if (r < len)
-                *reinterpret_cast<f32x4 *>(p.dg + ((t0 + r) * p.HV + hv) * D + c0) = lds_ld<f32x4>(sm, 4 * (r * RF + c0));
+                st_g4(p, ((t0 + r) * p.HV + hv) * D + c0, lds_ld<f32x4>(sm, 4 * (r * RF + c0)));
         }
     }
 }
@@ -869,15 +906,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
         const char *rec = p.prep + (slot * p.HV + hv) * bwd_prep_bytes(D);
         // every load of the chunk's operands in flight before the first store
         constexpr int NU8 = 64 * D / 8 / ST, NUP = 64 * 8 / ST;
-        bf16x8 xq[NU8], xr[NU8], xw[NU8], xo[NU8], xp[NUP];
+        bf16x8 xq[NU8], xr[NU8], xw[NU8], xp[NUP];
+        i32x4 xo[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + ST * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             xq[u] = *reinterpret_cast<const bf16x8 *>(rec + R.qh() + 2 * (r * D + c0));
             xr[u] = *reinterpret_cast<const bf16x8 *>(rec + R.rr() + 2 * (r * D + c0));
             xw[u] = *reinterpret_cast<const bf16x8 *>(rec + R.wy() + 2 * (r * D + c0));
-            xo[u] = r < len && !zero_do ? *reinterpret_cast<const bf16x8 *>(p.dout + ((t0 + r) * p.HV + hv) * D + c0)
-                                        : bf16x8{};
+            xo[u] = r < len && !zero_do ? ld_raw8(p.dout + ((t0 + r) * p.HV + hv) * D + c0) : i32x4{};
         }
 #pragma unroll
         for (int u = 0; u < NUP; ++u) {
@@ -892,7 +929,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
             lds_st<bf16x8>(sm, L::QH + o, xq[u]);
             lds_st<bf16x8>(sm, L::RR + o, xr[u]);
             lds_st<bf16x8>(sm, L::WY + o, xw[u]);
-            lds_st<bf16x8>(sm, L::DO + o, xo[u]);
+            lds_st<bf16x8>(sm, L::DO + o, io8_bf16(xo[u], p.io));
         }
 #pragma unroll
         for (int u = 0; u < NUP; ++u) {
@@ -972,8 +1009,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p)
             sq += p.dq_ws[o];
             sk += p.dk_ws[o];
         }
-        p.dq[i] = to_bf(sq);
-        p.dk[i] = to_bf(sk);
+        p.dq[i] = f32_io1(sq, p.io);
+        p.dk[i] = f32_io1(sk, p.io);
     }
 }
 

@@ -1608,6 +1608,25 @@ void launch_chunk_typed(const FwdParams &p, dim3 grid, hipStream_t stream)
 
 #ifdef GDN2_FWD_MIXED
 // ----------------------------------------------- K != V translation unit --
+// (also the backward's recompute at fp16 io or 16-bit g)
+template <int D, int IO>
+void launch_rec16(const FwdParams &p, dim3 grid, hipStream_t stream)
+{
+    if (p.gtype != G_F32) hipLaunchKernelGGL((chunk_fwd_kernel<D, D, IO, true, false, true>), grid, dim3(NTHR), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_fwd_kernel<D, D, IO, false, false, true>), grid, dim3(NTHR), 0, stream, p);
+}
+
+hipError_t launch_chunk_fwd_rec16(const FwdParams &p, unsigned grid, hipStream_t stream)
+{
+    if (!p.rec || (p.io == IO_BF16 && p.gtype == G_F32)) return hipErrorInvalidValue;
+    if (p.K == 128 && p.io == IO_F16) launch_rec16<128, IO_F16>(p, dim3(grid), stream);
+    else if (p.K == 128) launch_rec16<128, IO_BF16>(p, dim3(grid), stream);
+    else if (p.K == 64 && p.io == IO_F16) launch_rec16<64, IO_F16>(p, dim3(grid), stream);
+    else if (p.K == 64) launch_rec16<64, IO_BF16>(p, dim3(grid), stream);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd_mixed(const FwdParams &p, unsigned grid, hipStream_t stream)
 {
     if (p.rec || (p.pass == PASS_TRANSITION && p.tonly != 1)) return hipErrorInvalidValue;
@@ -1640,9 +1659,10 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream)
 {
     const int64_t items = (int64_t)p.N * p.HV * (p.seg_chunks ? p.nseg : 1);
     if (p.rec) {
-        // the backward's recompute: bf16 io, float32 g, no L2 normalisation
-        if (p.io != IO_BF16 || p.gtype != G_F32 || p.qk_l2norm || !p.ckpt || p.pass != PASS_OUTPUT || p.K != p.V)
-            return hipErrorInvalidValue;
+        // the backward's recompute: K == V, no L2 normalisation; bf16 io with
+        // float32 g here, the 16-bit combinations in the other translation unit
+        if (p.qk_l2norm || !p.ckpt || p.pass != PASS_OUTPUT || p.K != p.V) return hipErrorInvalidValue;
+        if (p.io != IO_BF16 || p.gtype != G_F32) return launch_chunk_fwd_rec16(p, (unsigned)items, stream);
         const dim3 grid((unsigned)items);
         if (p.K == 128)
             hipLaunchKernelGGL((chunk_fwd_kernel<128, 128, IO_BF16, false, false, true>), grid, dim3(NTHR), 0, stream, p);

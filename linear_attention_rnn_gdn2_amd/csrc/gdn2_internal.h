@@ -64,19 +64,22 @@ struct FwdParams {
 
 // Arguments of the backward kernels (all tensors dense, row-major).
 struct BwdParams {
-    const uint16_t *q, *k;       // [T, H, K] bf16
-    const uint16_t *v, *w;       // [T, HV, V] bf16
-    const float *g;              // [T, HV, K] float32
-    const uint16_t *beta;        // [T, HV, K] bf16
-    const uint16_t *dout;        // [T, HV, V] bf16
+    // q, k, v, w, beta, d_out and their gradients share one 16-bit io type
+    // (io: IO_BF16 or IO_F16); g and dg share gtype (G_F32, G_BF16, G_F16)
+    const uint16_t *q, *k;       // [T, H, K]
+    const uint16_t *v, *w;       // [T, HV, V]
+    const void *g;               // [T, HV, K]
+    const uint16_t *beta;        // [T, HV, K]
+    const uint16_t *dout;        // [T, HV, V]
+    int32_t io, gtype;
     const void *cu;              // [N + 1] int32 or int64, or nullptr
     int32_t cu64;
     const float *dht;            // [N, HV, K, V] gradient of the final state, or nullptr (zero)
     float *dh0;                  // [N, HV, K, V] gradient of the initial state, or nullptr
-    uint16_t *dq, *dk;           // [T, H, K] bf16
-    uint16_t *dv, *dw;           // [T, HV, V] bf16
-    uint16_t *dbeta;             // [T, HV, K] bf16
-    float *dg;                   // [T, HV, K] float32
+    uint16_t *dq, *dk;           // [T, H, K] io
+    uint16_t *dv, *dw;           // [T, HV, V] io
+    uint16_t *dbeta;             // [T, HV, K] io
+    void *dg;                    // [T, HV, K] gtype
     // workspace
     float *dq_ws, *dk_ws;        // [T, HV, K] per value head (grouped heads only)
     const float *s_ckpt;         // [nslots, HV, K, V] state entering each chunk
@@ -150,6 +153,9 @@ hipError_t launch_chunk_fwd(const FwdParams &p, hipStream_t stream);
 // translation unit of its own: whole sequences, a split run's output pass,
 // or its end-state walks (tonly == 1) on `grid` workgroups.
 hipError_t launch_chunk_fwd_mixed(const FwdParams &p, unsigned grid, hipStream_t stream);
+// The backward's recompute (p.rec) at fp16 io or 16-bit g, in the same
+// translation unit.
+hipError_t launch_chunk_fwd_rec16(const FwdParams &p, unsigned grid, hipStream_t stream);
 
 // Enqueue the token-by-token forward (decode and short spans): one
 // workgroup per (sequence, value head, 32 value columns).

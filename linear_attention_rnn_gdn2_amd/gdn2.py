@@ -258,11 +258,12 @@ def chunk_bwd(q, k, v, g, beta, w, d_out, scale=None, initial_state=None, cu_seq
               d_final_state=None, need_d_initial_state=True, grads=None):
     """Backward of :func:`chunk_fwd` on the current HIP stream.
 
-    q, k [T, H, K], v, w [T, HV, V], beta [T, HV, K], d_out [T, HV, V]: bf16;
-    g [T, HV, K], initial_state and d_final_state [N, HV, K, V]: float32 (the
-    states may be None: zero). Returns a dict with dq, dk (bf16 [T, H, K]),
-    dv, dw (bf16 [T, HV, V]), dbeta (bf16 [T, HV, K]), dg (float32
-    [T, HV, K]) and d_initial_state (float32 [N, HV, K, V], or None when not
+    q, k [T, H, K], v, w [T, HV, V], beta [T, HV, K], d_out [T, HV, V]: one
+    16-bit type, bf16 or float16; g [T, HV, K]: float32, bf16 or float16;
+    initial_state and d_final_state [N, HV, K, V]: float32 (the states may
+    be None: zero). Returns a dict with dq, dk ([T, H, K]), dv, dw
+    ([T, HV, V]), dbeta ([T, HV, K]) in q's type, dg ([T, HV, K]) in g's
+    type and d_initial_state (float32 [N, HV, K, V], or None when not
     requested). Tensors given in ``grads`` are written in place.
     """
     lib = load_library()
@@ -275,10 +276,9 @@ def chunk_bwd(q, k, v, g, beta, w, d_out, scale=None, initial_state=None, cu_seq
     N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
     dev = v.device
     out = dict(grads or {})
-    shapes = {"dq": ((T, H, K), torch.bfloat16), "dk": ((T, H, K), torch.bfloat16),
-              "dv": ((T, HV, V), torch.bfloat16), "dw": ((T, HV, V), torch.bfloat16),
-              "dbeta": ((T, HV, K), torch.bfloat16), "dg": ((T, HV, K), torch.float32),
-              "d_initial_state": ((N, HV, K, V), torch.float32)}
+    io, gt = q.dtype, g.dtype
+    shapes = {"dq": ((T, H, K), io), "dk": ((T, H, K), io), "dv": ((T, HV, V), io), "dw": ((T, HV, V), io),
+              "dbeta": ((T, HV, K), io), "dg": ((T, HV, K), gt), "d_initial_state": ((N, HV, K, V), torch.float32)}
     for n, (shp, dt) in shapes.items():
         if out.get(n) is None and (n != "d_initial_state" or need_d_initial_state):
             out[n] = torch.empty(shp, dtype=dt, device=dev)

@@ -281,6 +281,15 @@ def test_bwd_valid_calls(gdn2):
     assert bwd_status(gdn2, c, gr) == ("OK", "")
     c, gr = bwd_case(D=128)
     assert bwd_status(gdn2, c, gr)[0] == "OK"
+    # fp16 io and 16-bit g (the gradients in the inputs' types)
+    for io, gt in ((torch.float16, torch.float32), (torch.bfloat16, torch.bfloat16), (torch.float16, torch.float16)):
+        c, gr = bwd_case()
+        for n in ("q", "k", "v", "beta", "w", "d_out"):
+            c[n] = c[n].to(io)
+        for n in ("dq", "dk", "dv", "dw", "dbeta"):
+            gr[n] = gr[n].to(io)
+        c["g"], gr["dg"] = c["g"].to(gt), gr["dg"].to(gt)
+        assert bwd_status(gdn2, c, gr) == ("OK", ""), (io, gt)
     for opt in ("initial_state", "d_final_state"):
         c, gr = bwd_case()
         c[opt] = None
@@ -299,10 +308,13 @@ def test_bwd_valid_calls(gdn2):
     (lambda c, g: c.update(d_out=None), "NULL_ARG"),
     (lambda c, g: g.update(dq=None), "NULL_ARG"),
     (lambda c, g: g.update(dg=None), "NULL_ARG"),
-    (lambda c, g: c.update(q=c["q"].half()), "DTYPE"),     # bf16 only
-    (lambda c, g: c.update(g=c["g"].bfloat16()), "DTYPE"),  # float32 g only
+    (lambda c, g: c.update(q=c["q"].half()), "DTYPE"),     # q's type differs from k's
+    (lambda c, g: c.update(q=c["q"].float(), k=c["k"].float()), "DTYPE"),  # 16-bit io only
+    (lambda c, g: c.update(g=c["g"].double()), "DTYPE"),
+    (lambda c, g: c.update(g=c["g"].bfloat16()), "DTYPE"),  # dg must take g's type
     (lambda c, g: c.update(d_out=c["d_out"].float()), "DTYPE"),
     (lambda c, g: g.update(dg=g["dg"].bfloat16()), "DTYPE"),
+    (lambda c, g: g.update(dq=g["dq"].half()), "DTYPE"),
     (lambda c, g: g.update(dbeta=g["dbeta"].float()), "DTYPE"),
     (lambda c, g: c.update(initial_state=c["initial_state"].bfloat16()), "DTYPE"),
     (lambda c, g: c.update(d_out=c["d_out"][:60]), "SHAPE"),

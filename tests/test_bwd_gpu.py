@@ -209,3 +209,33 @@ def test_bwd_int64_cu_default_scale_no_initial_gradient(lib, c_oracle):
     ref1 = c_oracle(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], d1["w"], d1["scale"], d1["initial_state"], None,
                     d1["d_out"], d1["d_final_state"])
     assert_parity({n: got1[n].float().cpu().double().numpy() for n in GRADS}, ref1, "no cu_seqlens")
+
+
+@pytest.mark.parametrize("io,gt", [(torch.float16, torch.float32), (torch.bfloat16, torch.bfloat16),
+                                   (torch.float16, torch.float16), (torch.bfloat16, torch.float16)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_input_types(lib, c_oracle, io, gt, D):
+    """fp16 or bf16 q, k, v, beta, w, d_out with float32, bf16 or fp16 g
+    (the Flash-GDN-2 README's training paragraph: FP16/BF16 Q/K/V,
+    half/FP32 gates), ragged lengths, grouped heads, beta up to 2, and a
+    tenth of the channels at strong decay: the oracle differentiates the
+    same quantised values, and the gradients come back in the inputs' types
+    (dg in g's)."""
+    d = case((65, 0, 1, 300, 64), 2, 4, D, seed=31 + D, beta_max=2.0, g_extreme_max=8.0, extreme_frac=0.1)
+    for n in ("q", "k", "v", "beta", "w", "d_out"):
+        d[n] = d[n].float().to(io)
+    d["g"] = d["g"].to(gt)
+    dev = torch.device("cuda:0")
+    args = [d[n].to(dev) for n in ("q", "k", "v", "g", "beta", "w", "d_out")]
+    tag = f"io {io} g {gt} D {D}"
+    say(f"[bwd] {tag}: GPU")
+    got = lib.chunk_bwd(*args, scale=d["scale"], initial_state=d["initial_state"].to(dev),
+                        cu_seqlens=d["cu_seqlens"].to(dev), d_final_state=d["d_final_state"].to(dev))
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dw", "dbeta"):
+        assert got[n].dtype == io, (n, got[n].dtype)
+    assert got["dg"].dtype == gt and got["d_initial_state"].dtype == torch.float32
+    say(f"[bwd] {tag}: oracle")
+    ref = c_oracle(d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["scale"], d["initial_state"],
+                   d["cu_seqlens"].numpy(), d["d_out"], d["d_final_state"])
+    assert_parity({n: got[n].float().cpu().double().numpy() for n in GRADS}, ref, tag)
