@@ -306,20 +306,24 @@ def summarize_profiles(outdir: str, dest: str | None = None):
                    f"scaled by the 1 GiB copy calibration of the forward's runs: fetch x{fetch_scale:.3f}, "
                    f"write x{write_scale:.3f}", "",
                    "commands:", "  " + profile_command("bpmc_fetch"), "  " + profile_command("bpmc_write"), "",
-                   f"{'read MB':>10} {'write MB':>10}  kernel"]
-            per = {}
+                   f"per call: each kernel's bytes summed over its dispatches and divided by the number of "
+                   f"gdn2_chunk_bwd calls in the run (the gradient kernel runs once per call; split runs "
+                   f"dispatch some kernels more than once)", "",
+                   f"{'read MB':>10} {'write MB':>10} {'per call':>9}  kernel"]
+            per, calls = {}, {}
             for name, key, scale in (("bpmc_fetch", 0, fetch_scale), ("bpmc_write", 1, write_scale)):
                 rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
+                calls[name] = sum(1 for r in rows if "bwd_chunk_kernel" in r["Kernel_Name"])
                 for r in rows:
                     if ours(r["Kernel_Name"]):
                         per.setdefault(r["Kernel_Name"], ([], []))[key].append(
                             float(r["Counter_Value"]) * 1024 * scale)
+            nf, nw = max(calls["bpmc_fetch"], 1), max(calls["bpmc_write"], 1)
             total = 0.0
             for kname, (fv, wv) in sorted(per.items()):
-                rd = sum(fv) / len(fv) if fv else 0.0
-                wr = sum(wv) / len(wv) if wv else 0.0
+                rd, wr = sum(fv) / nf, sum(wv) / nw
                 total += rd + wr
-                bl.append(f"{rd/1e6:>10.1f} {wr/1e6:>10.1f}  {_short(kname)}")
+                bl.append(f"{rd/1e6:>10.1f} {wr/1e6:>10.1f} {len(fv) / nf:>9.1f}  {_short(kname)}")
             bl.append(f"sum over the kernels of one call: {total/1e6:.1f} MB")
         bl += _sq_lines(outdir, "b", "", ours, _chunk_heads(2), "backward, varlen")
         with open(os.path.join(dest, f"bwd_kernels_varlen_h32_d128.txt"), "w") as f:

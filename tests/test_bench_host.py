@@ -87,11 +87,14 @@ def test_counter_summary_on_synthetic_profiles(tmp_path):
     bwd_a = "void gdn2::(anonymous namespace)::bwd_chunk_kernel<128>(gdn2::BwdParams)"
     bwd_b = "void gdn2::(anonymous namespace)::bwd_state_kernel<128, false>(gdn2::BwdParams)"
     other = "void at::native::elementwise_kernel<128, 4>()"
+    # two backward calls per run; the state kernel dispatched twice per call
+    # (as in a split run)
     _write_csv(str(out / "bpmc_fetch" / "bpmc_fetch_counter_collection.csv"), ctr_hdr,
-               [[1, other, "FETCH_SIZE", 5e6], [2, bwd_a, "FETCH_SIZE", 1000.0], [3, bwd_a, "FETCH_SIZE", 3000.0],
-                [4, bwd_b, "FETCH_SIZE", 500.0]])
+               [[1, other, "FETCH_SIZE", 5e6], [2, bwd_a, "FETCH_SIZE", 1000.0], [3, bwd_a, "FETCH_SIZE", 3000.0]]
+               + [[4 + i, bwd_b, "FETCH_SIZE", 500.0] for i in range(4)])
     _write_csv(str(out / "bpmc_write" / "bpmc_write_counter_collection.csv"), ctr_hdr,
-               [[2, bwd_a, "WRITE_SIZE", 250.0], [4, bwd_b, "WRITE_SIZE", 750.0]])
+               [[2, bwd_a, "WRITE_SIZE", 250.0], [3, bwd_a, "WRITE_SIZE", 350.0]]
+               + [[4 + i, bwd_b, "WRITE_SIZE", 100.0] for i in range(4)])
     # SQ passes: 1,000 VALU instructions per (chunk, value head) of the
     # varlen call and rocprofv3's derived utilisations passed through
     ch = bench._chunk_heads(2)
@@ -122,12 +125,13 @@ def test_counter_summary_on_synthetic_profiles(tmp_path):
     assert "VALU 1000 (transcendental f32 80), MFMA 300, LDS 500, vector-memory reads 20" in txt
     assert "bank-conflict stall (LDSBankConflict) 1.25 %" in txt and "wait for LDS issue 40 " in txt
     assert "copyBuffer" not in txt.split("## SQ counters")[1]
-    # backward: bwd_chunk reads 2,000 KiB x 2 and writes 250 KiB, bwd_state
-    # reads 500 KiB x 2 and writes 750 KiB; torch's own kernels are left out
+    # backward, per call (two calls): bwd_chunk reads 4,000 KiB x 2 / 2 and
+    # writes 600 KiB / 2; bwd_state reads 2,000 KiB x 2 / 2 and writes
+    # 400 KiB / 2 over two dispatches per call; torch's own kernels are left out
     btxt = open(dest / "bwd_kernels_varlen_h32_d128.txt").read()
-    assert "     4.1        0.3  " + bwd_a in btxt
-    assert "     1.0        0.8  " + bwd_b in btxt
-    assert "sum over the kernels of one call: 6.1 MB" in btxt
+    assert "       4.1        0.3       1.0  " + bwd_a in btxt
+    assert "       2.0        0.2       2.0  " + bwd_b in btxt
+    assert "sum over the kernels of one call: 6.7 MB" in btxt
     assert "elementwise" not in btxt
 
 
