@@ -116,11 +116,14 @@ enum {
  * read; out and final_state must be preallocated and are fully written. The
  * library keeps no pointer after the call returns. When it splits sequences
  * (see gdn2_chunk_fwd_opts) it takes a stream-ordered workspace of
- * N * HV * nseg * (2 K V + K K) * 4 bytes with hipMallocAsync on `stream` and
- * returns it with hipFreeAsync on the same stream (nseg = segments per
- * sequence, at most ceil(ceil(T / 64) / segment chunks)); if that
- * allocation fails it runs the sequences whole instead. Otherwise it
- * allocates no device memory.
+ * N * HV * nseg * (2 K V + K K) * 4 bytes on `stream` and returns it with
+ * hipFreeAsync on the same stream (nseg = segments per sequence, at most
+ * ceil(ceil(T / 64) / segment chunks)); if that allocation fails it runs the
+ * sequences whole instead. Otherwise it allocates no device memory.
+ * Workspaces come from a memory pool the library creates on each device it
+ * runs on (hipMemPoolCreate) with an unlimited release threshold: freed
+ * workspace stays in that pool for later calls, so the pool holds up to the
+ * largest workspace any call has used until the process ends.
  *
  * Layout (GDN2_ERR_LAYOUT otherwise; strides are in elements, as the
  * FlashInfer parameter list has it, only the innermost dimension needs to be
@@ -351,7 +354,8 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  * MFMA operands, as in the forward.
  *
  * Ownership and memory: the caller owns every buffer; inputs are only read.
- * A stream-ordered workspace (hipMallocAsync / hipFreeAsync on `stream`) of
+ * A stream-ordered workspace (from the library's pool, see gdn2_chunk_fwd;
+ * released with hipFreeAsync on `stream`) of
  *   (T / 64 + N) * HV * (2 * K * V * 4 + 516 * K + 16384) bytes,
  *   plus 2 * T * HV * K * 4 bytes when HV > H (per-value-head dq and dk)
  * (rounded up per part) holds the checkpoints, the records and partial

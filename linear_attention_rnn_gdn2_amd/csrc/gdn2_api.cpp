@@ -468,6 +468,40 @@ int validate_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor *
 }  // namespace
 
 namespace {
+// Stream-ordered workspace from a pool the library owns on each device. Its
+// release threshold is unlimited: memory freed at the end of a call stays in
+// the pool for the next one instead of going back to the driver at the next
+// synchronisation (the backward's workspace is gigabytes, and mapping it
+// afresh every call costs a large share of a call). The pool thus keeps up
+// to the largest workspace any call has used, until the process ends.
+constexpr int kPoolDevices = 64;
+std::once_flag pool_once[kPoolDevices];
+hipMemPool_t pool_of[kPoolDevices];
+
+hipError_t ws_alloc(void **ptr, size_t bytes, hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kPoolDevices) return hipMallocAsync(ptr, bytes, stream);
+    std::call_once(pool_once[dev], [dev] {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) {
+            (void)hipGetLastError();
+            return;  // no pool: the device's default one below
+        }
+        uint64_t keep = UINT64_MAX;
+        if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) != hipSuccess) (void)hipGetLastError();
+        pool_of[dev] = pool;
+    });
+    if (pool_of[dev]) return hipMallocFromPoolAsync(ptr, bytes, pool_of[dev], stream);
+    return hipMallocAsync(ptr, bytes, stream);
+}
+
 // Workspace bytes per (sequence, value head, segment) of a split run: its
 // end state from a zero start and its entering state (K x V each), and its
 // transition map (K x K), all float32.
@@ -494,7 +528,7 @@ size_t split_workspace_bytes(const gdn2::FwdParams &p, int32_t split)
 // split > 0 giving more than one segment, the split run (transition pass,
 // combine, output pass). Its workspace is `fixed` when given (the caller
 // has checked that it is large enough), else stream-ordered
-// (hipMallocAsync / hipFreeAsync on `stream`; if that allocation fails the
+// (ws_alloc / hipFreeAsync on `stream`; if that allocation fails the
 // sequences run whole). The transition pass writes no checkpoints or
 // records; the output pass writes them per segment. Returns a gdn2 status
 // (and sets the error message).
@@ -507,7 +541,7 @@ int run_forward(gdn2::FwdParams p, int32_t split, hipStream_t stream, void *fixe
         const size_t sz_b = items * p.K * p.V * sizeof(float), sz_m = items * p.K * p.K * sizeof(float);
         void *ws = fixed;
         const bool own = !fixed;
-        if (own && hipMallocAsync(&ws, bytes, stream) != hipSuccess) ws = nullptr;
+        if (own && ws_alloc(&ws, bytes, stream) != hipSuccess) ws = nullptr;
         if (ws) {
             p.seg_chunks = split;
             p.nseg = (int32_t)nseg;
@@ -548,7 +582,7 @@ hipError_t run_bwd_state(gdn2::BwdParams p, int32_t split, hipStream_t stream)
         const size_t state = (size_t)p.K * p.V * sizeof(float);
         const size_t one = (size_t)p.N * p.HV * (size_t)nseg * state;
         void *ws = nullptr;
-        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && hipMallocAsync(&ws, 3 * one, stream) == hipSuccess) {
+        if (one / state == (size_t)p.N * p.HV * (size_t)nseg && ws_alloc(&ws, 3 * one, stream) == hipSuccess) {
             p.seg_chunks = split;
             p.nseg = (int32_t)nseg;
             p.wb = static_cast<float *>(ws);
@@ -709,7 +743,7 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     const size_t sz_qk = p.H != p.HV ? up((size_t)p.T * p.HV * p.K * sizeof(float)) : 0;
     const size_t total = 2 * sz_ck + sz_prep + 2 * sz_qk;
     void *ws = nullptr;
-    if (total > 0 && hipMallocAsync(&ws, total, stream) != hipSuccess)
+    if (total > 0 && ws_alloc(&ws, total, stream) != hipSuccess)
         return fail(GDN2_ERR_HIP, "backward workspace of %zu bytes could not be allocated", total);
     char *b = static_cast<char *>(ws);
     float *s_ckpt = reinterpret_cast<float *>(b);
