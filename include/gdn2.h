@@ -356,7 +356,7 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  * Ownership and memory: the caller owns every buffer; inputs are only read.
  * A stream-ordered workspace (from the library's pool, see gdn2_chunk_fwd;
  * released with hipFreeAsync on `stream`) of
- *   (T / 64 + N) * HV * (2 * K * V * 4 + 516 * K + 16384) bytes,
+ *   (T / 64 + N) * HV * (2 * K * V * 2 + 516 * K + 16384) bytes,
  *   plus 2 * T * HV * K * 4 bytes when HV > H (per-value-head dq and dk)
  * (rounded up per part) holds the checkpoints, the records and partial
  * gradients; if it cannot be allocated the call fails with GDN2_ERR_HIP and

@@ -734,7 +734,7 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     if (rc != GDN2_OK) return rc;
     // stream-ordered workspace: forward checkpoints, state-gradient
     // checkpoints, chunk records, per-value-head dq and dk
-    const size_t state = (size_t)p.K * p.V * sizeof(float);
+    const size_t state = (size_t)p.K * p.V * sizeof(uint16_t);  // bf16 checkpoints
     const size_t chunks = (size_t)p.nslots * (size_t)p.HV;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t sz_ck = up(chunks * state);
@@ -746,9 +746,9 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     if (total > 0 && ws_alloc(&ws, total, stream) != hipSuccess)
         return fail(GDN2_ERR_HIP, "backward workspace of %zu bytes could not be allocated", total);
     char *b = static_cast<char *>(ws);
-    float *s_ckpt = reinterpret_cast<float *>(b);
+    uint16_t *s_ckpt = reinterpret_cast<uint16_t *>(b);
     p.s_ckpt = s_ckpt;
-    p.ds_ckpt = reinterpret_cast<float *>(b + sz_ck);
+    p.ds_ckpt = reinterpret_cast<uint16_t *>(b + sz_ck);
     p.prep = b + 2 * sz_ck;
     p.dq_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep);
     p.dk_ws = reinterpret_cast<float *>(b + 2 * sz_ck + sz_prep + sz_qk);

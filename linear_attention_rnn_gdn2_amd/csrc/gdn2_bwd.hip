@@ -140,13 +140,13 @@ __device__ __forceinline__ f32x4 tile_mm(const char *sm, int xo, int lx, int yo,
     return acc;
 }
 
-// MFMA operand from a float32 row-major [D][D] matrix M in global memory:
+// MFMA operand from a bf16 row-major [D][D] matrix M in global memory:
 // M[r0 + j][c] for j = 0..7 (8 rows of one column; a Y operand whose k runs
 // down the rows), each row scaled by scl[r0 + j] if given.
-__device__ __forceinline__ bf16x8 col_frag(const float *M, int ld, int r0, int c, const float *scl)
+__device__ __forceinline__ bf16x8 col_frag(const uint16_t *M, int ld, int r0, int c, const float *scl)
 {
     f32x8 x;
-    for (int j = 0; j < 8; ++j) x[j] = M[(int64_t)(r0 + j) * ld + c] * (scl ? scl[r0 + j] : 1.0f);
+    for (int j = 0; j < 8; ++j) x[j] = bf16_bits_to_f32(M[(int64_t)(r0 + j) * ld + c]) * (scl ? scl[r0 + j] : 1.0f);
     return f32x8_to_bf16(x);
 }
 
@@ -452,8 +452,8 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
             __syncthreads();
         }
         const bool flagged = lds_ld<int>(sm, L::FLG) != 0;  // workgroup-uniform
-        const float *Sin = p.s_ckpt + kd_off;
-        const float *dSo = p.ds_ckpt + kd_off;
+        const uint16_t *Sin = p.s_ckpt + kd_off;  // bf16 checkpoints
+        const uint16_t *dSo = p.ds_ckpt + kd_off;
         const float *gmu = reinterpret_cast<const float *>(sm + L::GMU);
 
         // ---- U = T WV - wy_w S_in (bf16 [token][D] in RGA); wave wv takes
@@ -493,28 +493,23 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         {
             bf16x8 fr[D / 32], fc[D / 32];
             // row 16 ni + l16 of dS_out and of S_in, columns 32 ks + 8 q4 .. + 7:
-            // MFMA operands, and dgamma's direct part rowsum(S_in dS_out)
-            // in float32 (lanes q4 = 0..3 of a row together cover it; the
-            // waves of one column tile hold the same rows, the first stores)
-            f32x4 ro[D / 32][2], rs[D / 32][2];
+            // MFMA operands as stored (bf16), and dgamma's direct part
+            // rowsum(S_in dS_out) in float32 (lanes q4 = 0..3 of a row
+            // together cover it; the waves of one column tile hold the same
+            // rows, the first stores)
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 const int64_t o = (int64_t)(16 * ni + l16) * D + 32 * ks + 8 * q4;
-                ro[ks][0] = *reinterpret_cast<const f32x4 *>(dSo + o);
-                ro[ks][1] = *reinterpret_cast<const f32x4 *>(dSo + o + 4);
-                rs[ks][0] = *reinterpret_cast<const f32x4 *>(Sin + o);
-                rs[ks][1] = *reinterpret_cast<const f32x4 *>(Sin + o + 4);
+                fc[ks] = *reinterpret_cast<const bf16x8 *>(dSo + o);
+                fs[ks] = *reinterpret_cast<const bf16x8 *>(Sin + o);
             }
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) fr[ks] = col_frag(dSo, D, 32 * ks + 8 * q4, 16 * ni + l16, gmu);
             float sdot = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
-                fc[ks] = f32x8_to_bf16(__builtin_shufflevector(ro[ks][0], ro[ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                fs[ks] = f32x8_to_bf16(__builtin_shufflevector(rs[ks][0], rs[ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                for (int h = 0; h < 2; ++h)
-                    sdot += rs[ks][h][0] * ro[ks][h][0] + rs[ks][h][1] * ro[ks][h][1] + rs[ks][h][2] * ro[ks][h][2] +
-                            rs[ks][h][3] * ro[ks][h][3];
+                const f32x8 a = __builtin_convertvector(fs[ks], f32x8), b = __builtin_convertvector(fc[ks], f32x8);
+                for (int j = 0; j < 8; ++j) sdot = fmaf(a[j], b[j], sdot);
             }
             sdot += __shfl_xor(sdot, 16);
             sdot += __shfl_xor(sdot, 32);
@@ -939,10 +934,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
         if (tid < D) lds_st<float>(sm, L::GAM + 4 * tid, xg);
         // the gradient of this chunk's S_out
         if (save) {
-            float *dso = p.ds_ckpt + (slot * p.HV + hv) * D * D;
+            uint16_t *dso = p.ds_ckpt + (slot * p.HV + hv) * D * D;  // rounded to bf16
             for (int rt = 0; rt < NRT; ++rt)
                 for (int jt = 0; jt < NCT; ++jt)
-                    for (int e = 0; e < 4; ++e) dso[(16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = dS[rt][jt][e];
+                    for (int e = 0; e < 4; ++e)
+                        dso[(16 * rt + 4 * q4 + e) * D + vbase + 16 * jt + l16] = __builtin_bit_cast(uint16_t, (__bf16)dS[rt][jt][e]);
         }
         __syncthreads();
 

@@ -389,7 +389,7 @@ struct Chain {
     bool ident;       // entering state is the identity (transition pass, K == V)
     bool zero_v;      // values taken as zero (transition pass)
     bool out;         // write the output rows
-    float *ckpt;      // the state entering each chunk, chunk c at ckpt + c * HV * K * V (nullptr: none)
+    uint16_t *ckpt;   // the state entering each chunk (bf16), chunk c at ckpt + c * HV * K * V (nullptr: none)
     char *rec;        // each chunk's record, chunk c at rec + c * HV * bwd_prep_bytes(K) (REC kernels)
 };
 
@@ -1271,11 +1271,12 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         // token order.
         bf16x8 Ub[2][NCT], Sb[NKS][NCT];
         if (it > 0 && ch.ckpt) {
-            // the float32 state entering chunk it - 1 (for the backward)
-            float *const dst = ch.ckpt + (int64_t)(it - 1) * p.HV * (K * V) + vbase + l16;
+            // the state entering chunk it - 1, rounded to bf16 (for the backward)
+            uint16_t *const dst = ch.ckpt + (int64_t)(it - 1) * p.HV * (K * V) + vbase + l16;
             for (int rt = 0; rt < NRT; ++rt)
                 for (int jt = 0; jt < NCT; ++jt)
-                    for (int e = 0; e < 4; ++e) dst[state_chan(rt, q4, e) * V + 16 * jt] = S[rt][jt][e];
+                    for (int e = 0; e < 4; ++e)
+                        dst[state_chan(rt, q4, e) * V + 16 * jt] = __builtin_bit_cast(uint16_t, (__bf16)S[rt][jt][e]);
         }
         if (it > 0) {
             for (int ks = 0; ks < NKS; ++ks)

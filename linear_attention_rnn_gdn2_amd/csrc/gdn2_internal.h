@@ -52,11 +52,12 @@ struct FwdParams {
     float *wb;             // [N, HV, nseg, K, V] segment end state from a zero start (segment 0: from h0)
     float *wm;             // [N, HV, nseg, K, K] segment transition (state map S_in -> S_out minus wb)
     float *ws;             // [N, HV, nseg, K, V] entering state of segment j >= 1
-    // Optional: the float32 K-major state entering every chunk, written to
+    // Optional: the K-major state entering every chunk, rounded to bf16
+    // (the backward uses it as bf16 MFMA operands), written to
     // ckpt[slot][hv] with slot = cu[n] / 64 + n + c for chunk c of sequence
     // n (whole sequences, or the output pass of a split run; out may then
     // be nullptr: no output)
-    float *ckpt;
+    uint16_t *ckpt;        // bf16 [slot][HV][K][V]
     // Optional, with ckpt (bf16 io, float32 g, no L2 normalisation): every
     // chunk's record (PrepRecord) at rec + (slot * HV + hv) * bwd_prep_bytes(K)
     char *rec;
@@ -82,8 +83,8 @@ struct BwdParams {
     void *dg;                    // [T, HV, K] gtype
     // workspace
     float *dq_ws, *dk_ws;        // [T, HV, K] per value head (grouped heads only)
-    const float *s_ckpt;         // [nslots, HV, K, V] state entering each chunk
-    float *ds_ckpt;              // [nslots, HV, K, V] gradient of the state leaving each chunk
+    const uint16_t *s_ckpt;      // [nslots, HV, K, V] bf16: state entering each chunk
+    uint16_t *ds_ckpt;           // [nslots, HV, K, V] bf16: gradient of the state leaving each chunk
     char *prep;                  // [nslots, HV] x bwd_prep_bytes(K): each chunk's record (PrepRecord)
     int64_t T;
     int32_t N, H, HV, K, V;
