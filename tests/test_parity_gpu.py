@@ -115,11 +115,13 @@ def assert_slices(tag, out, fin, ro, rs, cu, min_len=1):
 
 
 @pytest.mark.parametrize("cfg,seed", [(0, None), (1, None), (2, None), (3, None), (4, None),
-                                      (2, 100), (2, 101), (2, 102), (4, 100), (4, 101), (4, 102)])
+                                      (2, 100), (2, 101), (2, 102), (4, 100), (4, 101), (4, 102),
+                                      (0, 100), (0, 101), (1, 100), (1, 101), (3, 100)])
 def test_workload_parity(lib, c_oracle, cfg, seed):
-    """Every workload at full size (seed = its id), and the headline and
-    long-decay workloads at three more seeds, against the C oracle: whole
-    tensors, then every (sequence, value head) slice."""
+    """Every workload at full size (seed = its id), the headline and
+    long-decay workloads at three more seeds and the others at one or two,
+    against the C oracle: whole tensors, then every (sequence, value head)
+    slice."""
     say(f"[workload {cfg} seed {seed}] {WORKLOADS[cfg].name}: drawing inputs")
     d = make_inputs(cfg, seed)
     say(f"[workload {cfg} seed {seed}] T={int(d['cu_seqlens'][-1])} running GPU")
