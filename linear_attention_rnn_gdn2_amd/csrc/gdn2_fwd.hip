@@ -1138,30 +1138,55 @@ __device__ __forceinline__ void t2_column(char *sm, int l16, int q4)
     }
 }
 
-// Phase AP of a state wave: its four tiles (t = 4 + rw + 4 m) of A and P
-// from the single-reference operands. Every operand read of the four tiles
-// is issued before the first product, so that their LDS round trips overlap
-// and the four accumulation chains interleave.
+// The state waves' tiles of A and P (t = 4..19), four per wave, grouped so
+// that a wave's tiles share operands: wave 0 A(3,0) P(3,0) A(3,1) P(3,1),
+// wave 1 A(3,2) P(3,2) P(3,3) P(2,2), wave 2 A(2,0) P(2,0) A(2,1) P(2,1),
+// wave 3 A(1,0) P(1,0) P(1,1) P(0,0). Four bits per entry (t - 4).
+__device__ __forceinline__ int ap_tile_of(int rw, int m) { return 4 + (int)((0x6870a291bfe5d4c3ull >> (4 * (4 * rw + m))) & 15); }
+
+// Phase AP of a state wave: its four tiles (ap_tile_of) of A and P from the
+// single-reference operands. Each distinct operand tile is read once: the
+// row side KB_i and QH_i of one row tile i (and QH_i2 of a second on odd
+// waves) and the column side RR_ja, RR_jb: at most five operand tiles per
+// wave instead of eight.
+// Every read is issued before the first product, so that their LDS round
+// trips overlap and the four accumulation chains interleave.
 template <int K, int V>
 __device__ __forceinline__ void state_ap_tiles(const char *sm, int o_k8, int it, int rw, f32x4 (&acc)[4])
 {
     using L = Lds<K, V>;
-    constexpr int RK = 2 * L::KP;
+    constexpr int RK = 2 * L::KP, NKS = K / 32;
     const char *const b_k8 = sm + o_k8;
     const int xq = L::QH + (it & 1) * L::QH_SZ;  // QH of this chunk for P tiles
-    bf16x8 ra[4][K / 32], xa[4][K / 32];
-    for (int m = 0; m < 4; ++m) {
-        const int t = 4 + rw + 4 * m;
-        const int i = tile_i(t), j = tile_j(t);
-        const int xo = (t >= 10 ? xq : L::KB) + 16 * i * RK;
-        for (int ks = 0; ks < K / 32; ++ks) {
-            ra[m][ks] = lds_ld<bf16x8>(b_k8, L::RR + 16 * j * RK + 64 * ks);
-            xa[m][ks] = lds_ld<bf16x8>(b_k8, xo + 64 * ks);
+    const int w = __builtin_amdgcn_readfirstlane(rw);
+    const bool odd = (w & 1) != 0;
+    const int ja = w == 1 ? 2 : 0, jb = ja + 1;            // column tiles
+    const int i0 = w < 2 ? 3 : w == 2 ? 2 : 1, i2 = w == 1 ? 2 : 0;  // row tiles
+    bf16x8 ra[NKS], rb[NKS], x0[NKS], x1[NKS], x2[NKS];
+    for (int ks = 0; ks < NKS; ++ks) {
+        ra[ks] = lds_ld<bf16x8>(b_k8, L::RR + 16 * ja * RK + 64 * ks);
+        rb[ks] = lds_ld<bf16x8>(b_k8, L::RR + 16 * jb * RK + 64 * ks);
+        x0[ks] = lds_ld<bf16x8>(b_k8, L::KB + 16 * i0 * RK + 64 * ks);
+        x1[ks] = lds_ld<bf16x8>(b_k8, xq + 16 * i0 * RK + 64 * ks);
+    }
+    if (odd)
+        for (int ks = 0; ks < NKS; ++ks) x2[ks] = lds_ld<bf16x8>(b_k8, xq + 16 * i2 * RK + 64 * ks);
+    for (int m = 0; m < 4; ++m) acc[m] = f32x4{0, 0, 0, 0};
+    if (odd) {
+        for (int ks = 0; ks < NKS; ++ks) {
+            acc[0] = mfma_bf16(ra[ks], x0[ks], acc[0]);
+            acc[1] = mfma_bf16(ra[ks], x1[ks], acc[1]);
+            acc[2] = mfma_bf16(rb[ks], x1[ks], acc[2]);
+            acc[3] = mfma_bf16(ra[ks], x2[ks], acc[3]);
+        }
+    } else {
+        for (int ks = 0; ks < NKS; ++ks) {
+            acc[0] = mfma_bf16(ra[ks], x0[ks], acc[0]);
+            acc[1] = mfma_bf16(ra[ks], x1[ks], acc[1]);
+            acc[2] = mfma_bf16(rb[ks], x0[ks], acc[2]);
+            acc[3] = mfma_bf16(rb[ks], x1[ks], acc[3]);
         }
     }
-    for (int m = 0; m < 4; ++m) acc[m] = f32x4{0, 0, 0, 0};
-    for (int ks = 0; ks < K / 32; ++ks)
-        for (int m = 0; m < 4; ++m) acc[m] = mfma_bf16(ra[m][ks], xa[m][ks], acc[m]);
 }
 
 // The causal part of the four tiles: A as float32 into AB, P as bf16 into PB.
@@ -1171,7 +1196,7 @@ __device__ __forceinline__ void state_ap_store(char *sm, const f32x4 (&acc)[4], 
     using L = Lds<K, V>;
     constexpr int RC = 2 * L::CP, RA = 4 * L::AP;
     for (int m = 0; m < 4; ++m) {
-        const int t = 4 + rw + 4 * m;
+        const int t = ap_tile_of(rw, m);
         const int i = tile_i(t), j = tile_j(t);
         const bool isP = t >= 10;
         const f32x4 x = ap_mask(acc[m], i == j, isP, l16, q4);
@@ -1376,7 +1401,7 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
             __syncthreads();  // ----------------------------------------- B2x
             const int xb = L::QH + ((it + 1) & 1) * L::QH_SZ, nbm = xbatches<K, V>(sm);
             for (int m = 0; m < 4; ++m) {
-                const int t = 4 + rw + 4 * m;
+                const int t = ap_tile_of(rw, m);
                 acc[m] = xtile<K, V>(sm, xb, tile_i(t), tile_j(t), t >= 10 ? 1 : 0, nbm, l16, q4, acc[m]);
             }
             state_ap_store<K, V>(sm, acc, rw, o_c4, o_a4, l16, q4);
