@@ -151,7 +151,7 @@ def _resource_lines(outdir, name, want):
     have = [(c, h) for c, h in cols if rows and c in rows[0]]
     seen, out = set(), ["VGPR as rocprofv3 prints it: its granule count times 4; gfx950 allocates 8 VGPRs per "
                         "granule, so the allocation is twice this figure (the compiler's resource remark for the "
-                        "forward kernel: 246 VGPRs, allocated 248)", "",
+                        "forward kernel: 253 VGPRs, allocated 256)", "",
                         "  ".join(f"{h:>9}" for _, h in have) + "  kernel"]
     for r in rows:
         if not want(r["Kernel_Name"]) or r["Kernel_Name"] in seen:
