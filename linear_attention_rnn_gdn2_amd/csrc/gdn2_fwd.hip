@@ -393,31 +393,47 @@ struct Chain {
     char *rec;        // each chunk's record, chunk c at rec + c * HV * bwd_prep_bytes(K) (REC kernels)
 };
 
-// Copy n 16-byte pieces of a [64][K] bf16 tile from LDS (row pitch lp bytes)
-// to a row-major global tile (row pitch 2 K bytes), piece e by thread
-// t + m NT; xm flips sign bits (0x80008000: negate every element).
+// Copy a [64][K] bf16 tile from LDS (row pitch lp bytes) to a row-major
+// global tile (row pitch 2 K bytes) in 16-byte pieces, piece e by thread
+// t + i NT; xm flips sign bits (0x80008000: negate every element). Every
+// LDS read is issued before the first store, so that the copy waits for
+// LDS once instead of once per piece.
 template <int K, int NT>
 __device__ __forceinline__ void rec_tile(char *dst, const char *sm, int lo, int lp, int t, uint32_t xm)
 {
     constexpr int PR = 2 * K / 16;  // pieces per row
-    for (int e = t; e < 64 * PR; e += NT) {
-        const int r = e / PR, cb = 16 * (e % PR);
-        const i32x4 x = lds_ld<i32x4>(sm, lo + r * lp + cb);
-        const int m = (int)xm;
-        *reinterpret_cast<i32x4 *>(dst + r * (2 * K) + cb) = i32x4{x[0] ^ m, x[1] ^ m, x[2] ^ m, x[3] ^ m};
+    constexpr int NE = 64 * PR, NI = (NE + NT - 1) / NT;
+    i32x4 x[NI];
+    for (int i = 0; i < NI; ++i) {
+        const int e0 = t + NT * i, e = e0 < NE ? e0 : NE - 1;  // a thread past the end re-reads the last piece
+        x[i] = lds_ld<i32x4>(sm, lo + (e / PR) * lp + 16 * (e % PR));
+    }
+    const int m = (int)xm;
+    for (int i = 0; i < NI; ++i) {
+        const int e = t + NT * i;
+        if (NE % NT == 0 || e < NE)
+            *reinterpret_cast<i32x4 *>(dst + (e / PR) * (2 * K) + 16 * (e % PR)) =
+                i32x4{x[i][0] ^ m, x[i][1] ^ m, x[i][2] ^ m, x[i][3] ^ m};
     }
 }
 
 // T (bf16 [64][64], LDS pitch lp) to the record: the 16x16 blocks above the
 // diagonal are never written in LDS (the products skip them) and go out as
-// zero; the diagonal blocks hold exact zeros above their diagonal.
+// zero; the diagonal blocks hold exact zeros above their diagonal. Reads
+// first, then stores, as in rec_tile.
 template <int NT>
 __device__ __forceinline__ void rec_t(char *dst, const char *sm, int lo, int lp, int t)
 {
-    for (int e = t; e < 64 * 8; e += NT) {
+    constexpr int NE = 64 * 8, NI = (NE + NT - 1) / NT;
+    i32x4 x[NI];
+    for (int i = 0; i < NI; ++i) {
+        const int e0 = t + NT * i, e = e0 < NE ? e0 : NE - 1;
         const int r = e >> 3, cb = 16 * (e & 7);
-        const i32x4 x = (cb >> 5) > (r >> 4) ? i32x4{0, 0, 0, 0} : lds_ld<i32x4>(sm, lo + r * lp + cb);
-        *reinterpret_cast<i32x4 *>(dst + r * 128 + cb) = x;
+        x[i] = (cb >> 5) > (r >> 4) ? i32x4{0, 0, 0, 0} : lds_ld<i32x4>(sm, lo + r * lp + cb);
+    }
+    for (int i = 0; i < NI; ++i) {
+        const int e = t + NT * i;
+        if (NE % NT == 0 || e < NE) *reinterpret_cast<i32x4 *>(dst + (e >> 3) * 128 + 16 * (e & 7)) = x[i];
     }
 }
 
@@ -1072,12 +1088,6 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // stalls until the CU's memory pipeline has room); WY and the next
         // phase E hide the latency
         load_keys<K, RPT, IO>(R, p, c0 + CH, chunk_len(c0 + CH, ch.te), ch.hk, ch.hv, row0, c0k);  // empty range past the end
-        // the backward's record of this chunk, first part: KB, RR
-        if constexpr (REC) {
-            constexpr PrepRecord PR{K};
-            char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
-            rec_tile<K, NROLE>(rc + PR.kb(), sm, L::KB, RK, rt, 0u);
-        }
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- WY: -wy_w for this wave's channel tiles but the last when there
@@ -1087,12 +1097,12 @@ __device__ __forceinline__ void key_role(char *smem, const FwdParams &p, const C
         // this chunk has read the previous ones)
         if constexpr (L2N)
             if (it + 1 < nc) norm_partials<K, V, RPT, IO>(R, sm, rt);
-        // second part: QH, P, T and 2^G_last (negated in flagged channels)
+        // the backward's record of this chunk, last part: T (complete at B4)
+        // and 2^G_last (negated in flagged channels); RR went out in phase
+        // E, KB, QH and P from the state waves in phase T2
         if constexpr (REC) {
             constexpr PrepRecord PR{K};
             char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
-            rec_tile<K, NROLE>(rc + PR.qh(), sm, qb, RK, rt, 0u);
-            rec_tile<64, NROLE>(rc + PR.p(), sm, L::PB, RC, rt, 0u);
             rec_t<NROLE>(rc + PR.t(), sm, L::TB, RC, rt);
             if (rt < K / 4) {
                 const f32x4 gm = lds_ld<f32x4>(sm, L::GAM + 16 * rt);
@@ -1430,6 +1440,19 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         if (rw == 0) t2_column<K, V, 0>(sm, l16, q4);
         else if (rw == 1) t2_column<K, V, 1>(sm, l16, q4);
         else if (rw == 2) t2_column<K, V, 2>(sm, l16, q4);
+        // the backward's record of this chunk: KB, QH and P (final since B3)
+        // from waves 1-3, whose block columns are short or empty and whose
+        // memory queue is idle here (behind the key waves' loads of the next
+        // chunk, these stores would hold up B4)
+        if constexpr (REC) {
+            if (rw > 0) {
+                constexpr PrepRecord PR{K};
+                char *const rc = ch.rec + (int64_t)it * p.HV * PR.bytes();
+                rec_tile<K, NROLE - 64>(rc + PR.kb(), sm, L::KB, RK, tid - 64, 0u);
+                rec_tile<K, NROLE - 64>(rc + PR.qh(), sm, L::QH + (it & 1) * L::QH_SZ, RK, tid - 64, 0u);
+                rec_tile<64, NROLE - 64>(rc + PR.p(), sm, L::PB, RC, tid - 64, 0u);
+            }
+        }
         __syncthreads();  // ------------------------------------------ B4
 
         // ---- WY: the last -wy_w channel tile of key wave rw (K = 128), then
