@@ -1583,51 +1583,81 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
 // The state pass is affine in the entering state, so a sequence cut into
 // segments j = 0 .. last has S_{j+1} = M_j S_j + B_j, with B_j the end state
 // of segment j from a zero start (from the true initial state for j = 0) and
-// M_j its K x K transition. One workgroup per (sequence, value head, 4
+// M_j its K x K transition. One workgroup per (sequence, value head, 16
 // columns) applies the recurrence in float32 and stores every entering state
-// S_j (j >= 1) for the output pass.
-constexpr int CMB_COLS = 4;  // state columns per workgroup; two per thread
+// S_j (j >= 1) for the output pass. Thread (r, cp) owns row r and columns
+// 2 cp, 2 cp + 1 of the block. M_j goes to LDS once per workgroup (instead
+// of a row per thread from the L2), double-buffered: M_{j+1} and B_{j+1} are
+// fetched while step j's products run, so a step costs one barrier and its
+// arithmetic, not a memory round trip. Each entry is B_j plus the products in
+// order k = 0 .. K-1, one fused multiply-add each.
+constexpr int CMB_COLS = 16;  // state columns per workgroup; two per thread
 
 template <int K>
 constexpr int cmb_threads() { return K * CMB_COLS / 2; }
 
+template <int K>
+struct CmbLds {
+    static constexpr int MP = K + 4;  // float pitch of a map row (16-byte reads of 8 rows: no bank conflict)
+    float m[2][K][MP];
+    float s[2][K][CMB_COLS];
+};
+
 template <int K, int V>
 __global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams p)
 {
-    __shared__ __attribute__((aligned(16))) float Sl[K][CMB_COLS];
+    constexpr int NT = cmb_threads<K>(), NL = K * K / 4 / NT;  // 16-byte pieces of a map per thread
+    static_assert(K * K % (4 * NT) == 0 && V % CMB_COLS == 0, "combine tiling");
+    __shared__ __attribute__((aligned(16))) CmbLds<K> L;
     const int ncb = V / CMB_COLS;
     const int chain = blockIdx.x / ncb, cb = blockIdx.x - chain * ncb;
     const int n = chain / p.HV;
     const int last = seg_last(seq_of(p, n), p.seg_chunks);
     if (last == 0) return;
-    const int t = threadIdx.x, r = t >> 1, c = CMB_COLS / 2 * (t & 1);
+    const int t = threadIdx.x, r = t / (CMB_COLS / 2), cp = t % (CMB_COLS / 2);
     const int64_t seg0 = (int64_t)chain * p.nseg * K * V;  // chain = n * HV + hv
     const int64_t map0 = (int64_t)chain * p.nseg * K * K;  // the maps: K x K each
-    const int col = cb * CMB_COLS + c;
-    float s0 = p.wb[seg0 + r * V + col], s1 = p.wb[seg0 + r * V + col + 1];
-    p.ws[seg0 + (int64_t)K * V + r * V + col] = s0;
-    p.ws[seg0 + (int64_t)K * V + r * V + col + 1] = s1;
+    const int col = cb * CMB_COLS + 2 * cp;
+    const int64_t rc = (int64_t)r * V + col;
+    f32x2 s = *reinterpret_cast<const f32x2 *>(p.wb + seg0 + rc);
+    *reinterpret_cast<f32x2 *>(p.ws + seg0 + (int64_t)K * V + rc) = s;
+    if (last < 2) return;
+    // M_1 and B_1
+    f32x4 mr[NL];
+    for (int i = 0; i < NL; ++i) mr[i] = *reinterpret_cast<const f32x4 *>(p.wm + map0 + (int64_t)K * K + 4 * (t + NT * i));
+    f32x2 b = *reinterpret_cast<const f32x2 *>(p.wb + seg0 + (int64_t)K * V + rc);
+    for (int i = 0; i < NL; ++i) {
+        const int e = 4 * (t + NT * i);
+        *reinterpret_cast<f32x4 *>(&L.m[1][e / K][e % K]) = mr[i];
+    }
     for (int j = 1; j < last; ++j) {
-        // row r of M_j and this thread's entries of B_j, all loads in flight
-        // together (one memory round trip per step)
-        const int64_t sj = seg0 + (int64_t)j * K * V;
-        const float *m = p.wm + map0 + (int64_t)j * K * K + (int64_t)r * K;
-        f32x4 mr[K / 4];
-        for (int k4 = 0; k4 < K / 4; ++k4) mr[k4] = *reinterpret_cast<const f32x4 *>(m + 4 * k4);
-        float a0 = p.wb[sj + r * V + col], a1 = p.wb[sj + r * V + col + 1];
-        __syncthreads();  // the previous step's reads of Sl are done
-        Sl[r][c] = s0;
-        Sl[r][c + 1] = s1;
-        __syncthreads();
-        for (int k4 = 0; k4 < K / 4; ++k4)
+        const int bj = j & 1;
+        *reinterpret_cast<f32x2 *>(&L.s[bj][r][2 * cp]) = s;
+        __syncthreads();  // M_j and S_j in LDS; step j - 1's reads of these buffers are done
+        const bool more = j + 1 < last;
+        f32x2 bn = {0.0f, 0.0f};
+        if (more) {
+            for (int i = 0; i < NL; ++i)
+                mr[i] = *reinterpret_cast<const f32x4 *>(p.wm + map0 + (int64_t)(j + 1) * K * K + 4 * (t + NT * i));
+            bn = *reinterpret_cast<const f32x2 *>(p.wb + seg0 + (int64_t)(j + 1) * K * V + rc);
+        }
+        float a0 = b[0], a1 = b[1];
+        for (int k4 = 0; k4 < K / 4; ++k4) {
+            const f32x4 m = *reinterpret_cast<const f32x4 *>(&L.m[bj][r][4 * k4]);
             for (int e = 0; e < 4; ++e) {
-                a0 = fmaf(mr[k4][e], Sl[4 * k4 + e][c], a0);
-                a1 = fmaf(mr[k4][e], Sl[4 * k4 + e][c + 1], a1);
+                const f32x2 x = *reinterpret_cast<const f32x2 *>(&L.s[bj][4 * k4 + e][2 * cp]);
+                a0 = fmaf(m[e], x[0], a0);
+                a1 = fmaf(m[e], x[1], a1);
             }
-        s0 = a0;
-        s1 = a1;
-        p.ws[sj + (int64_t)K * V + r * V + col] = s0;
-        p.ws[sj + (int64_t)K * V + r * V + col + 1] = s1;
+        }
+        s = f32x2{a0, a1};
+        *reinterpret_cast<f32x2 *>(p.ws + seg0 + (int64_t)(j + 1) * K * V + rc) = s;
+        if (more)
+            for (int i = 0; i < NL; ++i) {
+                const int e = 4 * (t + NT * i);
+                *reinterpret_cast<f32x4 *>(&L.m[bj ^ 1][e / K][e % K]) = mr[i];
+            }
+        b = bn;
     }
 }
 
