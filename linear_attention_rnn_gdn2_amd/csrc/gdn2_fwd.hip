@@ -1342,8 +1342,9 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
         load_values<V, RPTV, IO>(vr, wr, p, c0, len, ch.hv, emv.row0, emv.c0, ch.zero_v);
 
         // ---- S, second half: the output, computed transposed,
-        // O^T = scale (S^T QH^T + U^T P^T), stored as 4 consecutive values
-        // of an output row per lane; then S <- diag(2^G_last) S + KT^T U,
+        // O^T = scale (S^T QH^T + U^T P^T), 4 consecutive values of an
+        // output row per lane, staged in LDS and stored as 16-byte pieces;
+        // then S <- diag(2^G_last) S + KT^T U,
         // with KT^T operands from transpose reads of the row-major KT
         // (tokens in the permuted order of Ub).
         if (it > 0) {
@@ -1365,11 +1366,20 @@ __device__ __forceinline__ void state_role(char *smem, const FwdParams &p, const
                         const bf16x8 bp = cat4(lds_ld<bf16x4>(b_c4, o), lds_ld<bf16x4>(b_c4, o + 32));
                         for (int jt = 0; jt < NCT; ++jt) Y[jt] = mfma_bf16(Ub[ks][jt], bp, Y[jt]);
                     }
-                    if (row < lenp)
-                        for (int jt = 0; jt < NCT; ++jt)
-                            *reinterpret_cast<typename IoT<IO>::v4 *>(p.out + (cp + row) * p.so + ch.hv * p.hso + vbase +
-                                                                      16 * jt + 4 * q4) =
-                                __builtin_convertvector(Y[jt] * p.scale, typename IoT<IO>::v4);
+                    // staged in this wave's columns of the free WV region
+                    for (int jt = 0; jt < NCT; ++jt)
+                        lds_st<typename IoT<IO>::v4>(sm, L::WV + row * RV + 2 * (vbase + 16 * jt + 4 * q4),
+                                                     __builtin_convertvector(Y[jt] * p.scale, typename IoT<IO>::v4));
+                }
+                // ... and stored from there as 16-byte pieces of a row, the
+                // wave's VW columns of a row contiguous (its own LDS writes
+                // precede these reads: no barrier)
+                constexpr int PPR = VW / 8, RPI = 64 / PPR;  // pieces per row, rows per store
+                const int pr = lane / PPR, pc = 8 * (lane % PPR);
+                for (int m = 0; m < CH / RPI; ++m) {
+                    const int r = RPI * m + pr;
+                    const i32x4 x = lds_ld<i32x4>(sm, L::WV + r * RV + 2 * (vbase + pc));
+                    if (r < lenp) *reinterpret_cast<i32x4 *>(p.out + (cp + r) * p.so + ch.hv * p.hso + vbase + pc) = x;
                 }
             }
             // KT transpose reads: lane group l16 & 3 reads 4 channels, which
