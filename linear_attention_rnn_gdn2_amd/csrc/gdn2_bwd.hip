@@ -392,6 +392,7 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
     int n;
     int64_t c;
     if (!slot_owner(p.cu, p.cu64, p.T, p.N, slot, &n, &c)) return;  // no chunk in this slot
+    if (p.grp && p.grp[n] != p.gsel) return;  // the other launch's sequence
     const SeqRange sr = seq_of(p, n);
     const int64_t sb = sr.b, se = sr.e;
     const int64_t t0 = sb + c * 64;
@@ -407,9 +408,9 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         // dO (bf16 [token][D]; rows past the end zero) rides along with the
         // record; it goes to LDS once WV is no longer needed there
         i32x4 xdo[NU8];
+        i32x4 vr[NU8], wr[NU8];  // raw v, w rows: WV again and the epilogue's dv, dw
         {
             bf16x8 x[4][NU8], xpt[2];
-            i32x4 vr[NU8], wr[NU8];
             const int src[4] = {R.qh(), R.kb(), R.rr(), R.wy()};
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
@@ -563,16 +564,9 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         __syncthreads();
 
-        // ---- WV again (bf16 in RGA)
+        // ---- WV again (bf16 in RGA), from the v and w rows held in registers
+        // since the record load (no second read of either)
         {
-            i32x4 vr[NU8], wr[NU8];
-#pragma unroll
-            for (int u = 0; u < NU8; ++u) {
-                const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
-                const int64_t tv = ((t0 + r) * p.HV + hv) * D + c0;
-                vr[u] = r < len ? ld_raw8(p.v + tv) : i32x4{};
-                wr[u] = r < len ? ld_raw8(p.w + tv) : i32x4{};
-            }
 #pragma unroll
             for (int u = 0; u < NU8; ++u) {
                 const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
@@ -719,16 +713,14 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
         }
         constexpr int RF = L::RF, EF = L::EF;
         __syncthreads();  // every read of the regions below is done
-        // the row-parallel part's k, beta, v and w, in flight from here
-        i32x4 ek[NU8], eb[NU8], ev[NU8], ew[NU8];
+        // the row-parallel part's k and beta, in flight from here
+        i32x4 ek[NU8], eb[NU8];
 #pragma unroll
         for (int u = 0; u < NU8; ++u) {
             const int e = tid + CT * u, r = e / (D / 8), c0 = 8 * (e % (D / 8));
             const int64_t tk = ((t0 + r) * p.H + hk) * D + c0, tv = ((t0 + r) * p.HV + hv) * D + c0;
             ek[u] = r < len ? ld_raw8(p.k + tk) : i32x4{};
             eb[u] = r < len ? ld_raw8(p.beta + tv) : i32x4{};
-            ev[u] = r < len ? ld_raw8(p.v + tv) : i32x4{};
-            ew[u] = r < len ? ld_raw8(p.w + tv) : i32x4{};
         }
         if (tid < D) {
             // G_last's gradient: gamma rowsum(S_in dS_out) + GMU colsum(dKH RR)
@@ -795,8 +787,8 @@ __global__ __launch_bounds__(CT) void bwd_chunk_kernel(BwdParams p)
                 st_io8(p.dbeta + tv, db, p.io);
                 // dv = dWV w, dw = dWV v
                 const f32x8 dwv = __builtin_convertvector(lds_ld<bf16x8>(sm, L::DWV + 2 * (r * D + c0)), f32x8);
-                st_io8(p.dv + tv, dwv * io8_f32(ew[u], p.io), p.io);
-                st_io8(p.dw + tv, dwv * io8_f32(ev[u], p.io), p.io);
+                st_io8(p.dv + tv, dwv * io8_f32(wr[u], p.io), p.io);
+                st_io8(p.dw + tv, dwv * io8_f32(vr[u], p.io), p.io);
             }
             lds_st<f32x4>(sm, o, __builtin_shufflevector(dG, dG, 0, 1, 2, 3));
             lds_st<f32x4>(sm, o + 16, __builtin_shufflevector(dG, dG, 4, 5, 6, 7));
@@ -850,6 +842,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_state_kernel(BwdParams p)
     const int seg = SPLIT ? item % p.nseg : 0;
     if (SPLIT) item /= p.nseg;
     const int n = item / p.HV, hv = item % p.HV;
+    if (p.grp && p.grp[n] != p.gsel) return;  // the other launch's sequence
     const SeqRange sr = seq_of(p, n);
     const int64_t sb = sr.b, se = sr.e;
     const int nc = (int)chunks_of(sr);
@@ -1010,7 +1003,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p)
     }
 }
 
+// ------------------------------------------------------------- groups --
+// The two-stream schedule's groups: rank every sequence by its chunk count
+// (more first, ties to the lower index); the first nlong form group 0.
+__global__ __launch_bounds__(256) void bwd_group_kernel(BwdParams p, int32_t nlong, int32_t *grp)
+{
+    for (int n = threadIdx.x; n < p.N; n += blockDim.x) {
+        const int64_t cn = chunks_of(seq_of(p, n));
+        int rank = 0;
+        for (int j = 0; j < p.N; ++j) {
+            const int64_t cj = chunks_of(seq_of(p, j));
+            rank += cj > cn || (cj == cn && j < n);
+        }
+        grp[n] = rank < nlong ? 0 : 1;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_bwd_group(const BwdParams &p, int32_t nlong, int32_t *grp, hipStream_t stream)
+{
+    if (p.N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_group_kernel, dim3(1), dim3(256), 0, stream, p, nlong, grp);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_chunk(const BwdParams &p, hipStream_t stream)
 {

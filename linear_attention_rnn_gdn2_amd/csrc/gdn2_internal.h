@@ -61,6 +61,11 @@ struct FwdParams {
     // Optional, with ckpt (bf16 io, float32 g, no L2 normalisation): every
     // chunk's record (PrepRecord) at rec + (slot * HV + hv) * bwd_prep_bytes(K)
     char *rec;
+    // Optional sequence filter (the backward's two-stream schedule): with
+    // grp set, the workgroups of a sequence n with grp[n] != gsel return at
+    // once, so that two launches with gsel 0 and 1 share the work
+    const int32_t *grp = nullptr;  // [N]
+    int32_t gsel = 0;
 };
 
 // Arguments of the backward kernels (all tensors dense, row-major).
@@ -98,6 +103,9 @@ struct BwdParams {
     // entering gradient. wb, wm, ws: [N, HV, nseg, K, V] float32.
     int32_t seg_chunks, nseg, pass;
     float *wb, *wm, *ws;
+    // Optional sequence filter, as FwdParams::grp
+    const int32_t *grp = nullptr;  // [N]
+    int32_t gsel = 0;
 };
 
 // Byte offsets of one chunk's record in BwdParams::prep (K = V = D): the
@@ -169,6 +177,10 @@ hipError_t launch_recurrent_fwd(const FwdParams &p, hipStream_t stream);
 hipError_t launch_bwd_chunk(const BwdParams &p, hipStream_t stream);
 hipError_t launch_bwd_state(const BwdParams &p, hipStream_t stream);
 hipError_t launch_bwd_reduce(const BwdParams &p, hipStream_t stream);
+// The backward's two-stream schedule: grp[n] = 0 for the nlong sequences
+// with the most chunks (ties to the lower index), 1 for the others. One
+// workgroup; meant for N up to a few hundred.
+hipError_t launch_bwd_group(const BwdParams &p, int32_t nlong, int32_t *grp, hipStream_t stream);
 
 // Enqueue the segment combine of a split forward: ws[j + 1] = wm[j] ws[j] +
 // wb[j] in segment order, with ws[1] = wb[0].

@@ -239,3 +239,44 @@ def test_bwd_input_types(lib, c_oracle, io, gt, D):
     ref = c_oracle(d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["scale"], d["initial_state"],
                    d["cu_seqlens"].numpy(), d["d_out"], d["d_final_state"])
     assert_parity({n: got[n].float().cpu().double().numpy() for n in GRADS}, ref, tag)
+
+
+def test_bwd_two_groups_match_per_sequence_calls(lib, c_oracle):
+    """With whole sequences and between half of the compute units and all of
+    them in (sequence, value head) chains, the backward runs the longer half
+    of the sequences on the call's stream and the shorter half on a second
+    one. Every chain's arithmetic is its own either way, so each sequence's
+    gradients equal those of a call with that sequence alone, bit for bit
+    (ragged, 1-token and empty sequences, grouped heads, a tenth of the
+    channels at strong decay); and the batch matches the oracle."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    lengths = (700, 0, 65, 1, 300, 129)
+    N, T = len(lengths), sum(lengths)
+    HV = 2 * max(1, ncu // (2 * N))
+    H = HV // 2
+    if not (2 * N * HV > ncu and N * HV <= ncu and lib.split_plan(T, N, HV, ncu) == 0):
+        pytest.skip(f"{ncu} compute units: no shape of {N} sequences runs as two groups")
+    say(f"[bwd two groups] {ncu} CUs, N {N}, H {H}, HV {HV}")
+    d = case(lengths, H, HV, 64, seed=77, beta_max=2.0, g_extreme_max=8.0, extreme_frac=0.1)
+    dev = torch.device("cuda:0")
+    names = ("q", "k", "v", "g", "beta", "w", "d_out")
+    got = lib.chunk_bwd(*[d[n].to(dev) for n in names], scale=d["scale"], initial_state=d["initial_state"].to(dev),
+                        cu_seqlens=d["cu_seqlens"].to(dev), d_final_state=d["d_final_state"].to(dev))
+    torch.cuda.synchronize()
+    cu = d["cu_seqlens"].tolist()
+    for i in range(N):
+        b, e = cu[i], cu[i + 1]
+        if e == b:  # no chunk: the state gradient passes through
+            assert torch.equal(got["d_initial_state"][i].cpu(), d["d_final_state"][i])
+            continue
+        one = lib.chunk_bwd(*[d[n][b:e].to(dev) for n in names], scale=d["scale"],
+                            initial_state=d["initial_state"][i:i + 1].to(dev),
+                            d_final_state=d["d_final_state"][i:i + 1].to(dev))
+        torch.cuda.synchronize()
+        for n in GRADS:
+            part = got[n][i:i + 1] if n == "d_initial_state" else got[n][b:e]
+            assert torch.equal(part, one[n]), f"sequence {i} ({e - b} tokens): {n} differs"
+    say("[bwd two groups] oracle")
+    ref = c_oracle(d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["scale"], d["initial_state"],
+                   d["cu_seqlens"].numpy(), d["d_out"], d["d_final_state"])
+    assert_parity({n: got[n].float().cpu().double().numpy() for n in GRADS}, ref, "two groups")
