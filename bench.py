@@ -185,22 +185,42 @@ def _counter_means(outdir, names, want):
     return means, durs
 
 
-def _sq_lines(outdir, prefix, suffix, want, chunk_heads, title):
+def _bwd_calls(rows):
+    """gdn2_chunk_bwd calls in a profiled run: one dispatch of the group
+    ranking kernel per call that runs two groups of sequences, else one
+    dispatch of the gradient kernel per call."""
+    ids = lambda tag: {r.get("Dispatch_Id") for r in rows if tag in r["Kernel_Name"]}
+    return len(ids("bwd_group_kernel")) or len(ids("bwd_chunk_kernel"))
+
+
+def _sq_lines(outdir, prefix, suffix, want, chunk_heads, title, per_call=False):
     """The SQ counter passes of one workload, per kernel: rocprofv3's derived
     utilisations, and instruction counts per (64-token chunk, value head)
-    summed over the workgroup's waves."""
+    summed over the workgroup's waves. per_call: a kernel dispatched more
+    than once per call (the backward's two groups) has its counts summed
+    over the call's dispatches."""
     names = [prefix + n + suffix for n in SQ_PASSES]
     if not all(os.path.isdir(os.path.join(outdir, n)) for n in names):
         return []
     means, durs = _counter_means(outdir, names, want)
+    mult = {}
+    if per_call:
+        rows = _csv_rows(_find(os.path.join(outdir, names[0]), "_counter_collection.csv"))
+        calls = max(_bwd_calls(rows), 1)
+        for k in means:
+            n = len({r.get("Dispatch_Id") for r in rows
+                     if r["Kernel_Name"] == k[0] and int(r.get("Grid_Size") or 0) == k[1]})
+            mult[k] = n / calls if n else 1.0
     cmds = [profile_command(n) for n in names]
     out = ["", f"## SQ counters per launch ({title}; rocprofv3 --pmc, three passes)", "", "commands:"]
     out += ["  " + c for c in cmds]
     out += ["", f"per chunk-head: divided by the {chunk_heads} (64-token chunk, value head) pairs of one call", ""]
     for k, c in sorted(means.items()):
         g = lambda n: c.get(n, float("nan"))
-        ch = chunk_heads
-        out.append(_short(k[0]) + (f"  [grid {k[1]} threads]" if k[1] else ""))
+        m = mult.get(k, 1.0)
+        ch = chunk_heads / m  # counts per dispatch, over the chunk-heads of a call's dispatches
+        out.append(_short(k[0]) + (f"  [grid {k[1]} threads]" if k[1] else "")
+                   + (f"  [{m:.0f} dispatches per call: counts summed over them]" if m != 1.0 else ""))
         dur = durs.get(k)
         if dur:
             out.append(f"  mean dispatch {dur/1e3:.1f} us in the counter runs")
@@ -300,6 +320,24 @@ def summarize_profiles(outdir: str, dest: str | None = None):
         bl = [f"# rocprofv3 summary: GDN-2 backward (gdn2_chunk_bwd), varlen H32 D128", "", head, "",
               "## kernel-trace statistics", "", "command (from the repository root):",
               "  " + profile_command("bkt"), ""] + _stats_lines(outdir, "bkt")
+        try:
+            tr = _csv_rows(_find(os.path.join(outdir, "bkt"), "_kernel_trace.csv"))
+        except FileNotFoundError:
+            tr = []
+        ncall = _bwd_calls(tr)
+        if ncall and any("bwd_group_kernel" in r["Kernel_Name"] for r in tr):
+            tot = {}
+            for r in tr:
+                if ours(r["Kernel_Name"]):
+                    t = tot.setdefault(r["Kernel_Name"], [0, 0.0])
+                    t[0] += 1
+                    t[1] += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            bl += ["", f"per call ({ncall} calls): each call runs its sequences as two groups (the longer half on "
+                   f"the call's stream, the shorter half on a second stream, overlapping), so every pass is "
+                   f"dispatched twice and the sums below exceed the call's wall time", "",
+                   f"{'per call':>9} {'sum us':>10}  kernel"]
+            for kname, (n, ns) in sorted(tot.items(), key=lambda x: -x[1][1]):
+                bl.append(f"{n / ncall:>9.1f} {ns / ncall / 1e3:>10.1f}  {_short(kname)}")
         bl += ["", "## resources (kernel trace)", ""] + _resource_lines(outdir, "bkt", ours)
         if os.path.isdir(os.path.join(outdir, "bpmc_fetch")) and os.path.isdir(os.path.join(outdir, "bpmc_write")):
             bl += ["", "## HBM traffic per launch of each backward kernel (rocprofv3 --pmc, one counter per run)", "",
@@ -307,13 +345,14 @@ def summarize_profiles(outdir: str, dest: str | None = None):
                    f"write x{write_scale:.3f}", "",
                    "commands:", "  " + profile_command("bpmc_fetch"), "  " + profile_command("bpmc_write"), "",
                    f"per call: each kernel's bytes summed over its dispatches and divided by the number of "
-                   f"gdn2_chunk_bwd calls in the run (the gradient kernel runs once per call; split runs "
-                   f"dispatch some kernels more than once)", "",
+                   f"gdn2_chunk_bwd calls in the run (a call that runs its sequences as two groups on two "
+                   f"streams dispatches each pass twice, once per group; split runs dispatch some kernels "
+                   f"more than once)", "",
                    f"{'read MB':>10} {'write MB':>10} {'per call':>9}  kernel"]
             per, calls = {}, {}
             for name, key, scale in (("bpmc_fetch", 0, fetch_scale), ("bpmc_write", 1, write_scale)):
                 rows = _csv_rows(_find(os.path.join(outdir, name), "_counter_collection.csv"))
-                calls[name] = sum(1 for r in rows if "bwd_chunk_kernel" in r["Kernel_Name"])
+                calls[name] = _bwd_calls(rows)
                 for r in rows:
                     if ours(r["Kernel_Name"]):
                         per.setdefault(r["Kernel_Name"], ([], []))[key].append(
@@ -325,7 +364,7 @@ def summarize_profiles(outdir: str, dest: str | None = None):
                 total += rd + wr
                 bl.append(f"{rd/1e6:>10.1f} {wr/1e6:>10.1f} {len(fv) / nf:>9.1f}  {_short(kname)}")
             bl.append(f"sum over the kernels of one call: {total/1e6:.1f} MB")
-        bl += _sq_lines(outdir, "b", "", ours, _chunk_heads(2), "backward, varlen")
+        bl += _sq_lines(outdir, "b", "", ours, _chunk_heads(2), "backward, varlen", per_call=True)
         with open(os.path.join(dest, f"bwd_kernels_varlen_h32_d128.txt"), "w") as f:
             f.write("\n".join(bl) + "\n")
         log("\n".join(bl))

@@ -1520,7 +1520,8 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
     if (p.seg_chunks) item /= p.nseg;
     Chain ch;
     ch.n = item / p.HV;
-    if (p.grp && p.grp[ch.n] != p.gsel) return;  // the other launch's sequence
+    if constexpr (REC)  // (the backward's recompute only)
+        if (p.grp && p.grp[ch.n] != p.gsel) return;  // the other launch's sequence
     ch.hv = item - ch.n * p.HV;
     ch.hk = ch.hv / (p.HV / p.H);
     const SeqRange sr = seq_of(p, ch.n);
