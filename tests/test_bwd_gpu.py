@@ -241,23 +241,25 @@ def test_bwd_input_types(lib, c_oracle, io, gt, D):
     assert_parity({n: got[n].float().cpu().double().numpy() for n in GRADS}, ref, tag)
 
 
-def test_bwd_two_groups_match_per_sequence_calls(lib, c_oracle):
+@pytest.mark.parametrize("lengths", [(700, 0, 65, 1, 300, 129),
+                                     (0, 513, 0, 0, 64, 0)])  # the shorter half: empty sequences only
+def test_bwd_two_groups_match_per_sequence_calls(lib, c_oracle, lengths):
     """With whole sequences and between half of the compute units and all of
     them in (sequence, value head) chains, the backward runs the longer half
     of the sequences on the call's stream and the shorter half on a second
     one. Every chain's arithmetic is its own either way, so each sequence's
     gradients equal those of a call with that sequence alone, bit for bit
     (ragged, 1-token and empty sequences, grouped heads, a tenth of the
-    channels at strong decay); and the batch matches the oracle."""
+    channels at strong decay; a batch whose shorter half holds no chunk at
+    all); and the batch matches the oracle."""
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    lengths = (700, 0, 65, 1, 300, 129)
     N, T = len(lengths), sum(lengths)
     HV = 2 * max(1, ncu // (2 * N))
     H = HV // 2
     if not (2 * N * HV > ncu and N * HV <= ncu and lib.split_plan(T, N, HV, ncu) == 0):
         pytest.skip(f"{ncu} compute units: no shape of {N} sequences runs as two groups")
-    say(f"[bwd two groups] {ncu} CUs, N {N}, H {H}, HV {HV}")
-    d = case(lengths, H, HV, 64, seed=77, beta_max=2.0, g_extreme_max=8.0, extreme_frac=0.1)
+    say(f"[bwd two groups] {ncu} CUs, lengths {lengths}, H {H}, HV {HV}")
+    d = case(lengths, H, HV, 64, seed=77 + lengths[0], beta_max=2.0, g_extreme_max=8.0, extreme_frac=0.1)
     dev = torch.device("cuda:0")
     names = ("q", "k", "v", "g", "beta", "w", "d_out")
     got = lib.chunk_bwd(*[d[n].to(dev) for n in names], scale=d["scale"], initial_state=d["initial_state"].to(dev),
