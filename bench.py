@@ -85,7 +85,7 @@ SQ_PASSES = {
 _Q = "--no-cpu-baseline --no-peaks --no-extra"
 PROFILE_STEPS = {
     # name: (rocprofv3 options, bench.py options)
-    "kt": ("--kernel-trace --stats", f"--steps 10 --warmup 2 {_Q}"),
+    "kt": ("--kernel-trace --stats", f"--steps 20 --warmup 2 {_Q}"),
     "pmc_fetch": ("--pmc FETCH_SIZE", f"--steps 2 --warmup 1 {_Q}"),
     "pmc_write": ("--pmc WRITE_SIZE", f"--steps 2 --warmup 1 {_Q}"),
     "cal_fetch": ("--pmc FETCH_SIZE", "--copy-probe-mib 1024"),
