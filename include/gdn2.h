@@ -346,18 +346,31 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  * per pair of rows with e^(G_r - G_s) <= 1 (burn-gdn2 README, numerical
  * stability), at some extra cost for the chunks that have one.
  *
- * Evaluation: the forward runs again and keeps the float32 state entering
- * every chunk and each chunk's WY quantities (its record); one workgroup
+ * Evaluation: the forward runs again and keeps the state entering every
+ * chunk (rounded to bf16) and each chunk's WY quantities (its record); one workgroup
  * per (sequence, value head) carries the state gradient over the chunks in
  * reverse; a chunk-parallel pass forms every gradient; a last pass sums dq
  * and dk over grouped value heads (HV > H). Arithmetic is float32 with bf16
  * MFMA operands, as in the forward.
  *
+ * Streams: when every (sequence, value head) chain of the call can be
+ * resident at once (more than half of the device's compute units and at
+ * most all of them, whole sequences), the longer half of the sequences
+ * (by chunk count, ranked on the device) runs its passes on `stream` and
+ * the shorter half on a second stream. The library creates that stream
+ * per device on first use, at the default priority, and keeps it until
+ * the process ends. The work is forked from `stream` and joined back to it
+ * with events, so the call is ordered on `stream` like any other. The
+ * second stream is never created while `stream` is being captured into a
+ * graph (such a call runs on `stream` alone); once it exists, a capture
+ * takes it in through the events. Results are bit-identical either way.
+ *
  * Ownership and memory: the caller owns every buffer; inputs are only read.
  * A stream-ordered workspace (from the library's pool, see gdn2_chunk_fwd;
  * released with hipFreeAsync on `stream`) of
  *   (T / 64 + N) * HV * (2 * K * V * 2 + 516 * K + 16384) bytes,
- *   plus 2 * T * HV * K * 4 bytes when HV > H (per-value-head dq and dk)
+ *   plus 2 * T * HV * K * 4 bytes when HV > H (per-value-head dq and dk),
+ *   plus N * 4 bytes when the call runs as two groups (each sequence's group)
  * (rounded up per part) holds the checkpoints, the records and partial
  * gradients; if it cannot be allocated the call fails with GDN2_ERR_HIP and
  * enqueues nothing.
