@@ -362,8 +362,8 @@ int gdn2_chunk_fwd_check(const gdn2_tensor *q, const gdn2_tensor *k,
  * the process ends. The work is forked from `stream` and joined back to it
  * with events, so the call is ordered on `stream` like any other. The
  * second stream is never created while `stream` is being captured into a
- * graph (such a call runs on `stream` alone); once it exists, a capture
- * takes it in through the events. Results are bit-identical either way.
+ * graph (such a call runs on `stream` alone); graph capture of the
+ * backward is otherwise untested. Results are bit-identical either way.
  *
  * Ownership and memory: the caller owns every buffer; inputs are only read.
  * A stream-ordered workspace (from the library's pool, see gdn2_chunk_fwd;
