@@ -1,5 +1,6 @@
-"""GPU parity on seeded random configurations, forward and backward, against
-the FP64 oracles.
+"""GPU parity on seeded random configurations against the FP64 oracles:
+the chunked forward, the backward and the token-by-token entry; and the
+allocation-free entry against the allocating one, bit for bit.
 
 The hand-picked tests elsewhere each exercise one option at a time; here
 every configuration draws all of them together from a seeded generator:
@@ -131,3 +132,57 @@ def test_random_backward(lib, seed):
     ref = gdn2_recurrence_bwd_c(*[d[n] for n in NAMES], d["scale"], d["initial_state"], d["cu_seqlens"].numpy(),
                                 d_out, dht)
     assert_bwd_parity({n: got[n].float().cpu().double().numpy() for n in GRADS}, ref, tag)
+
+
+NOALLOC_BYTES = 64 << 20  # GDN2_NOALLOC_SCRATCH_BYTES in include/gdn2.h
+
+
+def split_bytes(o, split):
+    """The split run's workspace at segments of `split` chunks, as the
+    header states it: N * HV * nseg * (2 K V + K K) * 4 bytes."""
+    T, N = sum(o["lengths"]), len(o["lengths"])
+    nseg = (-(-T // 64) + split - 1) // split
+    return N * o["HV"] * nseg * (2 * o["K"] * o["V"] + o["K"] * o["K"]) * 4
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_recurrent(lib, seed):
+    """The token-by-token entry on the same kind of configurations."""
+    from oracle.c_oracle import gdn2_recurrence_c
+    o, d = draw_case(300 + seed, square=False)
+    keys = ("lengths", "K", "V", "H", "HV", "io", "gt", "strong", "init", "l2norm", "layout", "default_scale")
+    tag = f"recurrent seed {seed}: " + ", ".join(f"{k}={o[k]}" for k in keys)
+    say(f"[random] {tag}")
+    s0 = d["initial_state"]
+    if s0 is not None:
+        s0 = (s0.transpose(-1, -2).contiguous() if o["layout"] == "vk" else s0).to(DEV)
+    out, fin = lib.recurrent_fwd(*[d[n].to(DEV) for n in NAMES], scale=d["scale"], initial_state=s0,
+                                 cu_seqlens=d["cu_seqlens"].to(DEV), state_layout=o["layout"], qk_l2norm=o["l2norm"])
+    torch.cuda.synchronize()
+    fin = fin.transpose(-1, -2) if o["layout"] == "vk" else fin
+    ro, rs = gdn2_recurrence_c(*[d[n] for n in NAMES], d["scale"], d["initial_state"], d["cu_seqlens"],
+                               qk_l2norm=o["l2norm"])
+    assert_parity(tag, out.float(), fin.float(), ro, rs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_noalloc_equals_allocating(lib, seed):
+    """The allocation-free entry against the allocating one, bit for bit
+    (an explicit split whose workspace would exceed the scratch array is
+    drawn again as the automatic plan, which the entry fits to the array)."""
+    o, d = draw_case(200 + seed, square=False)
+    split = o["split"]
+    if split is not None and split > 0 and split_bytes(o, split) > NOALLOC_BYTES:
+        split = None
+    say(f"[random] noalloc seed {seed}: lengths {o['lengths']}, K {o['K']} V {o['V']} HV {o['HV']}, split {split}")
+    s0 = d["initial_state"]
+    if s0 is not None:
+        s0 = (s0.transpose(-1, -2).contiguous() if o["layout"] == "vk" else s0).to(DEV)
+    args = [d[n].to(DEV) for n in NAMES]
+    kw = dict(scale=d["scale"], initial_state=s0, cu_seqlens=d["cu_seqlens"].to(DEV), seq_split=split,
+              state_layout=o["layout"], qk_l2norm=o["l2norm"])
+    o1, f1 = lib.chunk_fwd(*args, **kw)
+    o2, f2 = torch.empty_like(o1), torch.empty_like(f1)
+    lib.chunk_fwd_noalloc(*args, out=o2, final_state=f2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
