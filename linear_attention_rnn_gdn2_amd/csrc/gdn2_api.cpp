@@ -822,7 +822,7 @@ int gdn2_chunk_bwd(const gdn2_tensor *q, const gdn2_tensor *k, const gdn2_tensor
     int frc = GDN2_OK;
     hipError_t e = hipSuccess;
     bool done = false;
-    if (two) {
+    if (two && dev >= 0 && dev < kPoolDevices) {
         std::lock_guard<std::mutex> lock(side_mu[dev]);
         const SideStream *side = side_stream(dev, stream);
         if (side) {
