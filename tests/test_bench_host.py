@@ -149,3 +149,67 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_backward_summary_with_two_groups(tmp_path):
+    """Two backward calls that each run two groups of sequences: one group
+    ranking dispatch per call, every pass dispatched twice per call. Bytes
+    and instruction counts are per call (summed over the call's dispatches),
+    and the kernel trace gives each kernel's time summed per call."""
+    out = tmp_path / "gpurun_out"
+    fwd = "void gdn2::(anonymous namespace)::chunk_fwd_kernel<128, 128, 0, false, false, false>(gdn2::FwdParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    stats_hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"]
+    ctr_hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write_csv(str(out / "kt" / "kt_kernel_stats.csv"), stats_hdr, [[fwd, 1, 900_000, 900_000, 100.0, 1, 1]])
+    _write_csv(str(out / "cal_fetch" / "cal_fetch_counter_collection.csv"), ctr_hdr, [[1, copy, "FETCH_SIZE", 524288.0]])
+    _write_csv(str(out / "cal_write" / "cal_write_counter_collection.csv"), ctr_hdr, [[1, copy, "WRITE_SIZE", 1048576.0]])
+    _write_csv(str(out / "pmc_fetch" / "pmc_fetch_counter_collection.csv"), ctr_hdr, [[2, fwd, "FETCH_SIZE", 1000.0]])
+    _write_csv(str(out / "pmc_write" / "pmc_write_counter_collection.csv"), ctr_hdr, [[2, fwd, "WRITE_SIZE", 500.0]])
+    grp = "gdn2::(anonymous namespace)::bwd_group_kernel(gdn2::BwdParams, int, int*)"
+    bwd_a = "void gdn2::(anonymous namespace)::bwd_chunk_kernel<128>(gdn2::BwdParams)"
+    # per call: the group kernel, then bwd_chunk for group 0 and group 1
+    # (1,000 and 3,000 KiB read); two calls
+    fetch, write, sq = [], [], []
+    i = 1
+    for call in range(2):
+        fetch.append([i, grp, "FETCH_SIZE", 0.0]); write.append([i, grp, "WRITE_SIZE", 0.0]); i += 1
+        for kib in (1000.0, 3000.0):
+            fetch.append([i, bwd_a, "FETCH_SIZE", kib]); write.append([i, bwd_a, "WRITE_SIZE", kib / 10])
+            i += 1
+    _write_csv(str(out / "bpmc_fetch" / "bpmc_fetch_counter_collection.csv"), ctr_hdr, fetch)
+    _write_csv(str(out / "bpmc_write" / "bpmc_write_counter_collection.csv"), ctr_hdr, write)
+    # SQ passes: each of a call's two bwd_chunk dispatches issues 500 VALU
+    # instructions per chunk-head of the call: 1,000 per chunk-head summed
+    ch = bench._chunk_heads(2)
+    for n, cs in bench.SQ_PASSES.items():
+        rows, j = [], 1
+        for call in range(2):
+            rows.append([j, grp, "SQ_WAVES", 4.0]); j += 1
+            for _ in range(2):
+                rows += [[j, bwd_a, c, (500.0 * ch if c == "SQ_INSTS_VALU" else 7.0)] for c in cs.split()]
+                j += 1
+        _write_csv(str(out / ("b" + n) / f"b{n}_counter_collection.csv"), ctr_hdr + ["Grid_Size"],
+                   [r + [9732096 if r[1] == bwd_a else 256] for r in rows])
+    # kernel trace: per call the group kernel (5 us) and bwd_chunk at 1.0
+    # and 2.0 ms
+    tr_hdr = ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    tr, t, j = [], 0, 1
+    for call in range(2):
+        tr.append([j, grp, t, t + 5_000]); j += 1
+        for dur in (1_000_000, 2_000_000):
+            tr.append([j, bwd_a, t, t + dur]); j += 1
+        t += 3_000_000
+    _write_csv(str(out / "bkt" / "bkt_kernel_trace.csv"), tr_hdr, tr)
+    _write_csv(str(out / "bkt" / "bkt_kernel_stats.csv"), stats_hdr, [[bwd_a, 4, 6_000_000, 1_500_000, 99.0, 1, 2]])
+    dest = tmp_path / "profiles"
+    dest.mkdir()
+    bench.summarize_profiles(str(out), dest=str(dest))
+    btxt = open(dest / "bwd_kernels_varlen_h32_d128.txt").read()
+    # per call: (1,000 + 3,000) KiB x 2 read, 400 KiB written, two dispatches
+    assert "       8.2        0.4       2.0  " + bwd_a in btxt
+    assert "per call (2 calls)" in btxt
+    assert "      2.0     3000.0  " + bwd_a in btxt
+    assert "      1.0        5.0  " + grp in btxt
+    assert "[2 dispatches per call: counts summed over them]" in btxt
+    assert "instructions per chunk-head: VALU 1000 " in btxt
