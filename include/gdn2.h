@@ -99,6 +99,13 @@ enum {
  * Value head hv reads q/k head hv / (HV / H) (contiguous groups of value
  * heads share one q/k head).
  *
+ * Conditioning: each token's transition I - (beta k) k^T (after the decay)
+ * has the eigenvalue 1 - beta |k|^2 along k. With unit-norm keys (or
+ * qk_l2norm) and beta in [0, 2] it stays within [-1, 1]; beyond that the
+ * recurrence itself amplifies every rounding, and no two evaluations of it
+ * (this library's or a float64 one) need agree. The accuracy figures of
+ * this library hold in the contracting range.
+ *
  * Optional arguments (the FlashInfer parameter-list defaults): g NULL means
  * g = 0, beta NULL means beta = 1, w NULL means w = 1, initial_state NULL
  * means a zero state, final_state NULL means the final state is not written,
