@@ -99,9 +99,10 @@ enum {
  * Value head hv reads q/k head hv / (HV / H) (contiguous groups of value
  * heads share one q/k head).
  *
- * Conditioning: each token's transition I - (beta k) k^T (after the decay)
- * has the eigenvalue 1 - beta |k|^2 along k. With unit-norm keys (or
- * qk_l2norm) and beta in [0, 2] it stays within [-1, 1]; beyond that the
+ * Conditioning: each token's transition I - k (beta * k)^T (after the
+ * decay; * elementwise) has the eigenvalue 1 - sum_c beta_c k_c^2, and all
+ * its other eigenvalues are 1. With unit-norm keys (or qk_l2norm) and beta
+ * in [0, 2] that eigenvalue stays within [-1, 1]; beyond that the
  * recurrence itself amplifies every rounding, and no two evaluations of it
  * (this library's or a float64 one) need agree. The accuracy figures of
  * this library hold in the contracting range.

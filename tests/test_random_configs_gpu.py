@@ -57,9 +57,10 @@ def draw_case(seed, square):
     already in the drawn types (the oracle sees the same quantised values).
     square: K = V and no in-kernel L2 normalisation (the backward's range).
     Rows of q and k are scaled away from unit length only where the kernel
-    normalises them: a key of norm |k| makes the transition I - beta k k^T
-    expansive once beta |k|^2 > 2 (an eigenvalue 1 - beta |k|^2 below -1),
-    and the recurrence then amplifies every rounding on both sides."""
+    normalises them: the transition I - k (beta * k)^T has the eigenvalue
+    1 - sum_c beta_c k_c^2, below -1 (expansive) once that sum exceeds 2,
+    which keys longer than 1 reach at beta near 2; the recurrence then
+    amplifies every rounding on both sides."""
     r = random.Random(seed)
     lengths = draw_lengths(r)
     K = r.choice((64, 128))
