@@ -305,3 +305,52 @@ def test_bwd_two_groups_match_per_sequence_calls(lib, c_oracle, lengths):
     ref = c_oracle(d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["scale"], d["initial_state"],
                    d["cu_seqlens"].numpy(), d["d_out"], d["d_final_state"])
     assert_parity({n: got[n].float().cpu().double().numpy() for n in GRADS}, ref, "two groups")
+
+
+def test_bwd_two_groups_from_two_host_threads(lib):
+    """Two host threads, each on its own stream, enqueue backward calls in
+    the two-group regime at the same time: both share the device's second
+    stream, whose fork and join each call enqueues under a lock. Every
+    result equals the same call's result made alone, bit for bit."""
+    import threading
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    lengths = (300, 65, 0, 200, 1, 129)
+    N, T = len(lengths), sum(lengths)
+    HV = 2 * max(1, ncu // (2 * N))
+    if not (2 * N * HV > ncu and N * HV <= ncu and lib.split_plan(T, N, HV, ncu) == 0):
+        pytest.skip(f"{ncu} compute units: no shape of {N} sequences runs as two groups")
+    dev = torch.device("cuda:0")
+    names = ("q", "k", "v", "g", "beta", "w", "d_out")
+    cases = []
+    for seed in (41, 42):
+        d = case(lengths, HV // 2, HV, 64, seed=seed)
+        cases.append(([d[n].to(dev) for n in names],
+                      dict(scale=d["scale"], initial_state=d["initial_state"].to(dev),
+                           cu_seqlens=d["cu_seqlens"].to(dev), d_final_state=d["d_final_state"].to(dev))))
+    alone = [lib.chunk_bwd(*a, **kw) for a, kw in cases]
+    torch.cuda.synchronize()
+    results, errors_seen = [[None] * 3, [None] * 3], []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream(device=dev)
+            a, kw = cases[i]
+            with torch.cuda.stream(s):
+                for r in range(3):
+                    results[i][r] = lib.chunk_bwd(*a, **kw)
+            s.synchronize()
+        except Exception as e:  # reported below, in the test's thread
+            errors_seen.append(repr(e))
+
+    say(f"[bwd two threads] N {N}, HV {HV}: two threads, three calls each")
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=120)
+    torch.cuda.synchronize()
+    assert not errors_seen, errors_seen
+    for i in range(2):
+        for r in range(3):
+            for n in GRADS:
+                assert torch.equal(results[i][r][n], alone[i][n]), f"thread {i} call {r}: {n} differs"
