@@ -68,7 +68,7 @@ def test_counter_summary_on_synthetic_profiles(tmp_path):
     1,048,576 KiB gives scale factors 2 and 1; a forward dispatch with
     FETCH_SIZE 1,000 KiB and WRITE_SIZE 500 KiB then moved 2,048,000 +
     512,000 bytes."""
-    out = tmp_path / "gpurun_out"
+    out = tmp_path / "prof_out"
     fwd = "void gdn2::(anonymous namespace)::chunk_fwd_kernel<128, 128, 0, false, false, false>(gdn2::FwdParams)"
     copy = "__amd_rocclr_copyBuffer"
     stats_hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"]
@@ -156,7 +156,7 @@ def test_backward_summary_with_two_groups(tmp_path):
     ranking dispatch per call, every pass dispatched twice per call. Bytes
     and instruction counts are per call (summed over the call's dispatches),
     and the kernel trace gives each kernel's time summed per call."""
-    out = tmp_path / "gpurun_out"
+    out = tmp_path / "prof_out"
     fwd = "void gdn2::(anonymous namespace)::chunk_fwd_kernel<128, 128, 0, false, false, false>(gdn2::FwdParams)"
     copy = "__amd_rocclr_copyBuffer"
     stats_hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"]
