@@ -642,7 +642,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (every chain of the GDN-2 "
+        print("bench.py measures one GPU only (every chain of the GDN-2 "
               "prefill is independent; multi-GPU sharding is not implemented). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
