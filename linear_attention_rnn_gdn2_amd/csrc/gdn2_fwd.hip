@@ -1597,79 +1597,102 @@ __global__ __launch_bounds__(NTHR) void chunk_fwd_kernel(FwdParams p)
 // of segment j from a zero start (from the true initial state for j = 0) and
 // M_j its K x K transition. One workgroup per (sequence, value head, 16
 // columns) applies the recurrence in float32 and stores every entering state
-// S_j (j >= 1) for the output pass. Thread (r, cp) owns row r and columns
-// 2 cp, 2 cp + 1 of the block. M_j goes to LDS once per workgroup (instead
-// of a row per thread from the L2), double-buffered: M_{j+1} and B_{j+1} are
-// fetched while step j's products run, so a step costs one barrier and its
-// arithmetic, not a memory round trip. Each entry is B_j plus the products in
-// order k = 0 .. K-1, one fused multiply-add each.
-constexpr int CMB_COLS = 16;  // state columns per workgroup; two per thread
-
-template <int K>
-constexpr int cmb_threads() { return K * CMB_COLS / 2; }
+// S_j (j >= 1) for the output pass. The product M_j S_j runs on float32 MFMA
+// (16x16x4): wave w owns the 16-row tiles w, w + 4 (K = 128) or w (K = 64)
+// of the 16 columns, each an accumulator started at B_j. The sum over k is
+// taken in the order k = q4 K/4 + kk (q4 the lane's k slot in an instruction,
+// kk the instruction), so that a lane's operands for consecutive
+// instructions are consecutive floats: M_j row-major and S_j transposed in
+// LDS, both read 16 bytes at a time without bank conflicts. M_j goes to LDS
+// once per workgroup, double-buffered: M_{j+1} and B_{j+1} are fetched while
+// step j's products run, so a step costs one barrier and its products, not a
+// memory round trip.
+constexpr int CMB_COLS = 16;    // state columns per workgroup: one MFMA column tile
+constexpr int CMB_THREADS = 256;  // four waves
 
 template <int K>
 struct CmbLds {
-    static constexpr int MP = K + 4;  // float pitch of a map row (16-byte reads of 8 rows: no bank conflict)
-    float m[2][K][MP];
-    float s[2][K][CMB_COLS];
+    static constexpr int P = K + 4;  // float pitch of a map row and of a transposed state column
+    float m[2][K][P];                // M_j, row-major
+    float st[2][CMB_COLS][P];        // S_j transposed: [column][row]
 };
 
 template <int K, int V>
-__global__ __launch_bounds__(cmb_threads<K>()) void seg_combine_kernel(FwdParams p)
+__global__ __launch_bounds__(CMB_THREADS) void seg_combine_kernel(FwdParams p)
 {
-    constexpr int NT = cmb_threads<K>(), NL = K * K / 4 / NT;  // 16-byte pieces of a map per thread
-    static_assert(K * K % (4 * NT) == 0 && V % CMB_COLS == 0, "combine tiling");
+    constexpr int NT = CMB_THREADS, NL = K * K / 4 / NT;  // 16-byte pieces of a map per thread
+    constexpr int RTW = K / 64;                           // 16-row tiles per wave
+    constexpr int KQ = K / 4;                             // instructions per tile and step
+    static_assert(K * K % (4 * NT) == 0 && V % CMB_COLS == 0 && K % 64 == 0, "combine tiling");
     __shared__ __attribute__((aligned(16))) CmbLds<K> L;
     const int ncb = V / CMB_COLS;
     const int chain = blockIdx.x / ncb, cb = blockIdx.x - chain * ncb;
     const int n = chain / p.HV;
     const int last = seg_last(seq_of(p, n), p.seg_chunks);
     if (last == 0) return;
-    const int t = threadIdx.x, r = t / (CMB_COLS / 2), cp = t % (CMB_COLS / 2);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, q4 = lane >> 4;
     const int64_t seg0 = (int64_t)chain * p.nseg * K * V;  // chain = n * HV + hv
     const int64_t map0 = (int64_t)chain * p.nseg * K * K;  // the maps: K x K each
-    const int col = cb * CMB_COLS + 2 * cp;
-    const int64_t rc = (int64_t)r * V + col;
-    f32x2 s = *reinterpret_cast<const f32x2 *>(p.wb + seg0 + rc);
-    *reinterpret_cast<f32x2 *>(p.ws + seg0 + (int64_t)K * V + rc) = s;
+    // this lane's elements (the MFMA result layout): rows row0[u] + e, e = 0..3,
+    // column c of the block
+    const int c = cb * CMB_COLS + l16;
+    int row0[RTW];
+    for (int u = 0; u < RTW; ++u) row0[u] = 16 * (w + 4 * u) + 4 * q4;
+    // S_1 = B_0
+    f32x4 s[RTW];
+    for (int u = 0; u < RTW; ++u)
+        for (int e = 0; e < 4; ++e) {
+            const int64_t o = (int64_t)(row0[u] + e) * V + c;
+            s[u][e] = p.wb[seg0 + o];
+            p.ws[seg0 + (int64_t)K * V + o] = s[u][e];
+        }
     if (last < 2) return;
     // M_1 and B_1
-    f32x4 mr[NL];
+    f32x4 mr[NL], b[RTW];
     for (int i = 0; i < NL; ++i) mr[i] = *reinterpret_cast<const f32x4 *>(p.wm + map0 + (int64_t)K * K + 4 * (t + NT * i));
-    f32x2 b = *reinterpret_cast<const f32x2 *>(p.wb + seg0 + (int64_t)K * V + rc);
+    for (int u = 0; u < RTW; ++u)
+        for (int e = 0; e < 4; ++e) b[u][e] = p.wb[seg0 + (int64_t)K * V + (int64_t)(row0[u] + e) * V + c];
     for (int i = 0; i < NL; ++i) {
-        const int e = 4 * (t + NT * i);
-        *reinterpret_cast<f32x4 *>(&L.m[1][e / K][e % K]) = mr[i];
+        const int x = 4 * (t + NT * i);
+        *reinterpret_cast<f32x4 *>(&L.m[1][x / K][x % K]) = mr[i];
     }
     for (int j = 1; j < last; ++j) {
         const int bj = j & 1;
-        *reinterpret_cast<f32x2 *>(&L.s[bj][r][2 * cp]) = s;
+        for (int u = 0; u < RTW; ++u) *reinterpret_cast<f32x4 *>(&L.st[bj][l16][row0[u]]) = s[u];
         __syncthreads();  // M_j and S_j in LDS; step j - 1's reads of these buffers are done
         const bool more = j + 1 < last;
-        f32x2 bn = {0.0f, 0.0f};
+        f32x4 bn[RTW];
+        for (int u = 0; u < RTW; ++u) bn[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (more) {
             for (int i = 0; i < NL; ++i)
                 mr[i] = *reinterpret_cast<const f32x4 *>(p.wm + map0 + (int64_t)(j + 1) * K * K + 4 * (t + NT * i));
-            bn = *reinterpret_cast<const f32x2 *>(p.wb + seg0 + (int64_t)(j + 1) * K * V + rc);
+            for (int u = 0; u < RTW; ++u)
+                for (int e = 0; e < 4; ++e)
+                    bn[u][e] = p.wb[seg0 + (int64_t)(j + 1) * K * V + (int64_t)(row0[u] + e) * V + c];
         }
-        float a0 = b[0], a1 = b[1];
-        for (int k4 = 0; k4 < K / 4; ++k4) {
-            const f32x4 m = *reinterpret_cast<const f32x4 *>(&L.m[bj][r][4 * k4]);
-            for (int e = 0; e < 4; ++e) {
-                const f32x2 x = *reinterpret_cast<const f32x2 *>(&L.s[bj][4 * k4 + e][2 * cp]);
-                a0 = fmaf(m[e], x[0], a0);
-                a1 = fmaf(m[e], x[1], a1);
+        // S_{j+1} = B_j + M_j S_j: lane (l16, q4) gives A = M[tile row l16][k]
+        // and B = S[k][column l16] at k = q4 K/4 + kk
+        f32x4 acc[RTW];
+        for (int u = 0; u < RTW; ++u) acc[u] = b[u];
+        const float *const sb = &L.st[bj][l16][q4 * KQ];
+#pragma unroll 2
+        for (int k4 = 0; k4 < KQ / 4; ++k4) {
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + 4 * k4);
+            for (int u = 0; u < RTW; ++u) {
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(&L.m[bj][16 * (w + 4 * u) + l16][q4 * KQ + 4 * k4]);
+                for (int e = 0; e < 4; ++e) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[u], 0, 0, 0);
             }
         }
-        s = f32x2{a0, a1};
-        *reinterpret_cast<f32x2 *>(p.ws + seg0 + (int64_t)(j + 1) * K * V + rc) = s;
+        for (int u = 0; u < RTW; ++u) {
+            s[u] = acc[u];
+            for (int e = 0; e < 4; ++e) p.ws[seg0 + (int64_t)(j + 1) * K * V + (int64_t)(row0[u] + e) * V + c] = s[u][e];
+        }
         if (more)
             for (int i = 0; i < NL; ++i) {
-                const int e = 4 * (t + NT * i);
-                *reinterpret_cast<f32x4 *>(&L.m[bj ^ 1][e / K][e % K]) = mr[i];
+                const int x = 4 * (t + NT * i);
+                *reinterpret_cast<f32x4 *>(&L.m[bj ^ 1][x / K][x % K]) = mr[i];
             }
-        b = bn;
+        for (int u = 0; u < RTW; ++u) b[u] = bn[u];
     }
 }
 
@@ -1734,13 +1757,13 @@ hipError_t launch_seg_combine(const FwdParams &p, hipStream_t stream)
 {
     const dim3 grid((unsigned)(p.N * p.HV * (p.V / CMB_COLS)));
     if (p.K == 128 && p.V == 128)
-        hipLaunchKernelGGL((seg_combine_kernel<128, 128>), grid, dim3(cmb_threads<128>()), 0, stream, p);
+        hipLaunchKernelGGL((seg_combine_kernel<128, 128>), grid, dim3(CMB_THREADS), 0, stream, p);
     else if (p.K == 64 && p.V == 64)
-        hipLaunchKernelGGL((seg_combine_kernel<64, 64>), grid, dim3(cmb_threads<64>()), 0, stream, p);
+        hipLaunchKernelGGL((seg_combine_kernel<64, 64>), grid, dim3(CMB_THREADS), 0, stream, p);
     else if (p.K == 128 && p.V == 64)
-        hipLaunchKernelGGL((seg_combine_kernel<128, 64>), grid, dim3(cmb_threads<128>()), 0, stream, p);
+        hipLaunchKernelGGL((seg_combine_kernel<128, 64>), grid, dim3(CMB_THREADS), 0, stream, p);
     else if (p.K == 64 && p.V == 128)
-        hipLaunchKernelGGL((seg_combine_kernel<64, 128>), grid, dim3(cmb_threads<64>()), 0, stream, p);
+        hipLaunchKernelGGL((seg_combine_kernel<64, 128>), grid, dim3(CMB_THREADS), 0, stream, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
