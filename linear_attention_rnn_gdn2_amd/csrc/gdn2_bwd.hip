@@ -338,30 +338,52 @@ __device__ __forceinline__ void exact_pass(char *sm, const BwdParams &p, int64_t
 #pragma unroll
     for (int h = 0; h < RPX; ++h) lds_st<float>(sm, sx + 4 * (RPX * part + h), gl[h] + inc - run);
     __syncthreads();
-    // rows part and 63 - part (RPX = 2) or part (RPX = 1): alpha and pi
-    // run over s <= r, kappa over r' >= r, so every thread has 65 terms
-    // per row of each kind
-#pragma unroll
-    for (int h = 0; h < RPX; ++h) {
-        const int r = h ? 63 - part : part;
-        const float Gr = lds_ld<float>(sm, sx + 4 * r);
-        float al = 0.0f, pi = 0.0f, ka = 0.0f;
-        for (int s2 = 0; s2 <= r; ++s2) {
-            const float ke = lds_ld<float>(sm, sx + 2 * A + 4 * s2) * ex2(Gr - lds_ld<float>(sm, sx + 4 * s2));
-            al = fmaf((float)lds_ld<__bf16>(sm, L::RGB + 2 * (r * L::RC + s2)), ke, al);
-            pi = fmaf((float)lds_ld<__bf16>(sm, L::PB + 2 * (r * L::RC + s2)), ke, pi);
-        }
-        for (int r2 = r; r2 < 64; ++r2) {
-            const float e = ex2(lds_ld<float>(sm, sx + 4 * r2) - Gr);
-            const float bk = lds_ld<float>(sm, sx + 3 * A + 4 * r2) * lds_ld<float>(sm, sx + 2 * A + 4 * r2);
-            const float w = (float)lds_ld<__bf16>(sm, L::RGB + 2 * (r2 * L::RC + r)) * bk +
-                            (float)lds_ld<__bf16>(sm, L::PB + 2 * (r2 * L::RC + r)) * lds_ld<float>(sm, sx + 1 * A + 4 * r2);
-            ka = fmaf(w, e, ka);
-        }
+    // alpha and pi of row r run over s <= r, kappa over r' >= r: one term
+    // of each kind per pair
+    auto ap_term = [&](int r, float Gr, int s2, float &al, float &pi) {
+        const float ke = lds_ld<float>(sm, sx + 2 * A + 4 * s2) * ex2(Gr - lds_ld<float>(sm, sx + 4 * s2));
+        al = fmaf((float)lds_ld<__bf16>(sm, L::RGB + 2 * (r * L::RC + s2)), ke, al);
+        pi = fmaf((float)lds_ld<__bf16>(sm, L::PB + 2 * (r * L::RC + s2)), ke, pi);
+    };
+    auto k_term = [&](int r, float Gr, int r2, float &ka) {
+        const float e = ex2(lds_ld<float>(sm, sx + 4 * r2) - Gr);
+        const float bk = lds_ld<float>(sm, sx + 3 * A + 4 * r2) * lds_ld<float>(sm, sx + 2 * A + 4 * r2);
+        const float w = (float)lds_ld<__bf16>(sm, L::RGB + 2 * (r2 * L::RC + r)) * bk +
+                        (float)lds_ld<__bf16>(sm, L::PB + 2 * (r2 * L::RC + r)) * lds_ld<float>(sm, sx + 1 * A + 4 * r2);
+        ka = fmaf(w, e, ka);
+    };
+    auto put = [&](int r, float al, float pi, float ka) {
         const int ro = L::RGC + 4 * (64 * x + r);
         lds_st<float>(sm, ro, al);
         lds_st<float>(sm, ro + A, pi);
         lds_st<float>(sm, ro + 2 * A, ka);
+    };
+    if constexpr (RPX == 2) {
+        // rows rl = part and rh = 63 - part. The sums of rl over s <= rl and
+        // of rh over r' >= rh both have part + 1 terms, those of rl over
+        // r' >= rl and of rh over s <= rh both 64 - part: each pair of sums
+        // shares one loop (every sum keeps its order of terms), so a wave
+        // runs 96 iterations instead of 192
+        const int rl = part, rh = 63 - part;
+        const float Gl = lds_ld<float>(sm, sx + 4 * rl), Gh = lds_ld<float>(sm, sx + 4 * rh);
+        float al_l = 0.0f, pi_l = 0.0f, ka_l = 0.0f, al_h = 0.0f, pi_h = 0.0f, ka_h = 0.0f;
+        for (int i = 0; i <= part; ++i) {
+            ap_term(rl, Gl, i, al_l, pi_l);
+            k_term(rh, Gh, rh + i, ka_h);
+        }
+        for (int i = 0; i < 64 - part; ++i) {
+            k_term(rl, Gl, rl + i, ka_l);
+            ap_term(rh, Gh, i, al_h, pi_h);
+        }
+        put(rl, al_l, pi_l, ka_l);
+        put(rh, al_h, pi_h, ka_h);
+    } else {
+        const int r = part;
+        const float Gr = lds_ld<float>(sm, sx + 4 * r);
+        float al = 0.0f, pi = 0.0f, ka = 0.0f;
+        for (int s2 = 0; s2 <= r; ++s2) ap_term(r, Gr, s2, al, pi);
+        for (int r2 = r; r2 < 64; ++r2) k_term(r, Gr, r2, ka);
+        put(r, al, pi, ka);
     }
     __syncthreads();
 }
